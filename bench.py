@@ -1,0 +1,140 @@
+"""Batch-1 Dual-AR decode benchmark on one MI355X.
+
+A step is one decoded frame (the Fast AR's nine greedy steps plus the Slow AR
+step, i.e. every row of the hot path) of the full FishAudio S2 shape on
+synthetic bf16 weights: 41-token prompt, then frames of greedy decode, one
+stream ("s2pro-native", Where it stands, measures this workload).  The timed
+region holds exactly K frames; weights, KV and state are resident in HBM.
+
+Prints one JSON line.  --gpus N with N > 1 exits: this build drives one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, weights, budget_s: float):
+    """The oracle as it stands, on this host's cores: a one-token prompt, then
+    whole frames (Fast loop + Slow step) until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    m = oracle.Model(cfg, weights)
+    st = m.new_state()
+    pre = st.prefill(np.array([7], np.int32))
+    h, c0 = pre["h"], pre["c0"]
+    frames = 0
+    t0 = time.perf_counter()
+    while True:
+        fl = m.fast_loop(h)
+        codes = np.concatenate([[c0], fl["codes"]]).astype(np.int32)
+        s = st.slow_step(codes)
+        h, c0 = s["h"], s["c0"]
+        frames += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": frames / dt, "unit": "frames/s", "cores": min(cores, os.cpu_count() or cores), "kind": "oracle",
+            "sample": f"{frames} frames of the {cfg['name']} shape after a 1-token prompt ({dt:.1f} s, fp64 oracle)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="full")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--kernel-iters", type=int, default=144)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py drives one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from dual_ar_codec_amd import metrics, s2ar, synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.config(args.config)
+    n_prompt = synth.prompt_lengths(cfg)[0]
+    need = n_prompt + max(args.steps, args.warmup) + 1
+    if need > cfg["max_context"]:
+        cfg = synth.config(args.config, max_context=(need + 63) // 64 * 64)
+    log(f"[bench] generating {cfg['name']} weights ({synth.weight_bytes(cfg) / 1e9:.2f} GB)")
+    t = time.perf_counter()
+    w = synth.make_weights(cfg)
+    log(f"[bench] weights in {time.perf_counter() - t:.1f} s; uploading")
+    toks, mask, codes = synth.make_prompt(cfg)
+    ctx = s2ar.Context(cfg, w)
+    log("[bench] prefill + warmup")
+    ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
+    if args.warmup:
+        ctx.decode_frames([0], args.warmup)
+    ctx.release(0)
+    ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} frames")
+    t0 = time.perf_counter()
+    out = ctx.decode_frames([0], args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert out.shape == (args.steps, 1, 10)
+    fps = args.steps / dt
+    ctx_mid = n_prompt + args.steps // 2
+    fb = metrics.frame_bytes(cfg, ctx_mid)
+    gbps = fb["total"] * fps / 1e9
+
+    log("[bench] dominant kernel (fused RMSNorm + gate/up + SwiGLU GEMV)")
+    ms, nbytes = ctx.time_kernel(0, args.kernel_iters)
+    k_gbps = nbytes / (ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "k_gemv<bf16, NCH=5, GEMV_NORM_SWIGLU> (Slow gate/up, 19456x2560)",
+                "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2)}
+    ctx.close()
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"[bench] CPU oracle baseline ({args.cpu_budget:.0f} s budget)")
+        cpu = cpu_baseline(cfg, w, args.cpu_budget)
+
+    line = {
+        "metric": "frames/s at batch 1 (full S2 shape), with codebook tok/s, HBM GB/s and RTF",
+        "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg["weight_dtype"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']}: {n_prompt}-token prompt, {args.steps} greedy frames, 1 stream",
+                   "slow_layers": cfg["slow"]["n_layers"], "fast_layers": cfg["fast"]["n_layers"],
+                   "hidden": cfg["slow"]["hidden"], "prompt": n_prompt, "frames": args.steps, "streams": 1},
+        "codebook_tok_s": round(metrics.codebook_tokens_per_s(fps), 1),
+        "rtf": round(metrics.rtf(fps), 5),
+        "frame_bytes": fb["total"],
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,914 @@
+// Host side of the s2ar C ABI: validation, weight upload and repacking, the paged KV pool,
+// per-stream device state, the frame's kernel sequence and its hipGraph capture.
+//
+// A frame follows the Dual-AR order of the pages ("SGLang Day-0 Support for FishAudio S2",
+// Architecture, Stage 2): the Fast AR's nine greedy steps on the Slow hidden, then the Slow
+// step on the frame's ten codes.  The engine runs it ahead: prefill leaves (h, c0) for frame 1,
+// and each decode call runs Fast(t) and then the Slow step that prepares frame t+1, so that
+// one captured graph serves every frame.  All per-frame variables (position, codes, hidden,
+// block table) live in device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "s2ar.h"
+
+namespace {
+
+thread_local std::string g_create_error;
+
+constexpr int kPageSize = 16;
+constexpr int kMaxStreams = 256;
+
+struct LayerW {
+  void* wqkv = nullptr;   // [(Hq + 2 Hkv) D][H]: wq rows, then wk rows, then wv rows
+  void* wo = nullptr;     // [H][Hq D]
+  void* wgu = nullptr;    // [2F][H]: row 2i = w_gate[i], row 2i+1 = w_up[i]
+  void* wdown = nullptr;  // [H][F]
+  float* attn_norm = nullptr;
+  float* mlp_norm = nullptr;
+  float* q_norm = nullptr;
+  float* k_norm = nullptr;
+};
+
+struct Graph {
+  hipGraph_t g = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+}  // namespace
+
+struct s2ar_ctx {
+  s2ar_config cfg{};
+  bool bf16 = true;
+  int esz = 2;
+  hipStream_t user_stream = nullptr;
+  hipStream_t stream = nullptr;
+  hipEvent_t ev_order = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
+  std::vector<void*> dev_allocs;
+  std::vector<void*> host_allocs;
+
+  // weights
+  void* embed = nullptr;
+  void* slow_head = nullptr;
+  void* codebook = nullptr;
+  void* fast_head = nullptr;
+  float* slow_final = nullptr;
+  float* fast_final = nullptr;
+  std::vector<LayerW> slow, fast;
+  float *rope_cos_s = nullptr, *rope_sin_s = nullptr, *rope_cos_f = nullptr, *rope_sin_f = nullptr;
+
+  // KV pools (bf16): slow [layers][n_pages][Hkv][page][D]; fast [layers][max_streams][Hkv][page][D]
+  uint16_t *kv_k = nullptr, *kv_v = nullptr, *fkv_k = nullptr, *fkv_v = nullptr;
+  size_t kv_layer = 0, fkv_layer = 0;
+  int n_pages = 0, bt_stride = 0;
+  int* d_bt = nullptr;       // [max_streams][bt_stride]
+  int* h_bt = nullptr;       // pinned mirror
+  int* d_fast_bt = nullptr;  // [max_streams]: stream s uses fast page s
+  std::vector<int> free_pages;
+  std::vector<std::vector<int>> stream_pages;
+
+  // per-stream device state
+  int* d_pos = nullptr;       // [max_streams] next Slow position
+  int* d_codes = nullptr;     // [max_streams][NC] current frame's codes
+  float* d_h = nullptr;       // [max_streams][H] final-normed Slow hidden
+  int* d_snap = nullptr;      // [max_streams][NC] codes emitted by the last frame
+  int* d_slot_ids = nullptr;  // [max_streams] = 0, 1, 2, ...
+  int* d_fast_pos = nullptr;  // [NC-1][max_streams] = j - 1
+  std::vector<int> pos;
+  std::vector<char> ready;
+
+  // workspace (batch row 0), every input vector zero-padded to pad_k
+  float *x = nullptr, *xf = nullptr, *qkv = nullptr, *att = nullptr, *act = nullptr;
+  float *slow_logits = nullptr, *fast_logits = nullptr, *z = nullptr;
+  float* am_val = nullptr;
+  int* am_idx = nullptr;
+  unsigned* am_counter = nullptr;
+  float *att_ml = nullptr, *att_o = nullptr;
+  unsigned* att_cnt = nullptr;
+  int max_chunks = 0;
+
+  // prompt staging
+  int* d_tokens = nullptr;
+  uint8_t* d_mask = nullptr;
+  int* d_pcodes = nullptr;
+
+  // pinned host staging
+  int* h_codes = nullptr;  // [max frames per call chunk][max_streams][NC]
+  int h_codes_frames = 0;
+  float* h_taps = nullptr;
+  size_t h_taps_floats = 0;
+  int* h_small = nullptr;  // small int staging (forced codes, own picks)
+
+  std::map<int, Graph> graphs;  // per stream id
+  std::string err;
+};
+
+namespace {
+
+int set_err(s2ar_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  else g_create_error = msg;
+  return code;
+}
+
+#define HIP_TRY(ctx, expr)                                                                          \
+  do {                                                                                              \
+    hipError_t e_ = (expr);                                                                         \
+    if (e_ != hipSuccess)                                                                           \
+      return set_err(ctx, S2AR_E_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_));         \
+  } while (0)
+
+int check_stack(const s2ar_stack& s, const char* name, int epc, std::string& why) {
+  char buf[256];
+  if (s.n_layers < 1 || s.hidden < 1 || s.n_q_heads < 1 || s.n_kv_heads < 1 || s.head_dim < 1 || s.ffn < 1) {
+    snprintf(buf, sizeof buf, "%s: every dimension must be >= 1", name);
+    why = buf;
+    return -1;
+  }
+  if (s.n_q_heads % s.n_kv_heads) {
+    snprintf(buf, sizeof buf, "%s: n_q_heads must be a multiple of n_kv_heads", name);
+    why = buf;
+    return -1;
+  }
+  const int g = s.n_q_heads / s.n_kv_heads;
+  if (!(s.head_dim == 64 || s.head_dim == 128) || !(g == 1 || g == 2 || g == 4 || g == 8)) {
+    snprintf(buf, sizeof buf, "%s: head_dim must be 64 or 128 and n_q_heads/n_kv_heads in {1,2,4,8}", name);
+    why = buf;
+    return -1;
+  }
+  const int64_t dims[3] = {s.hidden, (int64_t)s.n_q_heads * s.head_dim, s.ffn};
+  for (int64_t d : dims)
+    if (d % epc || d > 14336) {
+      snprintf(buf, sizeof buf, "%s: hidden, n_q_heads*head_dim and ffn must be multiples of %d and <= 14336", name, epc);
+      why = buf;
+      return -1;
+    }
+  return 0;
+}
+
+int validate_config(const s2ar_config* c, std::string& why) {
+  if (c->weight_dtype != 0 && c->weight_dtype != 1) {
+    why = "weight_dtype must be 0 (fp32) or 1 (bf16)";
+    return -1;
+  }
+  const int epc = c->weight_dtype == 1 ? 8 : 4;
+  if (check_stack(c->slow, "slow", epc, why) || check_stack(c->fast, "fast", epc, why)) return -1;
+  if (c->slow.hidden != c->fast.hidden) {
+    why = "fast.hidden must equal slow.hidden (the Slow hidden feeds the Fast AR)";
+    return -1;
+  }
+  if (c->n_codebooks < 2 || c->n_codebooks - 1 > kPageSize) {
+    why = "n_codebooks must be in [2, 17]";
+    return -1;
+  }
+  if (c->codebook_size < 1 || c->vocab_text < 0 || (int64_t)c->vocab_text + c->codebook_size > INT32_MAX / 2) {
+    why = "vocab_text >= 0 and codebook_size >= 1 required";
+    return -1;
+  }
+  if (c->page_size != kPageSize) {
+    why = "page_size must be 16";
+    return -1;
+  }
+  if (c->max_streams < 1 || c->max_streams > kMaxStreams || c->max_context < 1 || c->max_context > (1 << 20)) {
+    why = "max_streams must be in [1, 256] and max_context in [1, 2^20]";
+    return -1;
+  }
+  if (!(c->rope_theta > 0.0) || !(c->rms_eps >= 0.0)) {
+    why = "rope_theta must be > 0 and rms_eps >= 0";
+    return -1;
+  }
+  return 0;
+}
+
+int32_t n_tensors_for(const s2ar_config* c) { return 1 + 11 * c->slow.n_layers + 3 + 11 * c->fast.n_layers + 2; }
+
+// Expected element counts in canonical order.
+std::vector<int64_t> tensor_sizes(const s2ar_config* c) {
+  std::vector<int64_t> v;
+  const int64_t H = c->slow.hidden, V = (int64_t)c->vocab_text + c->codebook_size, K = c->codebook_size;
+  v.push_back(V * H);
+  auto layer = [&](const s2ar_stack& s) {
+    const int64_t Hd = s.hidden, qd = (int64_t)s.n_q_heads * s.head_dim, kd = (int64_t)s.n_kv_heads * s.head_dim;
+    v.push_back(Hd);
+    v.push_back(qd * Hd);
+    v.push_back(kd * Hd);
+    v.push_back(kd * Hd);
+    v.push_back(s.head_dim);
+    v.push_back(s.head_dim);
+    v.push_back(Hd * qd);
+    v.push_back(Hd);
+    v.push_back((int64_t)s.ffn * Hd);
+    v.push_back((int64_t)s.ffn * Hd);
+    v.push_back(Hd * s.ffn);
+  };
+  for (int l = 0; l < c->slow.n_layers; ++l) layer(c->slow);
+  v.push_back(H);
+  v.push_back(V * H);
+  v.push_back((int64_t)c->n_codebooks * K * H);
+  for (int l = 0; l < c->fast.n_layers; ++l) layer(c->fast);
+  v.push_back(H);
+  v.push_back(K * H);
+  return v;
+}
+
+float bf16_bits_to_float(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+float round_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  u &= 0xffff0000u;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+template <typename T>
+int dev_alloc(s2ar_ctx* c, T** p, size_t bytes) {
+  void* q = nullptr;
+  hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
+  if (e != hipSuccess) return set_err(c, e == hipErrorOutOfMemory ? S2AR_E_NOMEM : S2AR_E_DEVICE,
+                                      std::string("hipMalloc: ") + hipGetErrorString(e));
+  c->dev_allocs.push_back(q);
+  e = hipMemset(q, 0, bytes ? bytes : 16);
+  if (e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("hipMemset: ") + hipGetErrorString(e));
+  *p = static_cast<T*>(q);
+  return 0;
+}
+
+template <typename T>
+int host_alloc(s2ar_ctx* c, T** p, size_t bytes) {
+  void* q = nullptr;
+  hipError_t e = hipHostMalloc(&q, bytes ? bytes : 16, hipHostMallocDefault);
+  if (e != hipSuccess) return set_err(c, S2AR_E_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  c->host_allocs.push_back(q);
+  std::memset(q, 0, bytes ? bytes : 16);
+  *p = static_cast<T*>(q);
+  return 0;
+}
+
+// Upload a norm gain as fp32, zero-padded to pad_k.
+int upload_gain(s2ar_ctx* c, const s2ar_tensor& t, int n, float** out) {
+  const int np = s2k::pad_k(n);
+  std::vector<float> tmp(np, 0.f);
+  for (int i = 0; i < n; ++i)
+    tmp[i] = c->bf16 ? bf16_bits_to_float(static_cast<const uint16_t*>(t.host_ptr)[i])
+                     : static_cast<const float*>(t.host_ptr)[i];
+  if (int rc = dev_alloc(c, out, sizeof(float) * np)) return rc;
+  HIP_TRY(c, hipMemcpy(*out, tmp.data(), sizeof(float) * np, hipMemcpyHostToDevice));
+  return 0;
+}
+
+int upload_layer(s2ar_ctx* c, const s2ar_stack& s, const s2ar_tensor* t, LayerW* L) {
+  const size_t e = c->esz;
+  const size_t H = s.hidden, qd = (size_t)s.n_q_heads * s.head_dim, kd = (size_t)s.n_kv_heads * s.head_dim,
+               F = s.ffn;
+  if (int rc = upload_gain(c, t[0], s.hidden, &L->attn_norm)) return rc;
+  if (int rc = dev_alloc(c, &L->wqkv, (qd + 2 * kd) * H * e)) return rc;
+  char* q = static_cast<char*>(L->wqkv);
+  HIP_TRY(c, hipMemcpy(q, t[1].host_ptr, qd * H * e, hipMemcpyHostToDevice));
+  HIP_TRY(c, hipMemcpy(q + qd * H * e, t[2].host_ptr, kd * H * e, hipMemcpyHostToDevice));
+  HIP_TRY(c, hipMemcpy(q + (qd + kd) * H * e, t[3].host_ptr, kd * H * e, hipMemcpyHostToDevice));
+  if (int rc = upload_gain(c, t[4], s.head_dim, &L->q_norm)) return rc;
+  if (int rc = upload_gain(c, t[5], s.head_dim, &L->k_norm)) return rc;
+  if (int rc = dev_alloc(c, &L->wo, H * qd * e)) return rc;
+  HIP_TRY(c, hipMemcpy(L->wo, t[6].host_ptr, H * qd * e, hipMemcpyHostToDevice));
+  if (int rc = upload_gain(c, t[7], s.hidden, &L->mlp_norm)) return rc;
+  if (int rc = dev_alloc(c, &L->wgu, 2 * F * H * e)) return rc;
+  // interleave gate and up rows so that one wavefront computes both halves of a SwiGLU unit
+  HIP_TRY(c, hipMemcpy2D(L->wgu, 2 * H * e, t[8].host_ptr, H * e, H * e, F, hipMemcpyHostToDevice));
+  HIP_TRY(c, hipMemcpy2D(static_cast<char*>(L->wgu) + H * e, 2 * H * e, t[9].host_ptr, H * e, H * e, F,
+                         hipMemcpyHostToDevice));
+  if (int rc = dev_alloc(c, &L->wdown, H * F * e)) return rc;
+  HIP_TRY(c, hipMemcpy(L->wdown, t[10].host_ptr, H * F * e, hipMemcpyHostToDevice));
+  return 0;
+}
+
+// cos/sin table of rotate-half RoPE: angle = pos * theta^(-2i/D), computed in fp64, rounded
+// to fp32 and, for S2, to bf16 (SGLang Day-0 Support for FishAudio S2, Engineering Appendix).
+int upload_rope(s2ar_ctx* c, int D, int n_pos, float** cs, float** sn) {
+  const int hd = D / 2;
+  std::vector<float> vc((size_t)n_pos * hd), vs((size_t)n_pos * hd);
+  for (int p = 0; p < n_pos; ++p)
+    for (int i = 0; i < hd; ++i) {
+      const double inv = std::pow(c->cfg.rope_theta, -2.0 * (double)i / (double)D);
+      const double a = (double)p * inv;
+      float fc = (float)std::cos(a), fs = (float)std::sin(a);
+      if (c->cfg.rope_bf16) {
+        fc = round_to_bf16(fc);
+        fs = round_to_bf16(fs);
+      }
+      vc[(size_t)p * hd + i] = fc;
+      vs[(size_t)p * hd + i] = fs;
+    }
+  if (int rc = dev_alloc(c, cs, sizeof(float) * vc.size())) return rc;
+  if (int rc = dev_alloc(c, sn, sizeof(float) * vs.size())) return rc;
+  HIP_TRY(c, hipMemcpy(*cs, vc.data(), sizeof(float) * vc.size(), hipMemcpyHostToDevice));
+  HIP_TRY(c, hipMemcpy(*sn, vs.data(), sizeof(float) * vs.size(), hipMemcpyHostToDevice));
+  return 0;
+}
+
+void free_ctx(s2ar_ctx* c) {
+  if (!c) return;
+  if (c->stream) hipStreamSynchronize(c->stream);
+  for (auto& kv : c->graphs) {
+    if (kv.second.exec) hipGraphExecDestroy(kv.second.exec);
+    if (kv.second.g) hipGraphDestroy(kv.second.g);
+  }
+  for (void* p : c->dev_allocs) hipFree(p);
+  for (void* p : c->host_allocs) hipHostFree(p);
+  if (c->ev_order) hipEventDestroy(c->ev_order);
+  if (c->ev_t0) hipEventDestroy(c->ev_t0);
+  if (c->ev_t1) hipEventDestroy(c->ev_t1);
+  if (c->stream) hipStreamDestroy(c->stream);
+  delete c;
+}
+
+int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors, void* hip_stream, s2ar_ctx** out) {
+  s2ar_ctx* c = new (std::nothrow) s2ar_ctx();
+  if (!c) return set_err(nullptr, S2AR_E_NOMEM, "out of host memory");
+  c->cfg = *cfg;
+  c->bf16 = cfg->weight_dtype == 1;
+  c->esz = c->bf16 ? 2 : 4;
+  c->user_stream = static_cast<hipStream_t>(hip_stream);
+  auto fail = [&](int rc) {
+    g_create_error = c->err;
+    free_ctx(c);
+    return rc;
+  };
+#define C_TRY(expr)              \
+  do {                           \
+    int rc_ = (expr);            \
+    if (rc_) return fail(rc_);   \
+  } while (0)
+#define C_HIP(expr) C_TRY(([&]() -> int { HIP_TRY(c, (expr)); return 0; })())
+
+  C_HIP(hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking));
+  C_HIP(hipEventCreateWithFlags(&c->ev_order, hipEventDisableTiming));
+  C_HIP(hipEventCreate(&c->ev_t0));
+  C_HIP(hipEventCreate(&c->ev_t1));
+
+  const s2ar_config& g = c->cfg;
+  const int H = g.slow.hidden, NC = g.n_codebooks, K = g.codebook_size;
+  const int64_t V = (int64_t)g.vocab_text + K;
+  const size_t e = c->esz;
+
+  // weights
+  int ti = 0;
+  C_TRY(dev_alloc(c, &c->embed, (size_t)V * H * e));
+  C_HIP(hipMemcpy(c->embed, t[ti++].host_ptr, (size_t)V * H * e, hipMemcpyHostToDevice));
+  c->slow.resize(g.slow.n_layers);
+  for (int l = 0; l < g.slow.n_layers; ++l, ti += 11) C_TRY(upload_layer(c, g.slow, t + ti, &c->slow[l]));
+  C_TRY(upload_gain(c, t[ti++], H, &c->slow_final));
+  C_TRY(dev_alloc(c, &c->slow_head, (size_t)V * H * e));
+  C_HIP(hipMemcpy(c->slow_head, t[ti++].host_ptr, (size_t)V * H * e, hipMemcpyHostToDevice));
+  C_TRY(dev_alloc(c, &c->codebook, (size_t)NC * K * H * e));
+  C_HIP(hipMemcpy(c->codebook, t[ti++].host_ptr, (size_t)NC * K * H * e, hipMemcpyHostToDevice));
+  c->fast.resize(g.fast.n_layers);
+  for (int l = 0; l < g.fast.n_layers; ++l, ti += 11) C_TRY(upload_layer(c, g.fast, t + ti, &c->fast[l]));
+  C_TRY(upload_gain(c, t[ti++], H, &c->fast_final));
+  C_TRY(dev_alloc(c, &c->fast_head, (size_t)K * H * e));
+  C_HIP(hipMemcpy(c->fast_head, t[ti++].host_ptr, (size_t)K * H * e, hipMemcpyHostToDevice));
+  C_TRY(upload_rope(c, g.slow.head_dim, g.max_context, &c->rope_cos_s, &c->rope_sin_s));
+  C_TRY(upload_rope(c, g.fast.head_dim, NC - 1, &c->rope_cos_f, &c->rope_sin_f));
+
+  // KV pools
+  c->bt_stride = (g.max_context + kPageSize - 1) / kPageSize;
+  c->n_pages = c->bt_stride * g.max_streams;
+  c->kv_layer = (size_t)c->n_pages * g.slow.n_kv_heads * kPageSize * g.slow.head_dim;
+  c->fkv_layer = (size_t)g.max_streams * g.fast.n_kv_heads * kPageSize * g.fast.head_dim;
+  C_TRY(dev_alloc(c, &c->kv_k, c->kv_layer * g.slow.n_layers * 2));
+  C_TRY(dev_alloc(c, &c->kv_v, c->kv_layer * g.slow.n_layers * 2));
+  C_TRY(dev_alloc(c, &c->fkv_k, c->fkv_layer * g.fast.n_layers * 2));
+  C_TRY(dev_alloc(c, &c->fkv_v, c->fkv_layer * g.fast.n_layers * 2));
+  C_TRY(dev_alloc(c, &c->d_bt, sizeof(int) * c->n_pages));
+  C_TRY(host_alloc(c, &c->h_bt, sizeof(int) * c->n_pages));
+  {
+    std::vector<int> ids(g.max_streams), fpos((size_t)(NC - 1) * g.max_streams);
+    for (int s = 0; s < g.max_streams; ++s) ids[s] = s;
+    for (int j = 0; j < NC - 1; ++j)
+      for (int s = 0; s < g.max_streams; ++s) fpos[(size_t)j * g.max_streams + s] = j;
+    C_TRY(dev_alloc(c, &c->d_fast_bt, sizeof(int) * g.max_streams));
+    C_HIP(hipMemcpy(c->d_fast_bt, ids.data(), sizeof(int) * g.max_streams, hipMemcpyHostToDevice));
+    C_TRY(dev_alloc(c, &c->d_slot_ids, sizeof(int) * g.max_streams));
+    C_HIP(hipMemcpy(c->d_slot_ids, ids.data(), sizeof(int) * g.max_streams, hipMemcpyHostToDevice));
+    C_TRY(dev_alloc(c, &c->d_fast_pos, sizeof(int) * fpos.size()));
+    C_HIP(hipMemcpy(c->d_fast_pos, fpos.data(), sizeof(int) * fpos.size(), hipMemcpyHostToDevice));
+  }
+  // pages are handed out in a scrambled order so that a stream's pages are never contiguous
+  c->free_pages.resize(c->n_pages);
+  for (int i = 0; i < c->n_pages; ++i) c->free_pages[i] = i;
+  {
+    uint64_t st = 0x2545F4914F6CDD1DULL;
+    for (int i = c->n_pages - 1; i > 0; --i) {
+      st ^= st << 13;
+      st ^= st >> 7;
+      st ^= st << 17;
+      const int j = (int)(st % (uint64_t)(i + 1));
+      std::swap(c->free_pages[i], c->free_pages[j]);
+    }
+  }
+  c->stream_pages.assign(g.max_streams, {});
+
+  // state
+  C_TRY(dev_alloc(c, &c->d_pos, sizeof(int) * g.max_streams));
+  C_TRY(dev_alloc(c, &c->d_codes, sizeof(int) * g.max_streams * NC));
+  C_TRY(dev_alloc(c, &c->d_h, sizeof(float) * (size_t)g.max_streams * H));
+  C_TRY(dev_alloc(c, &c->d_snap, sizeof(int) * g.max_streams * NC));
+  c->pos.assign(g.max_streams, 0);
+  c->ready.assign(g.max_streams, 0);
+
+  // workspace
+  const int qkvd = (g.slow.n_q_heads + 2 * g.slow.n_kv_heads) * g.slow.head_dim;
+  const int qkvf = (g.fast.n_q_heads + 2 * g.fast.n_kv_heads) * g.fast.head_dim;
+  const int qd = std::max(g.slow.n_q_heads * g.slow.head_dim, g.fast.n_q_heads * g.fast.head_dim);
+  const int F = std::max(g.slow.ffn, g.fast.ffn);
+  C_TRY(dev_alloc(c, &c->x, sizeof(float) * s2k::pad_k(H)));
+  C_TRY(dev_alloc(c, &c->xf, sizeof(float) * s2k::pad_k(H)));
+  C_TRY(dev_alloc(c, &c->z, sizeof(float) * s2k::pad_k(H)));
+  C_TRY(dev_alloc(c, &c->qkv, sizeof(float) * std::max(qkvd, qkvf)));
+  C_TRY(dev_alloc(c, &c->att, sizeof(float) * s2k::pad_k(qd)));
+  C_TRY(dev_alloc(c, &c->act, sizeof(float) * s2k::pad_k(F)));
+  C_TRY(dev_alloc(c, &c->slow_logits, sizeof(float) * V));
+  C_TRY(dev_alloc(c, &c->fast_logits, sizeof(float) * K));
+  const int nb = std::max(s2k::gemv_blocks(s2k::GEMV_NORM_ARGMAX, (int)V), s2k::gemv_blocks(s2k::GEMV_NORM_ARGMAX, K));
+  C_TRY(dev_alloc(c, &c->am_val, sizeof(float) * nb));
+  C_TRY(dev_alloc(c, &c->am_idx, sizeof(int) * nb));
+  C_TRY(dev_alloc(c, &c->am_counter, sizeof(unsigned) * 64));
+  c->max_chunks = (g.max_context + 63) / 64;
+  const int hq = std::max(g.slow.n_q_heads, g.fast.n_q_heads);
+  const int dmax = std::max(g.slow.head_dim, g.fast.head_dim);
+  C_TRY(dev_alloc(c, &c->att_ml, sizeof(float) * 2 * hq * c->max_chunks));
+  C_TRY(dev_alloc(c, &c->att_o, sizeof(float) * (size_t)hq * c->max_chunks * dmax));
+  C_TRY(dev_alloc(c, &c->att_cnt, sizeof(unsigned) * std::max(g.slow.n_kv_heads, g.fast.n_kv_heads)));
+  C_TRY(dev_alloc(c, &c->d_tokens, sizeof(int) * g.max_context));
+  C_TRY(dev_alloc(c, &c->d_mask, (size_t)g.max_context));
+  C_TRY(dev_alloc(c, &c->d_pcodes, sizeof(int) * (size_t)g.max_context * NC));
+
+  c->h_codes_frames = 64;
+  C_TRY(host_alloc(c, &c->h_codes, sizeof(int) * (size_t)c->h_codes_frames * g.max_streams * NC));
+  const int Lf = g.fast.n_layers;
+  c->h_taps_floats = (size_t)H + (size_t)g.slow.n_layers * H + H + V + (size_t)(NC - 1) * Lf * H +
+                     (size_t)(NC - 1) * H + (size_t)(NC - 1) * K;
+  C_TRY(host_alloc(c, &c->h_taps, sizeof(float) * c->h_taps_floats));
+  C_TRY(host_alloc(c, &c->h_small, sizeof(int) * 4 * NC));
+  C_HIP(hipDeviceSynchronize());
+  *out = c;
+  return S2AR_OK;
+#undef C_TRY
+#undef C_HIP
+}
+
+// ------------------------------------------------------------------------------- frame pieces
+
+struct TapPlan {  // host destinations inside h_taps (nullptr = not wanted)
+  float *embed = nullptr, *slow_resid = nullptr, *slow_h = nullptr, *slow_logits = nullptr;
+  float *fast_resid = nullptr, *fast_z = nullptr, *fast_logits = nullptr;
+  int* own = nullptr;       // [NC]
+  int* next_c0 = nullptr;   // [1]
+  const int* forced = nullptr;  // pinned copy of the forced codes [NC]
+};
+
+struct Enq {
+  s2ar_ctx* c;
+  hipStream_t s;
+  hipError_t e = hipSuccess;
+  void chk(hipError_t r) {
+    if (e == hipSuccess && r != hipSuccess) e = r;
+  }
+  void d2h(void* dst, const void* src, size_t bytes) {
+    chk(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s));
+  }
+  void h2d(void* dst, const void* src, size_t bytes) {
+    chk(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s));
+  }
+
+  void gemv(int kind, const void* w, const float* x, const float* gain, float* y, int N, int K,
+            float* xnorm_out = nullptr, int lo = 0, int hi = 0, int* code_out = nullptr) {
+    s2k::GemvArgs a{};
+    a.w = w;
+    a.x = x;
+    a.gain = gain;
+    a.eps = (float)c->cfg.rms_eps;
+    a.y = y;
+    a.xnorm_out = xnorm_out;
+    a.N = N;
+    a.K = K;
+    a.am_lo = lo;
+    a.am_hi = hi;
+    a.am_val = c->am_val;
+    a.am_idx = c->am_idx;
+    a.am_counter = c->am_counter;
+    a.am_code_out = code_out;
+    chk(s2k::launch_gemv(kind, c->bf16, a, s));
+  }
+
+  // one stack of layers on the residual `x` of batch row 0 (stream slot `slot`)
+  void layers(bool is_slow, int slot, float* x, float* resid_tap) {
+    const s2ar_stack& st = is_slow ? c->cfg.slow : c->cfg.fast;
+    const std::vector<LayerW>& W = is_slow ? c->slow : c->fast;
+    const int H = st.hidden, D = st.head_dim, qd = st.n_q_heads * D;
+    const int qkvd = (st.n_q_heads + 2 * st.n_kv_heads) * D;
+    for (int l = 0; l < st.n_layers; ++l) {
+      const LayerW& L = W[l];
+      gemv(s2k::GEMV_NORM_STORE, L.wqkv, x, L.attn_norm, c->qkv, qkvd, H);
+      s2k::AttnArgs a{};
+      a.qkv = c->qkv;
+      a.q_norm = L.q_norm;
+      a.k_norm = L.k_norm;
+      a.slots = c->d_slot_ids + slot;
+      a.M = 1;
+      a.Hq = st.n_q_heads;
+      a.Hkv = st.n_kv_heads;
+      a.D = D;
+      a.page_size = kPageSize;
+      a.eps = (float)c->cfg.rms_eps;
+      a.scale = (float)(1.0 / std::sqrt((double)D));
+      a.out = c->att;
+      a.part_ml = c->att_ml;
+      a.part_o = c->att_o;
+      a.counters = c->att_cnt;
+      if (is_slow) {
+        a.rope_cos = c->rope_cos_s;
+        a.rope_sin = c->rope_sin_s;
+        a.pos = c->d_pos;
+        a.k_cache = c->kv_k + (size_t)l * c->kv_layer;
+        a.v_cache = c->kv_v + (size_t)l * c->kv_layer;
+        a.block_table = c->d_bt;
+        a.bt_stride = c->bt_stride;
+        a.max_chunks = c->max_chunks;
+      } else {
+        a.rope_cos = c->rope_cos_f;
+        a.rope_sin = c->rope_sin_f;
+        a.pos = fast_pos_ptr;
+        a.k_cache = c->fkv_k + (size_t)l * c->fkv_layer;
+        a.v_cache = c->fkv_v + (size_t)l * c->fkv_layer;
+        a.block_table = c->d_fast_bt;
+        a.bt_stride = 1;
+        a.max_chunks = 1;
+      }
+      chk(s2k::launch_attention(a, s));
+      gemv(s2k::GEMV_RESID, L.wo, c->att, nullptr, x, H, qd);
+      gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, x, L.mlp_norm, c->act, 2 * st.ffn, H);
+      gemv(s2k::GEMV_RESID, L.wdown, c->act, nullptr, x, H, st.ffn);
+      if (resid_tap) d2h(resid_tap + (size_t)l * H, x, sizeof(float) * H);
+    }
+  }
+  const int* fast_pos_ptr = nullptr;
+
+  // Slow final norm + head + constrained argmax -> codes[slot][0], h[slot]
+  void slow_head(int slot, const TapPlan* tp) {
+    const s2ar_config& g = c->cfg;
+    const int H = g.slow.hidden, V = g.vocab_text + g.codebook_size;
+    gemv(s2k::GEMV_NORM_ARGMAX, c->slow_head, c->x, c->slow_final, c->slow_logits, V, H,
+         c->d_h + (size_t)slot * H, g.vocab_text, V, c->d_codes + (size_t)slot * g.n_codebooks);
+    if (tp && tp->slow_h) d2h(tp->slow_h, c->d_h + (size_t)slot * H, sizeof(float) * H);
+    if (tp && tp->slow_logits) d2h(tp->slow_logits, c->slow_logits, sizeof(float) * V);
+    if (tp && tp->next_c0) d2h(tp->next_c0, c->d_codes + (size_t)slot * g.n_codebooks, sizeof(int));
+  }
+
+  // the 9 greedy Fast AR steps of stream `slot` on h[slot]
+  void fast_loop(int slot, const TapPlan* tp) {
+    const s2ar_config& g = c->cfg;
+    const int H = g.fast.hidden, K = g.codebook_size, NC = g.n_codebooks, Lf = g.fast.n_layers;
+    int* codes = c->d_codes + (size_t)slot * NC;
+    for (int j = 1; j < NC; ++j) {
+      chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, c->d_slot_ids + slot, c->d_codes, j, c->xf,
+                                 1, s));
+      fast_pos_ptr = c->d_fast_pos + (size_t)(j - 1) * g.max_streams;
+      layers(false, slot, c->xf, tp && tp->fast_resid ? tp->fast_resid + (size_t)(j - 1) * Lf * H : nullptr);
+      gemv(s2k::GEMV_NORM_ARGMAX, c->fast_head, c->xf, c->fast_final, c->fast_logits, K, H,
+           tp && tp->fast_z ? c->z : nullptr, 0, K, codes + j);
+      if (tp && tp->fast_z) d2h(tp->fast_z + (size_t)(j - 1) * H, c->z, sizeof(float) * H);
+      if (tp && tp->fast_logits) d2h(tp->fast_logits + (size_t)(j - 1) * K, c->fast_logits, sizeof(float) * K);
+      if (tp && tp->own) d2h(tp->own + j, codes + j, sizeof(int));
+      if (tp && tp->forced) h2d(codes + j, tp->forced + j, sizeof(int));
+    }
+  }
+
+  // Slow step on the frame's codes (snapshot them first), then advance the position.
+  void slow_step(int slot, const TapPlan* tp) {
+    const s2ar_config& g = c->cfg;
+    chk(s2k::launch_embed_codes(c->bf16, c->codebook, g.codebook_size, g.slow.hidden, g.n_codebooks,
+                                c->d_slot_ids + slot, c->d_codes, c->d_snap + (size_t)slot * g.n_codebooks, c->x,
+                                1, s));
+    if (tp && tp->embed) d2h(tp->embed, c->x, sizeof(float) * g.slow.hidden);
+    layers(true, slot, c->x, tp ? tp->slow_resid : nullptr);
+    slow_head(slot, tp);
+    chk(s2k::launch_advance(c->d_slot_ids + slot, c->d_pos, 1, s));
+  }
+
+  void frame(int slot, const TapPlan* tp) {
+    if (tp && tp->own) d2h(tp->own, c->d_codes + (size_t)slot * c->cfg.n_codebooks, sizeof(int));
+    if (tp && tp->forced) h2d(c->d_codes + (size_t)slot * c->cfg.n_codebooks, tp->forced, sizeof(int));
+    fast_loop(slot, tp);
+    slow_step(slot, tp);
+  }
+};
+
+int order_after_user(s2ar_ctx* c) {
+  HIP_TRY(c, hipEventRecord(c->ev_order, c->user_stream));
+  HIP_TRY(c, hipStreamWaitEvent(c->stream, c->ev_order, 0));
+  return 0;
+}
+
+// Give stream `s` pages for positions [0, upto).
+int ensure_pages(s2ar_ctx* c, int s, int upto) {
+  auto& pages = c->stream_pages[s];
+  const int need = (upto + kPageSize - 1) / kPageSize;
+  if (need > c->bt_stride) return set_err(c, S2AR_E_CAPACITY, "context would exceed max_context");
+  if (need - (int)pages.size() > (int)c->free_pages.size())
+    return set_err(c, S2AR_E_CAPACITY, "no free KV page");
+  const int first = (int)pages.size();
+  while ((int)pages.size() < need) {
+    const int p = c->free_pages.back();
+    c->free_pages.pop_back();
+    c->h_bt[s * c->bt_stride + (int)pages.size()] = p;
+    pages.push_back(p);
+  }
+  if (need > first)
+    HIP_TRY(c, hipMemcpyAsync(c->d_bt + s * c->bt_stride + first, c->h_bt + s * c->bt_stride + first,
+                              sizeof(int) * (need - first), hipMemcpyHostToDevice, c->stream));
+  return 0;
+}
+
+int check_streams(s2ar_ctx* c, const int32_t* ids, int32_t n, int frames) {
+  if (!ids || n < 1 || n > c->cfg.max_streams) return set_err(c, S2AR_E_ARG, "stream_ids must list 1..max_streams streams");
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= c->cfg.max_streams) return set_err(c, S2AR_E_RANGE, "stream id out of range");
+    for (int k = 0; k < i; ++k)
+      if (ids[k] == ids[i]) return set_err(c, S2AR_E_ARG, "stream ids must be distinct");
+    if (!c->ready[ids[i]]) return set_err(c, S2AR_E_STATE, "stream has not been prefilled");
+    if (c->pos[ids[i]] + frames > c->cfg.max_context)
+      return set_err(c, S2AR_E_CAPACITY, "context would exceed max_context");
+  }
+  int pages_needed = 0;
+  for (int i = 0; i < n; ++i) {
+    const int need = (c->pos[ids[i]] + frames + kPageSize - 1) / kPageSize;
+    pages_needed += std::max(0, need - (int)c->stream_pages[ids[i]].size());
+  }
+  if (pages_needed > (int)c->free_pages.size()) return set_err(c, S2AR_E_CAPACITY, "no free KV page");
+  return 0;
+}
+
+Graph* frame_graph(s2ar_ctx* c, int slot, int* rc) {
+  auto it = c->graphs.find(slot);
+  if (it != c->graphs.end()) return &it->second;
+  Graph g;
+  hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    *rc = set_err(c, S2AR_E_DEVICE, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  Enq q{c, c->stream};
+  q.frame(slot, nullptr);
+  e = hipStreamEndCapture(c->stream, &g.g);
+  if (q.e != hipSuccess || e != hipSuccess) {
+    if (g.g) hipGraphDestroy(g.g);
+    *rc = set_err(c, S2AR_E_DEVICE, std::string("graph capture: ") + hipGetErrorString(q.e != hipSuccess ? q.e : e));
+    return nullptr;
+  }
+  e = hipGraphInstantiate(&g.exec, g.g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(g.g);
+    *rc = set_err(c, S2AR_E_DEVICE, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  return &(c->graphs[slot] = g);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------ C ABI
+
+extern "C" {
+
+const char* s2ar_error_name(int code) {
+  switch (code) {
+    case S2AR_OK: return "S2AR_OK";
+    case S2AR_E_ARG: return "S2AR_E_ARG";
+    case S2AR_E_RANGE: return "S2AR_E_RANGE";
+    case S2AR_E_CAPACITY: return "S2AR_E_CAPACITY";
+    case S2AR_E_STATE: return "S2AR_E_STATE";
+    case S2AR_E_NOMEM: return "S2AR_E_NOMEM";
+    case S2AR_E_DEVICE: return "S2AR_E_DEVICE";
+    case S2AR_E_NUMERIC: return "S2AR_E_NUMERIC";
+  }
+  return "S2AR_E_UNKNOWN";
+}
+
+const char* s2ar_last_error(const s2ar_ctx* ctx) { return ctx ? ctx->err.c_str() : g_create_error.c_str(); }
+
+int s2ar_create(const s2ar_config* cfg, const s2ar_tensor* tensors, int32_t n_tensors, void* hip_stream,
+                s2ar_ctx** out) {
+  if (out) *out = nullptr;
+  if (!cfg || !tensors || !out) return set_err(nullptr, S2AR_E_ARG, "cfg, tensors and out must be non-null");
+  std::string why;
+  if (validate_config(cfg, why)) return set_err(nullptr, S2AR_E_ARG, why);
+  if (n_tensors != n_tensors_for(cfg)) return set_err(nullptr, S2AR_E_ARG, "n_tensors does not match the config");
+  const std::vector<int64_t> sizes = tensor_sizes(cfg);
+  const int64_t esz = cfg->weight_dtype == 1 ? 2 : 4;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (!tensors[i].host_ptr) return set_err(nullptr, S2AR_E_ARG, "tensor " + std::to_string(i) + " is null");
+    if (tensors[i].nbytes != sizes[i] * esz)
+      return set_err(nullptr, S2AR_E_ARG, "tensor " + std::to_string(i) + " has " + std::to_string(tensors[i].nbytes) +
+                                              " bytes, expected " + std::to_string(sizes[i] * esz));
+  }
+  int dev_count = 0;
+  if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count < 1)
+    return set_err(nullptr, S2AR_E_DEVICE, "no HIP device is visible");
+  return create_impl(cfg, tensors, n_tensors, hip_stream, out);
+}
+
+void s2ar_destroy(s2ar_ctx* ctx) { free_ctx(ctx); }
+
+int s2ar_prefill(s2ar_ctx* c, int32_t sid, const int32_t* tokens, const uint8_t* mask, const int32_t* codes,
+                 int32_t n) {
+  if (!c) return S2AR_E_ARG;
+  const s2ar_config& g = c->cfg;
+  if (!tokens || n < 1) return set_err(c, S2AR_E_ARG, "tokens must be non-null and n >= 1");
+  if (mask && !codes) return set_err(c, S2AR_E_ARG, "vq_codes are required with vq_mask");
+  if (sid < 0 || sid >= g.max_streams) return set_err(c, S2AR_E_RANGE, "stream id out of range");
+  if ((int64_t)c->pos[sid] + n > g.max_context) return set_err(c, S2AR_E_CAPACITY, "context would exceed max_context");
+  const int V = g.vocab_text + g.codebook_size, NC = g.n_codebooks;
+  for (int i = 0; i < n; ++i) {
+    if (mask && mask[i]) {
+      for (int k = 0; k < NC; ++k)
+        if (codes[(size_t)i * NC + k] < 0 || codes[(size_t)i * NC + k] >= g.codebook_size)
+          return set_err(c, S2AR_E_RANGE, "VQ code out of range at position " + std::to_string(i));
+    } else if (tokens[i] < 0 || tokens[i] >= V) {
+      return set_err(c, S2AR_E_RANGE, "token id out of range at position " + std::to_string(i));
+    }
+  }
+  const int need = (c->pos[sid] + n + kPageSize - 1) / kPageSize - (int)c->stream_pages[sid].size();
+  if (need > (int)c->free_pages.size()) return set_err(c, S2AR_E_CAPACITY, "no free KV page");
+
+  if (int rc = order_after_user(c)) return rc;
+  if (int rc = ensure_pages(c, sid, c->pos[sid] + n)) return rc;
+  HIP_TRY(c, hipMemcpyAsync(c->d_tokens, tokens, sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
+  if (mask) {
+    HIP_TRY(c, hipMemcpyAsync(c->d_mask, mask, (size_t)n, hipMemcpyHostToDevice, c->stream));
+    HIP_TRY(c, hipMemcpyAsync(c->d_pcodes, codes, sizeof(int) * (size_t)n * NC, hipMemcpyHostToDevice, c->stream));
+  }
+  Enq q{c, c->stream};
+  for (int p = 0; p < n; ++p) {
+    q.chk(s2k::launch_embed_prompt(c->bf16, c->embed, c->codebook, g.codebook_size, g.slow.hidden, NC, c->d_tokens,
+                                   mask ? c->d_mask : nullptr, c->d_pcodes, p, c->x, c->stream));
+    q.layers(true, sid, c->x, nullptr);
+    if (p == n - 1) q.slow_head(sid, nullptr);
+    q.chk(s2k::launch_advance(c->d_slot_ids + sid, c->d_pos, 1, c->stream));
+    if (q.e != hipSuccess) break;
+  }
+  if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("prefill launch: ") + hipGetErrorString(q.e));
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  c->pos[sid] += n;
+  c->ready[sid] = 1;
+  return S2AR_OK;
+}
+
+int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_frames, int32_t* codes_out) {
+  if (!c) return S2AR_E_ARG;
+  if (!codes_out || n_frames < 1) return set_err(c, S2AR_E_ARG, "codes_out must be non-null and n_frames >= 1");
+  if (int rc = check_streams(c, ids, n, n_frames)) return rc;
+  const int NC = c->cfg.n_codebooks;
+  std::vector<Graph*> gs(n);
+  for (int i = 0; i < n; ++i) {
+    int rc = 0;
+    gs[i] = frame_graph(c, ids[i], &rc);
+    if (!gs[i]) return rc;
+  }
+  if (int rc = order_after_user(c)) return rc;
+  for (int i = 0; i < n; ++i)
+    if (int rc = ensure_pages(c, ids[i], c->pos[ids[i]] + n_frames)) return rc;
+  int done = 0;
+  while (done < n_frames) {
+    const int chunk = std::min(n_frames - done, c->h_codes_frames * c->cfg.max_streams / n);
+    for (int f = 0; f < chunk; ++f)
+      for (int i = 0; i < n; ++i) {
+        HIP_TRY(c, hipGraphLaunch(gs[i]->exec, c->stream));
+        HIP_TRY(c, hipMemcpyAsync(c->h_codes + ((size_t)f * n + i) * NC, c->d_snap + (size_t)ids[i] * NC,
+                                  sizeof(int) * NC, hipMemcpyDeviceToHost, c->stream));
+      }
+    HIP_TRY(c, hipStreamSynchronize(c->stream));
+    std::memcpy(codes_out + (size_t)done * n * NC, c->h_codes, sizeof(int) * (size_t)chunk * n * NC);
+    done += chunk;
+  }
+  for (int i = 0; i < n; ++i) c->pos[ids[i]] += n_frames;
+  return S2AR_OK;
+}
+
+int s2ar_decode_frame(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t* codes_out) {
+  return s2ar_decode_frames(c, ids, n, 1, codes_out);
+}
+
+int s2ar_debug_frame(s2ar_ctx* c, int32_t sid, const int32_t* forced, s2ar_taps* taps) {
+  if (!c) return S2AR_E_ARG;
+  if (int rc = check_streams(c, &sid, 1, 1)) return rc;
+  const s2ar_config& g = c->cfg;
+  const int NC = g.n_codebooks, H = g.slow.hidden, K = g.codebook_size, V = g.vocab_text + K;
+  if (forced)
+    for (int k = 0; k < NC; ++k)
+      if (forced[k] < 0 || forced[k] >= K) return set_err(c, S2AR_E_RANGE, "forced code out of range");
+  s2ar_taps none{};
+  const s2ar_taps& T = taps ? *taps : none;
+  TapPlan tp;
+  float* f = c->h_taps;
+  tp.embed = f;
+  f += H;
+  tp.slow_resid = f;
+  f += (size_t)g.slow.n_layers * H;
+  tp.slow_h = f;
+  f += H;
+  tp.slow_logits = f;
+  f += V;
+  tp.fast_resid = f;
+  f += (size_t)(NC - 1) * g.fast.n_layers * H;
+  tp.fast_z = f;
+  f += (size_t)(NC - 1) * H;
+  tp.fast_logits = f;
+  tp.own = c->h_small;
+  tp.next_c0 = c->h_small + NC;
+  if (forced) {
+    std::memcpy(c->h_small + 2 * NC, forced, sizeof(int) * NC);
+    tp.forced = c->h_small + 2 * NC;
+  }
+  if (int rc = order_after_user(c)) return rc;
+  if (int rc = ensure_pages(c, sid, c->pos[sid] + 1)) return rc;
+  Enq q{c, c->stream};
+  q.frame(sid, &tp);
+  if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("debug frame: ") + hipGetErrorString(q.e));
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  c->pos[sid] += 1;
+  auto put = [](float* dst, const float* src, size_t n) {
+    if (dst) std::memcpy(dst, src, sizeof(float) * n);
+  };
+  put(T.slow_embed, tp.embed, H);
+  put(T.slow_resid, tp.slow_resid, (size_t)g.slow.n_layers * H);
+  put(T.slow_h, tp.slow_h, H);
+  put(T.slow_logits, tp.slow_logits, V);
+  put(T.fast_resid, tp.fast_resid, (size_t)(NC - 1) * g.fast.n_layers * H);
+  put(T.fast_z, tp.fast_z, (size_t)(NC - 1) * H);
+  put(T.fast_logits, tp.fast_logits, (size_t)(NC - 1) * K);
+  if (T.own_codes) std::memcpy(T.own_codes, tp.own, sizeof(int) * NC);
+  if (T.next_c0) *T.next_c0 = *tp.next_c0;
+  bool finite = true;
+  for (int i = 0; i < V && finite; ++i) finite = std::isfinite(tp.slow_logits[i]);
+  for (int i = 0; i < (NC - 1) * K && finite; ++i) finite = std::isfinite(tp.fast_logits[i]);
+  if (!finite) return set_err(c, S2AR_E_NUMERIC, "non-finite logits");
+  return S2AR_OK;
+}
+
+int s2ar_release_stream(s2ar_ctx* c, int32_t sid) {
+  if (!c) return S2AR_E_ARG;
+  if (sid < 0 || sid >= c->cfg.max_streams) return set_err(c, S2AR_E_RANGE, "stream id out of range");
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  for (int p : c->stream_pages[sid]) c->free_pages.push_back(p);
+  c->stream_pages[sid].clear();
+  c->pos[sid] = 0;
+  c->ready[sid] = 0;
+  const int zero = 0;
+  HIP_TRY(c, hipMemcpy(c->d_pos + sid, &zero, sizeof(int), hipMemcpyHostToDevice));
+  return S2AR_OK;
+}
+
+int s2ar_stream_position(const s2ar_ctx* c, int32_t sid, int32_t* pos_out) {
+  if (!c || !pos_out) return S2AR_E_ARG;
+  if (sid < 0 || sid >= c->cfg.max_streams) return S2AR_E_RANGE;
+  *pos_out = c->pos[sid];
+  return S2AR_OK;
+}
+
+int s2ar_time_kernel(s2ar_ctx* c, int32_t which, int32_t iters, float* avg_ms, int64_t* bytes_out) {
+  if (!c) return S2AR_E_ARG;
+  if (which != 0 || iters < 1 || !avg_ms) return set_err(c, S2AR_E_ARG, "which must be 0, iters >= 1, avg_ms non-null");
+  const s2ar_stack& st = c->cfg.slow;
+  Enq q{c, c->stream};
+  HIP_TRY(c, hipEventRecord(c->ev_t0, c->stream));
+  for (int i = 0; i < iters; ++i) {
+    const LayerW& L = c->slow[i % st.n_layers];
+    q.gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, c->x, L.mlp_norm, c->act, 2 * st.ffn, st.hidden);
+  }
+  HIP_TRY(c, hipEventRecord(c->ev_t1, c->stream));
+  if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("time kernel: ") + hipGetErrorString(q.e));
+  HIP_TRY(c, hipEventSynchronize(c->ev_t1));
+  float ms = 0.f;
+  HIP_TRY(c, hipEventElapsedTime(&ms, c->ev_t0, c->ev_t1));
+  *avg_ms = ms / (float)iters;
+  if (bytes_out)
+    *bytes_out = (int64_t)2 * st.ffn * st.hidden * c->esz + (int64_t)st.hidden * 4 * 2 + (int64_t)st.ffn * 4;
+  return S2AR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal launchers of the gfx950 kernels of the Dual-AR frame.  Host code in
+// engine.hip calls these; nothing here is part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s2k {
+
+// Epilogue of a weight-streaming GEMV y = W . xin (W: [N][K] row-major).
+enum GemvKind : int {
+  GEMV_NORM_STORE = 0,   // y[n] = W . rmsnorm(x)            (fused QKV projection)
+  GEMV_RESID = 1,        // y[n] += W . x                    (O / down projection + residual)
+  GEMV_NORM_SWIGLU = 2,  // rows (2i, 2i+1) = (gate_i, up_i): y[i] = silu(g) * u
+  GEMV_NORM_ARGMAX = 3,  // logits y[n] = W . rmsnorm(x); greedy pick over [lo, hi)
+};
+
+// x and gain must be readable up to pad_k(K) floats, with zeros past K.
+int pad_k(int K);
+
+struct GemvArgs {
+  const void* w;          // weights (bf16 bits or fp32), [N][K]
+  const float* x;         // input vector [pad_k(K)] (fp32, zero past K)
+  const float* gain;      // RMSNorm gain [pad_k(K)] (fp32, zero past K) for the NORM kinds
+  float eps;
+  float* y;               // output (see GemvKind)
+  float* xnorm_out;       // optional: normalised input written by block 0 ([K])
+  int N, K;
+  // greedy pick (GEMV_NORM_ARGMAX)
+  int am_lo, am_hi;
+  float* am_val;          // [n_blocks] per-block maxima
+  int* am_idx;            // [n_blocks] per-block arg maxima
+  unsigned* am_counter;   // zero between launches; reset by the last block
+  int* am_code_out;       // receives (argmax - am_lo)
+};
+
+// Number of workgroups a GEMV launch of this shape uses (sizes argmax partials).
+int gemv_blocks(int kind, int N);
+hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const float* qkv;        // [M][(Hq + 2 Hkv) D]: q heads, then k heads, then v heads
+  const float* q_norm;     // [D]
+  const float* k_norm;     // [D]
+  const float* rope_cos;   // [positions][D/2], already rounded as the model requires
+  const float* rope_sin;
+  const int* slots;        // [M] stream slot of each batch row
+  const int* pos;          // [slots] position of the new token (context = pos + 1)
+  uint16_t* k_cache;       // [pages][Hkv][page_size][D] bf16 bits (one layer)
+  uint16_t* v_cache;
+  const int* block_table;  // [slots][bt_stride]
+  int bt_stride;
+  float* out;              // [M][Hq D]
+  float* part_ml;          // [M][Hq][max_chunks][2] running (max, sum) per chunk
+  float* part_o;           // [M][Hq][max_chunks][D]
+  unsigned* counters;      // [M][Hkv], zero between launches
+  int max_chunks;          // grid extent along the context (chunks of 64 positions)
+  int M, Hq, Hkv, D, page_size;
+  float eps;
+  float scale;             // 1 / sqrt(D), applied to q after RoPE
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// x[b] = sum_k codebook[k][codes[slot][k]] (fp32, k ascending); codes_snap[b] = codes[slot].
+hipError_t launch_embed_codes(bool bf16, const void* codebook, int K, int H, int NC, const int* slots,
+                              const int* codes, int* codes_snap, float* x, int M, hipStream_t s);
+// Fast step j input: j == 1 -> h[slot]; j >= 2 -> codebook[j-1][codes[slot][j-1]].
+hipError_t launch_fast_input(bool bf16, const void* codebook, const float* h, int K, int H, int NC,
+                             const int* slots, const int* codes, int j, float* x, int M, hipStream_t s);
+// Prompt position p: mask[p] ? sum of codebook rows of codes[p] : embed[tokens[p]].
+hipError_t launch_embed_prompt(bool bf16, const void* embed, const void* codebook, int K, int H, int NC,
+                               const int* tokens, const uint8_t* mask, const int* codes, int p, float* x,
+                               hipStream_t s);
+// pos[slots[b]] += 1
+hipError_t launch_advance(const int* slots, int* pos, int M, hipStream_t s);
+
+}  // namespace s2k

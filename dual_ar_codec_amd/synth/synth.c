@@ -37,32 +37,43 @@ uint64_t synth_u64(uint64_t seed, uint64_t stream, uint64_t i) {
 
 static inline double unit53(uint64_t u) { return (double)(u >> 11) * 0x1.0p-53; }
 
-static inline double normal_at(uint64_t key, uint64_t i) {
-  uint64_t m = i >> 1;
-  double u1 = unit53(mix64(key + (2 * m + 1) * GOLDEN));
-  double u2 = unit53(mix64(key + (2 * m + 2) * GOLDEN));
-  double r = sqrt(-2.0 * log(1.0 - u1)); /* 1-u1 in (0,1] */
-  double t = 6.283185307179586476925286766559 * u2;
-  return (i & 1) ? r * sin(t) : r * cos(t);
-}
-
 static inline uint16_t f32_to_bf16_rne(float f) {
   union { float f; uint32_t u; } v = {f};
   uint32_t lsb = (v.u >> 16) & 1u;
   return (uint16_t)((v.u + 0x7fffu + lsb) >> 16);
 }
 
+/* Both members of Box-Muller pair m (elements 2m and 2m+1). */
+static inline void normal_pair(uint64_t key, uint64_t m, double* a, double* b) {
+  double u1 = unit53(mix64(key + (2 * m + 1) * GOLDEN));
+  double u2 = unit53(mix64(key + (2 * m + 2) * GOLDEN));
+  double r = sqrt(-2.0 * log(1.0 - u1));
+  double t = 6.283185307179586476925286766559 * u2;
+  *a = r * cos(t);
+  *b = r * sin(t);
+}
+
 void synth_normal_f32(uint64_t seed, uint64_t stream, int64_t n, double scale, float* out) {
   uint64_t key = stream_key(seed, stream);
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) out[i] = (float)(scale * normal_at(key, (uint64_t)i));
+  for (int64_t m = 0; m < (n + 1) / 2; ++m) {
+    double a, b;
+    normal_pair(key, (uint64_t)m, &a, &b);
+    out[2 * m] = (float)(scale * a);
+    if (2 * m + 1 < n) out[2 * m + 1] = (float)(scale * b);
+  }
 }
 
 /* The normal value is rounded to fp32 first, then to bf16 (round to nearest even). */
 void synth_normal_bf16(uint64_t seed, uint64_t stream, int64_t n, double scale, uint16_t* out) {
   uint64_t key = stream_key(seed, stream);
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne((float)(scale * normal_at(key, (uint64_t)i)));
+  for (int64_t m = 0; m < (n + 1) / 2; ++m) {
+    double a, b;
+    normal_pair(key, (uint64_t)m, &a, &b);
+    out[2 * m] = f32_to_bf16_rne((float)(scale * a));
+    if (2 * m + 1 < n) out[2 * m + 1] = f32_to_bf16_rne((float)(scale * b));
+  }
 }
 
 void synth_uniform_f32(uint64_t seed, uint64_t stream, int64_t n, double lo, double hi, float* out) {

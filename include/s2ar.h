@@ -1,0 +1,167 @@
+/*
+ * s2ar -- Dual-AR per-frame decode step (FishAudio S2 shape) on one MI355X.
+ *
+ * The model and what a frame is ("SGLang Day-0 Support for FishAudio S2",
+ * section Architecture, Stage 2; "s2pro-native", section What happens to a
+ * sentence; "Fish Audio Abre Codigo do S2", section Arquitetura Dual-AR):
+ *   - a Slow AR (Qwen3-style decoder: RMSNorm, GQA with QK-norm and RoPE,
+ *     SwiGLU) runs along time over a KV cache and picks one semantic code per
+ *     frame, with the pick restricted to the semantic ids (S2 page, Background
+ *     and Motivation: constrained decoding);
+ *   - a Fast AR runs 9 greedy steps on the Slow hidden state and picks the 9
+ *     residual codes;
+ *   - the frame's 10 codebook embeddings are summed and injected as the next
+ *     Slow input (VQ injection at masked positions).
+ * Prompt token ids plus optional 10-codebook VQ codes go in; one 10-code tuple
+ * per frame comes out (S2 page, Architecture, Stage 1 and Stage 3).
+ *
+ * Conventions for every call:
+ *   - returns S2AR_OK (0) or a negative S2AR_E_* code; nothing throws or aborts;
+ *   - arguments are validated before any device work; a failed call leaves the
+ *     context's state as it was (a failed S2AR_E_DEVICE call may leave it
+ *     unusable: destroy it);
+ *   - all pointers are HOST pointers unless stated otherwise; the library reads
+ *     host inputs only during the call and writes host outputs before it
+ *     returns;
+ *   - the context owns every device allocation (weights, KV pages, workspace,
+ *     captured graphs) and frees them in s2ar_destroy;
+ *   - a context is not thread-safe; calls are synchronous.
+ */
+#ifndef S2AR_H
+#define S2AR_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define S2AR_OK 0
+#define S2AR_E_ARG (-1)      /* null pointer, bad size, inconsistent config */
+#define S2AR_E_RANGE (-2)    /* token id, code or stream id out of range */
+#define S2AR_E_CAPACITY (-3) /* context would exceed max_context, or no free KV page */
+#define S2AR_E_STATE (-4)    /* call out of order (decode before prefill) */
+#define S2AR_E_NOMEM (-5)    /* device or host allocation failed */
+#define S2AR_E_DEVICE (-6)   /* HIP runtime error (message in s2ar_last_error) */
+#define S2AR_E_NUMERIC (-7)  /* non-finite logits (checked by s2ar_debug_frame only) */
+
+typedef struct s2ar_ctx s2ar_ctx;
+
+/* Shape of one transformer stack.  q heads per KV head = n_q_heads/n_kv_heads. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn;
+} s2ar_stack;
+
+typedef struct {
+  s2ar_stack slow, fast;  /* fast.hidden must equal slow.hidden: the Slow hidden feeds the Fast AR */
+  int32_t vocab_text;     /* text ids are [0, vocab_text); semantic code c has id vocab_text + c */
+  int32_t n_codebooks;    /* 10: one semantic + nine residual codebooks */
+  int32_t codebook_size;  /* entries per codebook */
+  double rope_theta;      /* RoPE base (1e6 for S2) */
+  double rms_eps;         /* RMSNorm epsilon, inside the square root */
+  int32_t weight_dtype;   /* 0: fp32 weights, 1: bf16 weights */
+  int32_t rope_bf16;      /* 1: round the cos/sin table to bf16 (S2 page, Engineering Appendix) */
+  int32_t max_streams;    /* concurrent decode streams (stream ids 0..max_streams-1) */
+  int32_t max_context;    /* Slow positions per stream, prompt plus frames */
+  int32_t page_size;      /* KV positions per page; must be 16 */
+} s2ar_config;
+
+/* One weight tensor in host memory: fp32, or bf16 bit patterns (uint16). */
+typedef struct {
+  const void* host_ptr;
+  int64_t nbytes;
+} s2ar_tensor;
+
+/*
+ * Create a context and upload the weights.
+ * tensors: n_tensors entries in canonical order
+ *   slow.embed [vocab_text+codebook_size][H]
+ *   per Slow layer: attn_norm[H], wq[Hq*D][H], wk[Hkv*D][H], wv[Hkv*D][H],
+ *     q_norm[D], k_norm[D], wo[H][Hq*D], mlp_norm[H], w_gate[F][H], w_up[F][H],
+ *     w_down[H][F]
+ *   slow.final_norm[H], slow.head[vocab_text+codebook_size][H],
+ *   codebook.embed[n_codebooks][codebook_size][H],
+ *   per Fast layer: the same eleven, fast.final_norm[H], fast.head[codebook_size][H]
+ * Matrices are row-major [out][in]; every tensor has weight_dtype elements and
+ * nbytes must equal its element count times the element size.
+ * hip_stream: a hipStream_t (may be NULL = the legacy default stream).  The
+ * library orders its work after the work already queued on it at each call.
+ * On success *out receives the context; on failure *out is set to NULL.
+ */
+int s2ar_create(const s2ar_config* cfg, const s2ar_tensor* tensors, int32_t n_tensors, void* hip_stream,
+                s2ar_ctx** out);
+
+/*
+ * Prefill n prompt positions of a stream (appending to its context).
+ * tokens: [n] ids in [0, vocab_text+codebook_size).  vq_mask: [n] or NULL;
+ * where vq_mask[i] != 0 the input is the sum of the ten codebook embeddings of
+ * vq_codes[i][0..9] (each in [0, codebook_size)) instead of the token's
+ * embedding (VQ injection: S2 page, Architecture, Stage 2; the voice-clone
+ * reference is prepended as VQ positions: Stage 1).  vq_codes: [n][n_codebooks]
+ * or NULL when vq_mask is NULL.
+ * The last position goes through the Slow head, which leaves the stream ready
+ * for its first frame.
+ */
+int s2ar_prefill(s2ar_ctx* ctx, int32_t stream_id, const int32_t* tokens, const uint8_t* vq_mask,
+                 const int32_t* vq_codes, int32_t n);
+
+/*
+ * Decode one frame for each listed stream (distinct ids, each prefilled).
+ * codes_out: [n_streams][n_codebooks]; entry 0 is the semantic code, 1..9 the
+ * residual codes, each in [0, codebook_size).  Each stream then advances by
+ * one Slow position (its next semantic code is computed ahead).
+ */
+int s2ar_decode_frame(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n_streams, int32_t* codes_out);
+
+/* Same as n_frames calls of s2ar_decode_frame with one final host copy;
+ * codes_out: [n_frames][n_streams][n_codebooks]. */
+int s2ar_decode_frames(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n_streams, int32_t n_frames,
+                       int32_t* codes_out);
+
+/* Forget a stream's context and return its KV pages to the pool. */
+int s2ar_release_stream(s2ar_ctx* ctx, int32_t stream_id);
+
+/* Current Slow position (= context length) of a stream, or a negative code. */
+int s2ar_stream_position(const s2ar_ctx* ctx, int32_t stream_id, int32_t* pos_out);
+
+/* Free everything the context owns.  NULL is a no-op. */
+void s2ar_destroy(s2ar_ctx* ctx);
+
+/* Message of the last failed call on ctx (or of the last failed s2ar_create
+ * when ctx is NULL); valid until the next call. */
+const char* s2ar_last_error(const s2ar_ctx* ctx);
+const char* s2ar_error_name(int code);
+
+/*
+ * Test and measurement support.
+ *
+ * s2ar_debug_frame decodes one frame of one stream like s2ar_decode_frame, but
+ * without the captured graph, copying intermediate values to host buffers
+ * (any may be NULL).  forced_codes ([n_codebooks] or NULL) are teacher-forced
+ * codes of this frame: forced_codes[0] replaces the semantic code computed
+ * ahead, forced_codes[j] replaces the Fast AR's own pick as the input of step
+ * j+1, and the forced tuple is what the next Slow step embeds.
+ */
+typedef struct {
+  float* slow_embed;   /* [H]  Slow input: sum of the frame's codebook rows */
+  float* slow_resid;   /* [slow.n_layers][H]  residual after each Slow layer */
+  float* slow_h;       /* [H]  final-normed Slow hidden (next frame's Fast input) */
+  float* slow_logits;  /* [vocab_text+codebook_size] */
+  float* fast_resid;   /* [9][fast.n_layers][H] */
+  float* fast_z;       /* [9][H]  final-normed Fast hidden per step */
+  float* fast_logits;  /* [9][codebook_size] */
+  int32_t* own_codes;  /* [n_codebooks]: the library's own picks this frame */
+  int32_t* next_c0;    /* [1]: own semantic pick for the next frame */
+} s2ar_taps;
+
+int s2ar_debug_frame(s2ar_ctx* ctx, int32_t stream_id, const int32_t* forced_codes, s2ar_taps* taps);
+
+/* Launch one kernel of the frame `iters` times on the context's stream,
+ * cycling over the layers, and report the mean duration of a launch measured
+ * with HIP events on that stream.  which: 0 = Slow fused RMSNorm + gate/up +
+ * SwiGLU GEMV.  bytes_out: algorithmic bytes of one launch. */
+int s2ar_time_kernel(s2ar_ctx* ctx, int32_t which, int32_t iters, float* avg_ms, int64_t* bytes_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,124 @@
+"""Teacher-forced comparison of the HIP path against the CPU oracle.
+
+Acceptance (per frame, same bf16 weights, the GPU forced with the oracle's own
+codes so both sides see identical inputs):
+  - cosine >= 0.9999 of the residual after every Slow and Fast layer and of the
+    final-normed hiddens;
+  - max |logit error| <= 2e-2 * max |logit| (Slow over the whole vocabulary,
+    Fast per step over the codebook);
+  - greedy picks identical wherever the oracle's top-1 minus top-2 margin
+    exceeds 5e-2.
+"""
+import numpy as np
+
+import oracle
+
+COS_MIN = 0.9999
+LOGIT_REL = 2e-2
+MARGIN = 5e-2
+
+
+def cosine(a, b):
+    a = np.ravel(a).astype(np.float64)
+    b = np.ravel(b).astype(np.float64)
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def logit_err(gpu, ref):
+    return float(np.max(np.abs(gpu.astype(np.float64) - ref)) / np.max(np.abs(ref)))
+
+
+class Report:
+    def __init__(self):
+        self.min_cos = 1.0
+        self.max_logit = 0.0
+        self.checked = 0
+        self.skipped = 0
+        self.mismatch = []
+
+    def cos(self, what, a, b):
+        c = cosine(a, b)
+        self.min_cos = min(self.min_cos, c)
+        assert c >= COS_MIN, f"{what}: cosine {c:.7f} < {COS_MIN}"
+
+    def logits(self, what, gpu, ref):
+        e = logit_err(gpu, ref)
+        self.max_logit = max(self.max_logit, e)
+        assert e <= LOGIT_REL, f"{what}: logit error {e:.3e} x max|logit|"
+
+    def token(self, what, gpu, ref, margin):
+        if margin > MARGIN:
+            self.checked += 1
+            if gpu != ref:
+                self.mismatch.append((what, gpu, ref, margin))
+        else:
+            self.skipped += 1
+
+    def finish(self):
+        assert not self.mismatch, f"greedy picks differ where the margin exceeds {MARGIN}: {self.mismatch[:5]}"
+        return dict(min_cos=self.min_cos, max_logit_rel=self.max_logit, tokens_checked=self.checked,
+                    tokens_skipped=self.skipped)
+
+
+def oracle_run(cfg, weights, tokens, mask, codes, n_frames):
+    """Oracle free-running decode with every tap; frame t = (fast taps, the Slow
+    step that follows frame t)."""
+    m = oracle.Model(cfg, weights)
+    st = m.new_state()
+    pre = st.prefill(tokens, mask, codes)
+    h, c0, c0m = pre["h"], pre["c0"], pre["margin"]
+    frames = []
+    for _ in range(n_frames):
+        fl = m.fast_loop(h, taps=True)
+        codes_t = np.concatenate([[c0], fl["codes"]]).astype(np.int32)
+        nxt = st.slow_step(codes_t, taps=True)
+        frames.append(dict(codes=codes_t, c0_margin=c0m, fast=fl, slow=nxt))
+        h, c0, c0m = nxt["h"], nxt["c0"], nxt["margin"]
+    return frames
+
+
+def compare_frames(ctx, stream, frames, cfg, report=None, gather_check=True):
+    """Drive the GPU teacher-forced through the oracle's frames and check each."""
+    r = report or Report()
+    K, Vt = cfg["codebook_size"], cfg["vocab_text"]
+    cb = None
+    for t, f in enumerate(frames):
+        g = ctx.debug_frame(stream, forced=f["codes"])
+        r.token(f"frame {t} c0", int(g["own_codes"][0]), int(f["codes"][0]), f["c0_margin"])
+        fl = f["fast"]
+        for j in range(9):
+            for l in range(cfg["fast"]["n_layers"]):
+                r.cos(f"frame {t} fast step {j + 1} layer {l}", g["fast_resid"][j, l], fl["resid"][j, l])
+            r.cos(f"frame {t} fast step {j + 1} z", g["fast_z"][j], fl["z"][j])
+            r.logits(f"frame {t} fast step {j + 1} logits", g["fast_logits"][j], fl["logits"][j])
+            r.token(f"frame {t} c{j + 1}", int(g["own_codes"][j + 1]), int(fl["codes"][j]), fl["margins"][j])
+            # the greedy pick is exactly the argmax of the kernel's own logits
+            assert int(g["own_codes"][j + 1]) == int(np.argmax(g["fast_logits"][j]))
+        s = f["slow"]
+        for l in range(cfg["slow"]["n_layers"]):
+            r.cos(f"frame {t} slow layer {l}", g["slow_resid"][l], s["resid"][l])
+        r.cos(f"frame {t} slow h", g["slow_h"], s["h"])
+        r.logits(f"frame {t} slow logits", g["slow_logits"], s["logits"])
+        r.token(f"frame {t} next c0", int(g["next_c0"]), int(s["c0"]), s["margin"])
+        assert int(g["next_c0"]) == int(np.argmax(g["slow_logits"][Vt:Vt + K]))
+        if gather_check:
+            if cb is None:
+                cb = codebook_f32(cfg, ctx)
+            want = np.zeros(cfg["slow"]["hidden"], np.float32)
+            for k in range(cfg["n_codebooks"]):
+                want = want + cb[k, f["codes"][k]]
+            assert np.array_equal(g["slow_embed"], want), f"frame {t}: gather-sum is not bit-exact"
+    return r
+
+
+_CB_CACHE = {}
+
+
+def codebook_f32(cfg, ctx):
+    return _CB_CACHE[id(ctx)]
+
+
+def remember_codebook(ctx, cfg, weights):
+    from dual_ar_codec_amd import synth
+    names = [n for n, _, _ in synth.tensor_specs(cfg)]
+    _CB_CACHE[id(ctx)] = synth.as_f32(weights[names.index("codebook.embed")])
