@@ -107,7 +107,7 @@ def main():
     k_gbps = nbytes / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "k_gemv<bf16, NCH=5, GEMV_NORM_SWIGLU> (Slow gate/up, 19456x2560)",
+                "kernel": "k_gemv2<bf16, NCH=5, GEMV_NORM_SWIGLU, R=2, WPB=4> (Slow gate/up, 19456x2560)",
                 "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2)}
     ctx.close()
 

@@ -26,6 +26,7 @@ thread_local std::string g_create_error;
 
 constexpr int kPageSize = 16;
 constexpr int kMaxStreams = 256;
+constexpr int kAttnSplit = 256;  // context positions per attention workgroup
 
 struct LayerW {
   void* wqkv = nullptr;   // [(Hq + 2 Hkv) D][H]: wq rows, then wk rows, then wv rows
@@ -65,9 +66,10 @@ struct s2ar_ctx {
   std::vector<LayerW> slow, fast;
   float *rope_cos_s = nullptr, *rope_sin_s = nullptr, *rope_cos_f = nullptr, *rope_sin_f = nullptr;
 
-  // KV pools (bf16): slow [layers][n_pages][Hkv][page][D]; fast [layers][max_streams][Hkv][page][D]
-  uint16_t *kv_k = nullptr, *kv_v = nullptr, *fkv_k = nullptr, *fkv_v = nullptr;
-  size_t kv_layer = 0, fkv_layer = 0;
+  // KV pools (fp32 or bf16): slow [layers][n_pages][Hkv][page][D]; fast [layers][max_streams][Hkv][page][D]
+  char *kv_k = nullptr, *kv_v = nullptr, *fkv_k = nullptr, *fkv_v = nullptr;
+  size_t kv_layer = 0, fkv_layer = 0;  // bytes per layer
+  int kv_esz = 4;
   int n_pages = 0, bt_stride = 0;
   int* d_bt = nullptr;       // [max_streams][bt_stride]
   int* h_bt = nullptr;       // pinned mirror
@@ -86,14 +88,13 @@ struct s2ar_ctx {
   std::vector<char> ready;
 
   // workspace (batch row 0), every input vector zero-padded to pad_k
-  float *x = nullptr, *xf = nullptr, *qkv = nullptr, *att = nullptr, *act = nullptr;
+  float *x = nullptr, *qkv = nullptr, *att = nullptr, *act = nullptr;
+  float* xf = nullptr;  // [max_streams][pad_k(H)]: Fast residual; holds h between frames
   float *slow_logits = nullptr, *fast_logits = nullptr, *z = nullptr;
   float* am_val = nullptr;
   int* am_idx = nullptr;
-  unsigned* am_counter = nullptr;
   float *att_ml = nullptr, *att_o = nullptr;
-  unsigned* att_cnt = nullptr;
-  int max_chunks = 0;
+  int max_splits = 0;
 
   // prompt staging
   int* d_tokens = nullptr;
@@ -179,6 +180,10 @@ int validate_config(const s2ar_config* c, std::string& why) {
   }
   if (c->max_streams < 1 || c->max_streams > kMaxStreams || c->max_context < 1 || c->max_context > (1 << 20)) {
     why = "max_streams must be in [1, 256] and max_context in [1, 2^20]";
+    return -1;
+  }
+  if (c->kv_dtype != 0 && c->kv_dtype != 1) {
+    why = "kv_dtype must be 0 (fp32) or 1 (bf16)";
     return -1;
   }
   if (!(c->rope_theta > 0.0) || !(c->rms_eps >= 0.0)) {
@@ -356,6 +361,12 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
 #define C_HIP(expr) C_TRY(([&]() -> int { HIP_TRY(c, (expr)); return 0; })())
 
   C_HIP(hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking));
+  {
+    int dev = 0, cus = 0;
+    C_HIP(hipGetDevice(&dev));
+    C_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    s2k::set_device_cus(cus);
+  }
   C_HIP(hipEventCreateWithFlags(&c->ev_order, hipEventDisableTiming));
   C_HIP(hipEventCreate(&c->ev_t0));
   C_HIP(hipEventCreate(&c->ev_t1));
@@ -387,12 +398,13 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   // KV pools
   c->bt_stride = (g.max_context + kPageSize - 1) / kPageSize;
   c->n_pages = c->bt_stride * g.max_streams;
-  c->kv_layer = (size_t)c->n_pages * g.slow.n_kv_heads * kPageSize * g.slow.head_dim;
-  c->fkv_layer = (size_t)g.max_streams * g.fast.n_kv_heads * kPageSize * g.fast.head_dim;
-  C_TRY(dev_alloc(c, &c->kv_k, c->kv_layer * g.slow.n_layers * 2));
-  C_TRY(dev_alloc(c, &c->kv_v, c->kv_layer * g.slow.n_layers * 2));
-  C_TRY(dev_alloc(c, &c->fkv_k, c->fkv_layer * g.fast.n_layers * 2));
-  C_TRY(dev_alloc(c, &c->fkv_v, c->fkv_layer * g.fast.n_layers * 2));
+  c->kv_esz = g.kv_dtype == 1 ? 2 : 4;
+  c->kv_layer = (size_t)c->n_pages * g.slow.n_kv_heads * kPageSize * g.slow.head_dim * c->kv_esz;
+  c->fkv_layer = (size_t)g.max_streams * g.fast.n_kv_heads * kPageSize * g.fast.head_dim * c->kv_esz;
+  C_TRY(dev_alloc(c, &c->kv_k, c->kv_layer * g.slow.n_layers));
+  C_TRY(dev_alloc(c, &c->kv_v, c->kv_layer * g.slow.n_layers));
+  C_TRY(dev_alloc(c, &c->fkv_k, c->fkv_layer * g.fast.n_layers));
+  C_TRY(dev_alloc(c, &c->fkv_v, c->fkv_layer * g.fast.n_layers));
   C_TRY(dev_alloc(c, &c->d_bt, sizeof(int) * c->n_pages));
   C_TRY(host_alloc(c, &c->h_bt, sizeof(int) * c->n_pages));
   {
@@ -436,7 +448,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   const int qd = std::max(g.slow.n_q_heads * g.slow.head_dim, g.fast.n_q_heads * g.fast.head_dim);
   const int F = std::max(g.slow.ffn, g.fast.ffn);
   C_TRY(dev_alloc(c, &c->x, sizeof(float) * s2k::pad_k(H)));
-  C_TRY(dev_alloc(c, &c->xf, sizeof(float) * s2k::pad_k(H)));
+  C_TRY(dev_alloc(c, &c->xf, sizeof(float) * (size_t)g.max_streams * s2k::pad_k(H)));
   C_TRY(dev_alloc(c, &c->z, sizeof(float) * s2k::pad_k(H)));
   C_TRY(dev_alloc(c, &c->qkv, sizeof(float) * std::max(qkvd, qkvf)));
   C_TRY(dev_alloc(c, &c->att, sizeof(float) * s2k::pad_k(qd)));
@@ -446,13 +458,11 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   const int nb = std::max(s2k::gemv_blocks(s2k::GEMV_NORM_ARGMAX, (int)V), s2k::gemv_blocks(s2k::GEMV_NORM_ARGMAX, K));
   C_TRY(dev_alloc(c, &c->am_val, sizeof(float) * nb));
   C_TRY(dev_alloc(c, &c->am_idx, sizeof(int) * nb));
-  C_TRY(dev_alloc(c, &c->am_counter, sizeof(unsigned) * 64));
-  c->max_chunks = (g.max_context + 63) / 64;
+  c->max_splits = (g.max_context + kAttnSplit - 1) / kAttnSplit;
   const int hq = std::max(g.slow.n_q_heads, g.fast.n_q_heads);
   const int dmax = std::max(g.slow.head_dim, g.fast.head_dim);
-  C_TRY(dev_alloc(c, &c->att_ml, sizeof(float) * 2 * hq * c->max_chunks));
-  C_TRY(dev_alloc(c, &c->att_o, sizeof(float) * (size_t)hq * c->max_chunks * dmax));
-  C_TRY(dev_alloc(c, &c->att_cnt, sizeof(unsigned) * std::max(g.slow.n_kv_heads, g.fast.n_kv_heads)));
+  C_TRY(dev_alloc(c, &c->att_ml, sizeof(float) * 2 * hq * c->max_splits));
+  C_TRY(dev_alloc(c, &c->att_o, sizeof(float) * (size_t)hq * c->max_splits * dmax));
   C_TRY(dev_alloc(c, &c->d_tokens, sizeof(int) * g.max_context));
   C_TRY(dev_alloc(c, &c->d_mask, (size_t)g.max_context));
   C_TRY(dev_alloc(c, &c->d_pcodes, sizeof(int) * (size_t)g.max_context * NC));
@@ -510,9 +520,33 @@ struct Enq {
     a.am_hi = hi;
     a.am_val = c->am_val;
     a.am_idx = c->am_idx;
-    a.am_counter = c->am_counter;
-    a.am_code_out = code_out;
     chk(s2k::launch_gemv(kind, c->bf16, a, s));
+  }
+
+  float* xf_of(int slot) const { return c->xf + (size_t)slot * s2k::pad_k(c->cfg.slow.hidden); }
+
+  // pass 2 of a head's greedy pick over rows [lo, hi), then the step's bookkeeping
+  void finish(int mode, int j, int slot, int lo, int hi, float* x) {
+    const s2ar_config& g = c->cfg;
+    const int rb = s2k::argmax_block_rows();
+    s2k::FinishArgs f{};
+    f.am_val = c->am_val;
+    f.am_idx = c->am_idx;
+    f.b0 = lo / rb;
+    f.b1 = (hi - 1) / rb;
+    f.lo = lo;
+    f.mode = mode;
+    f.j = j;
+    f.codes = c->d_codes + (size_t)slot * g.n_codebooks;
+    f.snap = c->d_snap + (size_t)slot * g.n_codebooks;
+    f.pos = c->d_pos + slot;
+    f.codebook = c->codebook;
+    f.h = c->d_h + (size_t)slot * g.slow.hidden;
+    f.x = x;
+    f.H = g.slow.hidden;
+    f.K = g.codebook_size;
+    f.NC = g.n_codebooks;
+    chk(s2k::launch_finish(c->bf16, f, s));
   }
 
   // one stack of layers on the residual `x` of batch row 0 (stream slot `slot`)
@@ -539,7 +573,8 @@ struct Enq {
       a.out = c->att;
       a.part_ml = c->att_ml;
       a.part_o = c->att_o;
-      a.counters = c->att_cnt;
+      a.kv_bf16 = c->cfg.kv_dtype == 1;
+      a.split = kAttnSplit;
       if (is_slow) {
         a.rope_cos = c->rope_cos_s;
         a.rope_sin = c->rope_sin_s;
@@ -548,7 +583,7 @@ struct Enq {
         a.v_cache = c->kv_v + (size_t)l * c->kv_layer;
         a.block_table = c->d_bt;
         a.bt_stride = c->bt_stride;
-        a.max_chunks = c->max_chunks;
+        a.max_splits = c->max_splits;
       } else {
         a.rope_cos = c->rope_cos_f;
         a.rope_sin = c->rope_sin_f;
@@ -557,9 +592,10 @@ struct Enq {
         a.v_cache = c->fkv_v + (size_t)l * c->fkv_layer;
         a.block_table = c->d_fast_bt;
         a.bt_stride = 1;
-        a.max_chunks = 1;
+        a.max_splits = 1;
       }
       chk(s2k::launch_attention(a, s));
+      if (a.max_splits > 1) chk(s2k::launch_attention_combine(a, s));
       gemv(s2k::GEMV_RESID, L.wo, c->att, nullptr, x, H, qd);
       gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, x, L.mlp_norm, c->act, 2 * st.ffn, H);
       gemv(s2k::GEMV_RESID, L.wdown, c->act, nullptr, x, H, st.ffn);
@@ -568,29 +604,38 @@ struct Enq {
   }
   const int* fast_pos_ptr = nullptr;
 
-  // Slow final norm + head + constrained argmax -> codes[slot][0], h[slot]
+  // Slow final norm + head + constrained argmax -> codes[slot][0] and h[slot]; the finisher
+  // also copies h into the Fast input and advances the stream's position
   void slow_head(int slot, const TapPlan* tp) {
     const s2ar_config& g = c->cfg;
     const int H = g.slow.hidden, V = g.vocab_text + g.codebook_size;
-    gemv(s2k::GEMV_NORM_ARGMAX, c->slow_head, c->x, c->slow_final, c->slow_logits, V, H,
-         c->d_h + (size_t)slot * H, g.vocab_text, V, c->d_codes + (size_t)slot * g.n_codebooks);
+    gemv(s2k::GEMV_NORM_ARGMAX, c->slow_head, c->x, c->slow_final, c->slow_logits, V, H, c->d_h + (size_t)slot * H,
+         g.vocab_text, V);
+    finish(s2k::FIN_SLOW, 0, slot, g.vocab_text, V, xf_of(slot));
     if (tp && tp->slow_h) d2h(tp->slow_h, c->d_h + (size_t)slot * H, sizeof(float) * H);
     if (tp && tp->slow_logits) d2h(tp->slow_logits, c->slow_logits, sizeof(float) * V);
     if (tp && tp->next_c0) d2h(tp->next_c0, c->d_codes + (size_t)slot * g.n_codebooks, sizeof(int));
   }
 
-  // the 9 greedy Fast AR steps of stream `slot` on h[slot]
+  // The 9 greedy Fast AR steps of stream `slot` on h[slot] (already copied into xf by the Slow
+  // finisher).  Without taps, each step's finisher gathers the next step's input (or, after the
+  // last step, the Slow input of the frame's ten codes); with taps the inputs are gathered by
+  // separate kernels after any forced code has been written.
   void fast_loop(int slot, const TapPlan* tp) {
     const s2ar_config& g = c->cfg;
     const int H = g.fast.hidden, K = g.codebook_size, NC = g.n_codebooks, Lf = g.fast.n_layers;
     int* codes = c->d_codes + (size_t)slot * NC;
     for (int j = 1; j < NC; ++j) {
-      chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, c->d_slot_ids + slot, c->d_codes, j, c->xf,
-                                 1, s));
+      float* xf = xf_of(slot);
+      if (tp)
+        chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, c->d_slot_ids + slot, c->d_codes, j, xf,
+                                   1, s));
       fast_pos_ptr = c->d_fast_pos + (size_t)(j - 1) * g.max_streams;
-      layers(false, slot, c->xf, tp && tp->fast_resid ? tp->fast_resid + (size_t)(j - 1) * Lf * H : nullptr);
-      gemv(s2k::GEMV_NORM_ARGMAX, c->fast_head, c->xf, c->fast_final, c->fast_logits, K, H,
-           tp && tp->fast_z ? c->z : nullptr, 0, K, codes + j);
+      layers(false, slot, xf, tp && tp->fast_resid ? tp->fast_resid + (size_t)(j - 1) * Lf * H : nullptr);
+      gemv(s2k::GEMV_NORM_ARGMAX, c->fast_head, xf, c->fast_final, c->fast_logits, K, H,
+           tp && tp->fast_z ? c->z : nullptr, 0, K);
+      const int mode = tp ? s2k::FIN_CODE : (j < NC - 1 ? s2k::FIN_FAST_NEXT : s2k::FIN_FAST_LAST);
+      finish(mode, j, slot, 0, K, j < NC - 1 ? xf : c->x);
       if (tp && tp->fast_z) d2h(tp->fast_z + (size_t)(j - 1) * H, c->z, sizeof(float) * H);
       if (tp && tp->fast_logits) d2h(tp->fast_logits + (size_t)(j - 1) * K, c->fast_logits, sizeof(float) * K);
       if (tp && tp->own) d2h(tp->own + j, codes + j, sizeof(int));
@@ -598,16 +643,18 @@ struct Enq {
     }
   }
 
-  // Slow step on the frame's codes (snapshot them first), then advance the position.
+  // Slow step on the frame's codes: the input (sum of the ten codebook rows) and the snapshot
+  // of the codes come from the last Fast finisher, or from an explicit gather with taps.
   void slow_step(int slot, const TapPlan* tp) {
     const s2ar_config& g = c->cfg;
-    chk(s2k::launch_embed_codes(c->bf16, c->codebook, g.codebook_size, g.slow.hidden, g.n_codebooks,
-                                c->d_slot_ids + slot, c->d_codes, c->d_snap + (size_t)slot * g.n_codebooks, c->x,
-                                1, s));
-    if (tp && tp->embed) d2h(tp->embed, c->x, sizeof(float) * g.slow.hidden);
+    if (tp) {
+      chk(s2k::launch_embed_codes(c->bf16, c->codebook, g.codebook_size, g.slow.hidden, g.n_codebooks,
+                                  c->d_slot_ids + slot, c->d_codes, c->d_snap + (size_t)slot * g.n_codebooks, c->x,
+                                  1, s));
+      if (tp->embed) d2h(tp->embed, c->x, sizeof(float) * g.slow.hidden);
+    }
     layers(true, slot, c->x, tp ? tp->slow_resid : nullptr);
     slow_head(slot, tp);
-    chk(s2k::launch_advance(c->d_slot_ids + slot, c->d_pos, 1, s));
   }
 
   void frame(int slot, const TapPlan* tp) {
@@ -650,10 +697,12 @@ int check_streams(s2ar_ctx* c, const int32_t* ids, int32_t n, int frames) {
     if (ids[i] < 0 || ids[i] >= c->cfg.max_streams) return set_err(c, S2AR_E_RANGE, "stream id out of range");
     for (int k = 0; k < i; ++k)
       if (ids[k] == ids[i]) return set_err(c, S2AR_E_ARG, "stream ids must be distinct");
+  }
+  for (int i = 0; i < n; ++i)
     if (!c->ready[ids[i]]) return set_err(c, S2AR_E_STATE, "stream has not been prefilled");
+  for (int i = 0; i < n; ++i)
     if (c->pos[ids[i]] + frames > c->cfg.max_context)
       return set_err(c, S2AR_E_CAPACITY, "context would exceed max_context");
-  }
   int pages_needed = 0;
   for (int i = 0; i < n; ++i) {
     const int need = (c->pos[ids[i]] + frames + kPageSize - 1) / kPageSize;
@@ -767,8 +816,8 @@ int s2ar_prefill(s2ar_ctx* c, int32_t sid, const int32_t* tokens, const uint8_t*
     q.chk(s2k::launch_embed_prompt(c->bf16, c->embed, c->codebook, g.codebook_size, g.slow.hidden, NC, c->d_tokens,
                                    mask ? c->d_mask : nullptr, c->d_pcodes, p, c->x, c->stream));
     q.layers(true, sid, c->x, nullptr);
-    if (p == n - 1) q.slow_head(sid, nullptr);
-    q.chk(s2k::launch_advance(c->d_slot_ids + sid, c->d_pos, 1, c->stream));
+    if (p == n - 1) q.slow_head(sid, nullptr);  // its finisher advances the position
+    else q.chk(s2k::launch_advance(c->d_slot_ids + sid, c->d_pos, 1, c->stream));
     if (q.e != hipSuccess) break;
   }
   if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("prefill launch: ") + hipGetErrorString(q.e));

@@ -25,12 +25,10 @@ struct GemvArgs {
   float* y;               // output (see GemvKind)
   float* xnorm_out;       // optional: normalised input written by block 0 ([K])
   int N, K;
-  // greedy pick (GEMV_NORM_ARGMAX)
+  // greedy pick, first pass (GEMV_NORM_ARGMAX): per-block maximum over rows in [lo, hi)
   int am_lo, am_hi;
-  float* am_val;          // [n_blocks] per-block maxima
+  float* am_val;          // [n_blocks] per-block maxima (-inf for blocks outside the range)
   int* am_idx;            // [n_blocks] per-block arg maxima
-  unsigned* am_counter;   // zero between launches; reset by the last block
-  int* am_code_out;       // receives (argmax - am_lo)
 };
 
 // Number of workgroups a GEMV launch of this shape uses (sizes argmax partials).
@@ -45,20 +43,46 @@ struct AttnArgs {
   const float* rope_sin;
   const int* slots;        // [M] stream slot of each batch row
   const int* pos;          // [slots] position of the new token (context = pos + 1)
-  uint16_t* k_cache;       // [pages][Hkv][page_size][D] bf16 bits (one layer)
-  uint16_t* v_cache;
+  void* k_cache;           // [pages][Hkv][page_size][D], fp32 or bf16 bits (one layer)
+  void* v_cache;
+  int kv_bf16;             // 1: caches hold bf16, 0: fp32
   const int* block_table;  // [slots][bt_stride]
   int bt_stride;
   float* out;              // [M][Hq D]
-  float* part_ml;          // [M][Hq][max_chunks][2] running (max, sum) per chunk
-  float* part_o;           // [M][Hq][max_chunks][D]
-  unsigned* counters;      // [M][Hkv], zero between launches
-  int max_chunks;          // grid extent along the context (chunks of 64 positions)
+  float* part_ml;          // [M][Hq][max_splits][2]: running max and sum of one context split
+  float* part_o;           // [M][Hq][max_splits][D]: unnormalised output of one split
+  int max_splits;          // grid extent along the context
+  int split;               // positions per split (multiple of 64)
   int M, Hq, Hkv, D, page_size;
   float eps;
   float scale;             // 1 / sqrt(D), applied to q after RoPE
 };
+// Attention of the new position over its context; a context longer than `split` is cut into
+// splits whose partial results launch_attention_combine merges (needed only when
+// max_splits > 1; it does nothing for contexts that fit one split).
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s);
+
+// Second pass of the greedy pick over per-block maxima of blocks [b0, b1] (ties to the lowest
+// index), followed by the step's bookkeeping (see FinishMode).
+enum FinishMode : int { FIN_CODE = 0, FIN_FAST_NEXT = 1, FIN_FAST_LAST = 2, FIN_SLOW = 3 };
+struct FinishArgs {
+  const float* am_val;
+  const int* am_idx;
+  int b0, b1, lo;
+  int mode;
+  int j;                 // index of the code being picked in codes[]
+  int* codes;            // [n_codebooks] codes of the stream's current frame
+  int* snap;             // FIN_FAST_LAST: copy of the finished frame's codes
+  int* pos;              // FIN_SLOW: the stream's Slow position
+  const void* codebook;  // [NC][K][H] (bf16 bits or fp32)
+  const float* h;        // FIN_SLOW: the final-normed Slow hidden
+  float* x;              // next input vector [H]
+  int H, K, NC;
+};
+hipError_t launch_finish(bool bf16, const FinishArgs& f, hipStream_t s);
+void set_device_cus(int n);
+int argmax_block_rows();
 
 // x[b] = sum_k codebook[k][codes[slot][k]] (fp32, k ascending); codes_snap[b] = codes[slot].
 hipError_t launch_embed_codes(bool bf16, const void* codebook, int K, int H, int NC, const int* slots,

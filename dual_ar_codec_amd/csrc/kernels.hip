@@ -20,6 +20,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
+
 namespace s2k {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -96,7 +98,6 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
   constexpr bool NORM = KIND != GEMV_RESID;
   __shared__ float red[GEMV_WAVES];
   __shared__ int bidx[GEMV_WAVES];
-  __shared__ int s_last;
 
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
         const float gt = acc[r];
         a.y[(row0 + r) >> 1] = gt / (1.0f + expf(-gt)) * acc[r + 1];
       }
-  } else {  // GEMV_NORM_ARGMAX
+  } else {  // GEMV_NORM_ARGMAX: logits, then this block's (max, argmax) over rows in [lo, hi)
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (lane == r && row0 + r < a.N) a.y[row0 + r] = acc[r];
@@ -250,50 +251,242 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
         }
       a.am_val[blockIdx.x] = v;
       a.am_idx[blockIdx.x] = i;
-      __threadfence();
-      const unsigned t = atomicAdd(a.am_counter, 1u);
-      s_last = (t == gridDim.x - 1);
+    }
+  }
+}
+
+int argmax_block_rows() { return GEMV_WAVES * rows_per_wave(GEMV_NORM_ARGMAX); }
+
+// Second pass of the greedy pick plus the bookkeeping that follows it (one block of 256):
+//   FIN_CODE:      codes[j] = pick
+//   FIN_FAST_NEXT: codes[j] = pick; x = codebook[j][pick]           (input of Fast step j+1)
+//   FIN_FAST_LAST: codes[j] = pick; x = sum_k codebook[k][codes[k]] (Slow input, k ascending),
+//                  snap = codes
+//   FIN_SLOW:      codes[0] = pick; x = h (input of Fast step 1); pos += 1
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_finish(const FinishArgs f) {
+  __shared__ float red[4];
+  __shared__ int bidx[4];
+  __shared__ int s_code;
+  const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
+  float v = -INFINITY;
+  int i = INT_MAX;
+  for (int b = f.b0 + threadIdx.x; b <= f.b1; b += 256) {
+    const float pv = f.am_val[b];
+    const int pi = f.am_idx[b];
+    if (pv > v || (pv == v && pi < i)) {
+      v = pv;
+      i = pi;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, WAVE);
+    const int oi = __shfl_xor(i, o, WAVE);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+  if (lane == 0) {
+    red[wid] = v;
+    bidx[wid] = i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    v = red[0];
+    i = bidx[0];
+    for (int w = 1; w < 4; ++w)
+      if (red[w] > v || (red[w] == v && bidx[w] < i)) {
+        v = red[w];
+        i = bidx[w];
+      }
+    s_code = (i == INT_MAX) ? 0 : i - f.lo;  // all-NaN logits: code 0 (the debug path flags it)
+  }
+  __syncthreads();
+  // every block found the same pick; block b handles elements [256 b, 256 b + 256) of the next
+  // input, block 0 the scalar bookkeeping (read before written: codes[j] is not read below)
+  const int code = s_code;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (f.mode == FIN_FAST_NEXT) {
+    if (e < f.H) f.x[e] = load_w<BF16>(f.codebook, ((size_t)f.j * f.K + code) * f.H + e);
+  } else if (f.mode == FIN_FAST_LAST) {
+    if (e < f.H) {
+      float acc = 0.f;
+      for (int k = 0; k < f.NC; ++k) {
+        const int ck = (k == f.j) ? code : f.codes[k];
+        acc += load_w<BF16>(f.codebook, ((size_t)k * f.K + ck) * f.H + e);
+      }
+      f.x[e] = acc;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < f.NC) f.snap[threadIdx.x] = (threadIdx.x == f.j) ? code : f.codes[threadIdx.x];
+  } else if (f.mode == FIN_SLOW) {
+    if (e < f.H) f.x[e] = f.h[e];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    f.codes[f.j] = code;
+    if (f.mode == FIN_SLOW) f.pos[0] += 1;
+  }
+}
+
+hipError_t launch_finish(bool bf16, const FinishArgs& f, hipStream_t s) {
+  const dim3 grid(f.mode == FIN_CODE ? 1 : (f.H + 255) / 256);
+  if (bf16) hipLaunchKernelGGL(k_finish<true>, grid, dim3(256), 0, s, f);
+  else hipLaunchKernelGGL(k_finish<false>, grid, dim3(256), 0, s, f);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Grid-stride weight-streaming GEMV.  A tile is WPB wavefronts x R rows; block b walks tiles
+// b, b + grid, ...  The next tile's weights are issued before the current tile is reduced
+// (register double buffer), and the input is staged in LDS once per block.  The greedy-pick
+// kind leaves one (max, argmax) per block, over all the rows the block visited.
+template <bool BF16, int NCH, int KIND, int R, int WPB>
+__global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
+  extern __shared__ float xs[];
+  constexpr int EPC = BF16 ? 8 : 4;
+  constexpr int NT = WPB * WAVE;
+  constexpr int K = NCH * WAVE * EPC;
+  constexpr int XL = (K + NT * 4 - 1) / (NT * 4);
+  constexpr bool NORM = KIND != GEMV_RESID;
+  constexpr int RPT = WPB * R;
+  __shared__ float red[WPB];
+  __shared__ int bidx[WPB];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wid = threadIdx.x / WAVE;
+  const int n_tiles = (a.N + RPT - 1) / RPT;
+  int tile = blockIdx.x;
+  if (tile >= n_tiles) return;
+  constexpr size_t row_bytes = (size_t)K * (BF16 ? 2 : 4);
+
+  f32x4 xv[XL], gv[XL];
+#pragma unroll
+  for (int t = 0; t < XL; ++t) {
+    const int k = (t * NT + threadIdx.x) * 4;
+    if (XL * NT * 4 == K || k < K) {
+      xv[t] = *reinterpret_cast<const f32x4*>(a.x + k);
+      if constexpr (NORM) gv[t] = *reinterpret_cast<const f32x4*>(a.gain + k);
+    }
+  }
+  u32x4 wa[R][NCH], wb[R][NCH];
+  auto issue = [&](u32x4 (&wv)[R][NCH], int tl) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(tl * RPT + wid * R + r, a.N - 1);
+      const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.w) + (size_t)row * row_bytes);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) wv[r][c] = __builtin_nontemporal_load(wp + c * WAVE + lane);
+    }
+  };
+  issue(wa, tile);
+  __builtin_amdgcn_sched_barrier(0);
+
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < XL; ++t) {
+    const int k = (t * NT + threadIdx.x) * 4;
+    if (XL * NT * 4 == K || k < K) {
+      *reinterpret_cast<f32x4*>(xs + k) = xv[t];
+      ss = fmaf(xv[t].x, xv[t].x, ss);
+      ss = fmaf(xv[t].y, xv[t].y, ss);
+      ss = fmaf(xv[t].z, xv[t].z, ss);
+      ss = fmaf(xv[t].w, xv[t].w, ss);
+    }
+  }
+  if constexpr (NORM) {
+    ss = wave_sum(ss);
+    if (lane == 0) red[wid] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) tot += red[w];
+    const float scale = rsqrtf(tot / (float)K + a.eps);
+    const bool keep = blockIdx.x == 0 && a.xnorm_out != nullptr;
+#pragma unroll
+    for (int t = 0; t < XL; ++t) {
+      const int k = (t * NT + threadIdx.x) * 4;
+      if (XL * NT * 4 == K || k < K) {
+        f32x4 v = xv[t];
+        v.x = v.x * scale * gv[t].x;
+        v.y = v.y * scale * gv[t].y;
+        v.z = v.z * scale * gv[t].z;
+        v.w = v.w * scale * gv[t].w;
+        *reinterpret_cast<f32x4*>(xs + k) = v;
+        if (keep) *reinterpret_cast<f32x4*>(a.xnorm_out + k) = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  auto process = [&](u32x4 (&wv)[R][NCH], int tl) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const float* xp = xs + (c * WAVE + lane) * EPC;
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = dot_chunk<BF16>(wv[r][c], xp, acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+    const int row0 = tl * RPT + wid * R;
+    if constexpr (KIND == GEMV_NORM_STORE) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane == r && row0 + r < a.N) a.y[row0 + r] = acc[r];
+    } else if constexpr (KIND == GEMV_RESID) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane == r && row0 + r < a.N) a.y[row0 + r] += acc[r];
+    } else if constexpr (KIND == GEMV_NORM_SWIGLU) {
+#pragma unroll
+      for (int r = 0; r < R; r += 2)
+        if (lane == r && row0 + r + 1 < a.N) {
+          const float gt = acc[r];
+          a.y[(row0 + r) >> 1] = gt / (1.0f + expf(-gt)) * acc[r + 1];
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        if (lane == r && row < a.N) a.y[row] = acc[r];
+        if (row >= a.am_lo && row < a.am_hi && row < a.N && acc[r] > bv) {
+          bv = acc[r];
+          bi = row;
+        }
+      }
+    }
+  };
+  while (true) {
+    const int t1 = tile + gridDim.x;
+    if (t1 < n_tiles) issue(wb, t1);
+    process(wa, tile);
+    if (t1 >= n_tiles) break;
+    const int t2 = t1 + gridDim.x;
+    if (t2 < n_tiles) issue(wa, t2);
+    process(wb, t1);
+    if (t2 >= n_tiles) break;
+    tile = t2;
+  }
+  if constexpr (KIND == GEMV_NORM_ARGMAX) {
+    if (lane == 0) {
+      red[wid] = bv;
+      bidx[wid] = bi;
     }
     __syncthreads();
-    if (s_last) {  // second pass: the last workgroup reduces the per-block picks
-      __threadfence();
-      constexpr int RB = GEMV_WAVES * R;
-      const int b0 = a.am_lo / RB, b1 = (a.am_hi - 1) / RB;
-      float v = -INFINITY;
-      int i = INT_MAX;
-      for (int b = b0 + threadIdx.x; b <= b1; b += GEMV_THREADS) {
-        const float pv = __hip_atomic_load(a.am_val + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int pi = __hip_atomic_load(a.am_idx + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (pv > v || (pv == v && pi < i)) {
-          v = pv;
-          i = pi;
+    if (threadIdx.x == 0) {
+      float v = red[0];
+      int i = bidx[0];
+      for (int w = 1; w < WPB; ++w)
+        if (red[w] > v || (red[w] == v && bidx[w] < i)) {
+          v = red[w];
+          i = bidx[w];
         }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(v, o, WAVE);
-        const int oi = __shfl_xor(i, o, WAVE);
-        if (ov > v || (ov == v && oi < i)) {
-          v = ov;
-          i = oi;
-        }
-      }
-      if (lane == 0) {
-        red[wid] = v;
-        bidx[wid] = i;
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        v = red[0];
-        i = bidx[0];
-        for (int w = 1; w < GEMV_WAVES; ++w)
-          if (red[w] > v || (red[w] == v && bidx[w] < i)) {
-            v = red[w];
-            i = bidx[w];
-          }
-        *a.am_code_out = (i == INT_MAX) ? 0 : i - a.am_lo;
-        *a.am_counter = 0u;
-      }
+      a.am_val[blockIdx.x] = v;
+      a.am_idx[blockIdx.x] = i;
     }
   }
 }
@@ -333,7 +526,26 @@ static hipError_t gemv_dispatch(const GemvArgs& a, hipStream_t s) {
 #undef S2_NCH
 }
 
+static int g_cus = 256;
+void set_device_cus(int n) { g_cus = n > 0 ? n : 256; }
+
+// Launch shapes of the grid-stride kernel, picked per matrix shape by a sweep on MI355X.
+template <int NCH, int KIND, int R, int WPB>
+static hipError_t gemv2_launch(const GemvArgs& a, int blocks_per_cu, hipStream_t s) {
+  const int tiles = (a.N + R * WPB - 1) / (R * WPB);
+  const int grid = std::min(tiles, g_cus * blocks_per_cu);
+  hipLaunchKernelGGL((k_gemv2<true, NCH, KIND, R, WPB>), dim3(grid), dim3(WPB * WAVE), (size_t)pad_k(a.K) * 4, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s) {
+  if (bf16 && a.K % (WAVE * 8) == 0) {
+    const int nch = a.K / (WAVE * 8);
+    if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch<5, GEMV_NORM_STORE, 1, 4>(a, 2, s);
+    if (kind == GEMV_RESID && nch == 8) return gemv2_launch<8, GEMV_RESID, 1, 2>(a, 4, s);
+    if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch<5, GEMV_NORM_SWIGLU, 2, 4>(a, 2, s);
+    if (kind == GEMV_RESID && nch == 19) return gemv2_launch<19, GEMV_RESID, 1, 2>(a, 2, s);
+  }
   switch (kind) {
     case GEMV_NORM_STORE: return bf16 ? gemv_dispatch<true, GEMV_NORM_STORE>(a, s) : gemv_dispatch<false, GEMV_NORM_STORE>(a, s);
     case GEMV_RESID: return bf16 ? gemv_dispatch<true, GEMV_RESID>(a, s) : gemv_dispatch<false, GEMV_RESID>(a, s);
@@ -344,199 +556,259 @@ hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode attention.  grid = (max_chunks, Hkv, M), block = G wavefronts (G = Hq / Hkv).
-template <int D, int G>
+// Decode attention.  grid = (max_splits, Hkv, M), block = G wavefronts (G = Hq / Hkv), one per
+// q head of the KV group.  A block walks its split in chunks of 64 positions (one per lane):
+// the chunk's K rows are staged in LDS, scores use the lane's row, the running softmax is
+// rescaled per chunk, and V rows are read straight from the cache in the weighted sum.
+
+template <bool KVB>
+struct KvT;
+template <>
+struct KvT<true> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float ld(const T* p, size_t i) { return bf_one(p[i]); }
+  static __device__ __forceinline__ T cvt(float f) { return f2bf(f); }
+  static __device__ __forceinline__ float round(float f) { return bf_one(f2bf(f)); }
+};
+template <>
+struct KvT<false> {
+  using T = float;
+  static __device__ __forceinline__ float ld(const T* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ T cvt(float f) { return f; }
+  static __device__ __forceinline__ float round(float f) { return f; }
+};
+
+// rotate-half RoPE of one head held as PER values per lane (element d = lane + 64 i); the
+// partner of element d is d +- D/2: the same lane when D = 128, lane ^ 32 when D = 64
+template <int D>
+__device__ __forceinline__ void rope_lane(float (&v)[D / WAVE], const float* crow, const float* srow, int lane) {
+  if constexpr (D == 128) {
+    const float cs = crow[lane], sn = srow[lane];
+    const float x0 = v[0], x1 = v[1];
+    v[0] = x0 * cs - x1 * sn;
+    v[1] = x1 * cs + x0 * sn;
+  } else {
+    const int i = lane & 31;
+    const float cs = crow[i], sn = srow[i];
+    const float partner = __shfl_xor(v[0], 32, WAVE);
+    v[0] = lane < 32 ? v[0] * cs - partner * sn : v[0] * cs + partner * sn;
+  }
+}
+
+template <int D, int G, bool KVB>
 __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
-  constexpr int CH = WAVE;     // positions per chunk: one per lane
-  constexpr int KSTR = D + 2;  // padded row stride of the K tile (bf16 elements)
+  using KV = KvT<KVB>;
+  using T = typename KV::T;
+  constexpr int CH = WAVE;                   // positions per chunk, one per lane in the scores
+  constexpr int NT = G * WAVE;               // threads
+  constexpr int KSTR = KVB ? D + 2 : D + 1;  // padded K row: consecutive lanes hit consecutive banks
   constexpr int PER = D / WAVE;
-  constexpr int HD = D / 2;
-  constexpr int CPR = D * 2 / 16;  // 16-byte pieces per cached row
+  constexpr int EP16 = 16 / sizeof(T);       // elements per 16-byte piece
+  constexpr int CPR = D / EP16;              // 16-byte pieces per row
+  constexpr int PIECES = CH * CPR / NT;      // K (and V) pieces per thread per chunk
+  constexpr int MAXSPLIT = 256;
+  static_assert(CH * CPR % NT == 0, "tile pieces must divide evenly");
   __shared__ float q_s[G][D];
   __shared__ float kn_s[D];
   __shared__ float vn_s[D];
-  __shared__ __attribute__((aligned(16))) uint16_t k_s[CH * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t v_s[CH * D];
+  __shared__ __attribute__((aligned(16))) T k_s[CH * KSTR];
+  __shared__ __attribute__((aligned(16))) T v_s[CH * D];
   __shared__ float p_s[G][CH];
-  __shared__ int s_last;
+  __shared__ int rowoff_s[MAXSPLIT];
 
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
   const int slot = a.slots[b];
   const int pos = a.pos[slot];
   const int ctx = pos + 1;
-  const int nch = (ctx + CH - 1) / CH;
-  if (c >= nch) return;
-  const int j0 = c * CH;
-  const int nvalid = min(CH, ctx - j0);
-  const bool has_new = pos >= j0 && pos < j0 + CH;
+  const int nsplit = (ctx + a.split - 1) / a.split;
+  if (sp >= nsplit) return;
+  const int s0 = sp * a.split, s1 = min(s0 + a.split, ctx);
+  const bool has_new = pos >= s0 && pos < s1;
   const int h = g * G + w;
   const float* qkv = a.qkv + (size_t)b * (a.Hq + 2 * a.Hkv) * D;
-  const float* crow = a.rope_cos + (size_t)pos * HD;
-  const float* srow = a.rope_sin + (size_t)pos * HD;
+  T* kc = static_cast<T*>(a.k_cache);
+  T* vc = static_cast<T*>(a.v_cache);
 
-  // per-head RMSNorm of q (and of the new k), then rotate-half RoPE at pos
-  {
-    float qv[PER], ss = 0.f;
+  // cache offsets of every position of the split: one page-table round trip
+  for (int t = threadIdx.x; t < s1 - s0; t += NT) {
+    const int jj = s0 + t;
+    const int page = a.block_table[slot * a.bt_stride + jj / a.page_size];
+    rowoff_s[t] = (int)((((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
+  }
+  // this wave's q head (and, for wave 0 of the split holding pos, the new k and v)
+  float qv[PER], kv[PER], vv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) qv[i] = qkv[h * D + lane + i * WAVE];
+  const bool mk = has_new && w == 0;
+  if (mk) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      qv[i] = qkv[h * D + lane + i * WAVE];
-      ss = fmaf(qv[i], qv[i], ss);
+      kv[i] = qkv[(size_t)(a.Hq + g) * D + lane + i * WAVE];
+      vv[i] = qkv[(size_t)(a.Hq + a.Hkv + g) * D + lane + i * WAVE];
     }
-    ss = wave_sum(ss);
-    const float r = rsqrtf(ss / (float)D + a.eps);
+  }
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.f, o_run[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) q_s[w][lane + i * WAVE] = qv[i] * r * a.q_norm[lane + i * WAVE];
-    if (has_new && w == 0) {
-      const float* kp = qkv + (size_t)(a.Hq + g) * D;
-      const float* vp = qkv + (size_t)(a.Hq + a.Hkv + g) * D;
-      float kv[PER];
-      ss = 0.f;
+  for (int i = 0; i < PER; ++i) o_run[i] = 0.f;
+  for (int j0 = s0; j0 < s1; j0 += CH) {
+    const int nv = min(CH, s1 - j0);
+    const int jn = has_new ? pos - j0 : -1;  // row of the new position in this chunk (if any)
+    // issue the chunk's K and V loads
+    u32x4 kt[PIECES], vt[PIECES];
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int pi = threadIdx.x + u * NT, j = pi / CPR, q = pi % CPR;
+      if (j < nv && j != jn) {
+        const int off = rowoff_s[j0 - s0 + j] + q * EP16;
+        kt[u] = *reinterpret_cast<const u32x4*>(kc + off);
+        vt[u] = *reinterpret_cast<const u32x4*>(vc + off);
+      }
+    }
+    if (j0 == s0) {  // QK-norm and RoPE while the tile is in flight
+      const float* crow = a.rope_cos + (size_t)pos * (D / 2);
+      const float* srow = a.rope_sin + (size_t)pos * (D / 2);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ss = fmaf(qv[i], qv[i], ss);
+      const float r = rsqrtf(wave_sum(ss) / (float)D + a.eps);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) qv[i] = qv[i] * r * a.q_norm[lane + i * WAVE];
+      rope_lane<D>(qv, crow, srow, lane);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) q_s[w][lane + i * WAVE] = qv[i] * a.scale;
+      if (mk) {
+        ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ss = fmaf(kv[i], kv[i], ss);
+        const float rk = rsqrtf(wave_sum(ss) / (float)D + a.eps);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) kv[i] = kv[i] * rk * a.k_norm[lane + i * WAVE];
+        rope_lane<D>(kv, crow, srow, lane);
+        const int page = a.block_table[slot * a.bt_stride + pos / a.page_size];
+        const size_t off = (((size_t)page * a.Hkv + g) * a.page_size + pos % a.page_size) * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int d = lane + i * WAVE;
+          kn_s[d] = KV::round(kv[i]);
+          vn_s[d] = KV::round(vv[i]);
+          kc[off + d] = KV::cvt(kv[i]);  // append the new position to the paged cache
+          vc[off + d] = KV::cvt(vv[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int pi = threadIdx.x + u * NT, j = pi / CPR, q = pi % CPR;
+      if (j < nv && j != jn) {
+        uint32_t* kd = reinterpret_cast<uint32_t*>(k_s + j * KSTR + q * EP16);
+        kd[0] = kt[u].x;
+        kd[1] = kt[u].y;
+        kd[2] = kt[u].z;
+        kd[3] = kt[u].w;
+        *reinterpret_cast<u32x4*>(v_s + j * D + q * EP16) = vt[u];
+      }
+    }
+    if (mk && jn >= 0 && jn < nv)
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        kv[i] = kp[lane + i * WAVE];
-        ss = fmaf(kv[i], kv[i], ss);
-        vn_s[lane + i * WAVE] = vp[lane + i * WAVE];
+        const int d = lane + i * WAVE;
+        k_s[jn * KSTR + d] = KV::cvt(kn_s[d]);
+        v_s[jn * D + d] = KV::cvt(vn_s[d]);
       }
-      ss = wave_sum(ss);
-      const float rk = rsqrtf(ss / (float)D + a.eps);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) kn_s[lane + i * WAVE] = kv[i] * rk * a.k_norm[lane + i * WAVE];
-    }
-  }
-  __syncthreads();
-  for (int i = lane; i < HD; i += WAVE) {
-    const float cs = crow[i], sn = srow[i];
-    const float x0 = q_s[w][i], x1 = q_s[w][i + HD];
-    q_s[w][i] = (x0 * cs - x1 * sn) * a.scale;
-    q_s[w][i + HD] = (x1 * cs + x0 * sn) * a.scale;
-    if (has_new && w == 0) {
-      const float k0 = kn_s[i], k1 = kn_s[i + HD];
-      kn_s[i] = k0 * cs - k1 * sn;
-      kn_s[i + HD] = k1 * cs + k0 * sn;
-    }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // stage the chunk's cached K/V rows (the new position comes from registers)
-  for (int i = threadIdx.x; i < CH * CPR; i += G * WAVE) {
-    const int j = i / CPR, q = i % CPR;
-    const int jj = j0 + j;
-    if (j < nvalid && jj != pos) {
-      const int page = a.block_table[slot * a.bt_stride + jj / a.page_size];
-      const size_t off = (((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D + q * 8;
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k_cache + off);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(a.v_cache + off);
-      uint32_t* kd = reinterpret_cast<uint32_t*>(k_s + j * KSTR + q * 8);
-      kd[0] = kv.x;
-      kd[1] = kv.y;
-      kd[2] = kv.z;
-      kd[3] = kv.w;
-      *reinterpret_cast<u32x4*>(v_s + j * D + q * 8) = vv;
+    float s = -INFINITY;
+    if (lane < nv) {
+      const T* kr = k_s + lane * KSTR;
+      float acc = 0.f;
+#pragma unroll 16
+      for (int d = 0; d < D; ++d) acc = fmaf(q_s[w][d], KV::ld(kr, d), acc);
+      s = acc;
     }
-  }
-  if (has_new && w == 0) {
-    const int jn = pos - j0;
-    const int page = a.block_table[slot * a.bt_stride + pos / a.page_size];
-    const size_t off = (((size_t)page * a.Hkv + g) * a.page_size + pos % a.page_size) * D;
+    const float m_new = fmaxf(m_run, wave_max(s));
+    const float p = (lane < nv) ? expf(s - m_new) : 0.f;
+    const float corr = expf(m_run - m_new);
+    l_run = l_run * corr + wave_sum(p);
+    p_s[w][lane] = p;
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int d = lane + i * WAVE;
-      const uint16_t kb = f2bf(kn_s[d]), vb = f2bf(vn_s[d]);
-      k_s[jn * KSTR + d] = kb;
-      v_s[jn * D + d] = vb;
-      a.k_cache[off + d] = kb;
-      a.v_cache[off + d] = vb;
-    }
-  }
-  __syncthreads();
-
-  // scores: lane = position, wavefront = q head
-  float s = -INFINITY;
-  if (lane < nvalid) {
-    const uint16_t* kr = k_s + lane * KSTR;
-    float acc = 0.f;
+    for (int i = 0; i < PER; ++i) o_run[i] *= corr;
 #pragma unroll 8
-    for (int d = 0; d < D; d += 2) {
-      const uint32_t kk = *reinterpret_cast<const uint32_t*>(kr + d);
-      acc = fmaf(q_s[w][d], bf_lo(kk), acc);
-      acc = fmaf(q_s[w][d + 1], bf_hi(kk), acc);
+    for (int j = 0; j < nv; ++j) {
+      const float pj = p_s[w][j];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o_run[i] = fmaf(pj, KV::ld(v_s, (size_t)j * D + lane + i * WAVE), o_run[i]);
     }
-    s = acc;
-  }
-  const float m = wave_max(s);
-  const float p = (lane < nvalid) ? expf(s - m) : 0.f;
-  const float l = wave_sum(p);
-  p_s[w][lane] = p;
-  __syncthreads();
-  float o[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  for (int j = 0; j < nvalid; ++j) {
-    const float pj = p_s[w][j];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = fmaf(pj, bf_one(v_s[j * D + lane + i * WAVE]), o[i]);
+    m_run = m_new;
+    __syncthreads();
   }
 
-  float* out = a.out + ((size_t)b * a.Hq + h) * D;
-  if (nch == 1) {
-    const float inv = 1.0f / l;
+  if (nsplit == 1) {
+    float* out = a.out + ((size_t)b * a.Hq + h) * D;
+    const float inv = 1.0f / l_run;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[lane + i * WAVE] = o[i] * inv;
+    for (int i = 0; i < PER; ++i) out[lane + i * WAVE] = o_run[i] * inv;
     return;
   }
-  const size_t pi = ((size_t)b * a.Hq + h) * a.max_chunks + c;
+  const size_t pi = ((size_t)b * a.Hq + h) * a.max_splits + sp;
   if (lane == 0) {
-    a.part_ml[pi * 2] = m;
-    a.part_ml[pi * 2 + 1] = l;
+    a.part_ml[pi * 2] = m_run;
+    a.part_ml[pi * 2 + 1] = l_run;
   }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) a.part_o[pi * D + lane + i * WAVE] = o[i];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned t = atomicAdd(a.counters + b * a.Hkv + g, 1u);
-    s_last = (t == (unsigned)nch - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // merge the chunks of q head h in chunk order
-  const size_t base = ((size_t)b * a.Hq + h) * a.max_chunks;
+  for (int i = 0; i < PER; ++i) a.part_o[pi * D + lane + i * WAVE] = o_run[i];
+}
+
+// Merge the splits of every q head in split order.  grid = (Hq, M), one wavefront each.
+template <int D>
+__global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
+  constexpr int PER = D / WAVE;
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int pos = a.pos[a.slots[b]];
+  const int nsplit = (pos + 1 + a.split - 1) / a.split;
+  if (nsplit == 1) return;  // the attention kernel wrote the output itself
+  const size_t base = ((size_t)b * a.Hq + h) * a.max_splits;
   float M = -INFINITY;
-  for (int cc = 0; cc < nch; ++cc)
-    M = fmaxf(M, __hip_atomic_load(a.part_ml + (base + cc) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  for (int c = 0; c < nsplit; ++c) M = fmaxf(M, a.part_ml[(base + c) * 2]);
   float L = 0.f, acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int cc = 0; cc < nch; ++cc) {
-    const float mc = __hip_atomic_load(a.part_ml + (base + cc) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float lc = __hip_atomic_load(a.part_ml + (base + cc) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float e = expf(mc - M);
-    L = fmaf(e, lc, L);
+  for (int c = 0; c < nsplit; ++c) {
+    const float e = expf(a.part_ml[(base + c) * 2] - M);
+    L = fmaf(e, a.part_ml[(base + c) * 2 + 1], L);
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      acc[i] = fmaf(e, __hip_atomic_load(a.part_o + (base + cc) * D + lane + i * WAVE, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT), acc[i]);
+    for (int i = 0; i < PER; ++i) acc[i] = fmaf(e, a.part_o[(base + c) * D + lane + i * WAVE], acc[i]);
   }
+  float* out = a.out + ((size_t)b * a.Hq + h) * D;
   const float inv = 1.0f / L;
 #pragma unroll
   for (int i = 0; i < PER; ++i) out[lane + i * WAVE] = acc[i] * inv;
-  if (threadIdx.x == 0) a.counters[b * a.Hkv + g] = 0u;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const dim3 grid(a.max_chunks, a.Hkv, a.M);
-#define S2_ATT(DD, GG)                                                          \
-  if (a.D == DD && G == GG) {                                                   \
-    hipLaunchKernelGGL((k_attn<DD, GG>), grid, dim3(GG * WAVE), 0, s, a);       \
-    return hipGetLastError();                                                   \
+  const dim3 grid(a.max_splits, a.Hkv, a.M);
+#define S2_ATT(DD, GG)                                                                         \
+  if (a.D == DD && G == GG) {                                                                  \
+    if (a.kv_bf16) hipLaunchKernelGGL((k_attn<DD, GG, true>), grid, dim3(GG * WAVE), 0, s, a);  \
+    else hipLaunchKernelGGL((k_attn<DD, GG, false>), grid, dim3(GG * WAVE), 0, s, a);           \
+    return hipGetLastError();                                                                  \
   }
   S2_ATT(64, 1) S2_ATT(64, 2) S2_ATT(64, 4) S2_ATT(64, 8)
   S2_ATT(128, 1) S2_ATT(128, 2) S2_ATT(128, 4) S2_ATT(128, 8)
 #undef S2_ATT
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.Hq, a.M);
+  if (a.D == 64) hipLaunchKernelGGL(k_attn_combine<64>, grid, dim3(WAVE), 0, s, a);
+  else if (a.D == 128) hipLaunchKernelGGL(k_attn_combine<128>, grid, dim3(WAVE), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -63,6 +63,7 @@ typedef struct {
   int32_t max_streams;    /* concurrent decode streams (stream ids 0..max_streams-1) */
   int32_t max_context;    /* Slow positions per stream, prompt plus frames */
   int32_t page_size;      /* KV positions per page; must be 16 */
+  int32_t kv_dtype;       /* KV cache element: 0 = fp32 (default), 1 = bf16 (half the KV bytes) */
 } s2ar_config;
 
 /* One weight tensor in host memory: fp32, or bf16 bit patterns (uint16). */

@@ -74,6 +74,12 @@ def test_full_teacher_forced_first_frames():
     assert rep["tokens_checked"] > 10
 
 
+def test_mid_bf16_kv_cache_teacher_forced():
+    """The optional bf16 KV cache (half the KV bytes) on the mid shape."""
+    rep = _teacher_forced("mid", n_frames=8, kv_dtype="bf16")
+    assert rep["tokens_checked"] > 0
+
+
 def test_vq_masked_prefill_teacher_forced():
     cfg = synth.config("mid")
     r = np.random.default_rng(5)
@@ -85,9 +91,10 @@ def test_vq_masked_prefill_teacher_forced():
     _teacher_forced("mid", n_frames=2, prompt=(toks, mask, codes))
 
 
-@pytest.mark.parametrize("n_prompt", [1, 15, 16, 17, 63, 64, 65])
-def test_page_and_chunk_boundaries(n_prompt):
-    cfg = synth.config("tiny", max_context=128)
+@pytest.mark.parametrize("n_prompt", [1, 15, 16, 17, 63, 64, 65, 255, 256, 300])
+def test_page_chunk_and_split_boundaries(n_prompt):
+    """Pages of 16, LDS chunks of 64 and attention splits of 256 positions."""
+    cfg = synth.config("tiny", max_context=320)
     w = synth.make_weights(cfg)
     toks = synth.uniform_ints(9, 77, n_prompt, 0, cfg["vocab_slow"])
     frames = oracle_run(cfg, w, toks, None, None, 3)
