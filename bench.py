@@ -61,6 +61,7 @@ def main():
     ap.add_argument("--config", default="full")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--kernel-iters", type=int, default=144)
+    ap.add_argument("--prefill", type=int, default=1, help="also time a 1200-position voice-clone prefill")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py drives one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
@@ -74,7 +75,9 @@ def main():
     torch.cuda.set_device(0)
     cfg = synth.config(args.config)
     n_prompt = synth.prompt_lengths(cfg)[0]
-    need = n_prompt + max(args.steps, args.warmup) + 1
+    vc = synth.config("voice_clone") if args.prefill else None
+    vc_len = synth.prompt_lengths(vc)[0] if vc else 0
+    need = max(n_prompt + max(args.steps, args.warmup) + 1, vc_len + 1)
     if need > cfg["max_context"]:
         cfg = synth.config(args.config, max_context=(need + 63) // 64 * 64)
     log(f"[bench] generating {cfg['name']} weights ({synth.weight_bytes(cfg) / 1e9:.2f} GB)")
@@ -82,7 +85,7 @@ def main():
     w = synth.make_weights(cfg)
     log(f"[bench] weights in {time.perf_counter() - t:.1f} s; uploading")
     toks, mask, codes = synth.make_prompt(cfg)
-    ctx = s2ar.Context(cfg, w)
+    ctx = s2ar.Context(cfg, w, max_streams=2)
     log("[bench] prefill + warmup")
     ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
     if args.warmup:
@@ -101,6 +104,27 @@ def main():
     ctx_mid = n_prompt + args.steps // 2
     fb = metrics.frame_bytes(cfg, ctx_mid)
     gbps = fb["total"] * fps / 1e9
+
+    prefill = None
+    if vc is not None:
+        # voice-clone prompt (1000 VQ positions + 200 text positions) on a second stream: the
+        # prefill's projections run as MFMA GEMMs
+        vt, vm, vcodes = synth.make_prompt(vc)
+        ctx.prefill(1, vt[:64], vm[:64], vcodes[:64])  # warm-up
+        ctx.release(1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ctx.prefill(1, vt, vm, vcodes)
+        torch.cuda.synchronize()
+        pt = time.perf_counter() - t0
+        s = cfg["slow"]
+        lin = 2.0 * vc_len * s["n_layers"] * metrics.layer_matrix_params(s)
+        att = 2.0 * 2 * s["n_layers"] * s["n_q_heads"] * s["head_dim"] * vc_len * (vc_len + 1) / 2
+        prefill = {"positions": vc_len, "ms": round(pt * 1e3, 2), "tflop": round((lin + att) / 1e12, 3),
+                   "tflop_s": round((lin + att) / pt / 1e12, 1), "peak_tflop_s": 2500.0,
+                   "mfma_frac": round((lin + att) / pt / 1e12 / 2500.0, 4),
+                   "note": "bf16 hi+lo split activations: 2 MFMA passes per algorithmic product"}
+        ctx.release(1)
 
     log("[bench] dominant kernel (fused RMSNorm + gate/up + SwiGLU GEMV)")
     ms, nbytes = ctx.time_kernel(0, args.kernel_iters)
@@ -132,6 +156,7 @@ def main():
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 

@@ -96,6 +96,14 @@ struct s2ar_ctx {
   float *att_ml = nullptr, *att_o = nullptr;
   int max_splits = 0;
 
+  // batched prefill (MFMA): chunk of up to pch prompt rows
+  int pch = 0;
+  bool mfma_prefill = false;
+  float *px = nullptr, *pqkv = nullptr, *patt = nullptr, *pact = nullptr, *prms = nullptr;
+  float *patt_ml = nullptr, *patt_o = nullptr;
+  int* d_iota = nullptr;  // [max_context] = 0, 1, 2, ...
+  int* h_pos_stage = nullptr;
+
   // prompt staging
   int* d_tokens = nullptr;
   uint8_t* d_mask = nullptr;
@@ -467,6 +475,29 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   C_TRY(dev_alloc(c, &c->d_mask, (size_t)g.max_context));
   C_TRY(dev_alloc(c, &c->d_pcodes, sizeof(int) * (size_t)g.max_context * NC));
 
+  // batched prefill on the matrix cores when the shapes allow it (bf16, N % 128, K % 32)
+  {
+    const s2ar_stack& st = g.slow;
+    const int qkvd_s = (st.n_q_heads + 2 * st.n_kv_heads) * st.head_dim, qd_s = st.n_q_heads * st.head_dim;
+    c->mfma_prefill = c->bf16 && qkvd_s % 128 == 0 && H % 128 == 0 && (2 * st.ffn) % 128 == 0 && H % 32 == 0 &&
+                      qd_s % 32 == 0 && st.ffn % 32 == 0;
+    if (c->mfma_prefill) {
+      c->pch = std::min(g.max_context, 512);
+      C_TRY(dev_alloc(c, &c->px, sizeof(float) * (size_t)c->pch * H));
+      C_TRY(dev_alloc(c, &c->pqkv, sizeof(float) * (size_t)c->pch * qkvd_s));
+      C_TRY(dev_alloc(c, &c->patt, sizeof(float) * (size_t)c->pch * qd_s));
+      C_TRY(dev_alloc(c, &c->pact, sizeof(float) * (size_t)c->pch * st.ffn));
+      C_TRY(dev_alloc(c, &c->prms, sizeof(float) * (size_t)c->pch));
+      C_TRY(dev_alloc(c, &c->patt_ml, sizeof(float) * (size_t)c->pch * st.n_q_heads * c->max_splits * 2));
+      C_TRY(dev_alloc(c, &c->patt_o, sizeof(float) * (size_t)c->pch * st.n_q_heads * c->max_splits * st.head_dim));
+      std::vector<int> iota(g.max_context);
+      for (int i = 0; i < g.max_context; ++i) iota[i] = i;
+      C_TRY(dev_alloc(c, &c->d_iota, sizeof(int) * g.max_context));
+      C_HIP(hipMemcpy(c->d_iota, iota.data(), sizeof(int) * g.max_context, hipMemcpyHostToDevice));
+    }
+  }
+  C_TRY(host_alloc(c, &c->h_pos_stage, sizeof(int) * 16));
+
   c->h_codes_frames = 64;
   C_TRY(host_alloc(c, &c->h_codes, sizeof(int) * (size_t)c->h_codes_frames * g.max_streams * NC));
   const int Lf = g.fast.n_layers;
@@ -575,6 +606,9 @@ struct Enq {
       a.part_o = c->att_o;
       a.kv_bf16 = c->cfg.kv_dtype == 1;
       a.split = kAttnSplit;
+      a.fixed_slot = -1;
+      a.row_pos = nullptr;
+      a.append = 1;
       if (is_slow) {
         a.rope_cos = c->rope_cos_s;
         a.rope_sin = c->rope_sin_s;
@@ -655,6 +689,91 @@ struct Enq {
     }
     layers(true, slot, c->x, tp ? tp->slow_resid : nullptr);
     slow_head(slot, tp);
+  }
+
+  // Prefill `rows` prompt rows (prompt indices p0.., positions pos0..) of stream `slot` on the
+  // matrix cores: every projection is one bf16 MFMA GEMM over all rows, the keys and values of
+  // the rows are appended first, then each row attends causally over the cache.
+  void prefill_rows(int slot, int p0, int pos0, int rows, bool has_mask) {
+    const s2ar_config& g = c->cfg;
+    const s2ar_stack& st = g.slow;
+    const int H = st.hidden, D = st.head_dim, qd = st.n_q_heads * D, F = st.ffn;
+    const int qkvd = (st.n_q_heads + 2 * st.n_kv_heads) * D;
+    const float eps = (float)g.rms_eps;
+    chk(s2k::launch_embed_rows(c->bf16, c->embed, c->codebook, g.codebook_size, H, g.n_codebooks, c->d_tokens,
+                               has_mask ? c->d_mask : nullptr, c->d_pcodes, p0, rows, c->px, H, s));
+    auto gemm = [&](const float* a, int lda, const float* scale, const float* gain, const void* w, float* out,
+                    int ldc, int N, int K, int epi) {
+      s2k::GemmArgs ga{};
+      ga.a = a;
+      ga.lda = lda;
+      ga.a_scale = scale;
+      ga.a_gain = gain;
+      ga.w = static_cast<const uint16_t*>(w);
+      ga.c = out;
+      ga.ldc = ldc;
+      ga.M = rows;
+      ga.N = N;
+      ga.K = K;
+      ga.epi = epi;
+      chk(s2k::launch_gemm(ga, s));
+    };
+    for (int l = 0; l < st.n_layers; ++l) {
+      const LayerW& L = c->slow[l];
+      chk(s2k::launch_row_rms(c->px, H, H, eps, c->prms, rows, s));
+      gemm(c->px, H, c->prms, L.attn_norm, L.wqkv, c->pqkv, qkvd, qkvd, H, s2k::GEMM_STORE);
+      s2k::PrefillKvArgs kv{};
+      kv.qkv = c->pqkv;
+      kv.ld = qkvd;
+      kv.k_norm = L.k_norm;
+      kv.rope_cos = c->rope_cos_s;
+      kv.rope_sin = c->rope_sin_s;
+      kv.k_cache = c->kv_k + (size_t)l * c->kv_layer;
+      kv.v_cache = c->kv_v + (size_t)l * c->kv_layer;
+      kv.kv_bf16 = g.kv_dtype == 1;
+      kv.block_table = c->d_bt + (size_t)slot * c->bt_stride;
+      kv.page_size = kPageSize;
+      kv.pos0 = pos0;
+      kv.Hq = st.n_q_heads;
+      kv.Hkv = st.n_kv_heads;
+      kv.D = D;
+      kv.eps = eps;
+      chk(s2k::launch_prefill_append(kv, rows, s));
+      s2k::AttnArgs a{};
+      a.qkv = c->pqkv;
+      a.q_norm = L.q_norm;
+      a.k_norm = L.k_norm;
+      a.rope_cos = c->rope_cos_s;
+      a.rope_sin = c->rope_sin_s;
+      a.slots = nullptr;
+      a.pos = nullptr;
+      a.k_cache = kv.k_cache;
+      a.v_cache = kv.v_cache;
+      a.kv_bf16 = kv.kv_bf16;
+      a.block_table = c->d_bt;
+      a.bt_stride = c->bt_stride;
+      a.out = c->patt;
+      a.part_ml = c->patt_ml;
+      a.part_o = c->patt_o;
+      a.max_splits = c->max_splits;
+      a.split = kAttnSplit;
+      a.M = rows;
+      a.Hq = st.n_q_heads;
+      a.Hkv = st.n_kv_heads;
+      a.D = D;
+      a.page_size = kPageSize;
+      a.eps = eps;
+      a.scale = (float)(1.0 / std::sqrt((double)D));
+      a.fixed_slot = slot;
+      a.row_pos = c->d_iota + pos0;
+      a.append = 0;
+      chk(s2k::launch_attention(a, s));
+      if (a.max_splits > 1) chk(s2k::launch_attention_combine(a, s));
+      gemm(c->patt, qd, nullptr, nullptr, L.wo, c->px, H, H, qd, s2k::GEMM_ADD);
+      chk(s2k::launch_row_rms(c->px, H, H, eps, c->prms, rows, s));
+      gemm(c->px, H, c->prms, L.mlp_norm, L.wgu, c->pact, F, 2 * F, H, s2k::GEMM_SWIGLU);
+      gemm(c->pact, F, nullptr, nullptr, L.wdown, c->px, H, H, F, s2k::GEMM_ADD);
+    }
   }
 
   void frame(int slot, const TapPlan* tp) {
@@ -812,13 +931,28 @@ int s2ar_prefill(s2ar_ctx* c, int32_t sid, const int32_t* tokens, const uint8_t*
     HIP_TRY(c, hipMemcpyAsync(c->d_pcodes, codes, sizeof(int) * (size_t)n * NC, hipMemcpyHostToDevice, c->stream));
   }
   Enq q{c, c->stream};
-  for (int p = 0; p < n; ++p) {
-    q.chk(s2k::launch_embed_prompt(c->bf16, c->embed, c->codebook, g.codebook_size, g.slow.hidden, NC, c->d_tokens,
-                                   mask ? c->d_mask : nullptr, c->d_pcodes, p, c->x, c->stream));
-    q.layers(true, sid, c->x, nullptr);
-    if (p == n - 1) q.slow_head(sid, nullptr);  // its finisher advances the position
-    else q.chk(s2k::launch_advance(c->d_slot_ids + sid, c->d_pos, 1, c->stream));
-    if (q.e != hipSuccess) break;
+  if (c->mfma_prefill && n >= 2) {
+    const int H = g.slow.hidden;
+    for (int p0 = 0; p0 < n && q.e == hipSuccess; p0 += c->pch) {
+      const int rows = std::min(c->pch, n - p0);
+      q.prefill_rows(sid, p0, c->pos[sid] + p0, rows, mask != nullptr);
+      if (p0 + rows == n) {  // the last row goes through the Slow head
+        q.chk(hipMemcpyAsync(c->x, c->px + (size_t)(rows - 1) * H, sizeof(float) * H, hipMemcpyDeviceToDevice,
+                             c->stream));
+        c->h_pos_stage[0] = c->pos[sid] + n - 1;  // the finisher advances it to pos + n
+        q.chk(hipMemcpyAsync(c->d_pos + sid, c->h_pos_stage, sizeof(int), hipMemcpyHostToDevice, c->stream));
+        q.slow_head(sid, nullptr);
+      }
+    }
+  } else {
+    for (int p = 0; p < n; ++p) {
+      q.chk(s2k::launch_embed_prompt(c->bf16, c->embed, c->codebook, g.codebook_size, g.slow.hidden, NC,
+                                     c->d_tokens, mask ? c->d_mask : nullptr, c->d_pcodes, p, c->x, c->stream));
+      q.layers(true, sid, c->x, nullptr);
+      if (p == n - 1) q.slow_head(sid, nullptr);  // its finisher advances the position
+      else q.chk(s2k::launch_advance(c->d_slot_ids + sid, c->d_pos, 1, c->stream));
+      if (q.e != hipSuccess) break;
+    }
   }
   if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("prefill launch: ") + hipGetErrorString(q.e));
   HIP_TRY(c, hipStreamSynchronize(c->stream));

@@ -56,6 +56,11 @@ struct AttnArgs {
   int M, Hq, Hkv, D, page_size;
   float eps;
   float scale;             // 1 / sqrt(D), applied to q after RoPE
+  // prompt rows (prefill): every batch row belongs to stream `fixed_slot` (>= 0) and sits at
+  // position row_pos[b]; with append == 0 the rows' keys and values are already in the cache
+  int fixed_slot;
+  const int* row_pos;
+  int append;
 };
 // Attention of the new position over its context; a context longer than `split` is cut into
 // splits whose partial results launch_attention_combine merges (needed only when
@@ -82,6 +87,46 @@ struct FinishArgs {
 };
 hipError_t launch_finish(bool bf16, const FinishArgs& f, hipStream_t s);
 void set_device_cus(int n);
+int device_cus();
+
+// ---- prefill (prefill.hip) ----
+enum GemmEpi : int { GEMM_STORE = 0, GEMM_ADD = 1, GEMM_SWIGLU = 2 };
+// C[M][N] (=, +=) bf16(A[M][K] * a_scale[m] * a_gain[k]) . W[N][K]^T with fp32 accumulation on the
+// matrix cores.  GEMM_SWIGLU: W rows (2i, 2i+1) = (gate_i, up_i); C[m][i] = silu(gate) * up.
+// Requires N % 128 == 0, K % 32 == 0, lda % 4 == 0.
+struct GemmArgs {
+  const float* a;          // [M][lda] fp32 activations
+  int lda;
+  const float* a_scale;    // [M] RMSNorm row scale or nullptr
+  const float* a_gain;     // [K] RMSNorm gain or nullptr
+  const uint16_t* w;       // [N][K] bf16 weights
+  float* c;                // [M][ldc]
+  int ldc;
+  int M, N, K;
+  int epi;
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+hipError_t launch_row_rms(const float* x, int ld, int H, float eps, float* scale, int M, hipStream_t s);
+
+struct PrefillKvArgs {
+  const float* qkv;        // [rows][ld] projections of the prompt rows
+  int ld;
+  const float* k_norm;
+  const float* rope_cos;
+  const float* rope_sin;
+  void* k_cache;           // one layer of the paged pool
+  void* v_cache;
+  int kv_bf16;
+  const int* block_table;  // the stream's row of the block table
+  int page_size;
+  int pos0;                // position of row 0
+  int Hq, Hkv, D;
+  float eps;
+};
+hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s);
+hipError_t launch_embed_rows(bool bf16, const void* emb, const void* cb, int K, int H, int NC, const int* tokens,
+                             const uint8_t* mask, const int* codes, int p0, int rows, float* x, int ldx,
+                             hipStream_t s);
 int argmax_block_rows();
 
 // x[b] = sum_k codebook[k][codes[slot][k]] (fp32, k ascending); codes_snap[b] = codes[slot].

@@ -528,6 +528,7 @@ static hipError_t gemv_dispatch(const GemvArgs& a, hipStream_t s) {
 
 static int g_cus = 256;
 void set_device_cus(int n) { g_cus = n > 0 ? n : 256; }
+int device_cus() { return g_cus; }
 
 // Launch shapes of the grid-stride kernel, picked per matrix shape by a sweep on MI355X.
 template <int NCH, int KIND, int R, int WPB>
@@ -618,13 +619,13 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
 
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
-  const int slot = a.slots[b];
-  const int pos = a.pos[slot];
+  const int slot = a.fixed_slot >= 0 ? a.fixed_slot : a.slots[b];
+  const int pos = a.row_pos ? a.row_pos[b] : a.pos[slot];
   const int ctx = pos + 1;
   const int nsplit = (ctx + a.split - 1) / a.split;
   if (sp >= nsplit) return;
   const int s0 = sp * a.split, s1 = min(s0 + a.split, ctx);
-  const bool has_new = pos >= s0 && pos < s1;
+  const bool has_new = a.append && pos >= s0 && pos < s1;
   const int h = g * G + w;
   const float* qkv = a.qkv + (size_t)b * (a.Hq + 2 * a.Hkv) * D;
   T* kc = static_cast<T*>(a.k_cache);
@@ -767,7 +768,7 @@ template <int D>
 __global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
   constexpr int PER = D / WAVE;
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int pos = a.pos[a.slots[b]];
+  const int pos = a.row_pos ? a.row_pos[b] : a.pos[a.fixed_slot >= 0 ? a.fixed_slot : a.slots[b]];
   const int nsplit = (pos + 1 + a.split - 1) / a.split;
   if (nsplit == 1) return;  // the attention kernel wrote the output itself
   const size_t base = ((size_t)b * a.Hq + h) * a.max_splits;
@@ -789,6 +790,7 @@ __global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.split > 256 || a.split % 64) return hipErrorInvalidValue;
   const int G = a.Hq / a.Hkv;
   const dim3 grid(a.max_splits, a.Hkv, a.M);
 #define S2_ATT(DD, GG)                                                                         \

@@ -1,0 +1,299 @@
+// gfx950 kernels of the prompt prefill (many positions at once).
+//
+// Prefill runs every Slow layer on P prompt positions, so its projections are real dense
+// contractions: C[P][N] = A[P][K] . W[N][K]^T with P up to a few thousand.  They run on the
+// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation): 128 x 128 (or 64 x 128) output
+// tiles per 256-thread workgroup, K in steps of 32 through double-buffered LDS.  The A loader
+// reads fp32 activations and applies the RMSNorm row scale and gain; each activation is then
+// split into bf16 hi + bf16 lo (lo = the rounding error of hi) and both halves multiply the bf16
+// weights, so the product carries ~16 bits of the activation instead of 8 (the weights are bf16
+// already, exactly).  Epilogues add the residual or form SwiGLU pairs.
+#include "kernels.h"
+
+#include <math.h>
+
+namespace s2k {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+namespace {
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t a = __float_as_uint(f);
+  a += 0x7fffu + ((a >> 16) & 1u);
+  return a >> 16;
+}
+
+// (bf16 hi, bf16 lo) of two floats, packed in two words: x = hi + lo + O(2^-17 |x|)
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+  const float r0 = x0 - __uint_as_float(h0 << 16), r1 = x1 - __uint_as_float(h1 << 16);
+  hi = h0 | (h1 << 16);
+  lo = bf16_bits(r0) | (bf16_bits(r1) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// MFMA GEMM.  Block = 4 wavefronts in a 2 x 2 grid; wavefront (wm, wn) owns rows
+// [wm BM/2, (wm+1) BM/2) and columns [64 wn, 64 wn + 64) of the block tile.
+template <int BM, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
+  constexpr int BN = 128, BK = 32, LS = BK + 8;  // LDS row stride (bf16): 80 bytes
+  constexpr int TM = BM / 2 / 16;                 // 16-row MFMA tiles per wavefront
+  constexpr int TN = 4;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LS];   // activation, bf16 hi
+  __shared__ __attribute__((aligned(16))) uint16_t Al[2][BM * LS];   // activation, bf16 lo
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int nk = g.K / BK;
+
+  // global -> register staging of one K step
+  // A: BM 128 -> thread t loads 16 fp32 of row t/2 at k (t%2)*16; BM 64 -> 8 fp32 of row t/4 at (t%4)*8
+  constexpr int AF = BM == 128 ? 16 : 8;
+  const int a_row = BM == 128 ? tid >> 1 : tid >> 2;
+  const int a_k = BM == 128 ? (tid & 1) * 16 : (tid & 3) * 8;
+  const int a_m = min(m0 + a_row, g.M - 1);
+  const float* a_src = g.a + (size_t)a_m * g.lda + a_k;
+  const float a_sc = g.a_scale ? g.a_scale[a_m] : 1.0f;
+  // W: thread t loads 32 bytes of row t/2 at k (t%2)*16
+  const int w_row = tid >> 1, w_k = (tid & 1) * 16;
+  const uint16_t* w_src = g.w + (size_t)(n0 + w_row) * g.K + w_k;
+
+  f32x4 ar[AF / 4];
+  u32x4 wr[2];
+  auto load = [&](int kt) {
+    const int k = kt * BK;
+#pragma unroll
+    for (int i = 0; i < AF / 4; ++i) ar[i] = *reinterpret_cast<const f32x4*>(a_src + k + 4 * i);
+    wr[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + k));
+    wr[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + k + 8));
+  };
+  auto stash = [&](int kt, int buf) {
+    const int k = kt * BK;
+    uint32_t p[AF / 2], q[AF / 2];
+#pragma unroll
+    for (int i = 0; i < AF / 4; ++i) {
+      f32x4 v = ar[i];
+      if (g.a_gain) {
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(g.a_gain + k + a_k + 4 * i);
+        v.x *= a_sc * gg.x;
+        v.y *= a_sc * gg.y;
+        v.z *= a_sc * gg.z;
+        v.w *= a_sc * gg.w;
+      }
+      split_bf16x2(v.x, v.y, p[2 * i], q[2 * i]);
+      split_bf16x2(v.z, v.w, p[2 * i + 1], q[2 * i + 1]);
+    }
+    uint16_t* ad = &As[buf][a_row * LS + a_k];
+    uint16_t* al = &Al[buf][a_row * LS + a_k];
+#pragma unroll
+    for (int i = 0; i < AF / 8; ++i) {
+      *reinterpret_cast<u32x4*>(ad + 8 * i) = u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
+      *reinterpret_cast<u32x4*>(al + 8 * i) = u32x4{q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]};
+    }
+    uint16_t* wd = &Ws[buf][w_row * LS + w_k];
+    *reinterpret_cast<u32x4*>(wd) = wr[0];
+    *reinterpret_cast<u32x4*>(wd + 8) = wr[1];
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  stash(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+    bf16x8 af[TM], afl[TM], bfr[TN];
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * (BM / 2) + i * 16 + fr) * LS + fk]);
+      afl[i] = *reinterpret_cast<const bf16x8*>(&Al[buf][(wm * (BM / 2) + i * 16 + fr) * LS + fk]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(&Ws[buf][(wn * 64 + j * 16 + fr) * LS + fk]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afl[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    if (kt + 1 < nk) stash(kt + 1, buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 4 (lane/16) + r, column lane % 16 of each 16 x 16 tile
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * 64 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + r;
+        const float v = acc[i][j][r];
+        if constexpr (EPI == GEMM_SWIGLU) {
+          const float up = __shfl_xor(v, 1, WAVE);  // columns 2i (gate) and 2i+1 (up) sit in adjacent lanes
+          if (m < g.M && (n & 1) == 0) g.c[(size_t)m * g.ldc + (n >> 1)] = v / (1.0f + expf(-v)) * up;
+        } else if (m < g.M) {
+          if constexpr (EPI == GEMM_ADD) g.c[(size_t)m * g.ldc + n] += v;
+          else g.c[(size_t)m * g.ldc + n] = v;
+        }
+      }
+    }
+}
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (g.N % 128 || g.K % 32 || g.M < 1) return hipErrorInvalidValue;
+  const bool small = (long)((g.M + 127) / 128) * (g.N / 128) < 2L * device_cus();
+  const int BM = small ? 64 : 128;
+  const dim3 grid(g.N / 128, (g.M + BM - 1) / BM);
+#define S2_GEMM(B, E) hipLaunchKernelGGL((k_gemm<B, E>), grid, dim3(256), 0, s, g)
+  if (small) {
+    if (g.epi == GEMM_STORE) S2_GEMM(64, GEMM_STORE);
+    else if (g.epi == GEMM_ADD) S2_GEMM(64, GEMM_ADD);
+    else S2_GEMM(64, GEMM_SWIGLU);
+  } else {
+    if (g.epi == GEMM_STORE) S2_GEMM(128, GEMM_STORE);
+    else if (g.epi == GEMM_ADD) S2_GEMM(128, GEMM_ADD);
+    else S2_GEMM(128, GEMM_SWIGLU);
+  }
+#undef S2_GEMM
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-row RMSNorm scale: scale[m] = 1 / sqrt(mean(x[m]^2) + eps).  One block per row.
+__global__ __launch_bounds__(256) void k_row_rms(const float* x, int ld, int H, float eps, float* scale) {
+  __shared__ float red[4];
+  const float* r = x + (size_t)blockIdx.x * ld;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += 256) ss = fmaf(r[k], r[k], ss);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) scale[blockIdx.x] = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+}
+
+hipError_t launch_row_rms(const float* x, int ld, int H, float eps, float* scale, int M, hipStream_t s) {
+  hipLaunchKernelGGL(k_row_rms, dim3(M), dim3(256), 0, s, x, ld, H, eps, scale);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Append the keys and values of prompt rows to the paged cache: per (row, KV head) one
+// wavefront applies the per-head RMSNorm and RoPE to k at position pos0 + row.
+template <int D, bool KVB>
+__global__ __launch_bounds__(64) void k_prefill_append(const PrefillKvArgs a) {
+  constexpr int PER = D / WAVE;
+  const int g = blockIdx.x, row = blockIdx.y, lane = threadIdx.x;
+  const int pos = a.pos0 + row;
+  const float* qkv = a.qkv + (size_t)row * a.ld;
+  float kv[PER], vv[PER], ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    kv[i] = qkv[(size_t)(a.Hq + g) * D + lane + i * WAVE];
+    vv[i] = qkv[(size_t)(a.Hq + a.Hkv + g) * D + lane + i * WAVE];
+    ss = fmaf(kv[i], kv[i], ss);
+  }
+  const float rk = rsqrtf(wave_sum(ss) / (float)D + a.eps);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) kv[i] = kv[i] * rk * a.k_norm[lane + i * WAVE];
+  const float* crow = a.rope_cos + (size_t)pos * (D / 2);
+  const float* srow = a.rope_sin + (size_t)pos * (D / 2);
+  if constexpr (D == 128) {
+    const float cs = crow[lane], sn = srow[lane];
+    const float x0 = kv[0], x1 = kv[1];
+    kv[0] = x0 * cs - x1 * sn;
+    kv[1] = x1 * cs + x0 * sn;
+  } else {
+    const int i = lane & 31;
+    const float cs = crow[i], sn = srow[i];
+    const float partner = __shfl_xor(kv[0], 32, WAVE);
+    kv[0] = lane < 32 ? kv[0] * cs - partner * sn : kv[0] * cs + partner * sn;
+  }
+  const int page = a.block_table[pos / a.page_size];
+  const size_t off = (((size_t)page * a.Hkv + g) * a.page_size + pos % a.page_size) * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = lane + i * WAVE;
+    if constexpr (KVB) {
+      uint32_t ku = __float_as_uint(kv[i]), vu = __float_as_uint(vv[i]);
+      ku += 0x7fffu + ((ku >> 16) & 1u);
+      vu += 0x7fffu + ((vu >> 16) & 1u);
+      static_cast<uint16_t*>(a.k_cache)[off + d] = (uint16_t)(ku >> 16);
+      static_cast<uint16_t*>(a.v_cache)[off + d] = (uint16_t)(vu >> 16);
+    } else {
+      static_cast<float*>(a.k_cache)[off + d] = kv[i];
+      static_cast<float*>(a.v_cache)[off + d] = vv[i];
+    }
+  }
+}
+
+hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s) {
+  const dim3 grid(a.Hkv, rows);
+  if (a.D == 128) {
+    if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_append<128, true>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((k_prefill_append<128, false>), grid, dim3(64), 0, s, a);
+  } else if (a.D == 64) {
+    if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_append<64, true>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((k_prefill_append<64, false>), grid, dim3(64), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Prompt embeddings of rows [p0, p0 + rows): text rows take embed[token]; masked rows take the
+// sum of their ten codebook rows (fp32, codebook order).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_embed_rows(const void* emb, const void* cb, int K, int H, int NC,
+                                                    const int* tokens, const uint8_t* mask, const int* codes, int p0,
+                                                    float* x, int ldx) {
+  const int row = blockIdx.y, p = p0 + row;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= H) return;
+  auto ld = [&](const void* base, size_t i) -> float {
+    if constexpr (BF16) return __uint_as_float(((uint32_t) static_cast<const uint16_t*>(base)[i]) << 16);
+    else return static_cast<const float*>(base)[i];
+  };
+  float acc = 0.f;
+  if (mask != nullptr && mask[p]) {
+    for (int k = 0; k < NC; ++k) acc += ld(cb, ((size_t)k * K + codes[(size_t)p * NC + k]) * H + e);
+  } else {
+    acc = ld(emb, (size_t)tokens[p] * H + e);
+  }
+  x[(size_t)row * ldx + e] = acc;
+}
+
+hipError_t launch_embed_rows(bool bf16, const void* emb, const void* cb, int K, int H, int NC, const int* tokens,
+                             const uint8_t* mask, const int* codes, int p0, int rows, float* x, int ldx,
+                             hipStream_t s) {
+  const dim3 grid((H + 255) / 256, rows);
+  if (bf16) hipLaunchKernelGGL(k_embed_rows<true>, grid, dim3(256), 0, s, emb, cb, K, H, NC, tokens, mask, codes, p0, x, ldx);
+  else hipLaunchKernelGGL(k_embed_rows<false>, grid, dim3(256), 0, s, emb, cb, K, H, NC, tokens, mask, codes, p0, x, ldx);
+  return hipGetLastError();
+}
+
+}  // namespace s2k

@@ -74,6 +74,27 @@ def test_full_teacher_forced_first_frames():
     assert rep["tokens_checked"] > 10
 
 
+@pytest.mark.timeout(1500)
+def test_voice_clone_prefill_teacher_forced():
+    """1000 VQ positions (sum of ten codebook rows) + 200 text positions at the full S2 shape,
+    prefilled on the matrix cores in chunks, then the first 2 frames checked layer by layer."""
+    rep = _teacher_forced("voice_clone", n_frames=2)
+    assert rep["tokens_checked"] > 5
+
+
+def test_prefill_in_two_calls_matches_one_prefill():
+    cfg = synth.config("mid")
+    w = synth.make_weights(cfg)
+    toks, _, _ = synth.make_prompt(cfg)
+    frames = oracle_run(cfg, w, toks, None, None, 3)
+    ctx = _ctx(cfg, w)
+    ctx.prefill(0, toks[:23])
+    ctx.prefill(0, toks[23:])
+    assert ctx.position(0) == len(toks)
+    compare_frames(ctx, 0, frames, cfg).finish()
+    ctx.close()
+
+
 def test_mid_bf16_kv_cache_teacher_forced():
     """The optional bf16 KV cache (half the KV bytes) on the mid shape."""
     rep = _teacher_forced("mid", n_frames=8, kv_dtype="bf16")
