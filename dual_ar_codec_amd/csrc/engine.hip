@@ -100,7 +100,6 @@ struct s2ar_ctx {
   int pch = 0;
   bool mfma_prefill = false;
   float *px = nullptr, *pqkv = nullptr, *patt = nullptr, *pact = nullptr, *prms = nullptr;
-  float *patt_ml = nullptr, *patt_o = nullptr;
   int* d_iota = nullptr;  // [max_context] = 0, 1, 2, ...
   int* h_pos_stage = nullptr;
 
@@ -117,6 +116,20 @@ struct s2ar_ctx {
   int* h_small = nullptr;  // small int staging (forced codes, own picks)
 
   std::map<int, Graph> graphs;  // per stream id
+
+  // batched multi-stream decode (up to 16 streams per launch, MFMA GEMVs)
+  bool batched_ok = false;
+  float *bx = nullptr, *bxf = nullptr, *bqkv = nullptr, *batt = nullptr, *bact = nullptr;
+  float *blogits = nullptr, *bscale = nullptr, *bpart = nullptr, *bam_val = nullptr;
+  int* bam_idx = nullptr;
+  float *batt_ml = nullptr, *batt_o = nullptr;
+  size_t bpart_floats = 0;
+  int* d_dbg_slots = nullptr;  // [16] batch slots of the eager batched frame
+  struct BatchGraph {
+    Graph g;
+    int* d_slots = nullptr;
+  };
+  std::map<std::vector<int>, BatchGraph> bgraphs;
   std::string err;
 };
 
@@ -340,6 +353,10 @@ void free_ctx(s2ar_ctx* c) {
     if (kv.second.exec) hipGraphExecDestroy(kv.second.exec);
     if (kv.second.g) hipGraphDestroy(kv.second.g);
   }
+  for (auto& kv : c->bgraphs) {
+    if (kv.second.g.exec) hipGraphExecDestroy(kv.second.g.exec);
+    if (kv.second.g.g) hipGraphDestroy(kv.second.g.g);
+  }
   for (void* p : c->dev_allocs) hipFree(p);
   for (void* p : c->host_allocs) hipHostFree(p);
   if (c->ev_order) hipEventDestroy(c->ev_order);
@@ -482,14 +499,12 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     c->mfma_prefill = c->bf16 && qkvd_s % 128 == 0 && H % 128 == 0 && (2 * st.ffn) % 128 == 0 && H % 32 == 0 &&
                       qd_s % 32 == 0 && st.ffn % 32 == 0;
     if (c->mfma_prefill) {
-      c->pch = std::min(g.max_context, 512);
+      c->pch = std::min(g.max_context, 2048);
       C_TRY(dev_alloc(c, &c->px, sizeof(float) * (size_t)c->pch * H));
       C_TRY(dev_alloc(c, &c->pqkv, sizeof(float) * (size_t)c->pch * qkvd_s));
       C_TRY(dev_alloc(c, &c->patt, sizeof(float) * (size_t)c->pch * qd_s));
       C_TRY(dev_alloc(c, &c->pact, sizeof(float) * (size_t)c->pch * st.ffn));
       C_TRY(dev_alloc(c, &c->prms, sizeof(float) * (size_t)c->pch));
-      C_TRY(dev_alloc(c, &c->patt_ml, sizeof(float) * (size_t)c->pch * st.n_q_heads * c->max_splits * 2));
-      C_TRY(dev_alloc(c, &c->patt_o, sizeof(float) * (size_t)c->pch * st.n_q_heads * c->max_splits * st.head_dim));
       std::vector<int> iota(g.max_context);
       for (int i = 0; i < g.max_context; ++i) iota[i] = i;
       C_TRY(dev_alloc(c, &c->d_iota, sizeof(int) * g.max_context));
@@ -497,6 +512,36 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     }
   }
   C_TRY(host_alloc(c, &c->h_pos_stage, sizeof(int) * 16));
+
+  // batched decode buffers (bf16 weights, every K a multiple of 128)
+  {
+    auto k_ok = [](const s2ar_stack& st) {
+      return st.hidden % 128 == 0 && (st.n_q_heads * st.head_dim) % 128 == 0 && st.ffn % 128 == 0;
+    };
+    c->batched_ok = c->bf16 && g.max_streams > 1 && k_ok(g.slow) && k_ok(g.fast);
+    if (c->batched_ok) {
+      const int MBt = 16;
+      const int qkvd_max = std::max((g.slow.n_q_heads + 2 * g.slow.n_kv_heads) * g.slow.head_dim,
+                                    (g.fast.n_q_heads + 2 * g.fast.n_kv_heads) * g.fast.head_dim);
+      const int qd_max = std::max(g.slow.n_q_heads * g.slow.head_dim, g.fast.n_q_heads * g.fast.head_dim);
+      const int f_max = std::max(g.slow.ffn, g.fast.ffn);
+      C_TRY(dev_alloc(c, &c->bx, sizeof(float) * MBt * s2k::pad_k(H)));
+      C_TRY(dev_alloc(c, &c->bxf, sizeof(float) * MBt * s2k::pad_k(H)));
+      C_TRY(dev_alloc(c, &c->bqkv, sizeof(float) * MBt * qkvd_max));
+      C_TRY(dev_alloc(c, &c->batt, sizeof(float) * MBt * qd_max));
+      C_TRY(dev_alloc(c, &c->bact, sizeof(float) * MBt * f_max));
+      C_TRY(dev_alloc(c, &c->blogits, sizeof(float) * MBt * V));
+      C_TRY(dev_alloc(c, &c->bscale, sizeof(float) * MBt));
+      c->bpart_floats = (size_t)32 * MBt * std::max(qkvd_max, std::max(H, 2 * f_max));
+      C_TRY(dev_alloc(c, &c->bpart, sizeof(float) * c->bpart_floats));
+      const int nbm = s2k::mgemv_blocks((int)V);
+      C_TRY(dev_alloc(c, &c->bam_val, sizeof(float) * (size_t)nbm * MBt));
+      C_TRY(dev_alloc(c, &c->bam_idx, sizeof(int) * (size_t)nbm * MBt));
+      C_TRY(dev_alloc(c, &c->batt_ml, sizeof(float) * 2 * MBt * hq * c->max_splits));
+      C_TRY(dev_alloc(c, &c->batt_o, sizeof(float) * (size_t)MBt * hq * c->max_splits * dmax));
+      C_TRY(dev_alloc(c, &c->d_dbg_slots, sizeof(int) * MBt));
+    }
+  }
 
   c->h_codes_frames = 64;
   C_TRY(host_alloc(c, &c->h_codes, sizeof(int) * (size_t)c->h_codes_frames * g.max_streams * NC));
@@ -663,7 +708,7 @@ struct Enq {
       float* xf = xf_of(slot);
       if (tp)
         chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, c->d_slot_ids + slot, c->d_codes, j, xf,
-                                   1, s));
+                                   H, 1, s));
       fast_pos_ptr = c->d_fast_pos + (size_t)(j - 1) * g.max_streams;
       layers(false, slot, xf, tp && tp->fast_resid ? tp->fast_resid + (size_t)(j - 1) * Lf * H : nullptr);
       gemv(s2k::GEMV_NORM_ARGMAX, c->fast_head, xf, c->fast_final, c->fast_logits, K, H,
@@ -683,8 +728,7 @@ struct Enq {
     const s2ar_config& g = c->cfg;
     if (tp) {
       chk(s2k::launch_embed_codes(c->bf16, c->codebook, g.codebook_size, g.slow.hidden, g.n_codebooks,
-                                  c->d_slot_ids + slot, c->d_codes, c->d_snap + (size_t)slot * g.n_codebooks, c->x,
-                                  1, s));
+                                  c->d_slot_ids + slot, c->d_codes, c->d_snap, c->x, g.slow.hidden, 1, s));
       if (tp->embed) d2h(tp->embed, c->x, sizeof(float) * g.slow.hidden);
     }
     layers(true, slot, c->x, tp ? tp->slow_resid : nullptr);
@@ -739,41 +783,217 @@ struct Enq {
       kv.D = D;
       kv.eps = eps;
       chk(s2k::launch_prefill_append(kv, rows, s));
+      s2k::PrefillAttnArgs pa{};
+      pa.qkv = c->pqkv;
+      pa.ld = qkvd;
+      pa.q_norm = L.q_norm;
+      pa.rope_cos = c->rope_cos_s;
+      pa.rope_sin = c->rope_sin_s;
+      pa.k_cache = kv.k_cache;
+      pa.v_cache = kv.v_cache;
+      pa.kv_bf16 = kv.kv_bf16;
+      pa.block_table = kv.block_table;
+      pa.page_size = kPageSize;
+      pa.out = c->patt;
+      pa.ld_out = qd;
+      pa.rows = rows;
+      pa.pos0 = pos0;
+      pa.Hq = st.n_q_heads;
+      pa.Hkv = st.n_kv_heads;
+      pa.D = D;
+      pa.eps = eps;
+      pa.scale = (float)(1.0 / std::sqrt((double)D));
+      chk(s2k::launch_prefill_attn(pa, s));
+      gemm(c->patt, qd, nullptr, nullptr, L.wo, c->px, H, H, qd, s2k::GEMM_ADD);
+      chk(s2k::launch_row_rms(c->px, H, H, eps, c->prms, rows, s));
+      gemm(c->px, H, c->prms, L.mlp_norm, L.wgu, c->pact, F, 2 * F, H, s2k::GEMM_SWIGLU);
+      gemm(c->pact, F, nullptr, nullptr, L.wdown, c->px, H, H, F, s2k::GEMM_ADD);
+    }
+  }
+
+  // ---- batched decode of M <= 16 streams (slots on the device in `slots`) ----
+  // Optional per-stream host destinations for the test-only eager batched frame.
+  struct BTap {
+    float *slow_resid = nullptr, *slow_h = nullptr, *slow_logits = nullptr, *fast_resid = nullptr;
+    float* fast_logits = nullptr;
+    int *own = nullptr, *next_c0 = nullptr;
+    const int* forced = nullptr;  // pinned [NC] or nullptr
+  };
+  const BTap* btp = nullptr;  // [M] when running the eager batched frame
+  const int* bslots_host = nullptr;
+  void mgemv(int epi, const void* w, const float* x, int ldx, const float* scale, const float* gain, float* out,
+             int ldo, int N, int K, int M, int lo = 0, int hi = 0) {
+    s2k::MgemvArgs a{};
+    a.x = x;
+    a.ldx = ldx;
+    a.x_scale = scale;
+    a.gain = gain;
+    a.w = static_cast<const uint16_t*>(w);
+    a.out = out;
+    a.ldo = ldo;
+    a.part = c->bpart;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.epi = epi;
+    a.am_lo = lo;
+    a.am_hi = hi;
+    a.am_val = c->bam_val;
+    a.am_idx = c->bam_idx;
+    // split K until the launch has about two blocks per CU (K / 128 divisible by S)
+    a.S = 1;
+    if (epi != s2k::MG_ARGMAX) {
+      const int nb = s2k::mgemv_blocks(N), slices = K / 128;
+      for (int S = 1; S <= 32; ++S) {
+        if (slices % S) continue;
+        if ((size_t)S * M * N > c->bpart_floats) break;
+        a.S = S;
+        if (nb * S >= 2 * s2k::device_cus()) break;
+      }
+    }
+    chk(s2k::launch_mgemv(a, s));
+  }
+
+  void layers_b(bool is_slow, int M, const int* slots, float* xres) {
+    const s2ar_config& g = c->cfg;
+    const s2ar_stack& st = is_slow ? g.slow : g.fast;
+    const std::vector<LayerW>& W = is_slow ? c->slow : c->fast;
+    const int H = st.hidden, D = st.head_dim, qd = st.n_q_heads * D, F = st.ffn;
+    const int qkvd = (st.n_q_heads + 2 * st.n_kv_heads) * D, ldx = s2k::pad_k(g.slow.hidden);
+    const float eps = (float)g.rms_eps;
+    for (int l = 0; l < st.n_layers; ++l) {
+      const LayerW& L = W[l];
+      chk(s2k::launch_row_rms(xres, ldx, H, eps, c->bscale, M, s));
+      mgemv(s2k::MG_STORE, L.wqkv, xres, ldx, c->bscale, L.attn_norm, c->bqkv, qkvd, qkvd, H, M);
       s2k::AttnArgs a{};
-      a.qkv = c->pqkv;
+      a.qkv = c->bqkv;
       a.q_norm = L.q_norm;
       a.k_norm = L.k_norm;
-      a.rope_cos = c->rope_cos_s;
-      a.rope_sin = c->rope_sin_s;
-      a.slots = nullptr;
-      a.pos = nullptr;
-      a.k_cache = kv.k_cache;
-      a.v_cache = kv.v_cache;
-      a.kv_bf16 = kv.kv_bf16;
-      a.block_table = c->d_bt;
-      a.bt_stride = c->bt_stride;
-      a.out = c->patt;
-      a.part_ml = c->patt_ml;
-      a.part_o = c->patt_o;
-      a.max_splits = c->max_splits;
-      a.split = kAttnSplit;
-      a.M = rows;
+      a.slots = slots;
+      a.M = M;
       a.Hq = st.n_q_heads;
       a.Hkv = st.n_kv_heads;
       a.D = D;
       a.page_size = kPageSize;
       a.eps = eps;
       a.scale = (float)(1.0 / std::sqrt((double)D));
-      a.fixed_slot = slot;
-      a.row_pos = c->d_iota + pos0;
-      a.append = 0;
+      a.out = c->batt;
+      a.part_ml = c->batt_ml;
+      a.part_o = c->batt_o;
+      a.kv_bf16 = g.kv_dtype == 1;
+      a.split = kAttnSplit;
+      a.fixed_slot = -1;
+      a.row_pos = nullptr;
+      a.append = 1;
+      if (is_slow) {
+        a.rope_cos = c->rope_cos_s;
+        a.rope_sin = c->rope_sin_s;
+        a.pos = c->d_pos;
+        a.k_cache = c->kv_k + (size_t)l * c->kv_layer;
+        a.v_cache = c->kv_v + (size_t)l * c->kv_layer;
+        a.block_table = c->d_bt;
+        a.bt_stride = c->bt_stride;
+        a.max_splits = c->max_splits;
+      } else {
+        a.rope_cos = c->rope_cos_f;
+        a.rope_sin = c->rope_sin_f;
+        a.pos = fast_pos_ptr;
+        a.k_cache = c->fkv_k + (size_t)l * c->fkv_layer;
+        a.v_cache = c->fkv_v + (size_t)l * c->fkv_layer;
+        a.block_table = c->d_fast_bt;
+        a.bt_stride = 1;
+        a.max_splits = 1;
+      }
       chk(s2k::launch_attention(a, s));
       if (a.max_splits > 1) chk(s2k::launch_attention_combine(a, s));
-      gemm(c->patt, qd, nullptr, nullptr, L.wo, c->px, H, H, qd, s2k::GEMM_ADD);
-      chk(s2k::launch_row_rms(c->px, H, H, eps, c->prms, rows, s));
-      gemm(c->px, H, c->prms, L.mlp_norm, L.wgu, c->pact, F, 2 * F, H, s2k::GEMM_SWIGLU);
-      gemm(c->pact, F, nullptr, nullptr, L.wdown, c->px, H, H, F, s2k::GEMM_ADD);
+      mgemv(s2k::MG_ADD, L.wo, c->batt, qd, nullptr, nullptr, xres, ldx, H, qd, M);
+      chk(s2k::launch_row_rms(xres, ldx, H, eps, c->bscale, M, s));
+      mgemv(s2k::MG_SWIGLU, L.wgu, xres, ldx, c->bscale, L.mlp_norm, c->bact, F, 2 * F, H, M);
+      mgemv(s2k::MG_ADD, L.wdown, c->bact, F, nullptr, nullptr, xres, ldx, H, F, M);
+      if (btp)
+        for (int b = 0; b < M; ++b) {
+          float* dst = is_slow ? btp[b].slow_resid : btp[b].fast_resid;
+          if (dst) d2h(dst + (size_t)(is_slow ? l : tap_step * st.n_layers + l) * H, xres + (size_t)b * ldx, sizeof(float) * H);
+        }
     }
+  }
+  int tap_step = 0;
+
+  void finish_b(int mode, int j, int M, const int* slots, int lo, int hi, float* x) {
+    const s2ar_config& g = c->cfg;
+    s2k::FinishBArgs f{};
+    f.am_val = c->bam_val;
+    f.am_idx = c->bam_idx;
+    f.b0 = lo / 64;
+    f.b1 = (hi - 1) / 64;
+    f.lo = lo;
+    f.mode = mode;
+    f.j = j;
+    f.slots = slots;
+    f.codes = c->d_codes;
+    f.snap = c->d_snap;
+    f.pos = c->d_pos;
+    f.codebook = c->codebook;
+    f.h = c->d_h;
+    f.x = x;
+    f.ldx = s2k::pad_k(g.slow.hidden);
+    f.x_res = c->bx;
+    f.scale = c->bscale;
+    f.gain = c->slow_final;
+    f.xf_slot = c->xf;
+    f.ld_xf_slot = s2k::pad_k(g.slow.hidden);
+    f.H = g.slow.hidden;
+    f.K = g.codebook_size;
+    f.NC = g.n_codebooks;
+    chk(s2k::launch_finish_b(c->bf16, f, M, s));
+  }
+
+  // one frame of M streams: the Fast loops of all streams in lock step, then their Slow steps
+  void frame_b(int M, const int* slots) {
+    const s2ar_config& g = c->cfg;
+    const int H = g.slow.hidden, K = g.codebook_size, NC = g.n_codebooks, V = g.vocab_text + K;
+    const int ldx = s2k::pad_k(H);
+    const float eps = (float)g.rms_eps;
+    auto code_ptr = [&](int b, int j) { return c->d_codes + (size_t)bslots_host[b] * NC + j; };
+    if (btp)
+      for (int b = 0; b < M; ++b) {
+        if (btp[b].own) d2h(btp[b].own, code_ptr(b, 0), sizeof(int));
+        if (btp[b].forced) h2d(code_ptr(b, 0), btp[b].forced, sizeof(int));
+      }
+    chk(s2k::launch_gather_h(c->d_h, slots, H, c->bxf, ldx, M, s));
+    for (int j = 1; j < NC; ++j) {
+      fast_pos_ptr = c->d_fast_pos + (size_t)(j - 1) * g.max_streams;
+      if (btp && j > 1)  // eager frame: the input honours forced codes
+        chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, slots, c->d_codes, j, c->bxf, ldx, M, s));
+      tap_step = j - 1;
+      layers_b(false, M, slots, c->bxf);
+      chk(s2k::launch_row_rms(c->bxf, ldx, H, eps, c->bscale, M, s));
+      mgemv(s2k::MG_ARGMAX, c->fast_head, c->bxf, ldx, c->bscale, c->fast_final, c->blogits, K, K, H, M, 0, K);
+      if (btp) {
+        finish_b(s2k::FIN_CODE, j, M, slots, 0, K, c->bxf);
+        for (int b = 0; b < M; ++b) {
+          if (btp[b].fast_logits) d2h(btp[b].fast_logits + (size_t)(j - 1) * K, c->blogits + (size_t)b * K, sizeof(float) * K);
+          if (btp[b].own) d2h(btp[b].own + j, code_ptr(b, j), sizeof(int));
+          if (btp[b].forced) h2d(code_ptr(b, j), btp[b].forced + j, sizeof(int));
+        }
+      } else {
+        finish_b(j < NC - 1 ? s2k::FIN_FAST_NEXT : s2k::FIN_FAST_LAST, j, M, slots, 0, K,
+                 j < NC - 1 ? c->bxf : c->bx);
+      }
+    }
+    if (btp)
+      chk(s2k::launch_embed_codes(c->bf16, c->codebook, K, H, NC, slots, c->d_codes, c->d_snap, c->bx, ldx, M, s));
+    layers_b(true, M, slots, c->bx);
+    chk(s2k::launch_row_rms(c->bx, ldx, H, eps, c->bscale, M, s));
+    mgemv(s2k::MG_ARGMAX, c->slow_head, c->bx, ldx, c->bscale, c->slow_final, c->blogits, V, V, H, M, g.vocab_text,
+          V);
+    finish_b(s2k::FIN_SLOW, 0, M, slots, g.vocab_text, V, c->bxf);
+    if (btp)
+      for (int b = 0; b < M; ++b) {
+        if (btp[b].slow_logits) d2h(btp[b].slow_logits, c->blogits + (size_t)b * V, sizeof(float) * V);
+        if (btp[b].slow_h) d2h(btp[b].slow_h, c->d_h + (size_t)bslots_host[b] * H, sizeof(float) * H);
+        if (btp[b].next_c0) d2h(btp[b].next_c0, code_ptr(b, 0), sizeof(int));
+      }
   }
 
   void frame(int slot, const TapPlan* tp) {
@@ -855,6 +1075,37 @@ Graph* frame_graph(s2ar_ctx* c, int slot, int* rc) {
     return nullptr;
   }
   return &(c->graphs[slot] = g);
+}
+
+s2ar_ctx::BatchGraph* batch_graph(s2ar_ctx* c, const std::vector<int>& ids, int* rc) {
+  auto it = c->bgraphs.find(ids);
+  if (it != c->bgraphs.end()) return &it->second;
+  s2ar_ctx::BatchGraph bg;
+  if (int r = dev_alloc(c, &bg.d_slots, sizeof(int) * 16)) {
+    *rc = r;
+    return nullptr;
+  }
+  hipError_t e = hipMemcpy(bg.d_slots, ids.data(), sizeof(int) * ids.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    *rc = set_err(c, S2AR_E_DEVICE, std::string("batch graph setup: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  Enq q{c, c->stream};
+  q.frame_b((int)ids.size(), bg.d_slots);
+  e = hipStreamEndCapture(c->stream, &bg.g.g);
+  if (q.e != hipSuccess || e != hipSuccess) {
+    if (bg.g.g) hipGraphDestroy(bg.g.g);
+    *rc = set_err(c, S2AR_E_DEVICE, std::string("batch graph capture: ") + hipGetErrorString(q.e != hipSuccess ? q.e : e));
+    return nullptr;
+  }
+  e = hipGraphInstantiate(&bg.g.exec, bg.g.g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(bg.g.g);
+    *rc = set_err(c, S2AR_E_DEVICE, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  return &(c->bgraphs[ids] = bg);
 }
 
 }  // namespace
@@ -966,6 +1217,38 @@ int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_fra
   if (!codes_out || n_frames < 1) return set_err(c, S2AR_E_ARG, "codes_out must be non-null and n_frames >= 1");
   if (int rc = check_streams(c, ids, n, n_frames)) return rc;
   const int NC = c->cfg.n_codebooks;
+  if (c->batched_ok && n > 1) {
+    // groups of up to 16 streams, one captured graph per group
+    std::vector<s2ar_ctx::BatchGraph*> groups;
+    for (int i0 = 0; i0 < n; i0 += 16) {
+      std::vector<int> gids(ids + i0, ids + std::min(n, i0 + 16));
+      int rc = 0;
+      s2ar_ctx::BatchGraph* bg = batch_graph(c, gids, &rc);
+      if (!bg) return rc;
+      groups.push_back(bg);
+    }
+    if (int rc = order_after_user(c)) return rc;
+    for (int i = 0; i < n; ++i)
+      if (int rc = ensure_pages(c, ids[i], c->pos[ids[i]] + n_frames)) return rc;
+    const int ms = c->cfg.max_streams;
+    int done = 0;
+    while (done < n_frames) {
+      const int chunk = std::min(n_frames - done, c->h_codes_frames * ms / std::max(ms, 1));
+      for (int f = 0; f < chunk; ++f) {
+        for (auto* bg : groups) HIP_TRY(c, hipGraphLaunch(bg->g.exec, c->stream));
+        HIP_TRY(c, hipMemcpyAsync(c->h_codes + (size_t)f * ms * NC, c->d_snap, sizeof(int) * ms * NC,
+                                  hipMemcpyDeviceToHost, c->stream));
+      }
+      HIP_TRY(c, hipStreamSynchronize(c->stream));
+      for (int f = 0; f < chunk; ++f)
+        for (int i = 0; i < n; ++i)
+          std::memcpy(codes_out + ((size_t)(done + f) * n + i) * NC, c->h_codes + ((size_t)f * ms + ids[i]) * NC,
+                      sizeof(int) * NC);
+      done += chunk;
+    }
+    for (int i = 0; i < n; ++i) c->pos[ids[i]] += n_frames;
+    return S2AR_OK;
+  }
   std::vector<Graph*> gs(n);
   for (int i = 0; i < n; ++i) {
     int rc = 0;
@@ -1051,6 +1334,80 @@ int s2ar_debug_frame(s2ar_ctx* c, int32_t sid, const int32_t* forced, s2ar_taps*
   for (int i = 0; i < (NC - 1) * K && finite; ++i) finite = std::isfinite(tp.fast_logits[i]);
   if (!finite) return set_err(c, S2AR_E_NUMERIC, "non-finite logits");
   return S2AR_OK;
+}
+
+int s2ar_debug_frame_batch(s2ar_ctx* c, const int32_t* ids, int32_t n, const int32_t* forced, s2ar_taps* taps) {
+  if (!c) return S2AR_E_ARG;
+  if (!c->batched_ok) return set_err(c, S2AR_E_ARG, "batched decode needs bf16 weights and K dims divisible by 128");
+  if (n > 16) return set_err(c, S2AR_E_ARG, "at most 16 streams per batched debug frame");
+  if (int rc = check_streams(c, ids, n, 1)) return rc;
+  const s2ar_config& g = c->cfg;
+  const int NC = g.n_codebooks, H = g.slow.hidden, K = g.codebook_size, V = g.vocab_text + K;
+  if (forced)
+    for (int i = 0; i < n * NC; ++i)
+      if (forced[i] < 0 || forced[i] >= K) return set_err(c, S2AR_E_RANGE, "forced code out of range");
+  const size_t per = (size_t)g.slow.n_layers * H + H + V + (size_t)(NC - 1) * g.fast.n_layers * H + (size_t)(NC - 1) * K;
+  float* stage = nullptr;
+  int* istage = nullptr;
+  if (hipHostMalloc(&stage, sizeof(float) * per * n, hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc(&istage, sizeof(int) * (size_t)n * NC * 3, hipHostMallocDefault) != hipSuccess) {
+    if (stage) hipHostFree(stage);
+    return set_err(c, S2AR_E_NOMEM, "pinned staging for taps");
+  }
+  std::vector<Enq::BTap> bt(n);
+  for (int b = 0; b < n; ++b) {
+    float* f = stage + per * b;
+    bt[b].slow_resid = f;
+    f += (size_t)g.slow.n_layers * H;
+    bt[b].slow_h = f;
+    f += H;
+    bt[b].slow_logits = f;
+    f += V;
+    bt[b].fast_resid = f;
+    f += (size_t)(NC - 1) * g.fast.n_layers * H;
+    bt[b].fast_logits = f;
+    bt[b].own = istage + (size_t)b * NC;
+    bt[b].next_c0 = istage + (size_t)n * NC + b;
+    if (forced) {
+      std::memcpy(istage + (size_t)2 * n * NC + (size_t)b * NC, forced + (size_t)b * NC, sizeof(int) * NC);
+      bt[b].forced = istage + (size_t)2 * n * NC + (size_t)b * NC;
+    }
+  }
+  std::vector<int> idv(ids, ids + n);
+  int rc = 0;
+  int* d_slots = c->d_dbg_slots;
+  hipError_t e = hipMemcpy(d_slots, ids, sizeof(int) * n, hipMemcpyHostToDevice);
+  if (e == hipSuccess && (rc = order_after_user(c)) == 0) {
+    for (int i = 0; i < n && rc == 0; ++i) rc = ensure_pages(c, ids[i], c->pos[ids[i]] + 1);
+    if (rc == 0) {
+      Enq q{c, c->stream};
+      q.btp = bt.data();
+      q.bslots_host = idv.data();
+      q.frame_b(n, d_slots);
+      e = q.e;
+      if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    }
+  }
+  if (rc == 0 && e != hipSuccess) rc = set_err(c, S2AR_E_DEVICE, std::string("batched debug frame: ") + hipGetErrorString(e));
+  if (rc == 0) {
+    for (int i = 0; i < n; ++i) c->pos[ids[i]] += 1;
+    for (int b = 0; b < n && taps; ++b) {
+      const s2ar_taps& T = taps[b];
+      auto put = [](float* dst, const float* src, size_t cnt) {
+        if (dst) std::memcpy(dst, src, sizeof(float) * cnt);
+      };
+      put(T.slow_resid, bt[b].slow_resid, (size_t)g.slow.n_layers * H);
+      put(T.slow_h, bt[b].slow_h, H);
+      put(T.slow_logits, bt[b].slow_logits, V);
+      put(T.fast_resid, bt[b].fast_resid, (size_t)(NC - 1) * g.fast.n_layers * H);
+      put(T.fast_logits, bt[b].fast_logits, (size_t)(NC - 1) * K);
+      if (T.own_codes) std::memcpy(T.own_codes, bt[b].own, sizeof(int) * NC);
+      if (T.next_c0) *T.next_c0 = *bt[b].next_c0;
+    }
+  }
+  hipHostFree(stage);
+  hipHostFree(istage);
+  return rc;
 }
 
 int s2ar_release_stream(s2ar_ctx* c, int32_t sid) {

@@ -124,22 +124,89 @@ struct PrefillKvArgs {
   float eps;
 };
 hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s);
+
+// Causal attention of prompt rows pos0 .. pos0 + rows - 1 over the stream's cache (their own keys
+// and values appended beforehand).  q heads are normalised and rotated here.
+struct PrefillAttnArgs {
+  const float* qkv;        // [rows][ld]
+  int ld;
+  const float* q_norm;
+  const float* rope_cos;
+  const float* rope_sin;
+  const void* k_cache;     // one layer of the paged pool
+  const void* v_cache;
+  int kv_bf16;
+  const int* block_table;  // the stream's row of the block table
+  int page_size;
+  float* out;              // [rows][ld_out]
+  int ld_out;
+  int rows, pos0, Hq, Hkv, D;
+  float eps, scale;
+};
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_embed_rows(bool bf16, const void* emb, const void* cb, int K, int H, int NC, const int* tokens,
                              const uint8_t* mask, const int* codes, int p0, int rows, float* x, int ldx,
                              hipStream_t s);
 int argmax_block_rows();
 
-// x[b] = sum_k codebook[k][codes[slot][k]] (fp32, k ascending); codes_snap[b] = codes[slot].
+// x[b] = sum_k codebook[k][codes[slot][k]] (fp32, k ascending); snap[slot] = codes[slot].
 hipError_t launch_embed_codes(bool bf16, const void* codebook, int K, int H, int NC, const int* slots,
-                              const int* codes, int* codes_snap, float* x, int M, hipStream_t s);
+                              const int* codes, int* snap, float* x, int ldx, int M, hipStream_t s);
 // Fast step j input: j == 1 -> h[slot]; j >= 2 -> codebook[j-1][codes[slot][j-1]].
 hipError_t launch_fast_input(bool bf16, const void* codebook, const float* h, int K, int H, int NC,
-                             const int* slots, const int* codes, int j, float* x, int M, hipStream_t s);
+                             const int* slots, const int* codes, int j, float* x, int ldx, int M, hipStream_t s);
 // Prompt position p: mask[p] ? sum of codebook rows of codes[p] : embed[tokens[p]].
 hipError_t launch_embed_prompt(bool bf16, const void* embed, const void* codebook, int K, int H, int NC,
                                const int* tokens, const uint8_t* mask, const int* codes, int p, float* x,
                                hipStream_t s);
 // pos[slots[b]] += 1
 hipError_t launch_advance(const int* slots, int* pos, int M, hipStream_t s);
+
+// ---- batched multi-stream decode (batch.hip) ----
+enum MgemvEpi : int { MG_STORE = 0, MG_ADD = 1, MG_SWIGLU = 2, MG_ARGMAX = 3 };
+// out[j][n] (=, +=) sum_k W[n][k] * x[j][k] * x_scale[j] * gain[k] for batch rows j < M <= 16, on
+// the matrix cores.  K must be a multiple of 128 * S; S > 1 splits K over blocks and reduces the
+// partials in split order.  MG_SWIGLU: W rows (2i, 2i+1) = (gate_i, up_i), out[j][i] = silu(g) u.
+// MG_ARGMAX (S == 1): out = logits and per-(block, row) maxima over rows [am_lo, am_hi).
+struct MgemvArgs {
+  const float* x;          // [M][ldx] fp32 batch rows
+  int ldx;
+  const float* x_scale;    // [M] RMSNorm row scale or nullptr
+  const float* gain;       // [K] RMSNorm gain or nullptr
+  const uint16_t* w;       // [N][K] bf16
+  float* out;              // [M][ldo]
+  int ldo;
+  float* part;             // [S][M][N] split partials (S > 1)
+  int M, N, K, S;
+  int epi;
+  int am_lo, am_hi;
+  float* am_val;           // [blocks][16]
+  int* am_idx;
+};
+int mgemv_blocks(int N);
+hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s);
+
+struct FinishBArgs {
+  const float* am_val;     // [blocks][16]
+  const int* am_idx;
+  int b0, b1, lo;
+  int mode, j;
+  const int* slots;        // [M] stream slot of each batch row
+  int* codes;              // [streams][NC]
+  int* snap;               // [streams][NC]
+  int* pos;                // [streams]
+  const void* codebook;
+  float* h;                // [streams][H]
+  float* x;                // [M][ldx] next input rows
+  int ldx;
+  const float* x_res;      // FIN_SLOW: batch residual rows [M][ldx]
+  const float* scale;      // FIN_SLOW: [M] final RMSNorm row scale
+  const float* gain;       // FIN_SLOW: final norm gain [H]
+  float* xf_slot;          // FIN_SLOW: also write h into the single-stream Fast residual of the slot
+  int ld_xf_slot;
+  int H, K, NC;
+};
+hipError_t launch_finish_b(bool bf16, const FinishBArgs& f, int M, hipStream_t s);
+hipError_t launch_gather_h(const float* h, const int* slots, int H, float* x, int ldx, int M, hipStream_t s);
 
 }  // namespace s2k

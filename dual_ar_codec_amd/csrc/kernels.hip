@@ -818,21 +818,21 @@ hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s) {
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_embed_codes(const void* cb, int K, int H, int NC, const int* slots,
-                                                     const int* codes, int* codes_snap, float* x) {
+                                                     const int* codes, int* codes_snap, float* x, int ldx) {
   const int b = blockIdx.y;
   const int slot = slots[b];
   const int* cd = codes + (size_t)slot * NC;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.x == 0 && threadIdx.x < NC) codes_snap[(size_t)b * NC + threadIdx.x] = cd[threadIdx.x];
+  if (blockIdx.x == 0 && threadIdx.x < NC) codes_snap[(size_t)slot * NC + threadIdx.x] = cd[threadIdx.x];
   if (i >= H) return;
   float acc = 0.f;
   for (int k = 0; k < NC; ++k) acc += load_w<BF16>(cb, ((size_t)k * K + cd[k]) * H + i);
-  x[(size_t)b * H + i] = acc;
+  x[(size_t)b * ldx + i] = acc;
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_fast_input(const void* cb, const float* hs, int K, int H, int NC,
-                                                    const int* slots, const int* codes, int j, float* x) {
+                                                    const int* slots, const int* codes, int j, float* x, int ldx) {
   const int b = blockIdx.y;
   const int slot = slots[b];
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -840,7 +840,7 @@ __global__ __launch_bounds__(256) void k_fast_input(const void* cb, const float*
   float v;
   if (j == 1) v = hs[(size_t)slot * H + i];
   else v = load_w<BF16>(cb, ((size_t)(j - 1) * K + codes[(size_t)slot * NC + j - 1]) * H + i);
-  x[(size_t)b * H + i] = v;
+  x[(size_t)b * ldx + i] = v;
 }
 
 template <bool BF16>
@@ -865,18 +865,18 @@ __global__ void k_advance(const int* slots, int* pos, int M) {
 }
 
 hipError_t launch_embed_codes(bool bf16, const void* cb, int K, int H, int NC, const int* slots, const int* codes,
-                              int* codes_snap, float* x, int M, hipStream_t s) {
+                              int* codes_snap, float* x, int ldx, int M, hipStream_t s) {
   const dim3 grid((H + 255) / 256, M);
-  if (bf16) hipLaunchKernelGGL(k_embed_codes<true>, grid, dim3(256), 0, s, cb, K, H, NC, slots, codes, codes_snap, x);
-  else hipLaunchKernelGGL(k_embed_codes<false>, grid, dim3(256), 0, s, cb, K, H, NC, slots, codes, codes_snap, x);
+  if (bf16) hipLaunchKernelGGL(k_embed_codes<true>, grid, dim3(256), 0, s, cb, K, H, NC, slots, codes, codes_snap, x, ldx);
+  else hipLaunchKernelGGL(k_embed_codes<false>, grid, dim3(256), 0, s, cb, K, H, NC, slots, codes, codes_snap, x, ldx);
   return hipGetLastError();
 }
 
 hipError_t launch_fast_input(bool bf16, const void* cb, const float* h, int K, int H, int NC, const int* slots,
-                             const int* codes, int j, float* x, int M, hipStream_t s) {
+                             const int* codes, int j, float* x, int ldx, int M, hipStream_t s) {
   const dim3 grid((H + 255) / 256, M);
-  if (bf16) hipLaunchKernelGGL(k_fast_input<true>, grid, dim3(256), 0, s, cb, h, K, H, NC, slots, codes, j, x);
-  else hipLaunchKernelGGL(k_fast_input<false>, grid, dim3(256), 0, s, cb, h, K, H, NC, slots, codes, j, x);
+  if (bf16) hipLaunchKernelGGL(k_fast_input<true>, grid, dim3(256), 0, s, cb, h, K, H, NC, slots, codes, j, x, ldx);
+  else hipLaunchKernelGGL(k_fast_input<false>, grid, dim3(256), 0, s, cb, h, K, H, NC, slots, codes, j, x, ldx);
   return hipGetLastError();
 }
 

@@ -265,6 +265,119 @@ hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Causal attention of a block of prompt rows.  grid = (ceil(rows / 64), Hkv); block = 2 * 64 * G
+// threads.  Thread t serves query row (t / 2) % 64 of q head g G + (t / 2) / 64 and half t % 2 of
+// its D dimensions (so q and the running output stay in registers).  Key/value tiles of 64 cached
+// positions are staged once in LDS and shared by all 64 G queries of the block; the running
+// softmax is rescaled per key.  Keys and values of the rows must already be in the cache.
+template <int D, int G, bool KVB>
+__global__ __launch_bounds__(2 * 64 * G) void k_prefill_attn(const PrefillAttnArgs a) {
+  constexpr int QT = 64, KT = 64, HD = D / 2, NT = 2 * QT * G;
+  __shared__ __attribute__((aligned(16))) float ks[KT][D + 4];
+  __shared__ __attribute__((aligned(16))) float vs[KT][D + 4];
+  __shared__ int rowoff[KT];
+  const int g = blockIdx.y, tid = threadIdx.x;
+  const int half = tid & 1, r = (tid >> 1) % QT, hl = (tid >> 1) / QT;
+  const int h = g * G + hl;
+  const int row0 = blockIdx.x * QT;
+  const int row = min(row0 + r, a.rows - 1);
+  const bool live = row0 + r < a.rows;
+  const int pos = a.pos0 + row;
+  const int last_pos = a.pos0 + min(row0 + QT, a.rows) - 1;  // largest position in the block
+
+  // q: per-head RMSNorm, RoPE (pairs d, d + D/2 sit in the two halves of this lane pair), scale
+  float q[HD];
+  const float* qp = a.qkv + (size_t)row * a.ld + h * D + half * HD;
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < HD; ++d) {
+    q[d] = qp[d];
+    ss = fmaf(q[d], q[d], ss);
+  }
+  ss += __shfl_xor(ss, 1, WAVE);
+  const float rq = rsqrtf(ss / (float)D + a.eps);
+  const float* crow = a.rope_cos + (size_t)pos * HD;
+  const float* srow = a.rope_sin + (size_t)pos * HD;
+#pragma unroll
+  for (int d = 0; d < HD; ++d) {
+    const float x = q[d] * rq * a.q_norm[half * HD + d];
+    const float partner = __shfl_xor(x, 1, WAVE);  // element d of the other half
+    const float cs = crow[d], sn = srow[d];
+    q[d] = (half == 0 ? x * cs - partner * sn : x * cs + partner * sn) * a.scale;
+  }
+
+  float m = -INFINITY, l = 0.f, o[HD];
+#pragma unroll
+  for (int d = 0; d < HD; ++d) o[d] = 0.f;
+  const float* kc = static_cast<const float*>(a.k_cache);
+  const float* vc = static_cast<const float*>(a.v_cache);
+  const uint16_t* kb = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vb = static_cast<const uint16_t*>(a.v_cache);
+  for (int j0 = 0; j0 <= last_pos; j0 += KT) {
+    const int nk = min(KT, last_pos + 1 - j0);
+    __syncthreads();  // the previous tile is no longer read
+    if (tid < KT) {
+      const int jj = j0 + tid;
+      const int page = a.block_table[min(jj, last_pos) / a.page_size];
+      rowoff[tid] = (int)((((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
+    }
+    __syncthreads();
+    for (int e = tid * 4; e < nk * D; e += NT * 4) {
+      const int j = e / D, d = e % D;
+      const size_t off = (size_t)rowoff[j] + d;
+      f32x4 kv4, vv4;
+      if constexpr (KVB) {
+        const uint2 k2 = *reinterpret_cast<const uint2*>(kb + off), v2 = *reinterpret_cast<const uint2*>(vb + off);
+        kv4 = f32x4{__uint_as_float(k2.x << 16), __uint_as_float(k2.x & 0xffff0000u), __uint_as_float(k2.y << 16),
+                    __uint_as_float(k2.y & 0xffff0000u)};
+        vv4 = f32x4{__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u), __uint_as_float(v2.y << 16),
+                    __uint_as_float(v2.y & 0xffff0000u)};
+      } else {
+        kv4 = *reinterpret_cast<const f32x4*>(kc + off);
+        vv4 = *reinterpret_cast<const f32x4*>(vc + off);
+      }
+      *reinterpret_cast<f32x4*>(&ks[j][d]) = kv4;
+      *reinterpret_cast<f32x4*>(&vs[j][d]) = vv4;
+    }
+    __syncthreads();
+    const int jmax = min(nk, pos - j0 + 1);  // causal: keys j0 .. pos
+    for (int j = 0; j < jmax; ++j) {
+      float sp = 0.f;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) sp = fmaf(q[d], ks[j][half * HD + d], sp);
+      const float sc = sp + __shfl_xor(sp, 1, WAVE);
+      const float mn = fmaxf(m, sc);
+      const float corr = expf(m - mn), p = expf(sc - mn);
+      l = l * corr + p;
+#pragma unroll
+      for (int d = 0; d < HD; ++d) o[d] = fmaf(p, vs[j][half * HD + d], o[d] * corr);
+      m = mn;
+    }
+  }
+  if (live) {
+    float* out = a.out + (size_t)row * a.ld_out + h * D + half * HD;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) out[d] = o[d] * inv;
+  }
+}
+
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  const dim3 grid((a.rows + 63) / 64, a.Hkv);
+#define S2_PA(DD, GG)                                                                                    \
+  if (a.D == DD && G == GG) {                                                                            \
+    if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_attn<DD, GG, true>), grid, dim3(2 * 64 * GG), 0, s, a);  \
+    else hipLaunchKernelGGL((k_prefill_attn<DD, GG, false>), grid, dim3(2 * 64 * GG), 0, s, a);           \
+    return hipGetLastError();                                                                            \
+  }
+  S2_PA(64, 1) S2_PA(64, 2) S2_PA(64, 4) S2_PA(64, 8)
+  S2_PA(128, 1) S2_PA(128, 2) S2_PA(128, 4) S2_PA(128, 8)
+#undef S2_PA
+  return hipErrorInvalidValue;
+}
+
 // Prompt embeddings of rows [p0, p0 + rows): text rows take embed[token]; masked rows take the
 // sum of their ten codebook rows (fp32, codebook order).
 template <bool BF16>

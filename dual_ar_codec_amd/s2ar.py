@@ -22,7 +22,7 @@ ERRORS = {-1: "S2AR_E_ARG", -2: "S2AR_E_RANGE", -3: "S2AR_E_CAPACITY", -4: "S2AR
 
 SYMBOLS = ("s2ar_create", "s2ar_prefill", "s2ar_decode_frame", "s2ar_decode_frames", "s2ar_release_stream",
            "s2ar_stream_position", "s2ar_destroy", "s2ar_last_error", "s2ar_error_name", "s2ar_debug_frame",
-           "s2ar_time_kernel")
+           "s2ar_time_kernel", "s2ar_debug_frame_batch")
 
 i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 
@@ -77,6 +77,7 @@ def lib():
         L.s2ar_error_name.restype = ctypes.c_char_p
         L.s2ar_debug_frame.argtypes = [vp, i32, vp, ctypes.POINTER(Taps)]
         L.s2ar_time_kernel.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i64)]
+        L.s2ar_debug_frame_batch.argtypes = [vp, vp, i32, vp, ctypes.POINTER(Taps)]
         _lib = L
     return _lib
 
@@ -193,6 +194,26 @@ class Context:
         self._check(lib().s2ar_debug_frame(self.h, int(stream_id), _p(f), ctypes.byref(taps)))
         out["next_c0"] = int(out["next_c0"][0])
         return out
+
+    def _tap_buffers(self):
+        cfg = self.cfg
+        Ls, Lf, H, K, NC = cfg["slow"]["n_layers"], cfg["fast"]["n_layers"], self.H, self.K, self.NC
+        return dict(slow_embed=np.zeros(H, np.float32), slow_resid=np.zeros((Ls, H), np.float32),
+                    slow_h=np.zeros(H, np.float32), slow_logits=np.zeros(self.V, np.float32),
+                    fast_resid=np.zeros((NC - 1, Lf, H), np.float32), fast_z=np.zeros((NC - 1, H), np.float32),
+                    fast_logits=np.zeros((NC - 1, K), np.float32), own_codes=np.zeros(NC, np.int32),
+                    next_c0=np.zeros(1, np.int32))
+
+    def debug_frame_batch(self, stream_ids, forced=None):
+        """Eager batched frame of several streams (the batched decode kernels) with taps."""
+        ids = np.ascontiguousarray(np.atleast_1d(stream_ids), np.int32)
+        outs = [self._tap_buffers() for _ in ids]
+        taps = (Taps * len(ids))(*[Taps(*[o[n].ctypes.data for n, _ in Taps._fields_]) for o in outs])
+        f = None if forced is None else np.ascontiguousarray(forced, np.int32)
+        self._check(lib().s2ar_debug_frame_batch(self.h, _p(ids), len(ids), _p(f), taps))
+        for o in outs:
+            o["next_c0"] = int(o["next_c0"][0])
+        return outs
 
     def time_kernel(self, which=0, iters=100):
         ms = ctypes.c_float()

@@ -156,6 +156,13 @@ typedef struct {
 
 int s2ar_debug_frame(s2ar_ctx* ctx, int32_t stream_id, const int32_t* forced_codes, s2ar_taps* taps);
 
+/* The batched multi-stream frame (the kernels s2ar_decode_frame uses for 2..16 streams), run
+ * without the captured graph: forced_codes [n][n_codebooks] or NULL, taps [n] (fast_z and
+ * slow_embed are not filled).  Needs bf16 weights and every K dimension divisible by 128
+ * (S2AR_E_ARG otherwise); n <= 16. */
+int s2ar_debug_frame_batch(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n, const int32_t* forced_codes,
+                           s2ar_taps* taps);
+
 /* Launch one kernel of the frame `iters` times on the context's stream,
  * cycling over the layers, and report the mean duration of a launch measured
  * with HIP events on that stream.  which: 0 = Slow fused RMSNorm + gate/up +

@@ -197,3 +197,90 @@ def test_errors_leave_state_unchanged():
         ctx.debug_frame(0, forced=np.full(10, cfg["codebook_size"], np.int32))
     assert e.value.code in (-2, -3)
     ctx.close()
+
+
+# ------------------------------------------------------------------------------ multi-stream
+
+def _oracle_frames_per_stream(cfg, w, prompts, n):
+    return [oracle_run(cfg, w, t, None, None, n) for t in prompts]
+
+
+def _compare_batch(ctx, ids, per_stream, cfg, rep):
+    """Drive the batched kernels teacher-forced through every stream's oracle frames."""
+    K, Vt = cfg["codebook_size"], cfg["vocab_text"]
+    n = len(per_stream[0])
+    for t in range(n):
+        forced = np.stack([fr[t]["codes"] for fr in per_stream])
+        outs = ctx.debug_frame_batch(ids, forced)
+        for b, (g, frs) in enumerate(zip(outs, per_stream)):
+            f = frs[t]
+            tag = f"stream {ids[b]} frame {t}"
+            rep.token(f"{tag} c0", int(g["own_codes"][0]), int(f["codes"][0]), f["c0_margin"])
+            for j in range(9):
+                for l in range(cfg["fast"]["n_layers"]):
+                    rep.cos(f"{tag} fast step {j + 1} layer {l}", g["fast_resid"][j, l], f["fast"]["resid"][j, l])
+                rep.logits(f"{tag} fast step {j + 1} logits", g["fast_logits"][j], f["fast"]["logits"][j])
+                rep.token(f"{tag} c{j + 1}", int(g["own_codes"][j + 1]), int(f["fast"]["codes"][j]), f["fast"]["margins"][j])
+                assert int(g["own_codes"][j + 1]) == int(np.argmax(g["fast_logits"][j]))
+            for l in range(cfg["slow"]["n_layers"]):
+                rep.cos(f"{tag} slow layer {l}", g["slow_resid"][l], f["slow"]["resid"][l])
+            rep.cos(f"{tag} slow h", g["slow_h"], f["slow"]["h"])
+            rep.logits(f"{tag} slow logits", g["slow_logits"], f["slow"]["logits"])
+            rep.token(f"{tag} next c0", int(g["next_c0"]), int(f["slow"]["c0"]), f["slow"]["margin"])
+            assert int(g["next_c0"]) == int(np.argmax(g["slow_logits"][Vt:Vt + K]))
+    return rep
+
+
+def _ragged_prompts(cfg, lens, seed):
+    return [synth.uniform_ints(seed, 900 + i, n, 0, cfg["vocab_text"]) for i, n in enumerate(lens)]
+
+
+def test_batched_multi_stream_teacher_forced_mid_ragged():
+    """Batched decode kernels (matrix-core GEMVs over several streams, ragged paged attention)."""
+    cfg = synth.config("mid", max_context=640)
+    w = synth.make_weights(cfg)
+    lens = [64, 17, 300, 130, 5]
+    prompts = _ragged_prompts(cfg, lens, 31)
+    per_stream = _oracle_frames_per_stream(cfg, w, prompts, 4)
+    ctx = _ctx(cfg, w, max_streams=6)
+    ids = [0, 2, 3, 4, 5]
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
+    _say(f"[parity] batched mid: {rep}")
+    ctx.close()
+
+
+@pytest.mark.timeout(1500)
+def test_batched_multi_stream_teacher_forced_full_shape():
+    """Batched decode at the full S2 shape, three streams with different contexts."""
+    cfg = synth.config("multi_stream", max_context=256)
+    w = synth.make_weights(cfg)
+    lens = [41, 9, 70]
+    prompts = _ragged_prompts(cfg, lens, 32)
+    per_stream = _oracle_frames_per_stream(cfg, w, prompts, 2)
+    ctx = _ctx(cfg, w, max_streams=4)
+    ids = [1, 0, 3]
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
+    _say(f"[parity] batched full: {rep}")
+    ctx.close()
+
+
+def test_batched_graph_equals_eager_batched_frame():
+    cfg = synth.config("mid", max_context=256)
+    w = synth.make_weights(cfg)
+    prompts = _ragged_prompts(cfg, [20, 33, 7], 33)
+    ids = [0, 1, 2]
+    runs = []
+    for eager in (False, True):
+        ctx = _ctx(cfg, w, max_streams=3)
+        for s_, p in zip(ids, prompts):
+            ctx.prefill(s_, p)
+        if eager:
+            runs.append(np.stack([np.stack([o["own_codes"] for o in ctx.debug_frame_batch(ids)]) for _ in range(6)]))
+        else:
+            runs.append(ctx.decode_frames(ids, 6))
+        ctx.close()
+    assert np.array_equal(runs[0], runs[1])
