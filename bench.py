@@ -53,6 +53,64 @@ def cpu_baseline(cfg, weights, budget_s: float):
             "sample": f"{frames} frames of the {cfg['name']} shape after a 1-token prompt ({dt:.1f} s, fp64 oracle)"}
 
 
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed FETCH_SIZE / WRITE_SIZE passes
+    (profiles/gate_up_hbm_traffic.json), or None when the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gate_up_hbm_traffic.json")
+    src = os.path.join(ROOT, "dual_ar_codec_amd", "csrc", "kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["kernels_hip_sha256"]:
+                return None
+        return rec["traffic_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def multi_stream(args, w, log):
+    """16 streams with ragged contexts (256..4096 random text positions, pages of 16 handed out in
+    a scrambled order), then batched decode steps: one step = one frame for every stream."""
+    import torch
+
+    from dual_ar_codec_amd import metrics, s2ar, synth
+
+    cfg = synth.config("multi_stream")
+    lens = synth.prompt_lengths(cfg)
+    n = cfg["n_streams"]
+    ctx = s2ar.Context(cfg, w, max_streams=n)
+    log(f"[bench] multi-stream prefill: {n} streams, {sum(lens)} positions")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(n):
+        toks, _, _ = synth.make_prompt(cfg, s_)
+        ctx.prefill(s_, toks)
+    torch.cuda.synchronize()
+    tp = time.perf_counter() - t0
+    ids = list(range(n))
+    ctx.decode_frames(ids, 2)  # warm-up (captures the batch graph)
+    torch.cuda.synchronize()
+    steps = args.multi_steps
+    t0 = time.perf_counter()
+    out = ctx.decode_frames(ids, steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert out.shape == (steps, n, 10)
+    ctx.close()
+    w_bytes = metrics.frame_bytes(cfg, 0)["weights"]
+    kv = sum(metrics.kv_bytes_per_position(cfg) * (L + 2 + steps // 2 + 1) for L in lens)
+    step_s = dt / steps
+    return {"workload": f"{n} streams, contexts {min(lens)}..{max(lens)} (sum {sum(lens)}), {steps} batched steps",
+            "frames_per_s": round(n / step_s, 1), "codebook_tok_s": round(10 * n / step_s, 1),
+            "ms_per_step": round(step_s * 1e3, 3), "per_stream_rtf": round(metrics.rtf(1.0 / step_s), 5),
+            "step_bytes": w_bytes + kv, "hbm_gbps": round((w_bytes + kv) / step_s / 1e9, 1),
+            "hbm_frac": round((w_bytes + kv) / step_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "prefill_s": round(tp, 2), "kv_dtype": "f32",
+            "note": "same synthetic weights as the batch-1 line (shapes identical)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,6 +120,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--kernel-iters", type=int, default=144)
     ap.add_argument("--prefill", type=int, default=1, help="also time a 1200-position voice-clone prefill")
+    ap.add_argument("--multi-steps", type=int, default=20, help="batched 16-stream decode steps (0 = skip)")
+    ap.add_argument("--copy-probe", type=int, default=0, help="run a 256 MiB copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py drives one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
@@ -130,10 +190,24 @@ def main():
     ms, nbytes = ctx.time_kernel(0, args.kernel_iters)
     k_gbps = nbytes / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                 "kernel": "k_gemv2<bf16, NCH=5, GEMV_NORM_SWIGLU, R=2, WPB=4> (Slow gate/up, 19456x2560)",
                 "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2)}
     ctx.close()
+
+    multi = None
+    if args.multi_steps > 0:
+        multi = multi_stream(args, w, log)
+
+    if args.copy_probe:
+        # a plain 256 MiB device copy, the reference for scaling HBM byte counters
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_budget > 0:
@@ -157,6 +231,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "multi_stream": multi,
     }
     print(json.dumps(line), flush=True)
 

@@ -55,9 +55,10 @@ def params_per_frame(cfg, head_rows: int | None = None) -> int:
 
 
 def kv_bytes_per_position(cfg) -> int:
-    """bf16 K and V of one Slow position over all layers."""
+    """K and V of one Slow position over all layers (fp32 cache by default, bf16 optional)."""
     s = cfg["slow"]
-    return s["n_layers"] * 2 * s["n_kv_heads"] * s["head_dim"] * 2
+    esz = 2 if cfg.get("kv_dtype", "f32") == "bf16" else 4
+    return s["n_layers"] * 2 * s["n_kv_heads"] * s["head_dim"] * esz
 
 
 def frame_bytes(cfg, context_len: int) -> dict:

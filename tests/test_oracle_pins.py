@@ -494,4 +494,5 @@ def test_byte_model_reproduces_params_per_frame():
     assert abs(slow / g["param_split"]["slow_about"] - 1) < 0.12
     assert abs(fast / g["param_split"]["fast_about"] - 1) < 0.02
     fb = metrics.frame_bytes(cfg, 100)
-    assert fb["weights"] > 15.5e9 and fb["kv"] == 147_456 * 101
+    assert fb["weights"] > 15.5e9 and fb["kv"] == 294_912 * 101  # fp32 K and V, 36 layers x 8 heads x 128
+    assert metrics.kv_bytes_per_position(dict(cfg, kv_dtype="bf16")) == 147_456
