@@ -4,15 +4,18 @@
 // once per step and used M times), but the M products per weight no longer fit the scalar FMA
 // budget.  k_mgemv maps them onto the matrix cores: 16 weight rows form the A operand of
 // v_mfma_f32_16x16x32_bf16 (straight from HBM, 64 contiguous bytes per lane), the streams'
-// activations form the 16-column B operand (staged in LDS in 128-wide K slices, split into
-// bf16 hi + lo so the product keeps ~16 activation bits).  Inside a 32-wide MFMA step the
-// k order is permuted identically for A and B, which lets each lane read contiguous weights.
-// Small-N matrices split K over several blocks and a reduction applies the epilogue in a fixed
-// split order (bitwise reproducible).
+// activations form the 16-column B operand (each lane reads its 32 fp32 activations from the
+// cache-resident input rows and splits them into bf16 hi + lo, so the product keeps ~16
+// activation bits).  Inside a 32-wide MFMA step the k order is permuted identically for A and B,
+// which lets each lane read contiguous weights and contiguous activations.  RMSNorm runs once per
+// row in k_norm_rows, which also folds the split partials of the preceding residual projection
+// in a fixed split order (bitwise reproducible).
 #include "kernels.h"
 
 #include <limits.h>
 #include <math.h>
+
+#include <algorithm>
 
 namespace s2k {
 
@@ -24,8 +27,10 @@ namespace {
 
 constexpr int WAVE = 64;
 constexpr int MB = 16;   // batch columns of one MFMA tile
-constexpr int KS = 128;  // K per staged slice
-constexpr int PD = 4;    // weight slices in flight per lane
+constexpr int KS = 128;  // K per slice (4 MFMA steps)
+constexpr int KC = 512;               // K of one activation chunk task
+constexpr int CS = KC / KS;           // slices per task (= weight slices in flight per lane)
+constexpr int XROW = KC + 8;          // LDS row stride in bf16 (padded against bank conflicts)
 
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   uint32_t a = __float_as_uint(f);
@@ -56,96 +61,263 @@ __device__ __forceinline__ float load_w(const void* p, size_t i) {
 
 }  // namespace
 
-// grid = (ceil(N / 64), S); block = 4 wavefronts, wavefront w owns weight rows
-// [64 bx + 16 w, +16) over the block's K range [K/S * by, K/S * (by + 1)).
+int mgemv_tiles(int N) { return (N + 63) / 64; }
+
+// LDS-only barrier: the fences are restricted to the local address space, so pending global
+// loads (the weight stream) and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Weights come in the tiled layout of k_tile_weights (each load instruction of a wavefront reads
+// 1 KB of contiguous memory; a row-major read of 16 rows would touch 64 separate lines).
+// Work items are (64-row tile, K split) pairs, numbered split-major (item = split * tiles + tile);
+// block b runs items [b * ipb, (b + 1) * ipb), each as K/S/512 chunk tasks of four 128-K slices.
+// Wavefront w owns rows [64 tile + 16 w, +16).  Per task the block's 16 activation rows of the
+// chunk go through LDS as bf16 hi + lo.  The pipeline is one task deep and free of conditional
+// loads (clamped addresses): during task t each thread first loads its share of task t+1's
+// activations, then, slice by slice, task t+1's weights, so waiting for the activations never
+// drains the weight stream.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
-  __shared__ __attribute__((aligned(16))) float xs[2][MB][KS + 4];
-  __shared__ float bv_s[4][MB];
-  __shared__ int bi_s[4][MB];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MB * XROW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 64 + w * 16;
-  const int kspan = a.K / a.S;
-  const int k0 = blockIdx.y * kspan;
-  const int nsl = kspan / KS;
-  const int row = min(n0 + i, a.N - 1);
-  const uint16_t* wr = a.w + (size_t)row * a.K + k0 + 32 * g;
+  const int ntiles = (a.N + 63) / 64;
+  const int it0 = blockIdx.x * a.ipb;
+  const int it1 = min(it0 + a.ipb, ntiles * a.S);
+  if (it0 >= it1) return;
+  const int kspan = a.K / a.S, nch = kspan / KC;
+  const int t0 = it0 * nch, t1 = it1 * nch;  // chunk tasks of this block
 
-  u32x4 wb[PD][4];
-  auto issue = [&](u32x4 (&d)[4], int sl) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(wr + sl * KS);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) d[t] = __builtin_nontemporal_load(p + t);
+  // activation share of a thread: row xr_row, 32 columns from xr_col of the chunk
+  const int xr_row = tid >> 4, xr_col = (tid & 15) * 32;
+  const float* xrow = a.x + (size_t)min(xr_row, a.M - 1) * a.ldx + xr_col;
+  const bool xlive = xr_row < a.M;
+  auto task_k = [&](int t, int& tile) {  // absolute K start of task t, and its tile
+    const int it = t / nch, ch = t - it * nch;
+    const int split = it / ntiles;
+    tile = it - split * ntiles;
+    return split * kspan + ch * KC;
   };
-#pragma unroll
-  for (int d = 0; d < PD; ++d)
-    if (d < nsl) issue(wb[d], d);
-
-  // X slice staging: thread t covers stream t / 16, k (t % 16) * 8 .. + 8 of the slice
-  const int xj = tid >> 4, xk = (tid & 15) * 8;
-  const float xsc = (xj < a.M && a.x_scale) ? a.x_scale[xj] : 1.0f;
-  auto stage = [&](int sl, int buf) {
-    f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-    const int k = k0 + sl * KS + xk;
-    if (xj < a.M) {
-      const float* src = a.x + (size_t)xj * a.ldx + k;
-      v0 = *reinterpret_cast<const f32x4*>(src);
-      v1 = *reinterpret_cast<const f32x4*>(src + 4);
-      if (a.gain) {
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gain + k);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gain + k + 4);
-        v0 = v0 * g0 * xsc;
-        v1 = v1 * g1 * xsc;
-      }
-    }
-    *reinterpret_cast<f32x4*>(&xs[buf][xj][xk]) = v0;
-    *reinterpret_cast<f32x4*>(&xs[buf][xj][xk + 4]) = v1;
+  const int ksl = a.K / KS;
+  auto wtile = [&](int tile, int k) {  // lane's first 16 B of slice k / 128 of its 16-row tile
+    return a.w + ((size_t)(tile * 4 + w) * ksl + k / KS) * (4 * 512) + lane * 8;
   };
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsl; s0 += PD) {
+  f32x4 xr[8];
+  u32x4 wb[CS][4];
+  {
+    int tile;
+    const int k = task_k(t0, tile);
+    const f32x4* q = reinterpret_cast<const f32x4*>(xrow + k);
 #pragma unroll
-    for (int d = 0; d < PD; ++d) {  // unrolled so that wb[d] is indexed statically
-      const int sl = s0 + d;
-      if (sl < nsl) {
-        const int buf = sl & 1;
-        stage(sl, buf);
-        __syncthreads();
+    for (int u = 0; u < 8; ++u) xr[u] = q[u];
+    const uint16_t* wr = wtile(tile, k);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // MFMA slot group g of step t holds k = 32 g + 8 t .. + 8 of this slice (same map for A and B)
-          const float* xp = &xs[buf][i][32 * g + 8 * t];
-          bf16x8 xh, xl;
-          split8(xp, xh, xl);
-          const bf16x8 wf = __builtin_bit_cast(bf16x8, wb[d][t]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xh, acc, 0, 0, 0);
-        }
-        if (sl + PD < nsl) issue(wb[d], sl + PD);
-      }
-    }
+    for (int sl = 0; sl < CS; ++sl)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        wb[sl][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (sl * 4 + t) * 512));
   }
 
-  // lane holds D[row 4 g + r][stream i] for r = 0..3
-  const int j = i;
-  if constexpr (EPI == MG_ARGMAX) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int t = t0; t < t1; ++t) {
+    // activations of task t -> LDS (hi, lo)
+    lds_barrier();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = n0 + 4 * g + r;
-      if (n < a.N && j < a.M) {
-        a.out[(size_t)j * a.ldo + n] = acc[r];
-        if (n >= a.am_lo && n < a.am_hi && acc[r] > bv) {
-          bv = acc[r];
-          bi = n;
+    for (int u = 0; u < 4; ++u) {
+      float v[8];
+      v[0] = xr[2 * u].x; v[1] = xr[2 * u].y; v[2] = xr[2 * u].z; v[3] = xr[2 * u].w;
+      v[4] = xr[2 * u + 1].x; v[5] = xr[2 * u + 1].y; v[6] = xr[2 * u + 1].z; v[7] = xr[2 * u + 1].w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = xlive ? v[e] : 0.f;
+      bf16x8 hi, lo;
+      split8(v, hi, lo);
+      *reinterpret_cast<bf16x8*>(&xs[0][xr_row * XROW + xr_col + 8 * u]) = hi;
+      *reinterpret_cast<bf16x8*>(&xs[1][xr_row * XROW + xr_col + 8 * u]) = lo;
+    }
+    lds_barrier();
+    // next task (the last one repeats itself): activations first, then weights slice by slice
+    int ntile;
+    const int nk = task_k(min(t + 1, t1 - 1), ntile);
+    {
+      const f32x4* q = reinterpret_cast<const f32x4*>(xrow + nk);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) xr[u] = q[u];
+    }
+    const uint16_t* nwr = wtile(ntile, nk);
+#pragma unroll
+    for (int sl = 0; sl < CS; ++sl) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        // MFMA slot group g of step st holds k = 32 g + 8 st .. + 8 of the slice (same map for A and B)
+        const int kl = sl * KS + 32 * g + 8 * st;
+        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&xs[0][i * XROW + kl]);
+        const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&xs[1][i * XROW + kl]);
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, wb[sl][st]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xh, acc, 0, 0, 0);
+      }
+      // keep the reload of wb[sl] after its last use, so it lands in the same registers
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        wb[sl][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(nwr + (sl * 4 + st) * 512));
+    }
+    const int it = t / nch;
+    if (t - it * nch == nch - 1) {
+      // item done: lane holds D[row 4 g + r][stream i], r = 0..3
+      const int split = it / ntiles, tile = it - split * ntiles;
+      const int n0 = tile * 64 + w * 16 + 4 * g;
+      if (EPI == MG_ARGMAX && a.S == 1) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + r;
+          if (n < a.N && i < a.M) {
+            a.out[(size_t)i * a.ldo + n] = acc[r];
+            if (n >= a.am_lo && n < a.am_hi && acc[r] > bv) {
+              bv = acc[r];
+              bi = n;
+            }
+          }
+        }
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) {
+          const float ov = __shfl_xor(bv, o, WAVE);
+          const int oi = __shfl_xor(bi, o, WAVE);
+          if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        if (g == 0) {
+          a.am_val[(size_t)(tile * 4 + w) * MB + i] = bv;
+          a.am_idx[(size_t)(tile * 4 + w) * MB + i] = bi;
+        }
+      } else if (a.S > 1 || EPI == MG_ADD) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + r;
+          if (n < a.N && i < a.M) a.part[((size_t)split * a.M + i) * a.N + n] = acc[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + r;
+          if (i >= a.M || n >= a.N) continue;
+          if constexpr (EPI == MG_STORE) a.out[(size_t)i * a.ldo + n] = acc[r];
+          else if constexpr (EPI == MG_SWIGLU) {
+            if ((r & 1) == 0) a.out[(size_t)i * a.ldo + (n >> 1)] = acc[r] / (1.0f + expf(-acc[r])) * acc[r + 1];
+          }
         }
       }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // reduce over the 4 row groups (lanes j, j+16, j+32, j+48), then over the 4 wavefronts
+  }
+}
+
+// Tiled copy of a row-major bf16 matrix [N][K] (K a multiple of 128) for k_mgemv: rows are padded
+// with zeros to a multiple of 64; the 16-row x 128-K block (16-row tile t, slice s) is 4 KB at
+// ((t * K / 128 + s) * 4) * 512 elements, and inside it MFMA step st of lane l = i + 16 g holds the
+// 8 elements W[16 t + i][128 s + 32 g + 8 st ...] at (st * 64 + l) * 8.
+__global__ __launch_bounds__(256) void k_tile_weights(const uint16_t* src, uint16_t* dst, int N, int K,
+                                                      size_t units) {
+  const int ksl = K / KS;
+  for (size_t o = blockIdx.x * (size_t)256 + threadIdx.x; o < units; o += (size_t)gridDim.x * 256) {
+    const int lane = (int)(o & 63), st = (int)((o >> 6) & 3);
+    const size_t rest = o >> 8;
+    const int sl = (int)(rest % ksl);
+    const size_t t16 = rest / ksl;
+    const size_t n = t16 * 16 + (lane & 15);
+    const int k = sl * KS + 32 * (lane >> 4) + 8 * st;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < (size_t)N) v = *reinterpret_cast<const u32x4*>(src + n * K + k);
+    *reinterpret_cast<u32x4*>(dst + o * 8) = v;
+  }
+}
+
+size_t tiled_weight_elems(int N, int K) { return (size_t)mgemv_tiles(N) * 64 * K; }
+
+hipError_t launch_tile_weights(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t s) {
+  if (K % KS) return hipErrorInvalidValue;
+  const size_t units = tiled_weight_elems(N, K) / 8;
+  hipLaunchKernelGGL(k_tile_weights, dim3((unsigned)std::min<size_t>((units + 255) / 256, 65536)), dim3(256), 0, s,
+                     src, dst, N, K, units);
+  return hipGetLastError();
+}
+
+// Fold pending split partials of an MG_ADD launch into the residual rows (split order), then
+// RMSNorm: xn[j] = x[j] / sqrt(mean(x[j]^2) + eps) * gain.  One 1024-thread block per batch row;
+// the partial loads are issued eight at a time, the second pass re-reads the thread's own
+// (cache-resident) elements.
+__global__ __launch_bounds__(1024) void k_norm_rows(NormRowsArgs a) {
+  __shared__ float red[16];
+  const int j = blockIdx.x;
+  float* x = a.x + (size_t)j * a.ldx;
+  const size_t pstride = (size_t)a.M * a.H;
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < a.H; e += 1024) {
+    float t = x[e];
+    const float* p = a.part + (size_t)j * a.H + e;
+    int s = 0;
+    for (; s + 8 <= a.S; s += 8) {
+      float v[8];
 #pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
+      for (int u = 0; u < 8; ++u) v[u] = p[(s + u) * pstride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t += v[u];
+    }
+    for (; s < a.S; ++s) t += p[s * pstride];
+    if (a.S > 0) x[e] = t;
+    ss = fmaf(t, t, ss);
+  }
+  if (!a.xn) return;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += red[w];
+  const float scale = rsqrtf(tot / (float)a.H + a.eps);
+  float* xn = a.xn + (size_t)j * a.ldx;
+  for (int e = threadIdx.x; e < a.H; e += 1024) xn[e] = x[e] * scale * a.gain[e];
+}
+
+hipError_t launch_norm_rows(const NormRowsArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_norm_rows, dim3(a.M), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+// Sum the K splits in split order and apply the epilogue.  grid = (ceil(N / 256), M).
+// MG_ARGMAX: logits plus the per-16-row-group maxima over [am_lo, am_hi).
+template <int EPI>
+__global__ __launch_bounds__(256) void k_mgemv_reduce(const MgemvArgs a) {
+  const int j = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const bool live = n < a.N;
+  float v = 0.f;
+  if (live)
+    for (int s = 0; s < a.S; ++s) v += a.part[((size_t)s * a.M + j) * a.N + n];
+  if constexpr (EPI == MG_STORE) {
+    if (live) a.out[(size_t)j * a.ldo + n] = v;
+  } else if constexpr (EPI == MG_SWIGLU) {
+    if (live && (n & 1) == 0) {
+      float u = 0.f;
+      for (int s = 0; s < a.S; ++s) u += a.part[((size_t)s * a.M + j) * a.N + n + 1];
+      a.out[(size_t)j * a.ldo + (n >> 1)] = v / (1.0f + expf(-v)) * u;
+    }
+  } else if constexpr (EPI == MG_ARGMAX) {
+    if (live) a.out[(size_t)j * a.ldo + n] = v;
+    float bv = (live && n >= a.am_lo && n < a.am_hi) ? v : -INFINITY;
+    int bi = (live && n >= a.am_lo && n < a.am_hi) ? n : INT_MAX;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
       const float ov = __shfl_xor(bv, o, WAVE);
       const int oi = __shfl_xor(bi, o, WAVE);
       if (ov > bv || (ov == bv && oi < bi)) {
@@ -153,71 +325,23 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
         bi = oi;
       }
     }
-    if (lane < 16) {
-      bv_s[w][lane] = bv;
-      bi_s[w][lane] = bi;
-    }
-    __syncthreads();
-    if (tid < MB) {
-      float v = bv_s[0][tid];
-      int ix = bi_s[0][tid];
-      for (int ww = 1; ww < 4; ++ww)
-        if (bv_s[ww][tid] > v || (bv_s[ww][tid] == v && bi_s[ww][tid] < ix)) {
-          v = bv_s[ww][tid];
-          ix = bi_s[ww][tid];
-        }
-      a.am_val[(size_t)blockIdx.x * MB + tid] = v;
-      a.am_idx[(size_t)blockIdx.x * MB + tid] = ix;
-    }
-  } else if (a.S > 1) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = n0 + 4 * g + r;
-      if (n < a.N && j < a.M) a.part[((size_t)blockIdx.y * a.M + j) * a.N + n] = acc[r];
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = n0 + 4 * g + r;
-      if (j >= a.M || n >= a.N) continue;
-      if constexpr (EPI == MG_STORE) a.out[(size_t)j * a.ldo + n] = acc[r];
-      else if constexpr (EPI == MG_ADD) a.out[(size_t)j * a.ldo + n] += acc[r];
-      else if constexpr (EPI == MG_SWIGLU) {
-        if ((r & 1) == 0) a.out[(size_t)j * a.ldo + (n >> 1)] = acc[r] / (1.0f + expf(-acc[r])) * acc[r + 1];
-      }
+    if ((n & 15) == 0 && n < a.N) {
+      a.am_val[(size_t)(n >> 4) * MB + j] = bv;
+      a.am_idx[(size_t)(n >> 4) * MB + j] = bi;
     }
   }
 }
-
-// Sum the K splits in split order and apply the epilogue.  grid = (ceil(N / 256), M).
-template <int EPI>
-__global__ __launch_bounds__(256) void k_mgemv_reduce(const MgemvArgs a) {
-  const int j = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= a.N) return;
-  float v = 0.f;
-  for (int s = 0; s < a.S; ++s) v += a.part[((size_t)s * a.M + j) * a.N + n];
-  if constexpr (EPI == MG_STORE) a.out[(size_t)j * a.ldo + n] = v;
-  else if constexpr (EPI == MG_ADD) a.out[(size_t)j * a.ldo + n] += v;
-  else if constexpr (EPI == MG_SWIGLU) {
-    if ((n & 1) == 0) {
-      float u = 0.f;
-      for (int s = 0; s < a.S; ++s) u += a.part[((size_t)s * a.M + j) * a.N + n + 1];
-      a.out[(size_t)j * a.ldo + (n >> 1)] = v / (1.0f + expf(-v)) * u;
-    }
-  }
-}
-
-int mgemv_blocks(int N) { return (N + 63) / 64; }
 
 hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s) {
-  if (a.M < 1 || a.M > MB || a.K % (KS * a.S) || (a.epi == MG_ARGMAX && a.S != 1)) return hipErrorInvalidValue;
-  const dim3 grid(mgemv_blocks(a.N), a.S);
+  const int items = mgemv_tiles(a.N) * a.S;
+  if (a.M < 1 || a.M > MB || a.S < 1 || a.K % a.S || (a.K / a.S) % KC || a.ipb < 1)
+    return hipErrorInvalidValue;
+  const dim3 grid((items + a.ipb - 1) / a.ipb);
 #define S2_MG(E)                                                                                      \
   case E:                                                                                             \
     hipLaunchKernelGGL(k_mgemv<E>, grid, dim3(256), 0, s, a);                                         \
-    if (a.S > 1 && E != MG_ARGMAX) hipLaunchKernelGGL(k_mgemv_reduce<E>, dim3((a.N + 255) / 256, a.M), \
-                                                      dim3(256), 0, s, a);                            \
+    if (a.S > 1 && E != MG_ADD)                                                                       \
+      hipLaunchKernelGGL(k_mgemv_reduce<E>, dim3((a.N + 255) / 256, a.M), dim3(256), 0, s, a);        \
     break;
   switch (a.epi) {
     S2_MG(MG_STORE)
@@ -297,7 +421,7 @@ __global__ __launch_bounds__(256) void k_finish_b(const FinishBArgs f) {
     // h[slot] = RMSNorm of the stream's residual (the vector the Slow head saw); it is also
     // the input of the next frame's first Fast step
     if (e < f.H) {
-      const float hv = f.x_res[(size_t)b * f.ldx + e] * f.scale[b] * f.gain[e];
+      const float hv = f.x_res[(size_t)b * f.ldx + e];  // already RMS-normalised with the final gain
       f.h[(size_t)slot * f.H + e] = hv;
       x[e] = hv;
       if (f.xf_slot) f.xf_slot[(size_t)slot * f.ld_xf_slot + e] = hv;

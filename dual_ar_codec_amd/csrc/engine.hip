@@ -37,6 +37,8 @@ struct LayerW {
   float* mlp_norm = nullptr;
   float* q_norm = nullptr;
   float* k_norm = nullptr;
+  // tiled copies of the four matrices for the batched multi-stream GEMVs (k_mgemv layout)
+  uint16_t *tqkv = nullptr, *to = nullptr, *tgu = nullptr, *tdown = nullptr;
 };
 
 struct Graph {
@@ -61,6 +63,7 @@ struct s2ar_ctx {
   void* slow_head = nullptr;
   void* codebook = nullptr;
   void* fast_head = nullptr;
+  uint16_t *slow_head_t = nullptr, *fast_head_t = nullptr;  // tiled copies (batched decode)
   float* slow_final = nullptr;
   float* fast_final = nullptr;
   std::vector<LayerW> slow, fast;
@@ -120,7 +123,7 @@ struct s2ar_ctx {
   // batched multi-stream decode (up to 16 streams per launch, MFMA GEMVs)
   bool batched_ok = false;
   float *bx = nullptr, *bxf = nullptr, *bqkv = nullptr, *batt = nullptr, *bact = nullptr;
-  float *blogits = nullptr, *bscale = nullptr, *bpart = nullptr, *bam_val = nullptr;
+  float *blogits = nullptr, *bxn = nullptr, *bpart = nullptr, *bam_val = nullptr;
   int* bam_idx = nullptr;
   float *batt_ml = nullptr, *batt_o = nullptr;
   size_t bpart_floats = 0;
@@ -513,10 +516,10 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   }
   C_TRY(host_alloc(c, &c->h_pos_stage, sizeof(int) * 16));
 
-  // batched decode buffers (bf16 weights, every K a multiple of 128)
+  // batched decode buffers (bf16 weights, every K a multiple of 512)
   {
     auto k_ok = [](const s2ar_stack& st) {
-      return st.hidden % 128 == 0 && (st.n_q_heads * st.head_dim) % 128 == 0 && st.ffn % 128 == 0;
+      return st.hidden % 512 == 0 && (st.n_q_heads * st.head_dim) % 512 == 0 && st.ffn % 512 == 0;
     };
     c->batched_ok = c->bf16 && g.max_streams > 1 && k_ok(g.slow) && k_ok(g.fast);
     if (c->batched_ok) {
@@ -531,12 +534,39 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
       C_TRY(dev_alloc(c, &c->batt, sizeof(float) * MBt * qd_max));
       C_TRY(dev_alloc(c, &c->bact, sizeof(float) * MBt * f_max));
       C_TRY(dev_alloc(c, &c->blogits, sizeof(float) * MBt * V));
-      C_TRY(dev_alloc(c, &c->bscale, sizeof(float) * MBt));
-      c->bpart_floats = (size_t)32 * MBt * std::max(qkvd_max, std::max(H, 2 * f_max));
+      C_TRY(dev_alloc(c, &c->bxn, sizeof(float) * MBt * s2k::pad_k(H)));
+      c->bpart_floats = (size_t)32 * MBt * std::max(std::max(qkvd_max, (int)K), std::max(H, 2 * f_max));
       C_TRY(dev_alloc(c, &c->bpart, sizeof(float) * c->bpart_floats));
-      const int nbm = s2k::mgemv_blocks((int)V);
-      C_TRY(dev_alloc(c, &c->bam_val, sizeof(float) * (size_t)nbm * MBt));
-      C_TRY(dev_alloc(c, &c->bam_idx, sizeof(int) * (size_t)nbm * MBt));
+      const int ngroups = 4 * s2k::mgemv_tiles((int)V);  // 16-row argmax groups
+      C_TRY(dev_alloc(c, &c->bam_val, sizeof(float) * (size_t)ngroups * MBt));
+      C_TRY(dev_alloc(c, &c->bam_idx, sizeof(int) * (size_t)ngroups * MBt));
+      // tiled weight copies for the batched GEMVs; dev_alloc zeroes on the null stream, which the
+      // non-blocking engine stream does not wait for, so every buffer is allocated (and the device
+      // synchronised) before the tiling kernels run
+      struct TileJob {
+        const void* src;
+        int N, K;
+        uint16_t** dst;
+      };
+      std::vector<TileJob> jobs;
+      for (int pass = 0; pass < 2; ++pass) {
+        const s2ar_stack& st = pass ? g.fast : g.slow;
+        std::vector<LayerW>& W = pass ? c->fast : c->slow;
+        const int qd = st.n_q_heads * st.head_dim, qkvd = (st.n_q_heads + 2 * st.n_kv_heads) * st.head_dim;
+        for (LayerW& L : W) {
+          jobs.push_back({L.wqkv, qkvd, st.hidden, &L.tqkv});
+          jobs.push_back({L.wo, st.hidden, qd, &L.to});
+          jobs.push_back({L.wgu, 2 * st.ffn, st.hidden, &L.tgu});
+          jobs.push_back({L.wdown, st.hidden, st.ffn, &L.tdown});
+        }
+      }
+      jobs.push_back({c->slow_head, (int)V, H, &c->slow_head_t});
+      jobs.push_back({c->fast_head, K, H, &c->fast_head_t});
+      for (const TileJob& j : jobs) C_TRY(dev_alloc(c, j.dst, sizeof(uint16_t) * s2k::tiled_weight_elems(j.N, j.K)));
+      C_HIP(hipDeviceSynchronize());
+      for (const TileJob& j : jobs)
+        C_HIP(s2k::launch_tile_weights(static_cast<const uint16_t*>(j.src), *j.dst, j.N, j.K, c->stream));
+      C_HIP(hipStreamSynchronize(c->stream));
       C_TRY(dev_alloc(c, &c->batt_ml, sizeof(float) * 2 * MBt * hq * c->max_splits));
       C_TRY(dev_alloc(c, &c->batt_o, sizeof(float) * (size_t)MBt * hq * c->max_splits * dmax));
       C_TRY(dev_alloc(c, &c->d_dbg_slots, sizeof(int) * MBt));
@@ -821,13 +851,13 @@ struct Enq {
   };
   const BTap* btp = nullptr;  // [M] when running the eager batched frame
   const int* bslots_host = nullptr;
-  void mgemv(int epi, const void* w, const float* x, int ldx, const float* scale, const float* gain, float* out,
-             int ldo, int N, int K, int M, int lo = 0, int hi = 0) {
+  // returns the number of K splits; an MG_ADD launch leaves that many partials in bpart for the
+  // next norm_b to fold into the residual
+  int mgemv(int epi, const void* w, const float* x, int ldx, float* out, int ldo, int N, int K, int M, int lo = 0,
+            int hi = 0) {
     s2k::MgemvArgs a{};
     a.x = x;
     a.ldx = ldx;
-    a.x_scale = scale;
-    a.gain = gain;
     a.w = static_cast<const uint16_t*>(w);
     a.out = out;
     a.ldo = ldo;
@@ -840,21 +870,48 @@ struct Enq {
     a.am_hi = hi;
     a.am_val = c->bam_val;
     a.am_idx = c->bam_idx;
-    // split K until the launch has about two blocks per CU (K / 128 divisible by S)
-    a.S = 1;
-    if (epi != s2k::MG_ARGMAX) {
-      const int nb = s2k::mgemv_blocks(N), slices = K / 128;
-      for (int S = 1; S <= 32; ++S) {
-        if (slices % S) continue;
-        if ((size_t)S * M * N > c->bpart_floats) break;
-        a.S = S;
-        if (nb * S >= 2 * s2k::device_cus()) break;
-      }
+    // Work split: T = tiles * K / 512 chunk tasks; blocks of 2-3 tasks stream best (fewer, longer
+    // blocks leave HBM idle at the start, more, shorter ones pay the pipeline fill per block).  An
+    // item spans nch chunks (a divisor of K / 512, as large as the task budget allows, fewer split
+    // partials); the Slow head keeps whole rows per item so that the argmax stays in the kernel.
+    const int tiles = s2k::mgemv_tiles(N), chunks = K / 512;
+    const long T = (long)tiles * chunks;
+    const int tpb = T >= 768 ? 3 : T >= 320 ? 2 : 1;
+    int nch = 1;
+    if (epi == s2k::MG_ARGMAX && tiles >= 512) nch = chunks;
+    else
+      for (int d = 1; d <= tpb; ++d)
+        if (chunks % d == 0) nch = d;
+    while ((size_t)(chunks / nch) * M * N > c->bpart_floats && nch < chunks) {
+      ++nch;
+      while (chunks % nch) ++nch;
     }
+    a.S = chunks / nch;
+    a.ipb = std::max(1, tpb / nch);
     chk(s2k::launch_mgemv(a, s));
+    return a.S;
   }
 
-  void layers_b(bool is_slow, int M, const int* slots, float* xres) {
+  // fold `pending` residual partials into xres, then bxn = RMSNorm(xres) * gain (gain == nullptr:
+  // fold only)
+  void norm_b(float* xres, int& pending, int H, int M, const float* gain) {
+    s2k::NormRowsArgs n{};
+    n.x = xres;
+    n.ldx = s2k::pad_k(c->cfg.slow.hidden);
+    n.part = c->bpart;
+    n.S = pending;
+    n.M = M;
+    n.H = H;
+    n.gain = gain;
+    n.eps = (float)c->cfg.rms_eps;
+    n.xn = gain ? c->bxn : nullptr;
+    chk(s2k::launch_norm_rows(n, s));
+    pending = 0;
+  }
+
+  // leaves the last down projection's partials pending (returned) for the final norm
+  int layers_b(bool is_slow, int M, const int* slots, float* xres) {
+    int pending = 0;
     const s2ar_config& g = c->cfg;
     const s2ar_stack& st = is_slow ? g.slow : g.fast;
     const std::vector<LayerW>& W = is_slow ? c->slow : c->fast;
@@ -863,8 +920,8 @@ struct Enq {
     const float eps = (float)g.rms_eps;
     for (int l = 0; l < st.n_layers; ++l) {
       const LayerW& L = W[l];
-      chk(s2k::launch_row_rms(xres, ldx, H, eps, c->bscale, M, s));
-      mgemv(s2k::MG_STORE, L.wqkv, xres, ldx, c->bscale, L.attn_norm, c->bqkv, qkvd, qkvd, H, M);
+      norm_b(xres, pending, H, M, L.attn_norm);
+      mgemv(s2k::MG_STORE, L.tqkv, c->bxn, ldx, c->bqkv, qkvd, qkvd, H, M);
       s2k::AttnArgs a{};
       a.qkv = c->bqkv;
       a.q_norm = L.q_norm;
@@ -906,16 +963,19 @@ struct Enq {
       }
       chk(s2k::launch_attention(a, s));
       if (a.max_splits > 1) chk(s2k::launch_attention_combine(a, s));
-      mgemv(s2k::MG_ADD, L.wo, c->batt, qd, nullptr, nullptr, xres, ldx, H, qd, M);
-      chk(s2k::launch_row_rms(xres, ldx, H, eps, c->bscale, M, s));
-      mgemv(s2k::MG_SWIGLU, L.wgu, xres, ldx, c->bscale, L.mlp_norm, c->bact, F, 2 * F, H, M);
-      mgemv(s2k::MG_ADD, L.wdown, c->bact, F, nullptr, nullptr, xres, ldx, H, F, M);
-      if (btp)
+      pending = mgemv(s2k::MG_ADD, L.to, c->batt, qd, nullptr, 0, H, qd, M);
+      norm_b(xres, pending, H, M, L.mlp_norm);
+      mgemv(s2k::MG_SWIGLU, L.tgu, c->bxn, ldx, c->bact, F, 2 * F, H, M);
+      pending = mgemv(s2k::MG_ADD, L.tdown, c->bact, F, nullptr, 0, H, F, M);
+      if (btp) {
+        norm_b(xres, pending, H, M, nullptr);
         for (int b = 0; b < M; ++b) {
           float* dst = is_slow ? btp[b].slow_resid : btp[b].fast_resid;
           if (dst) d2h(dst + (size_t)(is_slow ? l : tap_step * st.n_layers + l) * H, xres + (size_t)b * ldx, sizeof(float) * H);
         }
+      }
     }
+    return pending;
   }
   int tap_step = 0;
 
@@ -924,8 +984,8 @@ struct Enq {
     s2k::FinishBArgs f{};
     f.am_val = c->bam_val;
     f.am_idx = c->bam_idx;
-    f.b0 = lo / 64;
-    f.b1 = (hi - 1) / 64;
+    f.b0 = lo / 16;
+    f.b1 = (hi - 1) / 16;
     f.lo = lo;
     f.mode = mode;
     f.j = j;
@@ -937,9 +997,7 @@ struct Enq {
     f.h = c->d_h;
     f.x = x;
     f.ldx = s2k::pad_k(g.slow.hidden);
-    f.x_res = c->bx;
-    f.scale = c->bscale;
-    f.gain = c->slow_final;
+    f.x_res = c->bxn;
     f.xf_slot = c->xf;
     f.ld_xf_slot = s2k::pad_k(g.slow.hidden);
     f.H = g.slow.hidden;
@@ -966,9 +1024,9 @@ struct Enq {
       if (btp && j > 1)  // eager frame: the input honours forced codes
         chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, slots, c->d_codes, j, c->bxf, ldx, M, s));
       tap_step = j - 1;
-      layers_b(false, M, slots, c->bxf);
-      chk(s2k::launch_row_rms(c->bxf, ldx, H, eps, c->bscale, M, s));
-      mgemv(s2k::MG_ARGMAX, c->fast_head, c->bxf, ldx, c->bscale, c->fast_final, c->blogits, K, K, H, M, 0, K);
+      int pending = layers_b(false, M, slots, c->bxf);
+      norm_b(c->bxf, pending, H, M, c->fast_final);
+      mgemv(s2k::MG_ARGMAX, c->fast_head_t, c->bxn, ldx, c->blogits, K, K, H, M, 0, K);
       if (btp) {
         finish_b(s2k::FIN_CODE, j, M, slots, 0, K, c->bxf);
         for (int b = 0; b < M; ++b) {
@@ -983,10 +1041,9 @@ struct Enq {
     }
     if (btp)
       chk(s2k::launch_embed_codes(c->bf16, c->codebook, K, H, NC, slots, c->d_codes, c->d_snap, c->bx, ldx, M, s));
-    layers_b(true, M, slots, c->bx);
-    chk(s2k::launch_row_rms(c->bx, ldx, H, eps, c->bscale, M, s));
-    mgemv(s2k::MG_ARGMAX, c->slow_head, c->bx, ldx, c->bscale, c->slow_final, c->blogits, V, V, H, M, g.vocab_text,
-          V);
+    int pending = layers_b(true, M, slots, c->bx);
+    norm_b(c->bx, pending, H, M, c->slow_final);
+    mgemv(s2k::MG_ARGMAX, c->slow_head_t, c->bxn, ldx, c->blogits, V, V, H, M, g.vocab_text, V);
     finish_b(s2k::FIN_SLOW, 0, M, slots, g.vocab_text, V, c->bxf);
     if (btp)
       for (int b = 0; b < M; ++b) {

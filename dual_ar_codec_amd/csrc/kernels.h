@@ -164,27 +164,44 @@ hipError_t launch_advance(const int* slots, int* pos, int M, hipStream_t s);
 
 // ---- batched multi-stream decode (batch.hip) ----
 enum MgemvEpi : int { MG_STORE = 0, MG_ADD = 1, MG_SWIGLU = 2, MG_ARGMAX = 3 };
-// out[j][n] (=, +=) sum_k W[n][k] * x[j][k] * x_scale[j] * gain[k] for batch rows j < M <= 16, on
-// the matrix cores.  K must be a multiple of 128 * S; S > 1 splits K over blocks and reduces the
-// partials in split order.  MG_SWIGLU: W rows (2i, 2i+1) = (gate_i, up_i), out[j][i] = silu(g) u.
-// MG_ARGMAX (S == 1): out = logits and per-(block, row) maxima over rows [am_lo, am_hi).
+// out[j][n] = sum_k W[n][k] * x[j][k] for batch rows j < M <= 16, on the matrix cores (x already
+// normalised).  K splits into S ranges, each a multiple of 512; blocks run ipb (64-row tile,
+// split) items each.  MG_STORE / MG_SWIGLU reduce the splits in split
+// order; MG_ADD leaves part[s][j][n] for k_norm_rows to fold into the residual.  MG_SWIGLU: W rows
+// (2i, 2i+1) = (gate_i, up_i), out[j][i] = silu(g) u.  MG_ARGMAX: out = logits and
+// am_val/am_idx[16-row group][j] = maxima over rows [am_lo, am_hi) (ties to the lowest row).
 struct MgemvArgs {
-  const float* x;          // [M][ldx] fp32 batch rows
+  const float* x;          // [M][ldx] fp32 batch rows (normalised where a norm precedes)
   int ldx;
-  const float* x_scale;    // [M] RMSNorm row scale or nullptr
-  const float* gain;       // [K] RMSNorm gain or nullptr
-  const uint16_t* w;       // [N][K] bf16
+  const uint16_t* w;       // bf16 [N][K] in the tiled layout of launch_tile_weights
   float* out;              // [M][ldo]
   int ldo;
-  float* part;             // [S][M][N] split partials (S > 1)
+  float* part;             // [S][M][N] split partials (S > 1, and always for MG_ADD)
   int M, N, K, S;
+  int ipb;                 // items per block
   int epi;
   int am_lo, am_hi;
-  float* am_val;           // [blocks][16]
+  float* am_val;           // [N / 16][16]
   int* am_idx;
 };
-int mgemv_blocks(int N);
+int mgemv_tiles(int N);
 hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s);
+// Tiled copy for k_mgemv of a row-major bf16 [N][K] matrix (K a multiple of 128): 16-row x 128-K
+// blocks of 4 KB, rows zero-padded to a multiple of 64; tiled_weight_elems(N, K) elements.
+size_t tiled_weight_elems(int N, int K);
+hipError_t launch_tile_weights(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t s);
+
+// x[j] += sum_s part[s][j] (split order, when S > 0); xn[j] = RMSNorm(x[j]) * gain.  M rows.
+struct NormRowsArgs {
+  float* x;
+  int ldx;
+  const float* part;       // [S][M][H] pending residual partials
+  int S, M, H;
+  const float* gain;
+  float eps;
+  float* xn;               // [M][ldx] normalised rows (or nullptr: only fold the partials)
+};
+hipError_t launch_norm_rows(const NormRowsArgs& a, hipStream_t s);
 
 struct FinishBArgs {
   const float* am_val;     // [blocks][16]
@@ -199,9 +216,7 @@ struct FinishBArgs {
   float* h;                // [streams][H]
   float* x;                // [M][ldx] next input rows
   int ldx;
-  const float* x_res;      // FIN_SLOW: batch residual rows [M][ldx]
-  const float* scale;      // FIN_SLOW: [M] final RMSNorm row scale
-  const float* gain;       // FIN_SLOW: final norm gain [H]
+  const float* x_res;      // FIN_SLOW: final-normalised batch rows [M][ldx]
   float* xf_slot;          // FIN_SLOW: also write h into the single-stream Fast residual of the slot
   int ld_xf_slot;
   int H, K, NC;
