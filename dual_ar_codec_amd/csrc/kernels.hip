@@ -559,8 +559,8 @@ hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------------------------
 // Decode attention.  grid = (max_splits, Hkv, M), block = G wavefronts (G = Hq / Hkv), one per
 // q head of the KV group.  A block walks its split in chunks of 64 positions (one per lane):
-// the chunk's K rows are staged in LDS, scores use the lane's row, the running softmax is
-// rescaled per chunk, and V rows are read straight from the cache in the weighted sum.
+// the chunk's K and V rows are staged in LDS (the next chunk's loads are already in flight in
+// registers), scores use the lane's row, and the running softmax is rescaled per chunk.
 
 template <bool KVB>
 struct KvT;
@@ -651,14 +651,12 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
   }
   __syncthreads();
 
-  float m_run = -INFINITY, l_run = 0.f, o_run[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) o_run[i] = 0.f;
-  for (int j0 = s0; j0 < s1; j0 += CH) {
+  // K and V pieces of one chunk: issued a chunk ahead, so the loads of chunk c + 1 are in flight
+  // while chunk c is scored and accumulated
+  u32x4 kt[PIECES], vt[PIECES];
+  auto issue = [&](int j0) {
     const int nv = min(CH, s1 - j0);
-    const int jn = has_new ? pos - j0 : -1;  // row of the new position in this chunk (if any)
-    // issue the chunk's K and V loads
-    u32x4 kt[PIECES], vt[PIECES];
+    const int jn = has_new ? pos - j0 : -1;  // the new position is not in the cache yet
 #pragma unroll
     for (int u = 0; u < PIECES; ++u) {
       const int pi = threadIdx.x + u * NT, j = pi / CPR, q = pi % CPR;
@@ -668,38 +666,47 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
         vt[u] = *reinterpret_cast<const u32x4*>(vc + off);
       }
     }
-    if (j0 == s0) {  // QK-norm and RoPE while the tile is in flight
-      const float* crow = a.rope_cos + (size_t)pos * (D / 2);
-      const float* srow = a.rope_sin + (size_t)pos * (D / 2);
-      float ss = 0.f;
+  };
+  issue(s0);
+  {  // QK-norm and RoPE while the first tile is in flight
+    const float* crow = a.rope_cos + (size_t)pos * (D / 2);
+    const float* srow = a.rope_sin + (size_t)pos * (D / 2);
+    float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) ss = fmaf(qv[i], qv[i], ss);
-      const float r = rsqrtf(wave_sum(ss) / (float)D + a.eps);
+    for (int i = 0; i < PER; ++i) ss = fmaf(qv[i], qv[i], ss);
+    const float r = rsqrtf(wave_sum(ss) / (float)D + a.eps);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) qv[i] = qv[i] * r * a.q_norm[lane + i * WAVE];
-      rope_lane<D>(qv, crow, srow, lane);
+    for (int i = 0; i < PER; ++i) qv[i] = qv[i] * r * a.q_norm[lane + i * WAVE];
+    rope_lane<D>(qv, crow, srow, lane);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) q_s[w][lane + i * WAVE] = qv[i] * a.scale;
-      if (mk) {
-        ss = 0.f;
+    for (int i = 0; i < PER; ++i) q_s[w][lane + i * WAVE] = qv[i] * a.scale;
+    if (mk) {
+      ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) ss = fmaf(kv[i], kv[i], ss);
-        const float rk = rsqrtf(wave_sum(ss) / (float)D + a.eps);
+      for (int i = 0; i < PER; ++i) ss = fmaf(kv[i], kv[i], ss);
+      const float rk = rsqrtf(wave_sum(ss) / (float)D + a.eps);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) kv[i] = kv[i] * rk * a.k_norm[lane + i * WAVE];
-        rope_lane<D>(kv, crow, srow, lane);
-        const int page = a.block_table[slot * a.bt_stride + pos / a.page_size];
-        const size_t off = (((size_t)page * a.Hkv + g) * a.page_size + pos % a.page_size) * D;
+      for (int i = 0; i < PER; ++i) kv[i] = kv[i] * rk * a.k_norm[lane + i * WAVE];
+      rope_lane<D>(kv, crow, srow, lane);
+      const int page = a.block_table[slot * a.bt_stride + pos / a.page_size];
+      const size_t off = (((size_t)page * a.Hkv + g) * a.page_size + pos % a.page_size) * D;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int d = lane + i * WAVE;
-          kn_s[d] = KV::round(kv[i]);
-          vn_s[d] = KV::round(vv[i]);
-          kc[off + d] = KV::cvt(kv[i]);  // append the new position to the paged cache
-          vc[off + d] = KV::cvt(vv[i]);
-        }
+      for (int i = 0; i < PER; ++i) {
+        const int d = lane + i * WAVE;
+        kn_s[d] = KV::round(kv[i]);
+        vn_s[d] = KV::round(vv[i]);
+        kc[off + d] = KV::cvt(kv[i]);  // append the new position to the paged cache
+        vc[off + d] = KV::cvt(vv[i]);
       }
     }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f, o_run[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o_run[i] = 0.f;
+  for (int j0 = s0; j0 < s1; j0 += CH) {
+    const int nv = min(CH, s1 - j0);
+    const int jn = has_new ? pos - j0 : -1;  // row of the new position in this chunk (if any)
 #pragma unroll
     for (int u = 0; u < PIECES; ++u) {
       const int pi = threadIdx.x + u * NT, j = pi / CPR, q = pi % CPR;
@@ -720,6 +727,7 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
         v_s[jn * D + d] = KV::cvt(vn_s[d]);
       }
     __syncthreads();
+    if (j0 + CH < s1) issue(j0 + CH);
 
     float s = -INFINITY;
     if (lane < nv) {
