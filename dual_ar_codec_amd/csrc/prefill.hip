@@ -266,50 +266,73 @@ hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------------------------
-// Causal attention of a block of prompt rows.  grid = (ceil(rows / 64), Hkv); block = 2 * 64 * G
-// threads.  Thread t serves query row (t / 2) % 64 of q head g G + (t / 2) / 64 and half t % 2 of
-// its D dimensions (so q and the running output stay in registers).  Key/value tiles of 64 cached
-// positions are staged once in LDS and shared by all 64 G queries of the block; the running
-// softmax is rescaled per key.  Keys and values of the rows must already be in the cache.
+// Causal attention of a block of prompt rows on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, so
+// scores and weighted sums keep full fp32 inputs).  grid = (ceil(rows / 16), Hkv); block = G
+// wavefronts, wavefront w = q head g G + w over 16 query rows.  Per tile of 64 cached keys (staged
+// in LDS, shared by the G heads) a wavefront forms S^T = K Q^T: lane (i, c) (i = lane % 16,
+// c = lane / 16) then holds the scores of query row i against keys 4 c + r of each 16-key group,
+// which is exactly the A operand of the P V product when that group's four MFMA steps take the keys
+// 4 c + r (r = step).  The QK steps walk the head dimension in groups of 16 where lane (i, c) owns
+// dimensions 16 t + 4 c .. + 3, so K is read from LDS 16 bytes at a time.  The running softmax
+// (max, sum) is per query row; the output tile of 16 rows x 16 dimensions per MFMA is rescaled with
+// the row factors fetched from the lanes that own those rows.  Keys and values of the rows must
+// already be in the cache.
 template <int D, int G, bool KVB>
-__global__ __launch_bounds__(2 * 64 * G) void k_prefill_attn(const PrefillAttnArgs a) {
-  constexpr int QT = 64, KT = 64, HD = D / 2, NT = 2 * QT * G;
-  __shared__ __attribute__((aligned(16))) float ks[KT][D + 4];
-  __shared__ __attribute__((aligned(16))) float vs[KT][D + 4];
+__global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a) {
+  constexpr int QR = 16, KT = 64, KSTR = D + 4, NT = 64 * G, NDG = D / 16;
+  __shared__ __attribute__((aligned(16))) float ks[KT * KSTR];
+  __shared__ __attribute__((aligned(16))) float vs[KT * KSTR];
   __shared__ int rowoff[KT];
-  const int g = blockIdx.y, tid = threadIdx.x;
-  const int half = tid & 1, r = (tid >> 1) % QT, hl = (tid >> 1) / QT;
-  const int h = g * G + hl;
-  const int row0 = blockIdx.x * QT;
-  const int row = min(row0 + r, a.rows - 1);
-  const bool live = row0 + r < a.rows;
-  const int pos = a.pos0 + row;
-  const int last_pos = a.pos0 + min(row0 + QT, a.rows) - 1;  // largest position in the block
+  const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, c = lane >> 4;
+  const int h = g * G + w;
+  const int row0 = blockIdx.x * QR;
+  const int nrows = min(QR, a.rows - row0);
+  const int last_pos = a.pos0 + row0 + nrows - 1;  // largest position of the block
 
-  // q: per-head RMSNorm, RoPE (pairs d, d + D/2 sit in the two halves of this lane pair), scale
-  float q[HD];
-  const float* qp = a.qkv + (size_t)row * a.ld + h * D + half * HD;
-  float ss = 0.f;
+  // q of row i (lanes (i, 0..3) share it): per-head RMSNorm, RoPE, scale; lane (i, c) keeps
+  // dimensions 16 t + 4 c + e as q[4 t + e]
+  const int qrow = row0 + min(i, nrows - 1);
+  const int rpos = a.pos0 + qrow;
+  float q[D / 4];
+  {
+    const float* qp = a.qkv + (size_t)qrow * a.ld + h * D + 4 * c;
+    float ss = 0.f;
 #pragma unroll
-  for (int d = 0; d < HD; ++d) {
-    q[d] = qp[d];
-    ss = fmaf(q[d], q[d], ss);
-  }
-  ss += __shfl_xor(ss, 1, WAVE);
-  const float rq = rsqrtf(ss / (float)D + a.eps);
-  const float* crow = a.rope_cos + (size_t)pos * HD;
-  const float* srow = a.rope_sin + (size_t)pos * HD;
+    for (int t = 0; t < NDG; ++t) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(qp + 16 * t);
+      q[4 * t] = v.x;
+      q[4 * t + 1] = v.y;
+      q[4 * t + 2] = v.z;
+      q[4 * t + 3] = v.w;
+      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    }
+    ss += __shfl_xor(ss, 16, WAVE);
+    ss += __shfl_xor(ss, 32, WAVE);
+    const float rq = rsqrtf(ss / (float)D + a.eps);
 #pragma unroll
-  for (int d = 0; d < HD; ++d) {
-    const float x = q[d] * rq * a.q_norm[half * HD + d];
-    const float partner = __shfl_xor(x, 1, WAVE);  // element d of the other half
-    const float cs = crow[d], sn = srow[d];
-    q[d] = (half == 0 ? x * cs - partner * sn : x * cs + partner * sn) * a.scale;
+    for (int t = 0; t < NDG; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[4 * t + e] = q[4 * t + e] * rq * a.q_norm[16 * t + 4 * c + e];
+    // rotate-half pairs (d, d + D/2) sit in the same lane, groups t and t + D/32
+    const float* crow = a.rope_cos + (size_t)rpos * (D / 2);
+    const float* srow = a.rope_sin + (size_t)rpos * (D / 2);
+#pragma unroll
+    for (int t = 0; t < NDG / 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * t + 4 * c + e;
+        const float cs = crow[d], sn = srow[d];
+        const float x0 = q[4 * t + e], x1 = q[4 * (t + NDG / 2) + e];
+        q[4 * t + e] = (x0 * cs - x1 * sn) * a.scale;
+        q[4 * (t + NDG / 2) + e] = (x1 * cs + x0 * sn) * a.scale;
+      }
   }
 
-  float m = -INFINITY, l = 0.f, o[HD];
+  float m_i = -INFINITY, l_i = 0.f;  // softmax state of row i
+  f32x4 o[NDG];                       // o[t][r] = O[row 4 c + r][dim 16 t + i]
 #pragma unroll
-  for (int d = 0; d < HD; ++d) o[d] = 0.f;
+  for (int t = 0; t < NDG; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float* kc = static_cast<const float*>(a.k_cache);
   const float* vc = static_cast<const float*>(a.v_cache);
   const uint16_t* kb = static_cast<const uint16_t*>(a.k_cache);
@@ -318,59 +341,118 @@ __global__ __launch_bounds__(2 * 64 * G) void k_prefill_attn(const PrefillAttnAr
     const int nk = min(KT, last_pos + 1 - j0);
     __syncthreads();  // the previous tile is no longer read
     if (tid < KT) {
-      const int jj = j0 + tid;
-      const int page = a.block_table[min(jj, last_pos) / a.page_size];
+      const int jj = min(j0 + tid, last_pos);
+      const int page = a.block_table[jj / a.page_size];
       rowoff[tid] = (int)((((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
     }
     __syncthreads();
-    for (int e = tid * 4; e < nk * D; e += NT * 4) {
+    for (int e = tid * 4; e < KT * D; e += NT * 4) {
       const int j = e / D, d = e % D;
-      const size_t off = (size_t)rowoff[j] + d;
-      f32x4 kv4, vv4;
-      if constexpr (KVB) {
-        const uint2 k2 = *reinterpret_cast<const uint2*>(kb + off), v2 = *reinterpret_cast<const uint2*>(vb + off);
-        kv4 = f32x4{__uint_as_float(k2.x << 16), __uint_as_float(k2.x & 0xffff0000u), __uint_as_float(k2.y << 16),
-                    __uint_as_float(k2.y & 0xffff0000u)};
-        vv4 = f32x4{__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u), __uint_as_float(v2.y << 16),
-                    __uint_as_float(v2.y & 0xffff0000u)};
-      } else {
-        kv4 = *reinterpret_cast<const f32x4*>(kc + off);
-        vv4 = *reinterpret_cast<const f32x4*>(vc + off);
+      f32x4 kv4 = {0.f, 0.f, 0.f, 0.f}, vv4 = {0.f, 0.f, 0.f, 0.f};  // keys past the block stay finite
+      if (j < nk) {
+        const size_t off = (size_t)rowoff[j] + d;
+        if constexpr (KVB) {
+          const uint2 k2 = *reinterpret_cast<const uint2*>(kb + off), v2 = *reinterpret_cast<const uint2*>(vb + off);
+          kv4 = f32x4{__uint_as_float(k2.x << 16), __uint_as_float(k2.x & 0xffff0000u), __uint_as_float(k2.y << 16),
+                      __uint_as_float(k2.y & 0xffff0000u)};
+          vv4 = f32x4{__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u), __uint_as_float(v2.y << 16),
+                      __uint_as_float(v2.y & 0xffff0000u)};
+        } else {
+          kv4 = *reinterpret_cast<const f32x4*>(kc + off);
+          vv4 = *reinterpret_cast<const f32x4*>(vc + off);
+        }
       }
-      *reinterpret_cast<f32x4*>(&ks[j][d]) = kv4;
-      *reinterpret_cast<f32x4*>(&vs[j][d]) = vv4;
+      *reinterpret_cast<f32x4*>(&ks[j * KSTR + d]) = kv4;
+      *reinterpret_cast<f32x4*>(&vs[j * KSTR + d]) = vv4;
     }
     __syncthreads();
-    const int jmax = min(nk, pos - j0 + 1);  // causal: keys j0 .. pos
-    for (int j = 0; j < jmax; ++j) {
-      float sp = 0.f;
+
+    const int ngrp = min(KT / 16, (nk + 15) / 16);  // 16-key groups holding any key of the block
+    f32x4 st[KT / 16];
 #pragma unroll
-      for (int d = 0; d < HD; ++d) sp = fmaf(q[d], ks[j][half * HD + d], sp);
-      const float sc = sp + __shfl_xor(sp, 1, WAVE);
-      const float mn = fmaxf(m, sc);
-      const float corr = expf(m - mn), p = expf(sc - mn);
-      l = l * corr + p;
+    for (int kt = 0; kt < KT / 16; ++kt) {
+      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (kt < ngrp) {
 #pragma unroll
-      for (int d = 0; d < HD; ++d) o[d] = fmaf(p, vs[j][half * HD + d], o[d] * corr);
-      m = mn;
+        for (int t = 0; t < NDG; ++t) {
+          const f32x4 k4 = *reinterpret_cast<const f32x4*>(&ks[(kt * 16 + i) * KSTR + 16 * t + 4 * c]);
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.x, q[4 * t], st[kt], 0, 0, 0);
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.y, q[4 * t + 1], st[kt], 0, 0, 0);
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.z, q[4 * t + 2], st[kt], 0, 0, 0);
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.w, q[4 * t + 3], st[kt], 0, 0, 0);
+        }
+      }
+    }
+    // causal mask and online softmax of row i over this tile (lane (i, c) holds keys 16 kt + 4 c + r)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT / 16; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jl = kt * 16 + 4 * c + r;
+        const float v = (jl < nk && j0 + jl <= rpos) ? st[kt][r] : -INFINITY;
+        st[kt][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float m_new = fmaxf(m_i, mx);  // key j0 <= rpos always, so finite from the first tile on
+    const float corr = expf(m_i - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT / 16; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = expf(st[kt][r] - m_new);
+        st[kt][r] = p;
+        ps += p;
+      }
+    ps += __shfl_xor(ps, 16, WAVE);
+    ps += __shfl_xor(ps, 32, WAVE);
+    l_i = l_i * corr + ps;
+    m_i = m_new;
+    float cr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * c + r, WAVE);
+#pragma unroll
+    for (int t = 0; t < NDG; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[t][r] *= cr[r];
+    // O += P V: step r of key group kt takes keys 16 kt + 4 c + r (A = st[kt][r] as held)
+#pragma unroll
+    for (int kt = 0; kt < KT / 16; ++kt) {
+      if (kt < ngrp) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float* vrow = &vs[(kt * 16 + 4 * c + r) * KSTR + i];
+#pragma unroll
+          for (int t = 0; t < NDG; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(st[kt][r], vrow[16 * t], o[t], 0, 0, 0);
+        }
+      }
     }
   }
-  if (live) {
-    float* out = a.out + (size_t)row * a.ld_out + h * D + half * HD;
-    const float inv = 1.0f / l;
+  float inv[4];
 #pragma unroll
-    for (int d = 0; d < HD; ++d) out[d] = o[d] * inv;
+  for (int r = 0; r < 4; ++r) inv[r] = 1.0f / __shfl(l_i, 4 * c + r, WAVE);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + 4 * c + r;
+    if (row - row0 < nrows) {
+      float* out = a.out + (size_t)row * a.ld_out + h * D + i;
+#pragma unroll
+      for (int t = 0; t < NDG; ++t) out[16 * t] = o[t][r] * inv[r];
+    }
   }
 }
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const dim3 grid((a.rows + 63) / 64, a.Hkv);
-#define S2_PA(DD, GG)                                                                                    \
-  if (a.D == DD && G == GG) {                                                                            \
-    if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_attn<DD, GG, true>), grid, dim3(2 * 64 * GG), 0, s, a);  \
-    else hipLaunchKernelGGL((k_prefill_attn<DD, GG, false>), grid, dim3(2 * 64 * GG), 0, s, a);           \
-    return hipGetLastError();                                                                            \
+  const dim3 grid((a.rows + 15) / 16, a.Hkv);
+#define S2_PA(DD, GG)                                                                                 \
+  if (a.D == DD && G == GG) {                                                                         \
+    if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_attn<DD, GG, true>), grid, dim3(64 * GG), 0, s, a);   \
+    else hipLaunchKernelGGL((k_prefill_attn<DD, GG, false>), grid, dim3(64 * GG), 0, s, a);            \
+    return hipGetLastError();                                                                         \
   }
   S2_PA(64, 1) S2_PA(64, 2) S2_PA(64, 4) S2_PA(64, 8)
   S2_PA(128, 1) S2_PA(128, 2) S2_PA(128, 4) S2_PA(128, 8)
