@@ -164,8 +164,172 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
     }
 }
 
+// Larger-tile variant for long prompts: 8 wavefronts (WM x WN) per block, BK = 64 per stage,
+// LDS double-buffered plus two register staging sets, so a stage's global loads are issued two
+// stages before its compute.  Tiles are numbered with M fastest, and the blocks of one XCD
+// (block ids round-robin over the 8 XCDs) take a contiguous range of tiles, so the blocks that
+// share a weight column sit on one XCD and reuse it from that XCD's L2.
+template <int BM, int BN, int WM, int EPI>
+__global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
+  constexpr int WN = 8 / WM, BK = 64, LS = BK + 8;
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int AF = BM * BK / 512, A_TPR = BK / AF;  // fp32 A values per thread per stage
+  constexpr int WB = BN * BK / 512, W_TPR = BK / WB;  // bf16 W values per thread per stage
+  constexpr int STAGE = (2 * BM + BN) * LS;           // bf16 elements: A hi, A lo, W
+  static_assert(AF % 8 == 0 && WB % 8 == 0, "loader granularity");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv / WN, wn = wv % WN;
+  const int mt = (g.M + BM - 1) / BM, ntiles = mt * (g.N / BN);
+  const int xcd = blockIdx.x & 7, per = ntiles >> 3, rem = ntiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + (int)(blockIdx.x >> 3);
+  const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
+  const int nk = g.K / BK;
+
+  const int a_row = tid / A_TPR, a_k = (tid % A_TPR) * AF;
+  const int a_m = min(m0 + a_row, g.M - 1);
+  const float* a_src = g.a + (size_t)a_m * g.lda + a_k;
+  const float a_sc = g.a_scale ? g.a_scale[a_m] : 1.0f;
+  const int w_row = tid / W_TPR, w_k = (tid % W_TPR) * WB;
+  const uint16_t* w_src = g.w + (size_t)(n0 + w_row) * g.K + w_k;
+
+  f32x4 ar0[AF / 4], ar1[AF / 4];
+  u32x4 wr0[WB / 8], wr1[WB / 8];
+  auto load = [&](int kt, f32x4 (&ar)[AF / 4], u32x4 (&wr)[WB / 8]) {
+    const int k = min(kt, nk - 1) * BK;  // past the end: reload the last stage (never computed)
+#pragma unroll
+    for (int i = 0; i < AF / 4; ++i) ar[i] = *reinterpret_cast<const f32x4*>(a_src + k + 4 * i);
+#pragma unroll
+    for (int i = 0; i < WB / 8; ++i) wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + k + 8 * i));
+  };
+  auto stash = [&](int kt, int st, const f32x4 (&ar)[AF / 4], const u32x4 (&wr)[WB / 8]) {
+    const int k = min(kt, nk - 1) * BK;
+    uint16_t* ah = lds + st * STAGE;
+    uint16_t* al = ah + BM * LS;
+    uint16_t* ws = al + BM * LS;
+    uint32_t p[AF / 2], q[AF / 2];
+#pragma unroll
+    for (int i = 0; i < AF / 4; ++i) {
+      f32x4 v = ar[i];
+      if (g.a_gain) {
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(g.a_gain + k + a_k + 4 * i);
+        v.x *= a_sc * gg.x;
+        v.y *= a_sc * gg.y;
+        v.z *= a_sc * gg.z;
+        v.w *= a_sc * gg.w;
+      }
+      split_bf16x2(v.x, v.y, p[2 * i], q[2 * i]);
+      split_bf16x2(v.z, v.w, p[2 * i + 1], q[2 * i + 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < AF / 8; ++i) {
+      *reinterpret_cast<u32x4*>(ah + a_row * LS + a_k + 8 * i) = u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
+      *reinterpret_cast<u32x4*>(al + a_row * LS + a_k + 8 * i) = u32x4{q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]};
+    }
+#pragma unroll
+    for (int i = 0; i < WB / 8; ++i) *reinterpret_cast<u32x4*>(ws + w_row * LS + w_k + 8 * i) = wr[i];
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  auto compute = [&](int st) {
+    const uint16_t* ah = lds + st * STAGE;
+    const uint16_t* al = ah + BM * LS;
+    const uint16_t* ws = al + BM * LS;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8 bfr[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(ws + (wn * (BN / WN) + j * 16 + fr) * LS + ks * 32 + fk);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {  // one A row tile at a time keeps few fragments live
+        const int r = (wm * (BM / WM) + i * 16 + fr) * LS + ks * 32 + fk;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(ah + r);
+        const bf16x8 afl = *reinterpret_cast<const bf16x8*>(al + r);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afl, bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  load(0, ar0, wr0);
+  load(1, ar1, wr1);
+  stash(0, 0, ar0, wr0);
+  load(2, ar0, wr0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    compute(0);               // stage kt
+    stash(kt + 1, 1, ar1, wr1);
+    load(kt + 3, ar1, wr1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    compute(1);               // stage kt + 1
+    stash(kt + 2, 0, ar0, wr0);
+    load(kt + 4, ar0, wr0);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 4 (lane/16) + r, column lane % 16 of each 16 x 16 tile
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+        const float v = acc[i][j][r];
+        if constexpr (EPI == GEMM_SWIGLU) {
+          const float up = __shfl_xor(v, 1, WAVE);  // columns 2i (gate) and 2i+1 (up) sit in adjacent lanes
+          if (m < g.M && (n & 1) == 0) g.c[(size_t)m * g.ldc + (n >> 1)] = v / (1.0f + expf(-v)) * up;
+        } else if (m < g.M) {
+          if constexpr (EPI == GEMM_ADD) g.c[(size_t)m * g.ldc + n] += v;
+          else g.c[(size_t)m * g.ldc + n] = v;
+        }
+      }
+    }
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.N % 128 || g.K % 32 || g.M < 1) return hipErrorInvalidValue;
+  // long prompts: the 8-wavefront kernel, with the largest tile that still fills the CUs
+  if (g.K % 64 == 0 && g.M >= 256) {
+    const int cus = device_cus();
+    struct Cfg { int bm, bn; };
+    // (128 x 256 would need more than the 256 registers a wavefront of an 8-wavefront block gets)
+    const Cfg cfgs[3] = {{128, 128}, {64, 256}, {64, 128}};
+    int best = -1;
+    double best_eff = 0.0;
+    for (int c = 0; c < 3; ++c) {
+      if (g.N % cfgs[c].bn) continue;
+      const long t = (long)((g.M + cfgs[c].bm - 1) / cfgs[c].bm) * (g.N / cfgs[c].bn);
+      const double eff = (double)t / (double)(((t + cus - 1) / cus) * cus);
+      if (eff >= 0.75) { best = c; break; }  // largest tile first
+      if (eff > best_eff) { best_eff = eff; best = c; }
+    }
+    if (best >= 0) {
+      const long t = (long)((g.M + cfgs[best].bm - 1) / cfgs[best].bm) * (g.N / cfgs[best].bn);
+      const dim3 grid((unsigned)t);
+#define S2_G2(BM_, BN_)                                                                           \
+  if (cfgs[best].bm == BM_ && cfgs[best].bn == BN_) {                                             \
+    if (g.epi == GEMM_STORE) hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_STORE>), grid, dim3(512), 0, s, g);    \
+    else if (g.epi == GEMM_ADD) hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_ADD>), grid, dim3(512), 0, s, g);   \
+    else hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_SWIGLU>), grid, dim3(512), 0, s, g);                        \
+    return hipGetLastError();                                                                     \
+  }
+      S2_G2(128, 128) S2_G2(64, 256) S2_G2(64, 128)
+#undef S2_G2
+    }
+  }
   const bool small = (long)((g.M + 127) / 128) * (g.N / 128) < 2L * device_cus();
   const int BM = small ? 64 : 128;
   const dim3 grid(g.N / 128, (g.M + BM - 1) / BM);
