@@ -55,6 +55,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LS];   // activation, bf16 hi
   __shared__ __attribute__((aligned(16))) uint16_t Al[2][BM * LS];   // activation, bf16 lo
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LS];
+  extern __shared__ __attribute__((aligned(16))) float gs[];  // the RMSNorm gain [K], when there is one
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
     for (int i = 0; i < AF / 4; ++i) {
       f32x4 v = ar[i];
       if (g.a_gain) {
-        const f32x4 gg = *reinterpret_cast<const f32x4*>(g.a_gain + k + a_k + 4 * i);
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(gs + k + a_k + 4 * i);
         v.x *= a_sc * gg.x;
         v.y *= a_sc * gg.y;
         v.z *= a_sc * gg.z;
@@ -116,6 +117,10 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if (g.a_gain) {  // once per block, so that the stage loader reads no global memory outside its loads
+    for (int k = tid * 4; k < g.K; k += 256 * 4) *reinterpret_cast<f32x4*>(gs + k) = *reinterpret_cast<const f32x4*>(g.a_gain + k);
+    __syncthreads();
+  }
   load(0);
   stash(0, 0);
   __syncthreads();
@@ -178,9 +183,13 @@ __global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
   constexpr int STAGE = (2 * BM + BN) * LS;           // bf16 elements: A hi, A lo, W
   static_assert(AF % 8 == 0 && WB % 8 == 0, "loader granularity");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  extern __shared__ __attribute__((aligned(16))) float gs[];  // the RMSNorm gain [K], when there is one
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / WN, wn = wv % WN;
+  // the gain goes to LDS once, so that the stage loader reads no global memory outside its loads
+  if (g.a_gain)
+    for (int k = tid * 4; k < g.K; k += 512 * 4) *reinterpret_cast<f32x4*>(gs + k) = *reinterpret_cast<const f32x4*>(g.a_gain + k);
   const int mt = (g.M + BM - 1) / BM, ntiles = mt * (g.N / BN);
   const int xcd = blockIdx.x & 7, per = ntiles >> 3, rem = ntiles & 7;
   const int tile = xcd * per + min(xcd, rem) + (int)(blockIdx.x >> 3);
@@ -213,7 +222,7 @@ __global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
     for (int i = 0; i < AF / 4; ++i) {
       f32x4 v = ar[i];
       if (g.a_gain) {
-        const f32x4 gg = *reinterpret_cast<const f32x4*>(g.a_gain + k + a_k + 4 * i);
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(gs + k + a_k + 4 * i);
         v.x *= a_sc * gg.x;
         v.y *= a_sc * gg.y;
         v.z *= a_sc * gg.z;
@@ -263,6 +272,7 @@ __global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
 
   load(0, ar0, wr0);
   load(1, ar1, wr1);
+  if (g.a_gain) __syncthreads();  // gain in LDS
   stash(0, 0, ar0, wr0);
   load(2, ar0, wr0);
   __syncthreads();
@@ -302,7 +312,8 @@ __global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.N % 128 || g.K % 32 || g.M < 1) return hipErrorInvalidValue;
   // long prompts: the 8-wavefront kernel, with the largest tile that still fills the CUs
-  if (g.K % 64 == 0 && g.M >= 256) {
+  const size_t gain_lds = g.a_gain ? (size_t)g.K * 4 : 0;
+  if (g.K % 64 == 0 && g.M >= 256 && gain_lds <= 40 * 1024) {
     const int cus = device_cus();
     struct Cfg { int bm, bn; };
     // (128 x 256 would need more than the 256 registers a wavefront of an 8-wavefront block gets)
@@ -321,9 +332,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
       const dim3 grid((unsigned)t);
 #define S2_G2(BM_, BN_)                                                                           \
   if (cfgs[best].bm == BM_ && cfgs[best].bn == BN_) {                                             \
-    if (g.epi == GEMM_STORE) hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_STORE>), grid, dim3(512), 0, s, g);    \
-    else if (g.epi == GEMM_ADD) hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_ADD>), grid, dim3(512), 0, s, g);   \
-    else hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_SWIGLU>), grid, dim3(512), 0, s, g);                        \
+    if (g.epi == GEMM_STORE) hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_STORE>), grid, dim3(512), gain_lds, s, g); \
+    else if (g.epi == GEMM_ADD) hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_ADD>), grid, dim3(512), gain_lds, s, g); \
+    else hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_SWIGLU>), grid, dim3(512), gain_lds, s, g);                   \
     return hipGetLastError();                                                                     \
   }
       S2_G2(128, 128) S2_G2(64, 256) S2_G2(64, 128)
@@ -333,7 +344,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const bool small = (long)((g.M + 127) / 128) * (g.N / 128) < 2L * device_cus();
   const int BM = small ? 64 : 128;
   const dim3 grid(g.N / 128, (g.M + BM - 1) / BM);
-#define S2_GEMM(B, E) hipLaunchKernelGGL((k_gemm<B, E>), grid, dim3(256), 0, s, g)
+#define S2_GEMM(B, E) hipLaunchKernelGGL((k_gemm<B, E>), grid, dim3(256), gain_lds, s, g)
   if (small) {
     if (g.epi == GEMM_STORE) S2_GEMM(64, GEMM_STORE);
     else if (g.epi == GEMM_ADD) S2_GEMM(64, GEMM_ADD);
