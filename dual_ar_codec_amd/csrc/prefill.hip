@@ -178,10 +178,12 @@ template <int BM, int BN, int WM, int EPI>
 __global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
   constexpr int WN = 8 / WM, BK = 64, LS = BK + 8;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  constexpr int AF = BM * BK / 512, A_TPR = BK / AF;  // fp32 A values per thread per stage
-  constexpr int WB = BN * BK / 512, W_TPR = BK / WB;  // bf16 W values per thread per stage
+  // coalesced stage loads: one A load instruction of a wavefront covers 4 rows x 64 fp32 (16 lanes
+  // per row, 16 bytes each), one W load instruction 8 rows x 64 bf16 (8 lanes per row)
+  constexpr int AI = BM / 32;                         // A load instructions per thread per stage
+  constexpr int WI = BN / 64;                         // W load instructions per thread per stage
   constexpr int STAGE = (2 * BM + BN) * LS;           // bf16 elements: A hi, A lo, W
-  static_assert(AF % 8 == 0 && WB % 8 == 0, "loader granularity");
+  static_assert(AI >= 1 && WI >= 1, "tile too small for the loaders");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
   extern __shared__ __attribute__((aligned(16))) float gs[];  // the RMSNorm gain [K], when there is one
 
@@ -196,48 +198,57 @@ __global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
   const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
   const int nk = g.K / BK;
 
-  const int a_row = tid / A_TPR, a_k = (tid % A_TPR) * AF;
-  const int a_m = min(m0 + a_row, g.M - 1);
-  const float* a_src = g.a + (size_t)a_m * g.lda + a_k;
-  const float a_sc = g.a_scale ? g.a_scale[a_m] : 1.0f;
-  const int w_row = tid / W_TPR, w_k = (tid % W_TPR) * WB;
-  const uint16_t* w_src = g.w + (size_t)(n0 + w_row) * g.K + w_k;
+  // A rows of this thread: wv * (BM / 8) + 4 i + lane / 16, columns 4 (lane % 16) .. + 3
+  const int a_k = (lane & 15) * 4;
+  const float* a_src[AI];
+  float a_sc[AI];
+  int a_row[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    a_row[i] = wv * (BM / 8) + 4 * i + (lane >> 4);
+    const int m = min(m0 + a_row[i], g.M - 1);
+    a_src[i] = g.a + (size_t)m * g.lda + a_k;
+    a_sc[i] = g.a_scale ? g.a_scale[m] : 1.0f;
+  }
+  // W rows: wv * (BN / 8) + 8 i + lane / 8, columns 8 (lane % 8) .. + 7
+  const int w_k = (lane & 7) * 8;
+  const uint16_t* w_src = g.w + (size_t)(n0 + wv * (BN / 8) + (lane >> 3)) * g.K + w_k;
+  const int w_row0 = wv * (BN / 8) + (lane >> 3);
 
-  f32x4 ar0[AF / 4], ar1[AF / 4];
-  u32x4 wr0[WB / 8], wr1[WB / 8];
-  auto load = [&](int kt, f32x4 (&ar)[AF / 4], u32x4 (&wr)[WB / 8]) {
+  f32x4 ar0[AI], ar1[AI];
+  u32x4 wr0[WI], wr1[WI];
+  auto load = [&](int kt, f32x4 (&ar)[AI], u32x4 (&wr)[WI]) {
     const int k = min(kt, nk - 1) * BK;  // past the end: reload the last stage (never computed)
 #pragma unroll
-    for (int i = 0; i < AF / 4; ++i) ar[i] = *reinterpret_cast<const f32x4*>(a_src + k + 4 * i);
+    for (int i = 0; i < AI; ++i) ar[i] = *reinterpret_cast<const f32x4*>(a_src[i] + k);
 #pragma unroll
-    for (int i = 0; i < WB / 8; ++i) wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + k + 8 * i));
+    for (int i = 0; i < WI; ++i)
+      wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + (size_t)8 * i * g.K + k));
   };
-  auto stash = [&](int kt, int st, const f32x4 (&ar)[AF / 4], const u32x4 (&wr)[WB / 8]) {
+  auto stash = [&](int kt, int st, const f32x4 (&ar)[AI], const u32x4 (&wr)[WI]) {
     const int k = min(kt, nk - 1) * BK;
     uint16_t* ah = lds + st * STAGE;
     uint16_t* al = ah + BM * LS;
     uint16_t* ws = al + BM * LS;
-    uint32_t p[AF / 2], q[AF / 2];
+    f32x4 gg = {1.f, 1.f, 1.f, 1.f};
+    if (g.a_gain) gg = *reinterpret_cast<const f32x4*>(gs + k + a_k);
 #pragma unroll
-    for (int i = 0; i < AF / 4; ++i) {
+    for (int i = 0; i < AI; ++i) {
       f32x4 v = ar[i];
       if (g.a_gain) {
-        const f32x4 gg = *reinterpret_cast<const f32x4*>(gs + k + a_k + 4 * i);
-        v.x *= a_sc * gg.x;
-        v.y *= a_sc * gg.y;
-        v.z *= a_sc * gg.z;
-        v.w *= a_sc * gg.w;
+        v.x *= a_sc[i] * gg.x;
+        v.y *= a_sc[i] * gg.y;
+        v.z *= a_sc[i] * gg.z;
+        v.w *= a_sc[i] * gg.w;
       }
-      split_bf16x2(v.x, v.y, p[2 * i], q[2 * i]);
-      split_bf16x2(v.z, v.w, p[2 * i + 1], q[2 * i + 1]);
+      uint32_t p0, q0, p1, q1;
+      split_bf16x2(v.x, v.y, p0, q0);
+      split_bf16x2(v.z, v.w, p1, q1);
+      *reinterpret_cast<uint2*>(ah + a_row[i] * LS + a_k) = uint2{p0, p1};
+      *reinterpret_cast<uint2*>(al + a_row[i] * LS + a_k) = uint2{q0, q1};
     }
 #pragma unroll
-    for (int i = 0; i < AF / 8; ++i) {
-      *reinterpret_cast<u32x4*>(ah + a_row * LS + a_k + 8 * i) = u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
-      *reinterpret_cast<u32x4*>(al + a_row * LS + a_k + 8 * i) = u32x4{q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]};
-    }
-#pragma unroll
-    for (int i = 0; i < WB / 8; ++i) *reinterpret_cast<u32x4*>(ws + w_row * LS + w_k + 8 * i) = wr[i];
+    for (int i = 0; i < WI; ++i) *reinterpret_cast<u32x4*>(ws + (w_row0 + 8 * i) * LS + w_k) = wr[i];
   };
 
   f32x4 acc[TM][TN];
@@ -316,7 +327,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.K % 64 == 0 && g.M >= 256 && gain_lds <= 40 * 1024) {
     const int cus = device_cus();
     struct Cfg { int bm, bn; };
-    // (128 x 256 would need more than the 256 registers a wavefront of an 8-wavefront block gets)
+    // (128 x 256 needs more than the 256 registers a wavefront of an 8-wavefront block gets)
     const Cfg cfgs[3] = {{128, 128}, {64, 256}, {64, 128}};
     int best = -1;
     double best_eff = 0.0;
