@@ -169,19 +169,19 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
     }
 }
 
-// Larger-tile variant for long prompts: 8 wavefronts (WM x WN) per block, BK = 64 per stage,
+// Larger-tile variant for long prompts: NW wavefronts (WM x WN) per block, BK = 64 per stage,
 // LDS double-buffered plus two register staging sets, so a stage's global loads are issued two
 // stages before its compute.  Tiles are numbered with M fastest, and the blocks of one XCD
 // (block ids round-robin over the 8 XCDs) take a contiguous range of tiles, so the blocks that
 // share a weight column sit on one XCD and reuse it from that XCD's L2.
-template <int BM, int BN, int WM, int EPI>
-__global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
-  constexpr int WN = 8 / WM, BK = 64, LS = BK + 8;
+template <int BM, int BN, int NW, int WM, int EPI>
+__global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
+  constexpr int NT = NW * 64, WN = NW / WM, BK = 64, LS = BK + 8;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   // coalesced stage loads: one A load instruction of a wavefront covers 4 rows x 64 fp32 (16 lanes
   // per row, 16 bytes each), one W load instruction 8 rows x 64 bf16 (8 lanes per row)
-  constexpr int AI = BM / 32;                         // A load instructions per thread per stage
-  constexpr int WI = BN / 64;                         // W load instructions per thread per stage
+  constexpr int AI = BM / (4 * NW);                   // A load instructions per thread per stage
+  constexpr int WI = BN / (8 * NW);                   // W load instructions per thread per stage
   constexpr int STAGE = (2 * BM + BN) * LS;           // bf16 elements: A hi, A lo, W
   static_assert(AI >= 1 && WI >= 1, "tile too small for the loaders");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
@@ -191,36 +191,36 @@ __global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
   const int wm = wv / WN, wn = wv % WN;
   // the gain goes to LDS once, so that the stage loader reads no global memory outside its loads
   if (g.a_gain)
-    for (int k = tid * 4; k < g.K; k += 512 * 4) *reinterpret_cast<f32x4*>(gs + k) = *reinterpret_cast<const f32x4*>(g.a_gain + k);
+    for (int k = tid * 4; k < g.K; k += NT * 4) *reinterpret_cast<f32x4*>(gs + k) = *reinterpret_cast<const f32x4*>(g.a_gain + k);
   const int mt = (g.M + BM - 1) / BM, ntiles = mt * (g.N / BN);
   const int xcd = blockIdx.x & 7, per = ntiles >> 3, rem = ntiles & 7;
   const int tile = xcd * per + min(xcd, rem) + (int)(blockIdx.x >> 3);
   const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
   const int nk = g.K / BK;
 
-  // A rows of this thread: wv * (BM / 8) + 4 i + lane / 16, columns 4 (lane % 16) .. + 3
+  // A rows of this thread: a_row0 + 4 i, columns 4 (lane % 16) .. + 3 of the stage
   const int a_k = (lane & 15) * 4;
-  const float* a_src[AI];
+  const int a_row0 = wv * (BM / NW) + (lane >> 4);
+  int a_off[AI];  // row offsets into A (rows past M repeat the last row)
   float a_sc[AI];
-  int a_row[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    a_row[i] = wv * (BM / 8) + 4 * i + (lane >> 4);
-    const int m = min(m0 + a_row[i], g.M - 1);
-    a_src[i] = g.a + (size_t)m * g.lda + a_k;
+    const int m = min(m0 + a_row0 + 4 * i, g.M - 1);
+    a_off[i] = m * g.lda;
     a_sc[i] = g.a_scale ? g.a_scale[m] : 1.0f;
   }
-  // W rows: wv * (BN / 8) + 8 i + lane / 8, columns 8 (lane % 8) .. + 7
+  const float* a_src = g.a + a_k;
+  // W rows: w_row0 + 8 i, columns 8 (lane % 8) .. + 7
   const int w_k = (lane & 7) * 8;
-  const uint16_t* w_src = g.w + (size_t)(n0 + wv * (BN / 8) + (lane >> 3)) * g.K + w_k;
-  const int w_row0 = wv * (BN / 8) + (lane >> 3);
+  const int w_row0 = wv * (BN / NW) + (lane >> 3);
+  const uint16_t* w_src = g.w + (size_t)(n0 + w_row0) * g.K + w_k;
 
   f32x4 ar0[AI], ar1[AI];
   u32x4 wr0[WI], wr1[WI];
   auto load = [&](int kt, f32x4 (&ar)[AI], u32x4 (&wr)[WI]) {
     const int k = min(kt, nk - 1) * BK;  // past the end: reload the last stage (never computed)
 #pragma unroll
-    for (int i = 0; i < AI; ++i) ar[i] = *reinterpret_cast<const f32x4*>(a_src[i] + k);
+    for (int i = 0; i < AI; ++i) ar[i] = *reinterpret_cast<const f32x4*>(a_src + (size_t)a_off[i] + k);
 #pragma unroll
     for (int i = 0; i < WI; ++i)
       wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + (size_t)8 * i * g.K + k));
@@ -244,8 +244,8 @@ __global__ __launch_bounds__(512) void k_gemm2(const GemmArgs g) {
       uint32_t p0, q0, p1, q1;
       split_bf16x2(v.x, v.y, p0, q0);
       split_bf16x2(v.z, v.w, p1, q1);
-      *reinterpret_cast<uint2*>(ah + a_row[i] * LS + a_k) = uint2{p0, p1};
-      *reinterpret_cast<uint2*>(al + a_row[i] * LS + a_k) = uint2{q0, q1};
+      *reinterpret_cast<uint2*>(ah + (a_row0 + 4 * i) * LS + a_k) = uint2{p0, p1};
+      *reinterpret_cast<uint2*>(al + (a_row0 + 4 * i) * LS + a_k) = uint2{q0, q1};
     }
 #pragma unroll
     for (int i = 0; i < WI; ++i) *reinterpret_cast<u32x4*>(ws + (w_row0 + 8 * i) * LS + w_k) = wr[i];
@@ -326,13 +326,15 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const size_t gain_lds = g.a_gain ? (size_t)g.K * 4 : 0;
   if (g.K % 64 == 0 && g.M >= 256 && gain_lds <= 40 * 1024) {
     const int cus = device_cus();
-    struct Cfg { int bm, bn; };
-    // (128 x 256 needs more than the 256 registers a wavefront of an 8-wavefront block gets)
-    const Cfg cfgs[3] = {{128, 128}, {64, 256}, {64, 128}};
+    // Measured at P = 1200 on the full shape: very wide N (gate/up + SwiGLU, 19456 rows) runs best
+    // with 128 x 256 tiles on 4 wavefronts (64 x 128 each: fewest LDS reads per MFMA); the other shapes
+    // with 8 wavefronts of 64 x 32 on 128 x 128 tiles (more wavefronts hide load latency).
+    struct Cfg { int bm, bn, nw; };
+    const Cfg cfgs[4] = {{128, 256, 4}, {128, 128, 8}, {64, 256, 8}, {64, 128, 8}};
     int best = -1;
     double best_eff = 0.0;
-    for (int c = 0; c < 3; ++c) {
-      if (g.N % cfgs[c].bn) continue;
+    for (int c = 0; c < 4; ++c) {
+      if (g.N % cfgs[c].bn || (c == 0 && (g.N < 16384 || g.epi != GEMM_SWIGLU))) continue;
       const long t = (long)((g.M + cfgs[c].bm - 1) / cfgs[c].bm) * (g.N / cfgs[c].bn);
       const double eff = (double)t / (double)(((t + cus - 1) / cus) * cus);
       if (eff >= 0.75) { best = c; break; }  // largest tile first
@@ -341,14 +343,20 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     if (best >= 0) {
       const long t = (long)((g.M + cfgs[best].bm - 1) / cfgs[best].bm) * (g.N / cfgs[best].bn);
       const dim3 grid((unsigned)t);
-#define S2_G2(BM_, BN_)                                                                           \
-  if (cfgs[best].bm == BM_ && cfgs[best].bn == BN_) {                                             \
-    if (g.epi == GEMM_STORE) hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_STORE>), grid, dim3(512), gain_lds, s, g); \
-    else if (g.epi == GEMM_ADD) hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_ADD>), grid, dim3(512), gain_lds, s, g); \
-    else hipLaunchKernelGGL((k_gemm2<BM_, BN_, 2, GEMM_SWIGLU>), grid, dim3(512), gain_lds, s, g);                   \
+#define S2_G2(BM_, BN_, NW_, WM_)                                                                  \
+  if (cfgs[best].bm == BM_ && cfgs[best].bn == BN_ && cfgs[best].nw == NW_) {                     \
+    if (g.epi == GEMM_STORE)                                                                      \
+      hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_STORE>), grid, dim3(NW_ * 64), gain_lds, s, g); \
+    else if (g.epi == GEMM_ADD)                                                                   \
+      hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_ADD>), grid, dim3(NW_ * 64), gain_lds, s, g);   \
+    else hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_SWIGLU>), grid, dim3(NW_ * 64), gain_lds, s, g); \
     return hipGetLastError();                                                                     \
   }
-      S2_G2(128, 128) S2_G2(64, 256) S2_G2(64, 128)
+      if (best == 0) {  // SwiGLU only (the store and add epilogues do not fit the registers at this tile)
+        hipLaunchKernelGGL((k_gemm2<128, 256, 4, 2, GEMM_SWIGLU>), grid, dim3(256), gain_lds, s, g);
+        return hipGetLastError();
+      }
+      S2_G2(128, 128, 8, 2) S2_G2(64, 256, 8, 2) S2_G2(64, 128, 8, 2)
 #undef S2_G2
     }
   }
