@@ -62,6 +62,8 @@ __device__ __forceinline__ float load_w(const void* p, size_t i) {
 }  // namespace
 
 int mgemv_tiles(int N) { return (N + 63) / 64; }
+// row stride of the split partials [S][16][ldp]: N rounded up to whole 64-row tiles
+__host__ __device__ __forceinline__ size_t mgemv_ldp(int N) { return (size_t)((N + 63) / 64) * 64; }
 
 // LDS-only barrier: the fences are restricted to the local address space, so pending global
 // loads (the weight stream) and stores stay in flight across it.
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int n = n0 + r;
-          if (n < a.N && i < a.M) a.part[((size_t)split * a.M + i) * a.N + n] = acc[r];
+          if (n < a.N && i < a.M) a.part[((size_t)split * MB + i) * mgemv_ldp(a.N) + n] = acc[r];
         }
       } else {
 #pragma unroll
@@ -217,6 +219,86 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
         }
       }
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// Split-K form for every launch whose K splits into 512-wide ranges (S = K / 512): each item is one
+// (64-row tile, split) chunk, numbered split-major, so a block's consecutive items share their
+// activation chunk and LDS is refilled only when the split changes (outside the inner loop).  The
+// inner loop is straight-line: four slices of MFMA on the weight ring, the next item's weights
+// loaded slice by slice, and an unconditional 16-byte store of the item's partial sums into
+// part[split][16][ldp] (rows past M or N hold values nobody reads).
+__global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MB * XROW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int ntiles = (a.N + 63) / 64;
+  const int it0 = blockIdx.x * a.ipb;
+  const int it1 = min(it0 + a.ipb, ntiles * a.S);
+  if (it0 >= it1) return;
+  const int ksl = a.K / KS;
+  const size_t ldp = mgemv_ldp(a.N);
+  auto wtile = [&](int it) {
+    const int split = it / ntiles, tile = it - split * ntiles;
+    return a.w + ((size_t)(tile * 4 + w) * ksl + split * CS) * (4 * 512) + lane * 8;
+  };
+  u32x4 wb[CS][4];
+  {
+    const uint16_t* wr = wtile(it0);
+#pragma unroll
+    for (int sl = 0; sl < CS; ++sl)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        wb[sl][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (sl * 4 + t) * 512));
+  }
+  const int xr_row = tid >> 4, xr_col = (tid & 15) * 32;
+  const float* xrow = a.x + (size_t)min(xr_row, a.M - 1) * a.ldx + xr_col;
+  const bool xlive = xr_row < a.M;
+  int it = it0;
+  while (it < it1) {
+    const int split = it / ntiles;
+    const int run_end = min(it1, (split + 1) * ntiles);  // items of this split
+    if (it != it0) lds_barrier();
+    {
+      const f32x4* q = reinterpret_cast<const f32x4*>(xrow + split * KC);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 u0 = q[2 * u], u1 = q[2 * u + 1];
+        float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = xlive ? v[e] : 0.f;
+        bf16x8 hi, lo;
+        split8(v, hi, lo);
+        *reinterpret_cast<bf16x8*>(&xs[0][xr_row * XROW + xr_col + 8 * u]) = hi;
+        *reinterpret_cast<bf16x8*>(&xs[1][xr_row * XROW + xr_col + 8 * u]) = lo;
+      }
+    }
+    lds_barrier();
+    for (; it < run_end; ++it) {
+      const uint16_t* nwr = wtile(min(it + 1, it1 - 1));
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < CS; ++sl) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          // MFMA slot group g of step st holds k = 32 g + 8 st .. + 8 of the slice (same map for A and B)
+          const int kl = sl * KS + 32 * g + 8 * st;
+          const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&xs[0][i * XROW + kl]);
+          const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&xs[1][i * XROW + kl]);
+          const bf16x8 wf = __builtin_bit_cast(bf16x8, wb[sl][st]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xh, acc, 0, 0, 0);
+        }
+        // keep the reload of wb[sl] after its last use, so it lands in the same registers
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          wb[sl][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(nwr + (sl * 4 + st) * 512));
+      }
+      // lane holds D[row 4 g + r][stream i] of the item's tile
+      const int tile = it - split * ntiles;
+      *reinterpret_cast<f32x4*>(a.part + ((size_t)split * MB + i) * ldp + tile * 64 + w * 16 + 4 * g) = acc;
     }
   }
 }
@@ -259,11 +341,11 @@ __global__ __launch_bounds__(1024) void k_norm_rows(NormRowsArgs a) {
   __shared__ float red[16];
   const int j = blockIdx.x;
   float* x = a.x + (size_t)j * a.ldx;
-  const size_t pstride = (size_t)a.M * a.H;
+  const size_t ldp = mgemv_ldp(a.H), pstride = (size_t)MB * ldp;
   float ss = 0.f;
   for (int e = threadIdx.x; e < a.H; e += 1024) {
     float t = x[e];
-    const float* p = a.part + (size_t)j * a.H + e;
+    const float* p = a.part + (size_t)j * ldp + e;
     int s = 0;
     for (; s + 8 <= a.S; s += 8) {
       float v[8];
@@ -301,15 +383,16 @@ __global__ __launch_bounds__(256) void k_mgemv_reduce(const MgemvArgs a) {
   const int j = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   const bool live = n < a.N;
+  const size_t ldp = mgemv_ldp(a.N);
   float v = 0.f;
   if (live)
-    for (int s = 0; s < a.S; ++s) v += a.part[((size_t)s * a.M + j) * a.N + n];
+    for (int s = 0; s < a.S; ++s) v += a.part[((size_t)s * MB + j) * ldp + n];
   if constexpr (EPI == MG_STORE) {
     if (live) a.out[(size_t)j * a.ldo + n] = v;
   } else if constexpr (EPI == MG_SWIGLU) {
     if (live && (n & 1) == 0) {
       float u = 0.f;
-      for (int s = 0; s < a.S; ++s) u += a.part[((size_t)s * a.M + j) * a.N + n + 1];
+      for (int s = 0; s < a.S; ++s) u += a.part[((size_t)s * MB + j) * ldp + n + 1];
       a.out[(size_t)j * a.ldo + (n >> 1)] = v / (1.0f + expf(-v)) * u;
     }
   } else if constexpr (EPI == MG_ARGMAX) {
@@ -337,10 +420,12 @@ hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s) {
   if (a.M < 1 || a.M > MB || a.S < 1 || a.K % a.S || (a.K / a.S) % KC || a.ipb < 1)
     return hipErrorInvalidValue;
   const dim3 grid((items + a.ipb - 1) / a.ipb);
+  const bool split_form = a.S == a.K / KC;  // one 512-wide chunk per item: k_mgemv_s
 #define S2_MG(E)                                                                                      \
   case E:                                                                                             \
-    hipLaunchKernelGGL(k_mgemv<E>, grid, dim3(256), 0, s, a);                                         \
-    if (a.S > 1 && E != MG_ADD)                                                                       \
+    if (split_form) hipLaunchKernelGGL(k_mgemv_s, grid, dim3(256), 0, s, a);                           \
+    else hipLaunchKernelGGL(k_mgemv<E>, grid, dim3(256), 0, s, a);                                     \
+    if ((a.S > 1 || split_form) && E != MG_ADD)                                                       \
       hipLaunchKernelGGL(k_mgemv_reduce<E>, dim3((a.N + 255) / 256, a.M), dim3(256), 0, s, a);        \
     break;
   switch (a.epi) {

@@ -870,24 +870,17 @@ struct Enq {
     a.am_hi = hi;
     a.am_val = c->bam_val;
     a.am_idx = c->bam_idx;
-    // Work split: T = tiles * K / 512 chunk tasks; blocks of 2-3 tasks stream best (fewer, longer
-    // blocks leave HBM idle at the start, more, shorter ones pay the pipeline fill per block).  An
-    // item spans nch chunks (a divisor of K / 512, as large as the task budget allows, fewer split
-    // partials); the Slow head keeps whole rows per item so that the argmax stays in the kernel.
+    // Work split.  Every launch but the Slow head takes one 512-wide K chunk per item (S = K / 512,
+    // the straight-line split-K kernel) with about one block per CU; the Slow head (many tiles)
+    // keeps whole rows per item so that the greedy pick stays in the kernel.
     const int tiles = s2k::mgemv_tiles(N), chunks = K / 512;
-    const long T = (long)tiles * chunks;
-    const int tpb = T >= 768 ? 3 : T >= 320 ? 2 : 1;
-    int nch = 1;
-    if (epi == s2k::MG_ARGMAX && tiles >= 512) nch = chunks;
-    else
-      for (int d = 1; d <= tpb; ++d)
-        if (chunks % d == 0) nch = d;
-    while ((size_t)(chunks / nch) * M * N > c->bpart_floats && nch < chunks) {
-      ++nch;
-      while (chunks % nch) ++nch;
+    if (epi == s2k::MG_ARGMAX && tiles >= 512) {
+      a.S = 1;
+      a.ipb = 1;
+    } else {
+      a.S = chunks;
+      a.ipb = std::max(1, (tiles * chunks + s2k::device_cus() - 1) / s2k::device_cus());
     }
-    a.S = chunks / nch;
-    a.ipb = std::max(1, tpb / nch);
     chk(s2k::launch_mgemv(a, s));
     return a.S;
   }
