@@ -98,6 +98,9 @@ struct s2ar_ctx {
   int* am_idx = nullptr;
   float *att_ml = nullptr, *att_o = nullptr;
   int max_splits = 0;
+  // batched decode: positions per attention workgroup (16 streams of 920..3948 positions measured
+  // 9.80 ms per step at 192, 10.20 at 256, 10.52 at 128)
+  int attn_split_b = 192, max_splits_b = 0;
 
   // batched prefill (MFMA): chunk of up to pch prompt rows
   int pch = 0;
@@ -567,8 +570,9 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
       for (const TileJob& j : jobs)
         C_HIP(s2k::launch_tile_weights(static_cast<const uint16_t*>(j.src), *j.dst, j.N, j.K, c->stream));
       C_HIP(hipStreamSynchronize(c->stream));
-      C_TRY(dev_alloc(c, &c->batt_ml, sizeof(float) * 2 * MBt * hq * c->max_splits));
-      C_TRY(dev_alloc(c, &c->batt_o, sizeof(float) * (size_t)MBt * hq * c->max_splits * dmax));
+      c->max_splits_b = (g.max_context + c->attn_split_b - 1) / c->attn_split_b;
+      C_TRY(dev_alloc(c, &c->batt_ml, sizeof(float) * 2 * MBt * hq * c->max_splits_b));
+      C_TRY(dev_alloc(c, &c->batt_o, sizeof(float) * (size_t)MBt * hq * c->max_splits_b * dmax));
       C_TRY(dev_alloc(c, &c->d_dbg_slots, sizeof(int) * MBt));
     }
   }
@@ -931,7 +935,7 @@ struct Enq {
       a.part_ml = c->batt_ml;
       a.part_o = c->batt_o;
       a.kv_bf16 = g.kv_dtype == 1;
-      a.split = kAttnSplit;
+      a.split = c->attn_split_b;
       a.fixed_slot = -1;
       a.row_pos = nullptr;
       a.append = 1;
@@ -943,7 +947,7 @@ struct Enq {
         a.v_cache = c->kv_v + (size_t)l * c->kv_layer;
         a.block_table = c->d_bt;
         a.bt_stride = c->bt_stride;
-        a.max_splits = c->max_splits;
+        a.max_splits = c->max_splits_b;
       } else {
         a.rope_cos = c->rope_cos_f;
         a.rope_sin = c->rope_sin_f;
