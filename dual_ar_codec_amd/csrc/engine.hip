@@ -918,9 +918,13 @@ struct Enq {
     for (int l = 0; l < st.n_layers; ++l) {
       const LayerW& L = W[l];
       norm_b(xres, pending, H, M, L.attn_norm);
-      mgemv(s2k::MG_STORE, L.tqkv, c->bxn, ldx, c->bqkv, qkvd, qkvd, H, M);
+      // q, k, v stay as split-K partials; the attention kernel sums them as it loads them
+      const int qkv_S = mgemv(s2k::MG_ADD, L.tqkv, c->bxn, ldx, nullptr, 0, qkvd, H, M);
       s2k::AttnArgs a{};
       a.qkv = c->bqkv;
+      a.qkv_part = c->bpart;
+      a.qkv_S = qkv_S;
+      a.qkv_ldp = s2k::mgemv_tiles(qkvd) * 64;
       a.q_norm = L.q_norm;
       a.k_norm = L.k_norm;
       a.slots = slots;

@@ -61,6 +61,11 @@ struct AttnArgs {
   int fixed_slot;
   const int* row_pos;
   int append;
+  // batched decode: q, k, v are the sum of qkv_S split-K partials qkv_part[s][16][qkv_ldp]
+  // (batch row b at row b of each split) instead of qkv; qkv_S == 0 reads qkv
+  const float* qkv_part;
+  int qkv_S;
+  int qkv_ldp;
 };
 // Attention of the new position over its context; a context longer than `split` is cut into
 // splits whose partial results launch_attention_combine merges (needed only when

@@ -638,15 +638,31 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     rowoff_s[t] = (int)((((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
   }
   // this wave's q head (and, for wave 0 of the split holding pos, the new k and v)
+  // element n of this row's q | k | v vector (summing the split partials in split order)
+  auto qkv_at = [&](int n) -> float {
+    if (a.qkv_S == 0) return qkv[n];
+    const float* p = a.qkv_part + (size_t)b * a.qkv_ldp + n;
+    const size_t st = (size_t)16 * a.qkv_ldp;
+    float v = 0.f;
+    for (int s0 = 0; s0 < a.qkv_S; s0 += 8) {  // eight loads in flight at a time
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = (s0 + u < a.qkv_S) ? p[(s0 + u) * st] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < a.qkv_S) v += t[u];
+    }
+    return v;
+  };
   float qv[PER], kv[PER], vv[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) qv[i] = qkv[h * D + lane + i * WAVE];
+  for (int i = 0; i < PER; ++i) qv[i] = qkv_at(h * D + lane + i * WAVE);
   const bool mk = has_new && w == 0;
   if (mk) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      kv[i] = qkv[(size_t)(a.Hq + g) * D + lane + i * WAVE];
-      vv[i] = qkv[(size_t)(a.Hq + a.Hkv + g) * D + lane + i * WAVE];
+      kv[i] = qkv_at((a.Hq + g) * D + lane + i * WAVE);
+      vv[i] = qkv_at((a.Hq + a.Hkv + g) * D + lane + i * WAVE);
     }
   }
   __syncthreads();
