@@ -253,8 +253,15 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
         wb[sl][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (sl * 4 + t) * 512));
   }
   const int xr_row = tid >> 4, xr_col = (tid & 15) * 32;
-  const float* xrow = a.x + (size_t)min(xr_row, a.M - 1) * a.ldx + xr_col;
+  const int xr_m = min(xr_row, a.M - 1);
+  const float* xrow = a.x + (size_t)xr_m * a.ldx + xr_col;
   const bool xlive = xr_row < a.M;
+  float xsc = 1.f;  // RMSNorm row scale (same sum order in every consumer)
+  if (a.ssq) {
+    float tot = 0.f;
+    for (int c = 0; c < a.nssq; ++c) tot += a.ssq[(size_t)xr_m * a.nssq + c];
+    xsc = rsqrtf(tot / (float)a.K + a.eps);
+  }
   int it = it0;
   while (it < it1) {
     const int split = it / ntiles;
@@ -262,10 +269,17 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
     if (it != it0) lds_barrier();
     {
       const f32x4* q = reinterpret_cast<const f32x4*>(xrow + split * KC);
+      const f32x4* gq = a.ssq ? reinterpret_cast<const f32x4*>(a.gain + split * KC + xr_col) : nullptr;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f32x4 u0 = q[2 * u], u1 = q[2 * u + 1];
         float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        if (a.ssq) {
+          const f32x4 g0 = gq[2 * u], g1 = gq[2 * u + 1];
+          const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] * xsc * gv[e];
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = xlive ? v[e] : 0.f;
         bf16x8 hi, lo;
@@ -371,6 +385,40 @@ __global__ __launch_bounds__(1024) void k_norm_rows(NormRowsArgs a) {
   for (int e = threadIdx.x; e < a.H; e += 1024) xn[e] = x[e] * scale * a.gain[e];
 }
 
+__global__ __launch_bounds__(256) void k_fold_rows(const FoldArgs f) {
+  __shared__ float red[4];
+  const int j = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  float t = 0.f;
+  if (e < f.H) {
+    float* x = f.x + (size_t)j * f.ldx;
+    t = x[e];
+    const float* p = f.part + (size_t)j * mgemv_ldp(f.H) + e;
+    const size_t st = (size_t)MB * mgemv_ldp(f.H);
+    for (int s0 = 0; s0 < f.S; s0 += 8) {  // eight loads in flight at a time, added in split order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (s0 + u < f.S) ? p[(s0 + u) * st] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < f.S) t += v[u];
+    }
+    if (f.S > 0) x[e] = t;
+  }
+  float ss = t * t;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, WAVE);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) f.ssq[(size_t)j * gridDim.x + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+int fold_chunks(int H) { return (H + 255) / 256; }
+
+hipError_t launch_fold_rows(const FoldArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_fold_rows, dim3(fold_chunks(a.H), a.M), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_norm_rows(const NormRowsArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_norm_rows, dim3(a.M), dim3(1024), 0, s, a);
   return hipGetLastError();
@@ -421,6 +469,7 @@ hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 grid((items + a.ipb - 1) / a.ipb);
   const bool split_form = a.S == a.K / KC;  // one 512-wide chunk per item: k_mgemv_s
+  if (a.ssq && !split_form) return hipErrorInvalidValue;  // the input norm lives in k_mgemv_s only
 #define S2_MG(E)                                                                                      \
   case E:                                                                                             \
     if (split_form) hipLaunchKernelGGL(k_mgemv_s, grid, dim3(256), 0, s, a);                           \

@@ -126,7 +126,7 @@ struct s2ar_ctx {
   // batched multi-stream decode (up to 16 streams per launch, MFMA GEMVs)
   bool batched_ok = false;
   float *bx = nullptr, *bxf = nullptr, *bqkv = nullptr, *batt = nullptr, *bact = nullptr;
-  float *blogits = nullptr, *bxn = nullptr, *bpart = nullptr, *bam_val = nullptr;
+  float *blogits = nullptr, *bxn = nullptr, *bpart = nullptr, *bam_val = nullptr, *bssq = nullptr;
   int* bam_idx = nullptr;
   float *batt_ml = nullptr, *batt_o = nullptr;
   size_t bpart_floats = 0;
@@ -538,6 +538,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
       C_TRY(dev_alloc(c, &c->bact, sizeof(float) * MBt * f_max));
       C_TRY(dev_alloc(c, &c->blogits, sizeof(float) * MBt * V));
       C_TRY(dev_alloc(c, &c->bxn, sizeof(float) * MBt * s2k::pad_k(H)));
+      C_TRY(dev_alloc(c, &c->bssq, sizeof(float) * MBt * s2k::fold_chunks(H)));
       c->bpart_floats = (size_t)32 * MBt * std::max(std::max(qkvd_max, (int)K), std::max(H, 2 * f_max));
       C_TRY(dev_alloc(c, &c->bpart, sizeof(float) * c->bpart_floats));
       const int ngroups = 4 * s2k::mgemv_tiles((int)V);  // 16-row argmax groups
@@ -857,8 +858,10 @@ struct Enq {
   const int* bslots_host = nullptr;
   // returns the number of K splits; an MG_ADD launch leaves that many partials in bpart for the
   // next norm_b to fold into the residual
+  // norm_gain != nullptr: the input rows are RMS-normalised on the fly with the sums of squares
+  // that fold_b left in bssq
   int mgemv(int epi, const void* w, const float* x, int ldx, float* out, int ldo, int N, int K, int M, int lo = 0,
-            int hi = 0) {
+            int hi = 0, const float* norm_gain = nullptr) {
     s2k::MgemvArgs a{};
     a.x = x;
     a.ldx = ldx;
@@ -878,7 +881,13 @@ struct Enq {
     // the straight-line split-K kernel) with about one block per CU; the Slow head (many tiles)
     // keeps whole rows per item so that the greedy pick stays in the kernel.
     const int tiles = s2k::mgemv_tiles(N), chunks = K / 512;
-    if (epi == s2k::MG_ARGMAX && tiles >= 512) {
+    if (norm_gain) {
+      a.ssq = c->bssq;
+      a.nssq = s2k::fold_chunks(K);
+      a.gain = norm_gain;
+      a.eps = (float)c->cfg.rms_eps;
+    }
+    if (epi == s2k::MG_ARGMAX && tiles >= 512 && !norm_gain) {
       a.S = 1;
       a.ipb = 1;
     } else {
@@ -887,6 +896,20 @@ struct Enq {
     }
     chk(s2k::launch_mgemv(a, s));
     return a.S;
+  }
+
+  // fold `pending` residual partials into xres and leave the per-chunk sums of squares in bssq
+  void fold_b(float* xres, int& pending, int H, int M) {
+    s2k::FoldArgs f{};
+    f.x = xres;
+    f.ldx = s2k::pad_k(c->cfg.slow.hidden);
+    f.part = c->bpart;
+    f.S = pending;
+    f.M = M;
+    f.H = H;
+    f.ssq = c->bssq;
+    chk(s2k::launch_fold_rows(f, s));
+    pending = 0;
   }
 
   // fold `pending` residual partials into xres, then bxn = RMSNorm(xres) * gain (gain == nullptr:
@@ -917,9 +940,9 @@ struct Enq {
     const float eps = (float)g.rms_eps;
     for (int l = 0; l < st.n_layers; ++l) {
       const LayerW& L = W[l];
-      norm_b(xres, pending, H, M, L.attn_norm);
+      fold_b(xres, pending, H, M);
       // q, k, v stay as split-K partials; the attention kernel sums them as it loads them
-      const int qkv_S = mgemv(s2k::MG_ADD, L.tqkv, c->bxn, ldx, nullptr, 0, qkvd, H, M);
+      const int qkv_S = mgemv(s2k::MG_ADD, L.tqkv, xres, ldx, nullptr, 0, qkvd, H, M, 0, 0, L.attn_norm);
       s2k::AttnArgs a{};
       a.qkv = c->bqkv;
       a.qkv_part = c->bpart;
@@ -965,8 +988,8 @@ struct Enq {
       chk(s2k::launch_attention(a, s));
       if (a.max_splits > 1) chk(s2k::launch_attention_combine(a, s));
       pending = mgemv(s2k::MG_ADD, L.to, c->batt, qd, nullptr, 0, H, qd, M);
-      norm_b(xres, pending, H, M, L.mlp_norm);
-      mgemv(s2k::MG_SWIGLU, L.tgu, c->bxn, ldx, c->bact, F, 2 * F, H, M);
+      fold_b(xres, pending, H, M);
+      mgemv(s2k::MG_SWIGLU, L.tgu, xres, ldx, c->bact, F, 2 * F, H, M, 0, 0, L.mlp_norm);
       pending = mgemv(s2k::MG_ADD, L.tdown, c->bact, F, nullptr, 0, H, F, M);
       if (btp) {
         norm_b(xres, pending, H, M, nullptr);
@@ -1026,8 +1049,8 @@ struct Enq {
         chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, slots, c->d_codes, j, c->bxf, ldx, M, s));
       tap_step = j - 1;
       int pending = layers_b(false, M, slots, c->bxf);
-      norm_b(c->bxf, pending, H, M, c->fast_final);
-      mgemv(s2k::MG_ARGMAX, c->fast_head_t, c->bxn, ldx, c->blogits, K, K, H, M, 0, K);
+      fold_b(c->bxf, pending, H, M);
+      mgemv(s2k::MG_ARGMAX, c->fast_head_t, c->bxf, ldx, c->blogits, K, K, H, M, 0, K, c->fast_final);
       if (btp) {
         finish_b(s2k::FIN_CODE, j, M, slots, 0, K, c->bxf);
         for (int b = 0; b < M; ++b) {

@@ -188,6 +188,12 @@ struct MgemvArgs {
   int am_lo, am_hi;
   float* am_val;           // [N / 16][16]
   int* am_idx;
+  // optional RMSNorm of the input rows, applied while they are staged (split-K form only):
+  // x[j][k] / sqrt(sum_c ssq[j][c] / K + eps) * gain[k]
+  const float* ssq;        // [M][nssq] partial sums of squares (k_fold_rows), or nullptr
+  int nssq;
+  const float* gain;
+  float eps;
 };
 int mgemv_tiles(int N);
 hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s);
@@ -207,6 +213,17 @@ struct NormRowsArgs {
   float* xn;               // [M][ldx] normalised rows (or nullptr: only fold the partials)
 };
 hipError_t launch_norm_rows(const NormRowsArgs& a, hipStream_t s);
+// x[j] += sum_s part[s][j] (split order, S >= 0) and ssq[j][c] = sum of x[j][e]^2 over the 256-wide
+// chunk c (ceil(H / 256) chunks).  grid = (chunks, M).
+struct FoldArgs {
+  float* x;
+  int ldx;
+  const float* part;       // [S][16][ldp] pending residual partials
+  int S, M, H;
+  float* ssq;              // [M][ceil(H / 256)]
+};
+int fold_chunks(int H);
+hipError_t launch_fold_rows(const FoldArgs& a, hipStream_t s);
 
 struct FinishBArgs {
   const float* am_val;     // [blocks][16]
