@@ -82,6 +82,17 @@ def test_voice_clone_prefill_teacher_forced():
     assert rep["tokens_checked"] > 5
 
 
+def test_prefill_longer_than_one_row_block():
+    """A 2100-position prompt at the mid shape: the matrix-core prefill runs it as two row blocks
+    (2048 + 52), the second attending over the first block's cached keys."""
+    cfg = synth.config("mid", max_context=2176)
+    toks = synth.uniform_ints(77, 0, 2100, 0, cfg["vocab_text"])
+    mask = np.zeros(len(toks), np.uint8)
+    codes = np.zeros((len(toks), cfg["n_codebooks"]), np.int32)
+    rep = _teacher_forced("mid", n_frames=2, prompt=(toks, mask, codes), max_context=2176)
+    assert rep["tokens_checked"] > 5
+
+
 def test_prefill_in_two_calls_matches_one_prefill():
     cfg = synth.config("mid")
     w = synth.make_weights(cfg)
@@ -248,6 +259,22 @@ def test_batched_multi_stream_teacher_forced_mid_ragged():
         ctx.prefill(s_, p)
     rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
     _say(f"[parity] batched mid: {rep}")
+    ctx.close()
+
+
+def test_batched_sixteen_streams_mid():
+    """A full batch of 16 streams (every MFMA column live) with ragged contexts of 5..300 positions."""
+    cfg = synth.config("mid", max_context=384)
+    lens = [5, 300, 17, 64, 65, 128, 33, 250, 7, 190, 96, 16, 201, 45, 150, 80]
+    prompts = _ragged_prompts(cfg, lens, 41)
+    w = synth.make_weights(cfg)
+    per_stream = _oracle_frames_per_stream(cfg, w, prompts, 2)
+    ctx = _ctx(cfg, w, max_streams=16)
+    ids = list(range(16))[::-1]
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
+    _say(f"[parity] batched 16 streams mid: {rep}")
     ctx.close()
 
 
