@@ -193,6 +193,13 @@ def main():
                 "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                 "kernel": "k_gemv2<bf16, NCH=5, GEMV_NORM_SWIGLU, R=2, WPB=4> (Slow gate/up, 19456x2560)",
                 "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2)}
+    # context: a plain streaming read of the same weights, the rate no arithmetic slows down
+    ctx.time_kernel(1, 4)  # first launches load the kernel's code object: not timed
+    sms, sbytes = ctx.time_kernel(1, args.kernel_iters)
+    s_gbps = sbytes / (sms * 1e-3) / 1e9
+    roofline["stream_read_context"] = {"gbps": round(s_gbps, 1), "frac_of_peak": round(s_gbps / HBM_PEAK_GBPS, 4),
+                                       "avg_launch_us": round(sms * 1e3, 2),
+                                       "gemv_over_stream": round(k_gbps / s_gbps, 4)}
     ctx.close()
 
     multi = None

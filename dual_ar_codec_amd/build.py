@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libs2ar.so")
-SOURCES = ["engine.hip", "kernels.hip", "prefill.hip", "batch.hip"]
+SOURCES = ["engine.hip", "kernels.hip", "prefill.hip", "batch.hip", "measure.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",

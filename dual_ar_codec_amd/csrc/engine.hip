@@ -130,6 +130,7 @@ struct s2ar_ctx {
   int* bam_idx = nullptr;
   float *batt_ml = nullptr, *batt_o = nullptr;
   size_t bpart_floats = 0;
+  uint32_t* d_sink = nullptr;  // never-taken store target of the streaming-read measurement
   int* d_dbg_slots = nullptr;  // [16] batch slots of the eager batched frame
   struct BatchGraph {
     Graph g;
@@ -470,6 +471,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   C_TRY(dev_alloc(c, &c->d_codes, sizeof(int) * g.max_streams * NC));
   C_TRY(dev_alloc(c, &c->d_h, sizeof(float) * (size_t)g.max_streams * H));
   C_TRY(dev_alloc(c, &c->d_snap, sizeof(int) * g.max_streams * NC));
+  C_TRY(dev_alloc(c, &c->d_sink, sizeof(uint32_t)));
   c->pos.assign(g.max_streams, 0);
   c->ready.assign(g.max_streams, 0);
 
@@ -1513,13 +1515,16 @@ int s2ar_stream_position(const s2ar_ctx* c, int32_t sid, int32_t* pos_out) {
 
 int s2ar_time_kernel(s2ar_ctx* c, int32_t which, int32_t iters, float* avg_ms, int64_t* bytes_out) {
   if (!c) return S2AR_E_ARG;
-  if (which != 0 || iters < 1 || !avg_ms) return set_err(c, S2AR_E_ARG, "which must be 0, iters >= 1, avg_ms non-null");
+  if (which < 0 || which > 1 || iters < 1 || !avg_ms)
+    return set_err(c, S2AR_E_ARG, "which must be 0 or 1, iters >= 1, avg_ms non-null");
   const s2ar_stack& st = c->cfg.slow;
+  const size_t wbytes = (size_t)2 * st.ffn * st.hidden * c->esz;
   Enq q{c, c->stream};
   HIP_TRY(c, hipEventRecord(c->ev_t0, c->stream));
   for (int i = 0; i < iters; ++i) {
     const LayerW& L = c->slow[i % st.n_layers];
-    q.gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, c->x, L.mlp_norm, c->act, 2 * st.ffn, st.hidden);
+    if (which == 0) q.gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, c->x, L.mlp_norm, c->act, 2 * st.ffn, st.hidden);
+    else q.chk(s2k::launch_stream_read(L.wgu, wbytes, c->d_sink, c->stream));
   }
   HIP_TRY(c, hipEventRecord(c->ev_t1, c->stream));
   if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("time kernel: ") + hipGetErrorString(q.e));
@@ -1528,7 +1533,7 @@ int s2ar_time_kernel(s2ar_ctx* c, int32_t which, int32_t iters, float* avg_ms, i
   HIP_TRY(c, hipEventElapsedTime(&ms, c->ev_t0, c->ev_t1));
   *avg_ms = ms / (float)iters;
   if (bytes_out)
-    *bytes_out = (int64_t)2 * st.ffn * st.hidden * c->esz + (int64_t)st.hidden * 4 * 2 + (int64_t)st.ffn * 4;
+    *bytes_out = which == 0 ? (int64_t)wbytes + (int64_t)st.hidden * 4 * 2 + (int64_t)st.ffn * 4 : (int64_t)wbytes;
   return S2AR_OK;
 }
 

@@ -167,6 +167,9 @@ hipError_t launch_embed_prompt(bool bf16, const void* embed, const void* codeboo
 // pos[slots[b]] += 1
 hipError_t launch_advance(const int* slots, int* pos, int M, hipStream_t s);
 
+// Plain streaming read of [p, p + bytes) (measure.hip): context for the GEMV rates.
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
+
 // ---- batched multi-stream decode (batch.hip) ----
 enum MgemvEpi : int { MG_STORE = 0, MG_ADD = 1, MG_SWIGLU = 2, MG_ARGMAX = 3 };
 // out[j][n] = sum_k W[n][k] * x[j][k] for batch rows j < M <= 16, on the matrix cores (x already

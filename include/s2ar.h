@@ -158,15 +158,17 @@ int s2ar_debug_frame(s2ar_ctx* ctx, int32_t stream_id, const int32_t* forced_cod
 
 /* The batched multi-stream frame (the kernels s2ar_decode_frame uses for 2..16 streams), run
  * without the captured graph: forced_codes [n][n_codebooks] or NULL, taps [n] (fast_z and
- * slow_embed are not filled).  Needs bf16 weights and every K dimension divisible by 128
+ * slow_embed are not filled).  Needs bf16 weights and every K dimension divisible by 512
  * (S2AR_E_ARG otherwise); n <= 16. */
 int s2ar_debug_frame_batch(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n, const int32_t* forced_codes,
                            s2ar_taps* taps);
 
-/* Launch one kernel of the frame `iters` times on the context's stream,
- * cycling over the layers, and report the mean duration of a launch measured
- * with HIP events on that stream.  which: 0 = Slow fused RMSNorm + gate/up +
- * SwiGLU GEMV.  bytes_out: algorithmic bytes of one launch. */
+/* Launch one kernel `iters` times on the context's stream, cycling over the
+ * layers, and report the mean duration of a launch measured with HIP events on
+ * that stream.  which: 0 = Slow fused RMSNorm + gate/up + SwiGLU GEMV;
+ * 1 = a plain streaming read of the same gate/up weights (no arithmetic: the
+ * device's practical read rate, context for 0).  bytes_out: algorithmic bytes of
+ * one launch.  S2AR_E_ARG for another which, iters < 1 or a null avg_ms. */
 int s2ar_time_kernel(s2ar_ctx* ctx, int32_t which, int32_t iters, float* avg_ms, int64_t* bytes_out);
 
 #ifdef __cplusplus

@@ -210,6 +210,22 @@ def test_errors_leave_state_unchanged():
     ctx.close()
 
 
+def test_time_kernel_gemv_and_stream_read():
+    """The bench's timing entry: the gate/up GEMV and the plain streaming read of the same weights."""
+    cfg = synth.config("mid")
+    w = synth.make_weights(cfg)
+    ctx = _ctx(cfg, w)
+    ms0, b0 = ctx.time_kernel(0, 4)
+    ms1, b1 = ctx.time_kernel(1, 4)
+    s = cfg["slow"]
+    assert b1 == 2 * s["ffn"] * s["hidden"] * 2 and b0 > b1
+    assert ms0 > 0 and ms1 > 0
+    with pytest.raises(s2ar.S2arError) as e:
+        ctx.time_kernel(2, 1)
+    assert e.value.code == -1
+    ctx.close()
+
+
 # ------------------------------------------------------------------------------ multi-stream
 
 def _oracle_frames_per_stream(cfg, w, prompts, n):
