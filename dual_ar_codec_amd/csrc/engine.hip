@@ -105,7 +105,9 @@ struct s2ar_ctx {
   // batched prefill (MFMA): chunk of up to pch prompt rows
   int pch = 0;
   bool mfma_prefill = false;
-  float *px = nullptr, *pqkv = nullptr, *patt = nullptr, *pact = nullptr, *prms = nullptr;
+  float *px = nullptr, *pqkv = nullptr;
+  // bf16 hi / lo planes of the GEMM inputs: normalised residual, attention output, SwiGLU output
+  uint16_t *pxh = nullptr, *pxl = nullptr, *patth = nullptr, *pattl = nullptr, *pacth = nullptr, *pactl = nullptr;
   int* d_iota = nullptr;  // [max_context] = 0, 1, 2, ...
   int* h_pos_stage = nullptr;
 
@@ -510,9 +512,12 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
       c->pch = std::min(g.max_context, 2048);
       C_TRY(dev_alloc(c, &c->px, sizeof(float) * (size_t)c->pch * H));
       C_TRY(dev_alloc(c, &c->pqkv, sizeof(float) * (size_t)c->pch * qkvd_s));
-      C_TRY(dev_alloc(c, &c->patt, sizeof(float) * (size_t)c->pch * qd_s));
-      C_TRY(dev_alloc(c, &c->pact, sizeof(float) * (size_t)c->pch * st.ffn));
-      C_TRY(dev_alloc(c, &c->prms, sizeof(float) * (size_t)c->pch));
+      C_TRY(dev_alloc(c, &c->pxh, sizeof(uint16_t) * (size_t)c->pch * H));
+      C_TRY(dev_alloc(c, &c->pxl, sizeof(uint16_t) * (size_t)c->pch * H));
+      C_TRY(dev_alloc(c, &c->patth, sizeof(uint16_t) * (size_t)c->pch * qd_s));
+      C_TRY(dev_alloc(c, &c->pattl, sizeof(uint16_t) * (size_t)c->pch * qd_s));
+      C_TRY(dev_alloc(c, &c->pacth, sizeof(uint16_t) * (size_t)c->pch * st.ffn));
+      C_TRY(dev_alloc(c, &c->pactl, sizeof(uint16_t) * (size_t)c->pch * st.ffn));
       std::vector<int> iota(g.max_context);
       for (int i = 0; i < g.max_context; ++i) iota[i] = i;
       C_TRY(dev_alloc(c, &c->d_iota, sizeof(int) * g.max_context));
@@ -783,15 +788,16 @@ struct Enq {
     const float eps = (float)g.rms_eps;
     chk(s2k::launch_embed_rows(c->bf16, c->embed, c->codebook, g.codebook_size, H, g.n_codebooks, c->d_tokens,
                                has_mask ? c->d_mask : nullptr, c->d_pcodes, p0, rows, c->px, H, s));
-    auto gemm = [&](const float* a, int lda, const float* scale, const float* gain, const void* w, float* out,
-                    int ldc, int N, int K, int epi) {
+    auto gemm = [&](const uint16_t* a_hi, const uint16_t* a_lo, int lda, const void* w, float* out, uint16_t* out_hi,
+                    uint16_t* out_lo, int ldc, int N, int K, int epi) {
       s2k::GemmArgs ga{};
-      ga.a = a;
+      ga.a_hi = a_hi;
+      ga.a_lo = a_lo;
       ga.lda = lda;
-      ga.a_scale = scale;
-      ga.a_gain = gain;
       ga.w = static_cast<const uint16_t*>(w);
       ga.c = out;
+      ga.c_hi = out_hi;
+      ga.c_lo = out_lo;
       ga.ldc = ldc;
       ga.M = rows;
       ga.N = N;
@@ -801,8 +807,8 @@ struct Enq {
     };
     for (int l = 0; l < st.n_layers; ++l) {
       const LayerW& L = c->slow[l];
-      chk(s2k::launch_row_rms(c->px, H, H, eps, c->prms, rows, s));
-      gemm(c->px, H, c->prms, L.attn_norm, L.wqkv, c->pqkv, qkvd, qkvd, H, s2k::GEMM_STORE);
+      chk(s2k::launch_norm_split(c->px, H, H, eps, L.attn_norm, c->pxh, c->pxl, H, rows, s));
+      gemm(c->pxh, c->pxl, H, L.wqkv, c->pqkv, nullptr, nullptr, qkvd, qkvd, H, s2k::GEMM_STORE);
       s2k::PrefillKvArgs kv{};
       kv.qkv = c->pqkv;
       kv.ld = qkvd;
@@ -831,7 +837,8 @@ struct Enq {
       pa.kv_bf16 = kv.kv_bf16;
       pa.block_table = kv.block_table;
       pa.page_size = kPageSize;
-      pa.out = c->patt;
+      pa.out_hi = c->patth;
+      pa.out_lo = c->pattl;
       pa.ld_out = qd;
       pa.rows = rows;
       pa.pos0 = pos0;
@@ -841,10 +848,10 @@ struct Enq {
       pa.eps = eps;
       pa.scale = (float)(1.0 / std::sqrt((double)D));
       chk(s2k::launch_prefill_attn(pa, s));
-      gemm(c->patt, qd, nullptr, nullptr, L.wo, c->px, H, H, qd, s2k::GEMM_ADD);
-      chk(s2k::launch_row_rms(c->px, H, H, eps, c->prms, rows, s));
-      gemm(c->px, H, c->prms, L.mlp_norm, L.wgu, c->pact, F, 2 * F, H, s2k::GEMM_SWIGLU);
-      gemm(c->pact, F, nullptr, nullptr, L.wdown, c->px, H, H, F, s2k::GEMM_ADD);
+      gemm(c->patth, c->pattl, qd, L.wo, c->px, nullptr, nullptr, H, H, qd, s2k::GEMM_ADD);
+      chk(s2k::launch_norm_split(c->px, H, H, eps, L.mlp_norm, c->pxh, c->pxl, H, rows, s));
+      gemm(c->pxh, c->pxl, H, L.wgu, nullptr, c->pacth, c->pactl, F, 2 * F, H, s2k::GEMM_SWIGLU);
+      gemm(c->pacth, c->pactl, F, L.wdown, c->px, nullptr, nullptr, H, H, F, s2k::GEMM_ADD);
     }
   }
 

@@ -100,18 +100,22 @@ enum GemmEpi : int { GEMM_STORE = 0, GEMM_ADD = 1, GEMM_SWIGLU = 2 };
 // matrix cores.  GEMM_SWIGLU: W rows (2i, 2i+1) = (gate_i, up_i); C[m][i] = silu(gate) * up.
 // Requires N % 128 == 0, K % 32 == 0, lda % 4 == 0.
 struct GemmArgs {
-  const float* a;          // [M][lda] fp32 activations
+  const uint16_t* a_hi;    // [M][lda] activations as bf16 high parts
+  const uint16_t* a_lo;    // [M][lda] and bf16 low parts (x - hi, rounded): x = hi + lo + O(2^-17 |x|)
   int lda;
-  const float* a_scale;    // [M] RMSNorm row scale or nullptr
-  const float* a_gain;     // [K] RMSNorm gain or nullptr
   const uint16_t* w;       // [N][K] bf16 weights
-  float* c;                // [M][ldc]
+  float* c;                // [M][ldc] fp32 output (GEMM_STORE, GEMM_ADD)
+  uint16_t* c_hi;          // GEMM_SWIGLU: [M][ldc] silu(g) u as bf16 high and low planes
+  uint16_t* c_lo;
   int ldc;
   int M, N, K;
   int epi;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
-hipError_t launch_row_rms(const float* x, int ld, int H, float eps, float* scale, int M, hipStream_t s);
+// RMSNorm of M rows and the bf16 split of the result: hi/lo planes of x[m] * (scale[m] * gain),
+// scale = 1 / sqrt(mean(x[m]^2) + eps).  One 256-thread block per row.
+hipError_t launch_norm_split(const float* x, int ld, int H, float eps, const float* gain, uint16_t* hi, uint16_t* lo,
+                             int ldo, int M, hipStream_t s);
 
 struct PrefillKvArgs {
   const float* qkv;        // [rows][ld] projections of the prompt rows
@@ -143,7 +147,8 @@ struct PrefillAttnArgs {
   int kv_bf16;
   const int* block_table;  // the stream's row of the block table
   int page_size;
-  float* out;              // [rows][ld_out]
+  uint16_t* out_hi;        // [rows][ld_out] attention output as bf16 high and low planes (the
+  uint16_t* out_lo;        // O projection's input)
   int ld_out;
   int rows, pos0, Hq, Hkv, D;
   float eps, scale;

@@ -2,12 +2,11 @@
 //
 // Prefill runs every Slow layer on P prompt positions, so its projections are real dense
 // contractions: C[P][N] = A[P][K] . W[N][K]^T with P up to a few thousand.  They run on the
-// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation): 128 x 128 (or 64 x 128) output
-// tiles per 256-thread workgroup, K in steps of 32 through double-buffered LDS.  The A loader
-// reads fp32 activations and applies the RMSNorm row scale and gain; each activation is then
-// split into bf16 hi + bf16 lo (lo = the rounding error of hi) and both halves multiply the bf16
-// weights, so the product carries ~16 bits of the activation instead of 8 (the weights are bf16
-// already, exactly).  Epilogues add the residual or form SwiGLU pairs.
+// matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Every activation matrix is held
+// as two bf16 planes, hi = bf16(x) and lo = bf16(x - hi), written once by the kernel that
+// produces it (the RMSNorm + split row kernel, the prefill attention, the SwiGLU epilogue); both
+// planes multiply the bf16 weights, so the product carries ~16 bits of the activation instead of 8
+// (the weights are bf16 already, exactly).  Epilogues store, add the residual or form SwiGLU pairs.
 #include "kernels.h"
 
 #include <math.h>
@@ -28,14 +27,6 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return a >> 16;
 }
 
-// (bf16 hi, bf16 lo) of two floats, packed in two words: x = hi + lo + O(2^-17 |x|)
-__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
-  const float r0 = x0 - __uint_as_float(h0 << 16), r1 = x1 - __uint_as_float(h1 << 16);
-  hi = h0 | (h1 << 16);
-  lo = bf16_bits(r0) | (bf16_bits(r1) << 16);
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
@@ -45,7 +36,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
-// MFMA GEMM.  Block = 4 wavefronts in a 2 x 2 grid; wavefront (wm, wn) owns rows
+// MFMA GEMM.  The activations arrive split into bf16 hi and lo planes (k_norm_split, the prefill
+// attention and the SwiGLU epilogue write them), so the stage loaders only copy.  Block = 4 wavefronts in a 2 x 2 grid; wavefront (wm, wn) owns rows
 // [wm BM/2, (wm+1) BM/2) and columns [64 wn, 64 wn + 64) of the block tile.
 template <int BM, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
@@ -55,56 +47,42 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LS];   // activation, bf16 hi
   __shared__ __attribute__((aligned(16))) uint16_t Al[2][BM * LS];   // activation, bf16 lo
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LS];
-  extern __shared__ __attribute__((aligned(16))) float gs[];  // the RMSNorm gain [K], when there is one
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int nk = g.K / BK;
 
-  // global -> register staging of one K step
-  // A: BM 128 -> thread t loads 16 fp32 of row t/2 at k (t%2)*16; BM 64 -> 8 fp32 of row t/4 at (t%4)*8
-  constexpr int AF = BM == 128 ? 16 : 8;
+  // global -> register staging of one K step (32 bf16 = 64 bytes per row and plane)
+  // A: BM 128 -> thread t copies 16 bf16 of row t/2 at k (t%2)*16 from each plane; BM 64 -> 8 of row t/4
+  constexpr int AE = BM == 128 ? 16 : 8;
   const int a_row = BM == 128 ? tid >> 1 : tid >> 2;
   const int a_k = BM == 128 ? (tid & 1) * 16 : (tid & 3) * 8;
   const int a_m = min(m0 + a_row, g.M - 1);
-  const float* a_src = g.a + (size_t)a_m * g.lda + a_k;
-  const float a_sc = g.a_scale ? g.a_scale[a_m] : 1.0f;
+  const uint16_t* ah_src = g.a_hi + (size_t)a_m * g.lda + a_k;
+  const uint16_t* al_src = g.a_lo + (size_t)a_m * g.lda + a_k;
   // W: thread t loads 32 bytes of row t/2 at k (t%2)*16
   const int w_row = tid >> 1, w_k = (tid & 1) * 16;
   const uint16_t* w_src = g.w + (size_t)(n0 + w_row) * g.K + w_k;
 
-  f32x4 ar[AF / 4];
+  u32x4 ahr[AE / 8], alr[AE / 8];
   u32x4 wr[2];
   auto load = [&](int kt) {
     const int k = kt * BK;
 #pragma unroll
-    for (int i = 0; i < AF / 4; ++i) ar[i] = *reinterpret_cast<const f32x4*>(a_src + k + 4 * i);
+    for (int i = 0; i < AE / 8; ++i) {
+      ahr[i] = *reinterpret_cast<const u32x4*>(ah_src + k + 8 * i);
+      alr[i] = *reinterpret_cast<const u32x4*>(al_src + k + 8 * i);
+    }
     wr[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + k));
     wr[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + k + 8));
   };
   auto stash = [&](int kt, int buf) {
-    const int k = kt * BK;
-    uint32_t p[AF / 2], q[AF / 2];
+    (void)kt;
 #pragma unroll
-    for (int i = 0; i < AF / 4; ++i) {
-      f32x4 v = ar[i];
-      if (g.a_gain) {
-        const f32x4 gg = *reinterpret_cast<const f32x4*>(gs + k + a_k + 4 * i);
-        v.x *= a_sc * gg.x;
-        v.y *= a_sc * gg.y;
-        v.z *= a_sc * gg.z;
-        v.w *= a_sc * gg.w;
-      }
-      split_bf16x2(v.x, v.y, p[2 * i], q[2 * i]);
-      split_bf16x2(v.z, v.w, p[2 * i + 1], q[2 * i + 1]);
-    }
-    uint16_t* ad = &As[buf][a_row * LS + a_k];
-    uint16_t* al = &Al[buf][a_row * LS + a_k];
-#pragma unroll
-    for (int i = 0; i < AF / 8; ++i) {
-      *reinterpret_cast<u32x4*>(ad + 8 * i) = u32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
-      *reinterpret_cast<u32x4*>(al + 8 * i) = u32x4{q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]};
+    for (int i = 0; i < AE / 8; ++i) {
+      *reinterpret_cast<u32x4*>(&As[buf][a_row * LS + a_k + 8 * i]) = ahr[i];
+      *reinterpret_cast<u32x4*>(&Al[buf][a_row * LS + a_k + 8 * i]) = alr[i];
     }
     uint16_t* wd = &Ws[buf][w_row * LS + w_k];
     *reinterpret_cast<u32x4*>(wd) = wr[0];
@@ -117,10 +95,6 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (g.a_gain) {  // once per block, so that the stage loader reads no global memory outside its loads
-    for (int k = tid * 4; k < g.K; k += 256 * 4) *reinterpret_cast<f32x4*>(gs + k) = *reinterpret_cast<const f32x4*>(g.a_gain + k);
-    __syncthreads();
-  }
   load(0);
   stash(0, 0);
   __syncthreads();
@@ -160,7 +134,12 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
         const float v = acc[i][j][r];
         if constexpr (EPI == GEMM_SWIGLU) {
           const float up = __shfl_xor(v, 1, WAVE);  // columns 2i (gate) and 2i+1 (up) sit in adjacent lanes
-          if (m < g.M && (n & 1) == 0) g.c[(size_t)m * g.ldc + (n >> 1)] = v / (1.0f + expf(-v)) * up;
+          if (m < g.M && (n & 1) == 0) {
+            const float y = v / (1.0f + expf(-v)) * up;
+            const uint32_t h = bf16_bits(y);
+            g.c_hi[(size_t)m * g.ldc + (n >> 1)] = (uint16_t)h;
+            g.c_lo[(size_t)m * g.ldc + (n >> 1)] = (uint16_t)bf16_bits(y - __uint_as_float(h << 16));
+          }
         } else if (m < g.M) {
           if constexpr (EPI == GEMM_ADD) g.c[(size_t)m * g.ldc + n] += v;
           else g.c[(size_t)m * g.ldc + n] = v;
@@ -178,77 +157,57 @@ template <int BM, int BN, int NW, int WM, int EPI>
 __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   constexpr int NT = NW * 64, WN = NW / WM, BK = 64, LS = BK + 8;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  // coalesced stage loads: one A load instruction of a wavefront covers 4 rows x 64 fp32 (16 lanes
-  // per row, 16 bytes each), one W load instruction 8 rows x 64 bf16 (8 lanes per row)
-  constexpr int AI = BM / (4 * NW);                   // A load instructions per thread per stage
+  // coalesced stage loads: one load instruction of a wavefront covers 8 rows x 64 bf16 (8 lanes per
+  // row, 16 bytes each) of an activation plane or of the weights
+  constexpr int AI = BM / (8 * NW);                   // load instructions per thread per stage and A plane
   constexpr int WI = BN / (8 * NW);                   // W load instructions per thread per stage
   constexpr int STAGE = (2 * BM + BN) * LS;           // bf16 elements: A hi, A lo, W
   static_assert(AI >= 1 && WI >= 1, "tile too small for the loaders");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-  extern __shared__ __attribute__((aligned(16))) float gs[];  // the RMSNorm gain [K], when there is one
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / WN, wn = wv % WN;
-  // the gain goes to LDS once, so that the stage loader reads no global memory outside its loads
-  if (g.a_gain)
-    for (int k = tid * 4; k < g.K; k += NT * 4) *reinterpret_cast<f32x4*>(gs + k) = *reinterpret_cast<const f32x4*>(g.a_gain + k);
   const int mt = (g.M + BM - 1) / BM, ntiles = mt * (g.N / BN);
   const int xcd = blockIdx.x & 7, per = ntiles >> 3, rem = ntiles & 7;
   const int tile = xcd * per + min(xcd, rem) + (int)(blockIdx.x >> 3);
   const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
   const int nk = g.K / BK;
+  (void)NT;
 
-  // A rows of this thread: a_row0 + 4 i, columns 4 (lane % 16) .. + 3 of the stage
-  const int a_k = (lane & 15) * 4;
-  const int a_row0 = wv * (BM / NW) + (lane >> 4);
-  int a_off[AI];  // row offsets into A (rows past M repeat the last row)
-  float a_sc[AI];
+  // A rows of this thread: a_row0 + 8 i, columns 8 (lane % 8) .. + 7 of the stage, both planes
+  const int r_k = (lane & 7) * 8;
+  const int a_row0 = wv * (BM / NW) + (lane >> 3);
+  size_t a_off[AI];  // row offsets into A (rows past M repeat the last row)
 #pragma unroll
-  for (int i = 0; i < AI; ++i) {
-    const int m = min(m0 + a_row0 + 4 * i, g.M - 1);
-    a_off[i] = m * g.lda;
-    a_sc[i] = g.a_scale ? g.a_scale[m] : 1.0f;
-  }
-  const float* a_src = g.a + a_k;
-  // W rows: w_row0 + 8 i, columns 8 (lane % 8) .. + 7
-  const int w_k = (lane & 7) * 8;
+  for (int i = 0; i < AI; ++i) a_off[i] = (size_t)min(m0 + a_row0 + 8 * i, g.M - 1) * g.lda + r_k;
+  // W rows: w_row0 + 8 i
   const int w_row0 = wv * (BN / NW) + (lane >> 3);
-  const uint16_t* w_src = g.w + (size_t)(n0 + w_row0) * g.K + w_k;
+  const uint16_t* w_src = g.w + (size_t)(n0 + w_row0) * g.K + r_k;
 
-  f32x4 ar0[AI], ar1[AI];
+  u32x4 ah0[AI], al0[AI], ah1[AI], al1[AI];
   u32x4 wr0[WI], wr1[WI];
-  auto load = [&](int kt, f32x4 (&ar)[AI], u32x4 (&wr)[WI]) {
+  auto load = [&](int kt, u32x4 (&ah)[AI], u32x4 (&al)[AI], u32x4 (&wr)[WI]) {
     const int k = min(kt, nk - 1) * BK;  // past the end: reload the last stage (never computed)
 #pragma unroll
-    for (int i = 0; i < AI; ++i) ar[i] = *reinterpret_cast<const f32x4*>(a_src + (size_t)a_off[i] + k);
+    for (int i = 0; i < AI; ++i) {
+      ah[i] = *reinterpret_cast<const u32x4*>(g.a_hi + a_off[i] + k);
+      al[i] = *reinterpret_cast<const u32x4*>(g.a_lo + a_off[i] + k);
+    }
 #pragma unroll
     for (int i = 0; i < WI; ++i)
       wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + (size_t)8 * i * g.K + k));
   };
-  auto stash = [&](int kt, int st, const f32x4 (&ar)[AI], const u32x4 (&wr)[WI]) {
-    const int k = min(kt, nk - 1) * BK;
-    uint16_t* ah = lds + st * STAGE;
-    uint16_t* al = ah + BM * LS;
-    uint16_t* ws = al + BM * LS;
-    f32x4 gg = {1.f, 1.f, 1.f, 1.f};
-    if (g.a_gain) gg = *reinterpret_cast<const f32x4*>(gs + k + a_k);
+  auto stash = [&](int st, const u32x4 (&ah)[AI], const u32x4 (&al)[AI], const u32x4 (&wr)[WI]) {
+    uint16_t* sh = lds + st * STAGE;
+    uint16_t* sl = sh + BM * LS;
+    uint16_t* sw = sl + BM * LS;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      f32x4 v = ar[i];
-      if (g.a_gain) {
-        v.x *= a_sc[i] * gg.x;
-        v.y *= a_sc[i] * gg.y;
-        v.z *= a_sc[i] * gg.z;
-        v.w *= a_sc[i] * gg.w;
-      }
-      uint32_t p0, q0, p1, q1;
-      split_bf16x2(v.x, v.y, p0, q0);
-      split_bf16x2(v.z, v.w, p1, q1);
-      *reinterpret_cast<uint2*>(ah + (a_row0 + 4 * i) * LS + a_k) = uint2{p0, p1};
-      *reinterpret_cast<uint2*>(al + (a_row0 + 4 * i) * LS + a_k) = uint2{q0, q1};
+      *reinterpret_cast<u32x4*>(sh + (a_row0 + 8 * i) * LS + r_k) = ah[i];
+      *reinterpret_cast<u32x4*>(sl + (a_row0 + 8 * i) * LS + r_k) = al[i];
     }
 #pragma unroll
-    for (int i = 0; i < WI; ++i) *reinterpret_cast<u32x4*>(ws + (w_row0 + 8 * i) * LS + w_k) = wr[i];
+    for (int i = 0; i < WI; ++i) *reinterpret_cast<u32x4*>(sw + (w_row0 + 8 * i) * LS + r_k) = wr[i];
   };
 
   f32x4 acc[TM][TN];
@@ -281,21 +240,20 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
     }
   };
 
-  load(0, ar0, wr0);
-  load(1, ar1, wr1);
-  if (g.a_gain) __syncthreads();  // gain in LDS
-  stash(0, 0, ar0, wr0);
-  load(2, ar0, wr0);
+  load(0, ah0, al0, wr0);
+  load(1, ah1, al1, wr1);
+  stash(0, ah0, al0, wr0);
+  load(2, ah0, al0, wr0);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     compute(0);               // stage kt
-    stash(kt + 1, 1, ar1, wr1);
-    load(kt + 3, ar1, wr1);
+    stash(1, ah1, al1, wr1);  // stage kt + 1
+    load(kt + 3, ah1, al1, wr1);
     __syncthreads();
     if (kt + 1 >= nk) break;
     compute(1);               // stage kt + 1
-    stash(kt + 2, 0, ar0, wr0);
-    load(kt + 4, ar0, wr0);
+    stash(0, ah0, al0, wr0);  // stage kt + 2
+    load(kt + 4, ah0, al0, wr0);
     __syncthreads();
   }
 
@@ -311,7 +269,12 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
         const float v = acc[i][j][r];
         if constexpr (EPI == GEMM_SWIGLU) {
           const float up = __shfl_xor(v, 1, WAVE);  // columns 2i (gate) and 2i+1 (up) sit in adjacent lanes
-          if (m < g.M && (n & 1) == 0) g.c[(size_t)m * g.ldc + (n >> 1)] = v / (1.0f + expf(-v)) * up;
+          if (m < g.M && (n & 1) == 0) {
+            const float y = v / (1.0f + expf(-v)) * up;
+            const uint32_t h = bf16_bits(y);
+            g.c_hi[(size_t)m * g.ldc + (n >> 1)] = (uint16_t)h;
+            g.c_lo[(size_t)m * g.ldc + (n >> 1)] = (uint16_t)bf16_bits(y - __uint_as_float(h << 16));
+          }
         } else if (m < g.M) {
           if constexpr (EPI == GEMM_ADD) g.c[(size_t)m * g.ldc + n] += v;
           else g.c[(size_t)m * g.ldc + n] = v;
@@ -323,8 +286,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.N % 128 || g.K % 32 || g.M < 1) return hipErrorInvalidValue;
   // long prompts: the 8-wavefront kernel, with the largest tile that still fills the CUs
-  const size_t gain_lds = g.a_gain ? (size_t)g.K * 4 : 0;
-  if (g.K % 64 == 0 && g.M >= 256 && gain_lds <= 40 * 1024) {
+  if (g.epi == GEMM_SWIGLU ? (!g.c_hi || !g.c_lo) : !g.c) return hipErrorInvalidValue;
+  if (g.K % 64 == 0 && g.M >= 256) {
     const int cus = device_cus();
     // Measured at P = 1200 on the full shape: very wide N (gate/up + SwiGLU, 19456 rows) runs best
     // with 128 x 256 tiles on 4 wavefronts (64 x 128 each: fewest LDS reads per MFMA); the other shapes
@@ -346,14 +309,14 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
 #define S2_G2(BM_, BN_, NW_, WM_)                                                                  \
   if (cfgs[best].bm == BM_ && cfgs[best].bn == BN_ && cfgs[best].nw == NW_) {                     \
     if (g.epi == GEMM_STORE)                                                                      \
-      hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_STORE>), grid, dim3(NW_ * 64), gain_lds, s, g); \
+      hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_STORE>), grid, dim3(NW_ * 64), 0, s, g); \
     else if (g.epi == GEMM_ADD)                                                                   \
-      hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_ADD>), grid, dim3(NW_ * 64), gain_lds, s, g);   \
-    else hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_SWIGLU>), grid, dim3(NW_ * 64), gain_lds, s, g); \
+      hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_ADD>), grid, dim3(NW_ * 64), 0, s, g);   \
+    else hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_SWIGLU>), grid, dim3(NW_ * 64), 0, s, g); \
     return hipGetLastError();                                                                     \
   }
       if (best == 0) {  // SwiGLU only (the store and add epilogues do not fit the registers at this tile)
-        hipLaunchKernelGGL((k_gemm2<128, 256, 4, 2, GEMM_SWIGLU>), grid, dim3(256), gain_lds, s, g);
+        hipLaunchKernelGGL((k_gemm2<128, 256, 4, 2, GEMM_SWIGLU>), grid, dim3(256), 0, s, g);
         return hipGetLastError();
       }
       S2_G2(128, 128, 8, 2) S2_G2(64, 256, 8, 2) S2_G2(64, 128, 8, 2)
@@ -363,7 +326,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const bool small = (long)((g.M + 127) / 128) * (g.N / 128) < 2L * device_cus();
   const int BM = small ? 64 : 128;
   const dim3 grid(g.N / 128, (g.M + BM - 1) / BM);
-#define S2_GEMM(B, E) hipLaunchKernelGGL((k_gemm<B, E>), grid, dim3(256), gain_lds, s, g)
+#define S2_GEMM(B, E) hipLaunchKernelGGL((k_gemm<B, E>), grid, dim3(256), 0, s, g)
   if (small) {
     if (g.epi == GEMM_STORE) S2_GEMM(64, GEMM_STORE);
     else if (g.epi == GEMM_ADD) S2_GEMM(64, GEMM_ADD);
@@ -378,8 +341,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Per-row RMSNorm scale: scale[m] = 1 / sqrt(mean(x[m]^2) + eps).  One block per row.
-__global__ __launch_bounds__(256) void k_row_rms(const float* x, int ld, int H, float eps, float* scale) {
+// RMSNorm of a row and its bf16 split: hi = bf16(y), lo = bf16(y - hi) with y = x * (scale * gain),
+// scale = 1 / sqrt(mean(x^2) + eps).  One block per row; the GEMMs read the two planes.
+__global__ __launch_bounds__(256) void k_norm_split(const float* x, int ld, int H, float eps, const float* gain,
+                                                    uint16_t* hi, uint16_t* lo, int ldo) {
   __shared__ float red[4];
   const float* r = x + (size_t)blockIdx.x * ld;
   float ss = 0.f;
@@ -387,11 +352,20 @@ __global__ __launch_bounds__(256) void k_row_rms(const float* x, int ld, int H, 
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  if (threadIdx.x == 0) scale[blockIdx.x] = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  const float scale = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  uint16_t* oh = hi + (size_t)blockIdx.x * ldo;
+  uint16_t* ol = lo + (size_t)blockIdx.x * ldo;
+  for (int k = threadIdx.x; k < H; k += 256) {
+    const float y = r[k] * (scale * gain[k]);
+    const uint32_t h = bf16_bits(y);
+    oh[k] = (uint16_t)h;
+    ol[k] = (uint16_t)bf16_bits(y - __uint_as_float(h << 16));
+  }
 }
 
-hipError_t launch_row_rms(const float* x, int ld, int H, float eps, float* scale, int M, hipStream_t s) {
-  hipLaunchKernelGGL(k_row_rms, dim3(M), dim3(256), 0, s, x, ld, H, eps, scale);
+hipError_t launch_norm_split(const float* x, int ld, int H, float eps, const float* gain, uint16_t* hi, uint16_t* lo,
+                             int ldo, int M, hipStream_t s) {
+  hipLaunchKernelGGL(k_norm_split, dim3(M), dim3(256), 0, s, x, ld, H, eps, gain, hi, lo, ldo);
   return hipGetLastError();
 }
 
@@ -632,9 +606,15 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
   for (int r = 0; r < 4; ++r) {
     const int row = row0 + 4 * c + r;
     if (row - row0 < nrows) {
-      float* out = a.out + (size_t)row * a.ld_out + h * D + i;
+      uint16_t* oh = a.out_hi + (size_t)row * a.ld_out + h * D + i;
+      uint16_t* ol = a.out_lo + (size_t)row * a.ld_out + h * D + i;
 #pragma unroll
-      for (int t = 0; t < NDG; ++t) out[16 * t] = o[t][r] * inv[r];
+      for (int t = 0; t < NDG; ++t) {
+        const float y = o[t][r] * inv[r];
+        const uint32_t hb = bf16_bits(y);
+        oh[16 * t] = (uint16_t)hb;
+        ol[16 * t] = (uint16_t)bf16_bits(y - __uint_as_float(hb << 16));
+      }
     }
   }
 }
