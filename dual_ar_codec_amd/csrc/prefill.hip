@@ -288,40 +288,26 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // long prompts: the 8-wavefront kernel, with the largest tile that still fills the CUs
   if (g.epi == GEMM_SWIGLU ? (!g.c_hi || !g.c_lo) : !g.c) return hipErrorInvalidValue;
   if (g.K % 64 == 0 && g.M >= 256) {
-    const int cus = device_cus();
-    // Measured at P = 1200 on the full shape: very wide N (gate/up + SwiGLU, 19456 rows) runs best
-    // with 128 x 256 tiles on 4 wavefronts (64 x 128 each: fewest LDS reads per MFMA); the other shapes
-    // with 8 wavefronts of 64 x 32 on 128 x 128 tiles (more wavefronts hide load latency).
-    struct Cfg { int bm, bn, nw; };
-    const Cfg cfgs[4] = {{128, 256, 4}, {128, 128, 8}, {64, 256, 8}, {64, 128, 8}};
-    int best = -1;
-    double best_eff = 0.0;
-    for (int c = 0; c < 4; ++c) {
-      if (g.N % cfgs[c].bn || (c == 0 && (g.N < 16384 || g.epi != GEMM_SWIGLU))) continue;
-      const long t = (long)((g.M + cfgs[c].bm - 1) / cfgs[c].bm) * (g.N / cfgs[c].bn);
-      const double eff = (double)t / (double)(((t + cus - 1) / cus) * cus);
-      if (eff >= 0.75) { best = c; break; }  // largest tile first
-      if (eff > best_eff) { best_eff = eff; best = c; }
+    // Measured at P = 1200 on the full shape (copy-only stage loaders): the wide gate/up + SwiGLU
+    // product runs best on 128 x 256 tiles (64 x 128 per wavefront; its store and add forms would
+    // spill), the other shapes on 64 x 256 tiles, both with 8 wavefronts.
+    const int mt128 = (g.M + 127) / 128, mt64 = (g.M + 63) / 64;
+    if (g.epi == GEMM_SWIGLU && g.N % 256 == 0 && g.N >= 16384) {
+      hipLaunchKernelGGL((k_gemm2<128, 256, 8, 2, GEMM_SWIGLU>), dim3(mt128 * (g.N / 256)), dim3(512), 0, s, g);
+      return hipGetLastError();
     }
-    if (best >= 0) {
-      const long t = (long)((g.M + cfgs[best].bm - 1) / cfgs[best].bm) * (g.N / cfgs[best].bn);
-      const dim3 grid((unsigned)t);
-#define S2_G2(BM_, BN_, NW_, WM_)                                                                  \
-  if (cfgs[best].bm == BM_ && cfgs[best].bn == BN_ && cfgs[best].nw == NW_) {                     \
-    if (g.epi == GEMM_STORE)                                                                      \
-      hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_STORE>), grid, dim3(NW_ * 64), 0, s, g); \
-    else if (g.epi == GEMM_ADD)                                                                   \
-      hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_ADD>), grid, dim3(NW_ * 64), 0, s, g);   \
-    else hipLaunchKernelGGL((k_gemm2<BM_, BN_, NW_, WM_, GEMM_SWIGLU>), grid, dim3(NW_ * 64), 0, s, g); \
-    return hipGetLastError();                                                                     \
-  }
-      if (best == 0) {  // SwiGLU only (the store and add epilogues do not fit the registers at this tile)
-        hipLaunchKernelGGL((k_gemm2<128, 256, 4, 2, GEMM_SWIGLU>), grid, dim3(256), 0, s, g);
-        return hipGetLastError();
-      }
-      S2_G2(128, 128, 8, 2) S2_G2(64, 256, 8, 2) S2_G2(64, 128, 8, 2)
-#undef S2_G2
+    if (g.N % 256 == 0) {
+      const dim3 grid(mt64 * (g.N / 256));
+      if (g.epi == GEMM_STORE) hipLaunchKernelGGL((k_gemm2<64, 256, 8, 2, GEMM_STORE>), grid, dim3(512), 0, s, g);
+      else if (g.epi == GEMM_ADD) hipLaunchKernelGGL((k_gemm2<64, 256, 8, 2, GEMM_ADD>), grid, dim3(512), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm2<64, 256, 8, 2, GEMM_SWIGLU>), grid, dim3(512), 0, s, g);
+      return hipGetLastError();
     }
+    const dim3 grid(mt128 * (g.N / 128));
+    if (g.epi == GEMM_STORE) hipLaunchKernelGGL((k_gemm2<128, 128, 8, 2, GEMM_STORE>), grid, dim3(512), 0, s, g);
+    else if (g.epi == GEMM_ADD) hipLaunchKernelGGL((k_gemm2<128, 128, 8, 2, GEMM_ADD>), grid, dim3(512), 0, s, g);
+    else hipLaunchKernelGGL((k_gemm2<128, 128, 8, 2, GEMM_SWIGLU>), grid, dim3(512), 0, s, g);
+    return hipGetLastError();
   }
   const bool small = (long)((g.M + 127) / 128) * (g.N / 128) < 2L * device_cus();
   const int BM = small ? 64 : 128;
