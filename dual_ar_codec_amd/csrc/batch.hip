@@ -12,6 +12,8 @@
 // in a fixed split order (bitwise reproducible).
 #include "kernels.h"
 
+#include <type_traits>
+
 #include <limits.h>
 #include <math.h>
 
@@ -31,6 +33,10 @@ constexpr int KS = 128;  // K per slice (4 MFMA steps)
 constexpr int KC = 512;               // K of one activation chunk task
 constexpr int CS = KC / KS;           // slices per task (= weight slices in flight per lane)
 constexpr int XROW = KC + 8;          // LDS row stride in bf16 (padded against bank conflicts)
+// buffer resources: the fourth descriptor word of a raw (untyped) gfx9 buffer, and the nontemporal
+// cache-policy bit of a buffer load
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   uint32_t a = __float_as_uint(f);
@@ -105,8 +111,15 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
     return split * kspan + ch * KC;
   };
   const int ksl = a.K / KS;
-  auto wtile = [&](int tile, int k) {  // lane's first 16 B of slice k / 128 of its 16-row tile
-    return a.w + ((size_t)(tile * 4 + w) * ksl + k / KS) * (4 * 512) + lane * 8;
+  // weights through a buffer resource (wave-uniform byte offset of slice k / 128 of the
+  // wavefront's 16-row tile, constant lane offset), as in k_mgemv_s below
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int lane_off = lane * 16;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w), (short)0, (int)((size_t)ntiles * 64 * a.K * 2), kBufferWord3);
+  auto wtile = [&](int tile, int k) { return ((tile * 4 + wu) * ksl + k / KS) * 4096; };
+  auto wld = [&](int base, int piece) {
+    return __builtin_amdgcn_raw_buffer_load_b128(wrs, lane_off, base + piece * 1024, kNonTemporal);
   };
 
   f32x4 xr[8];
@@ -117,16 +130,19 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
     const f32x4* q = reinterpret_cast<const f32x4*>(xrow + k);
 #pragma unroll
     for (int u = 0; u < 8; ++u) xr[u] = q[u];
-    const uint16_t* wr = wtile(tile, k);
+    const int wr = wtile(tile, k);
 #pragma unroll
     for (int sl = 0; sl < CS; ++sl)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        wb[sl][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (sl * 4 + t) * 512));
+      for (int t = 0; t < 4; ++t) wb[sl][t] = wld(wr, sl * 4 + t);
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int t = t0; t < t1; ++t) {
+  // one task; with LOAD the next task's activations, then its weights slice by slice, are loaded
+  // behind the MFMAs (the block's last task, run after the loop, loads nothing, so no weight is
+  // read twice and the loop has no branch between the two forms)
+  auto step = [&](int t, auto load_next) {
+    constexpr bool LOAD = decltype(load_next)::value;
     // activations of task t -> LDS (hi, lo)
     lds_barrier();
 #pragma unroll
@@ -142,32 +158,35 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
       *reinterpret_cast<bf16x8*>(&xs[1][xr_row * XROW + xr_col + 8 * u]) = lo;
     }
     lds_barrier();
-    // next task (the last one repeats itself): activations first, then weights slice by slice
-    int ntile;
-    const int nk = task_k(min(t + 1, t1 - 1), ntile);
     {
-      const f32x4* q = reinterpret_cast<const f32x4*>(xrow + nk);
+      int ntile;
+      const int nk = task_k(LOAD ? t + 1 : t, ntile);
+      if constexpr (LOAD) {
+        const f32x4* q = reinterpret_cast<const f32x4*>(xrow + nk);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) xr[u] = q[u];
-    }
-    const uint16_t* nwr = wtile(ntile, nk);
-#pragma unroll
-    for (int sl = 0; sl < CS; ++sl) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        // MFMA slot group g of step st holds k = 32 g + 8 st .. + 8 of the slice (same map for A and B)
-        const int kl = sl * KS + 32 * g + 8 * st;
-        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&xs[0][i * XROW + kl]);
-        const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&xs[1][i * XROW + kl]);
-        const bf16x8 wf = __builtin_bit_cast(bf16x8, wb[sl][st]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xh, acc, 0, 0, 0);
+        for (int u = 0; u < 8; ++u) xr[u] = q[u];
       }
-      // keep the reload of wb[sl] after its last use, so it lands in the same registers
-      __builtin_amdgcn_sched_barrier(0);
+      const int nwr = wtile(ntile, nk);
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        wb[sl][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(nwr + (sl * 4 + st) * 512));
+      for (int sl = 0; sl < CS; ++sl) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          // MFMA slot group g of step st holds k = 32 g + 8 st .. + 8 of the slice (same map for A and B)
+          const int kl = sl * KS + 32 * g + 8 * st;
+          const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&xs[0][i * XROW + kl]);
+          const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&xs[1][i * XROW + kl]);
+          const bf16x8 wf = __builtin_bit_cast(bf16x8, wb[sl][st]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xh, acc, 0, 0, 0);
+        }
+        if constexpr (LOAD) {
+          // keep the reload of wb[sl] after its last use (see k_mgemv_s)
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("" : "+a"(acc)::"memory");
+#pragma unroll
+          for (int st = 0; st < 4; ++st) wb[sl][st] = wld(nwr, sl * 4 + st);
+        }
+      }
     }
     const int it = t / nch;
     if (t - it * nch == nch - 1) {
@@ -220,7 +239,9 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
       }
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  }
+  };
+  for (int t = t0; t < t1 - 1; ++t) step(t, std::true_type{});
+  step(t1 - 1, std::false_type{});
 }
 
 // Split-K form for every launch whose K splits into 512-wide ranges (S = K / 512): each item is one
@@ -239,18 +260,28 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
   if (it0 >= it1) return;
   const int ksl = a.K / KS;
   const size_t ldp = mgemv_ldp(a.N);
+  // Weights are read through a buffer resource: the item's byte offset is wave-uniform (a scalar
+  // register) and the lane's offset is constant, so the loop holds no 64-bit address arithmetic
+  // that could compete with the weight ring for registers (a copy of a ring register forces a wait
+  // for its load).  The resource's size bound covers the whole tiled matrix.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int lane_off = lane * 16;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w), (short)0, (int)((size_t)ntiles * 64 * a.K * 2), kBufferWord3);
   auto wtile = [&](int it) {
     const int split = it / ntiles, tile = it - split * ntiles;
-    return a.w + ((size_t)(tile * 4 + w) * ksl + split * CS) * (4 * 512) + lane * 8;
+    return ((tile * 4 + wu) * ksl + split * CS) * 4096;
+  };
+  auto wld = [&](int base, int piece) {
+    return __builtin_amdgcn_raw_buffer_load_b128(wrs, lane_off, base + piece * 1024, kNonTemporal);
   };
   u32x4 wb[CS][4];
   {
-    const uint16_t* wr = wtile(it0);
+    const int wr = wtile(it0);
 #pragma unroll
     for (int sl = 0; sl < CS; ++sl)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        wb[sl][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (sl * 4 + t) * 512));
+      for (int t = 0; t < 4; ++t) wb[sl][t] = wld(wr, sl * 4 + t);
   }
   const int xr_row = tid >> 4, xr_col = (tid & 15) * 32;
   const int xr_m = min(xr_row, a.M - 1);
@@ -263,7 +294,7 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
     xsc = rsqrtf(tot / (float)a.K + a.eps);
   }
   int it = it0;
-  while (it < it1) {
+  while (true) {
     const int split = it / ntiles;
     const int run_end = min(it1, (split + 1) * ntiles);  // items of this split
     if (it != it0) lds_barrier();
@@ -289,8 +320,11 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
       }
     }
     lds_barrier();
-    for (; it < run_end; ++it) {
-      const uint16_t* nwr = wtile(min(it + 1, it1 - 1));
+    // one item; with LOAD the next item's weights are loaded slice by slice behind the MFMAs (the
+    // block's last item loads nothing, so no weight is read twice)
+    auto item = [&](auto load_next) {
+      constexpr bool LOAD = decltype(load_next)::value;
+      const int nwr = wtile(LOAD ? it + 1 : it);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int sl = 0; sl < CS; ++sl) {
@@ -304,15 +338,28 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xh, acc, 0, 0, 0);
         }
-        // keep the reload of wb[sl] after its last use, so it lands in the same registers
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LOAD) {
+          // keep the reload of wb[sl] after its last use, so it lands in the same registers: the
+          // empty statement takes the accumulator (so the slice's MFMAs come first) and orders
+          // memory (so no reload moves above it)
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("" : "+a"(acc)::"memory");
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          wb[sl][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(nwr + (sl * 4 + st) * 512));
+          for (int st = 0; st < 4; ++st) wb[sl][st] = wld(nwr, sl * 4 + st);
+        }
       }
       // lane holds D[row 4 g + r][stream i] of the item's tile
       const int tile = it - split * ntiles;
       *reinterpret_cast<f32x4*>(a.part + ((size_t)split * MB + i) * ldp + tile * 64 + w * 16 + 4 * g) = acc;
+    };
+    // the loop itself has no branch (a branch between the two item forms inside it would make
+    // the compiler copy the weight ring at the join and wait for its loads); the block's last item
+    // runs after it, once its split's activations are staged
+    const int loop_end = min(run_end, it1 - 1);
+    for (; it < loop_end; ++it) item(std::true_type{});
+    if (it == it1 - 1 && it < run_end) {
+      item(std::false_type{});
+      break;
     }
   }
 }
@@ -470,6 +517,7 @@ hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s) {
   const dim3 grid((items + a.ipb - 1) / a.ipb);
   const bool split_form = a.S == a.K / KC;  // one 512-wide chunk per item: k_mgemv_s
   if (a.ssq && !split_form) return hipErrorInvalidValue;  // the input norm lives in k_mgemv_s only
+  if (tiled_weight_elems(a.N, a.K) * 2 > (size_t)INT_MAX) return hipErrorInvalidValue;  // buffer-resource range
 #define S2_MG(E)                                                                                      \
   case E:                                                                                             \
     if (split_form) hipLaunchKernelGGL(k_mgemv_s, grid, dim3(256), 0, s, a);                           \
