@@ -530,7 +530,9 @@ static int g_cus = 256;
 void set_device_cus(int n) { g_cus = n > 0 ? n : 256; }
 int device_cus() { return g_cus; }
 
-// Launch shapes of the grid-stride kernel, picked per matrix shape by a sweep on MI355X.
+// Launch shapes of the grid-stride kernel, picked per matrix shape on MI355X: it is used where it
+// beat the one-shot kernel inside a whole frame (QKV and gate/up); the residual GEMVs (O, down) take
+// the one-shot kernel, whose every wavefront issues all the loads of its row at once.
 template <int NCH, int KIND, int R, int WPB>
 static hipError_t gemv2_launch(const GemvArgs& a, int blocks_per_cu, hipStream_t s) {
   const int tiles = (a.N + R * WPB - 1) / (R * WPB);
@@ -543,9 +545,7 @@ hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s) {
   if (bf16 && a.K % (WAVE * 8) == 0) {
     const int nch = a.K / (WAVE * 8);
     if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch<5, GEMV_NORM_STORE, 1, 4>(a, 2, s);
-    if (kind == GEMV_RESID && nch == 8) return gemv2_launch<8, GEMV_RESID, 1, 2>(a, 4, s);
     if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch<5, GEMV_NORM_SWIGLU, 2, 4>(a, 2, s);
-    if (kind == GEMV_RESID && nch == 19) return gemv2_launch<19, GEMV_RESID, 1, 2>(a, 2, s);
   }
   switch (kind) {
     case GEMV_NORM_STORE: return bf16 ? gemv_dispatch<true, GEMV_NORM_STORE>(a, s) : gemv_dispatch<false, GEMV_NORM_STORE>(a, s);
