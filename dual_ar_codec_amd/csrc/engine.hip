@@ -27,6 +27,8 @@ thread_local std::string g_create_error;
 constexpr int kPageSize = 16;
 constexpr int kMaxStreams = 256;
 constexpr int kAttnSplit = 256;  // context positions per attention workgroup
+// prefill attention: at most this many 64-key tiles per workgroup (longer causal ranges are split)
+constexpr int kPrefillAttnTiles = 8;
 
 struct LayerW {
   void* wqkv = nullptr;   // [(Hq + 2 Hkv) D][H]: wq rows, then wk rows, then wv rows
@@ -106,6 +108,8 @@ struct s2ar_ctx {
   int pch = 0;
   bool mfma_prefill = false;
   float *px = nullptr, *pqkv = nullptr;
+  // prefill attention key splits: unnormalised outputs and row states of the splits
+  float *patt_o = nullptr, *patt_ml = nullptr;
   // bf16 hi / lo planes of the GEMM inputs: normalised residual, attention output, SwiGLU output
   uint16_t *pxh = nullptr, *pxl = nullptr, *patth = nullptr, *pattl = nullptr, *pacth = nullptr, *pactl = nullptr;
   int* d_iota = nullptr;  // [max_context] = 0, 1, 2, ...
@@ -511,6 +515,11 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     if (c->mfma_prefill) {
       c->pch = std::min(g.max_context, 2048);
       C_TRY(dev_alloc(c, &c->px, sizeof(float) * (size_t)c->pch * H));
+      {
+        const int nsp = s2k::prefill_attn_splits(c->pch, g.max_context - c->pch, kPrefillAttnTiles);
+        C_TRY(dev_alloc(c, &c->patt_o, sizeof(float) * (size_t)nsp * c->pch * qd_s));
+        C_TRY(dev_alloc(c, &c->patt_ml, sizeof(float) * 2 * (size_t)nsp * c->pch * st.n_q_heads));
+      }
       C_TRY(dev_alloc(c, &c->pqkv, sizeof(float) * (size_t)c->pch * qkvd_s));
       C_TRY(dev_alloc(c, &c->pxh, sizeof(uint16_t) * (size_t)c->pch * H));
       C_TRY(dev_alloc(c, &c->pxl, sizeof(uint16_t) * (size_t)c->pch * H));
@@ -847,6 +856,9 @@ struct Enq {
       pa.D = D;
       pa.eps = eps;
       pa.scale = (float)(1.0 / std::sqrt((double)D));
+      pa.tps = kPrefillAttnTiles;
+      pa.part_o = c->patt_o;
+      pa.part_ml = c->patt_ml;
       chk(s2k::launch_prefill_attn(pa, s));
       gemm(c->patth, c->pattl, qd, L.wo, c->px, nullptr, nullptr, H, H, qd, s2k::GEMM_ADD);
       chk(s2k::launch_norm_split(c->px, H, H, eps, L.mlp_norm, c->pxh, c->pxl, H, rows, s));

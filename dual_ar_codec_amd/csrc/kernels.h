@@ -152,8 +152,17 @@ struct PrefillAttnArgs {
   int ld_out;
   int rows, pos0, Hq, Hkv, D;
   float eps, scale;
+  // Key splits: a row block whose causal key range spans more than tps tiles of 64 keys is served
+  // by ceil(tiles / tps) workgroups (the heaviest row blocks first).  Each writes its unnormalised
+  // output and its per-row (max, sum) to part_o [split][rows][Hq][D] and part_ml [split][rows][Hq][2];
+  // a second kernel merges them in split order into the planes.  1 <= tps <= 8.
+  int tps;
+  float* part_o;
+  float* part_ml;
 };
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);
+// Key splits the largest row block of a prefill of `rows` rows at positions pos0.. takes.
+int prefill_attn_splits(int rows, int pos0, int tps);
 hipError_t launch_embed_rows(bool bf16, const void* emb, const void* cb, int K, int H, int NC, const int* tokens,
                              const uint8_t* mask, const int* codes, int p0, int rows, float* x, int ldx,
                              hipStream_t s);

@@ -431,18 +431,48 @@ hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s
 // (max, sum) is per query row; the output tile of 16 rows x 16 dimensions per MFMA is rescaled with
 // the row factors fetched from the lanes that own those rows.  Keys and values of the rows must
 // already be in the cache.
+constexpr int PA_QR = 16, PA_KT = 64;  // query rows per row block, keys per tile
+constexpr int PA_MAXT = 8;              // most tiles per workgroup (longer key ranges are split)
+
+// key splits of row block rb (tiles of its causal key range over tps, at least 1)
+__host__ __device__ inline int pa_splits(int rb, int rows, int pos0, int tps) {
+  const int tiles = (pos0 + min(rb * PA_QR + PA_QR, rows) + PA_KT - 1) / PA_KT;
+  return tps > 0 ? (tiles + tps - 1) / tps : 1;
+}
+
+int prefill_attn_splits(int rows, int pos0, int tps) { return pa_splits((rows + PA_QR - 1) / PA_QR - 1, rows, pos0, tps); }
+
 template <int D, int G, bool KVB>
 __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a) {
-  constexpr int QR = 16, KT = 64, KSTR = D + 4, NT = 64 * G, NDG = D / 16;
+  constexpr int QR = PA_QR, KT = PA_KT, KSTR = D + 4, NT = 64 * G, NDG = D / 16;
   __shared__ __attribute__((aligned(16))) float ks[KT * KSTR];
   __shared__ __attribute__((aligned(16))) float vs[KT * KSTR];
-  __shared__ int rowoff[KT];
+  __shared__ int rowoff[PA_MAXT * KT];
   const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int i = lane & 15, c = lane >> 4;
   const int h = g * G + w;
-  const int row0 = blockIdx.x * QR;
+  // workgroup -> (row block, key split): the workgroups walk the row blocks from the last (the most
+  // keys) down, each row block taking its splits of at most tps tiles in order
+  int rb = (a.rows + QR - 1) / QR - 1, sp = blockIdx.x, nsp;
+  while (true) {
+    nsp = pa_splits(rb, a.rows, a.pos0, a.tps);
+    if (sp < nsp || rb == 0) break;
+    sp -= nsp;
+    --rb;
+  }
+  if (sp >= nsp) return;  // (a grid larger than the split count)
+  const int row0 = rb * QR;
   const int nrows = min(QR, a.rows - row0);
   const int last_pos = a.pos0 + row0 + nrows - 1;  // largest position of the block
+  // keys [j_begin, j_end) of this split, at most PA_MAXT tiles
+  const int j_begin = sp * a.tps * KT;
+  const int j_end = min((sp + 1) * a.tps * KT, last_pos + 1);
+  // cache offsets of every key of the split: one page-table round trip
+  for (int t = tid; t < j_end - j_begin; t += NT) {
+    const int jj = j_begin + t;
+    const int page = a.block_table[jj / a.page_size];
+    rowoff[t] = (int)((((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
+  }
 
   // q of row i (lanes (i, 0..3) share it): per-head RMSNorm, RoPE, scale; lane (i, c) keeps
   // dimensions 16 t + 4 c + e as q[4 t + e]
@@ -491,33 +521,39 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
   const float* vc = static_cast<const float*>(a.v_cache);
   const uint16_t* kb = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vb = static_cast<const uint16_t*>(a.v_cache);
-  for (int j0 = 0; j0 <= last_pos; j0 += KT) {
-    const int nk = min(KT, last_pos + 1 - j0);
-    __syncthreads();  // the previous tile is no longer read
-    if (tid < KT) {
-      const int jj = min(j0 + tid, last_pos);
-      const int page = a.block_table[jj / a.page_size];
-      rowoff[tid] = (int)((((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
-    }
-    __syncthreads();
-    for (int e = tid * 4; e < KT * D; e += NT * 4) {
-      const int j = e / D, d = e % D;
-      f32x4 kv4 = {0.f, 0.f, 0.f, 0.f}, vv4 = {0.f, 0.f, 0.f, 0.f};  // keys past the block stay finite
-      if (j < nk) {
-        const size_t off = (size_t)rowoff[j] + d;
+  // a thread's 16-byte K and V pieces of a tile, loaded in batches of PB with every load of a batch
+  // issued before the first is used: keys past the tile's end read the last key (in bounds) and are
+  // zeroed after the loads, so no load sits behind a branch
+  constexpr int PT = KT * D / 4 / NT, PB = PT < 8 ? PT : 8;
+  static_assert(PT * NT * 4 == KT * D && PT % PB == 0, "tile pieces must divide evenly");
+  for (int j0 = j_begin; j0 < j_end; j0 += KT) {
+    const int nk = min(KT, j_end - j0);
+    __syncthreads();  // the previous tile is no longer read (and, first, the offsets are in LDS)
+#pragma unroll
+    for (int u0 = 0; u0 < PT; u0 += PB) {
+      f32x4 kr[PB], vr[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int e = (tid + (u0 + u) * NT) * 4, j = e / D, d = e % D;
+        const size_t off = (size_t)rowoff[j0 - j_begin + min(j, nk - 1)] + d;
         if constexpr (KVB) {
           const uint2 k2 = *reinterpret_cast<const uint2*>(kb + off), v2 = *reinterpret_cast<const uint2*>(vb + off);
-          kv4 = f32x4{__uint_as_float(k2.x << 16), __uint_as_float(k2.x & 0xffff0000u), __uint_as_float(k2.y << 16),
-                      __uint_as_float(k2.y & 0xffff0000u)};
-          vv4 = f32x4{__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u), __uint_as_float(v2.y << 16),
-                      __uint_as_float(v2.y & 0xffff0000u)};
+          kr[u] = f32x4{__uint_as_float(k2.x << 16), __uint_as_float(k2.x & 0xffff0000u), __uint_as_float(k2.y << 16),
+                        __uint_as_float(k2.y & 0xffff0000u)};
+          vr[u] = f32x4{__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u), __uint_as_float(v2.y << 16),
+                        __uint_as_float(v2.y & 0xffff0000u)};
         } else {
-          kv4 = *reinterpret_cast<const f32x4*>(kc + off);
-          vv4 = *reinterpret_cast<const f32x4*>(vc + off);
+          kr[u] = *reinterpret_cast<const f32x4*>(kc + off);
+          vr[u] = *reinterpret_cast<const f32x4*>(vc + off);
         }
       }
-      *reinterpret_cast<f32x4*>(&ks[j * KSTR + d]) = kv4;
-      *reinterpret_cast<f32x4*>(&vs[j * KSTR + d]) = vv4;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int e = (tid + (u0 + u) * NT) * 4, j = e / D, d = e % D;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};  // keys past the tile stay finite (and carry no weight)
+        *reinterpret_cast<f32x4*>(&ks[j * KSTR + d]) = j < nk ? kr[u] : z;
+        *reinterpret_cast<f32x4*>(&vs[j * KSTR + d]) = j < nk ? vr[u] : z;
+      }
     }
     __syncthreads();
 
@@ -550,14 +586,17 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    const float m_new = fmaxf(m_i, mx);  // key j0 <= rpos always, so finite from the first tile on
-    const float corr = expf(m_i - m_new);
+    // A row's first key split always holds key 0 <= rpos, so m is finite from its first tile on; in
+    // a later split a row may have no key yet (m still -inf), and then every weight is 0
+    const float m_new = fmaxf(m_i, mx);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float corr = expf(m_i - m_ref);
     float ps = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT / 16; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = expf(st[kt][r] - m_new);
+        const float p = expf(st[kt][r] - m_ref);
         st[kt][r] = p;
         ps += p;
       }
@@ -585,6 +624,23 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
       }
     }
   }
+  if (nsp > 1) {  // a split's unnormalised output and row state, merged by k_prefill_attn_combine
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 4 * c + r;
+      if (row - row0 < nrows) {
+        float* po = a.part_o + (((size_t)sp * a.rows + row) * a.Hq + h) * D + i;
+#pragma unroll
+        for (int t = 0; t < NDG; ++t) po[16 * t] = o[t][r];
+      }
+    }
+    if (c == 0 && i < nrows) {
+      float* pml = a.part_ml + (((size_t)sp * a.rows + row0 + i) * a.Hq + h) * 2;
+      pml[0] = m_i;
+      pml[1] = l_i;
+    }
+    return;
+  }
   float inv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) inv[r] = 1.0f / __shfl(l_i, 4 * c + r, WAVE);
@@ -605,9 +661,82 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
   }
 }
 
+// Merge the key splits of the row blocks that have several, in split order: per row and q head,
+// M = max m_s, L = sum e^(m_s - M) l_s, y = sum e^(m_s - M) o_s / L, written as the bf16 planes.
+// grid = (row blocks, Hq), 4 wavefronts of 4 rows each; lane holds dimensions lane + 64 u.  A row's
+// loads for up to 8 splits are all issued before the first is used (longer ranges loop).
+template <int D>
+__global__ __launch_bounds__(256) void k_prefill_attn_combine(const PrefillAttnArgs a) {
+  constexpr int PER = D / 64, SB = 8;
+  const int rb = blockIdx.x, h = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nsp = pa_splits(rb, a.rows, a.pos0, a.tps);
+  if (nsp == 1) return;  // written by the attention kernel
+  const int row0 = rb * PA_QR, nrows = min(PA_QR, a.rows - row0);
+  for (int ri = wv; ri < nrows; ri += 4) {
+    const int row = row0 + ri;
+    float M = -INFINITY, L = 0.f, acc[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) acc[u] = 0.f;
+    for (int s0 = 0; s0 < nsp; s0 += SB) {
+      float m[SB], l[SB], o[SB][PER];
+#pragma unroll
+      for (int q = 0; q < SB; ++q) {
+        const size_t base = ((size_t)min(s0 + q, nsp - 1) * a.rows + row) * a.Hq + h;  // in bounds
+        m[q] = a.part_ml[base * 2];
+        l[q] = a.part_ml[base * 2 + 1];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) o[q][u] = a.part_o[base * D + lane + 64 * u];
+      }
+      // running merge in split order (a split with no key of this row: m = -inf, weight 0)
+#pragma unroll
+      for (int q = 0; q < SB; ++q) {
+        if (s0 + q >= nsp) break;
+        const float Mn = fmaxf(M, m[q]);
+        const float ca = expf(M - Mn), cb = expf(m[q] - Mn);  // M = -inf only before the first split
+        L = L * ca + l[q] * cb;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc[u] = acc[u] * ca + o[q][u] * cb;
+        M = Mn;
+      }
+    }
+    const float inv = 1.0f / L;
+    uint16_t* oh = a.out_hi + (size_t)row * a.ld_out + h * D;
+    uint16_t* ol = a.out_lo + (size_t)row * a.ld_out + h * D;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const float y = acc[u] * inv;
+      const uint32_t hb = bf16_bits(y);
+      oh[lane + 64 * u] = (uint16_t)hb;
+      ol[lane + 64 * u] = (uint16_t)bf16_bits(y - __uint_as_float(hb << 16));
+    }
+  }
+}
+
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const dim3 grid((a.rows + 15) / 16, a.Hkv);
+  const int nb = (a.rows + PA_QR - 1) / PA_QR;
+  if (a.tps < 1 || a.tps > PA_MAXT || a.rows < 1) return hipErrorInvalidValue;
+  int blocks = 0;
+  for (int rb = 0; rb < nb; ++rb) blocks += pa_splits(rb, a.rows, a.pos0, a.tps);
+  if (blocks > nb && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;
+  const dim3 grid(blocks, a.Hkv);
+  if (blocks > nb) {  // some row block has several splits: attention, then the merge
+    hipError_t e = hipSuccess;
+#define S2_PA(DD, GG)                                                                                 \
+    if (a.D == DD && G == GG) {                                                                       \
+      if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_attn<DD, GG, true>), grid, dim3(64 * GG), 0, s, a); \
+      else hipLaunchKernelGGL((k_prefill_attn<DD, GG, false>), grid, dim3(64 * GG), 0, s, a);          \
+      e = hipGetLastError();                                                                          \
+      if (e != hipSuccess) return e;                                                                  \
+      hipLaunchKernelGGL(k_prefill_attn_combine<DD>, dim3(nb, a.Hq), dim3(256), 0, s, a);             \
+      return hipGetLastError();                                                                       \
+    }
+    S2_PA(64, 1) S2_PA(64, 2) S2_PA(64, 4) S2_PA(64, 8)
+    S2_PA(128, 1) S2_PA(128, 2) S2_PA(128, 4) S2_PA(128, 8)
+#undef S2_PA
+    (void)e;
+    return hipErrorInvalidValue;
+  }
 #define S2_PA(DD, GG)                                                                                 \
   if (a.D == DD && G == GG) {                                                                         \
     if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_attn<DD, GG, true>), grid, dim3(64 * GG), 0, s, a);   \

@@ -93,6 +93,24 @@ def test_prefill_longer_than_one_row_block():
     assert rep["tokens_checked"] > 5
 
 
+def test_prefill_key_splits_unaligned_second_call():
+    """A 23-token prefill, then 1180 more positions in a second call at the mid shape.  The second
+    call's causal key ranges reach 1203 keys, so its row blocks are served by up to three key-split
+    workgroups, and because the rows start at position 23 the 512-key split boundaries fall inside
+    row blocks: some rows have no key in a split and must contribute nothing to it."""
+    cfg = synth.config("mid", max_context=1280)
+    w = synth.make_weights(cfg)
+    toks = synth.uniform_ints(78, 0, 1203, 0, cfg["vocab_text"])
+    frames = oracle_run(cfg, w, toks, None, None, 2)
+    ctx = _ctx(cfg, w)
+    ctx.prefill(0, toks[:23])
+    ctx.prefill(0, toks[23:])
+    assert ctx.position(0) == len(toks)
+    rep = compare_frames(ctx, 0, frames, cfg).finish()
+    _say(f"[parity] mid, 23 + 1180 prompt: {rep}")
+    ctx.close()
+
+
 def test_prefill_in_two_calls_matches_one_prefill():
     cfg = synth.config("mid")
     w = synth.make_weights(cfg)
