@@ -420,17 +420,19 @@ hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------------------------
-// Causal attention of a block of prompt rows on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, so
-// scores and weighted sums keep full fp32 inputs).  grid = (ceil(rows / 16), Hkv); block = G
-// wavefronts, wavefront w = q head g G + w over 16 query rows.  Per tile of 64 cached keys (staged
-// in LDS, shared by the G heads) a wavefront forms S^T = K Q^T: lane (i, c) (i = lane % 16,
-// c = lane / 16) then holds the scores of query row i against keys 4 c + r of each 16-key group,
-// which is exactly the A operand of the P V product when that group's four MFMA steps take the keys
-// 4 c + r (r = step).  The QK steps walk the head dimension in groups of 16 where lane (i, c) owns
-// dimensions 16 t + 4 c .. + 3, so K is read from LDS 16 bytes at a time.  The running softmax
-// (max, sum) is per query row; the output tile of 16 rows x 16 dimensions per MFMA is rescaled with
-// the row factors fetched from the lanes that own those rows.  Keys and values of the rows must
-// already be in the cache.
+// Causal attention of a block of prompt rows on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16)
+// with every fp32 operand split as x = hi + lo (two bf16): each product takes hi*hi + hi*lo +
+// lo*hi, so scores and weighted sums keep about 16 bits of every input (the lo*lo term and the
+// split's own rounding are below 2^-15 of the product).  A workgroup of G wavefronts serves one
+// (16-row block, KV group, key split); wavefront w is q head g G + w.  Per tile of 64 cached keys,
+// staged in LDS as bf16 hi / lo planes (K as [key][dim], V transposed to [dim][key]) and shared
+// by the G heads, a wavefront forms S^T = K Q^T: lane (i, c) (i = lane % 16, c = lane / 16) holds
+// A = K[key][8 dims], B = Q[row i][the same 8 dims], and the result puts the scores of row i
+// against keys 16 kt + 4 c + r in st[kt][r].  For P V the contraction over 32 keys takes, in lane
+// (i, c), the keys 32 m + 4 c + r and 32 m + 16 + 4 c + r (r < 4): exactly the scores that lane
+// already holds, with V read from the transposed planes 8 bytes at a time.  The running softmax
+// (max, sum) is per query row; the 16-row x 16-dimension output tiles are rescaled with the row
+// factors fetched from the lanes that own those rows.  Keys and values must already be cached.
 constexpr int PA_QR = 16, PA_KT = 64;  // query rows per row block, keys per tile
 constexpr int PA_MAXT = 8;              // most tiles per workgroup (longer key ranges are split)
 
@@ -442,11 +444,31 @@ __host__ __device__ inline int pa_splits(int rb, int rows, int pos0, int tps) {
 
 int prefill_attn_splits(int rows, int pos0, int tps) { return pa_splits((rows + PA_QR - 1) / PA_QR - 1, rows, pos0, tps); }
 
+// two bf16 halves (element 0 low) of hi and lo of four fp32 values
+__device__ __forceinline__ void split4(const float (&x)[4], uint2& hi, uint2& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = bf16_bits(x[e]);
+    l[e] = bf16_bits(x[e] - __uint_as_float(h[e] << 16));
+  }
+  hi = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  lo = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint2 a, uint2 b) {
+  return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
 template <int D, int G, bool KVB>
 __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a) {
-  constexpr int QR = PA_QR, KT = PA_KT, KSTR = D + 4, NT = 64 * G, NDG = D / 16;
-  __shared__ __attribute__((aligned(16))) float ks[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) float vs[KT * KSTR];
+  constexpr int QR = PA_QR, KT = PA_KT, NT = 64 * G, NDS = D / 32, NDT = D / 16;
+  constexpr int KS = D + 8;    // bf16 row stride of the K planes [key][dim]
+  constexpr int VS = KT + 12;  // bf16 row stride of the transposed V planes [dim][key]
+  __shared__ __attribute__((aligned(16))) uint16_t kh[KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t kl[KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t vh[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[D * VS];
   __shared__ int rowoff[PA_MAXT * KT];
   const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int i = lane & 15, c = lane >> 4;
@@ -474,105 +496,146 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
     rowoff[t] = (int)((((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
   }
 
-  // q of row i (lanes (i, 0..3) share it): per-head RMSNorm, RoPE, scale; lane (i, c) keeps
-  // dimensions 16 t + 4 c + e as q[4 t + e]
+  // q of row i (lanes (i, 0..3) share it): per-head RMSNorm, RoPE, scale; lane (i, c) keeps the
+  // dimensions 32 ds + 8 c + r as the bf16 hi / lo operands qh[ds], ql[ds]
   const int qrow = row0 + min(i, nrows - 1);
   const int rpos = a.pos0 + qrow;
-  float q[D / 4];
+  bf16x8 qh[NDS], ql[NDS];
   {
-    const float* qp = a.qkv + (size_t)qrow * a.ld + h * D + 4 * c;
+    float q[NDS][8];
+    const float* qp = a.qkv + (size_t)qrow * a.ld + h * D + 8 * c;
     float ss = 0.f;
 #pragma unroll
-    for (int t = 0; t < NDG; ++t) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(qp + 16 * t);
-      q[4 * t] = v.x;
-      q[4 * t + 1] = v.y;
-      q[4 * t + 2] = v.z;
-      q[4 * t + 3] = v.w;
-      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    for (int ds = 0; ds < NDS; ++ds) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(qp + 32 * ds);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(qp + 32 * ds + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        q[ds][r] = v[r];
+        ss = fmaf(v[r], v[r], ss);
+      }
     }
     ss += __shfl_xor(ss, 16, WAVE);
     ss += __shfl_xor(ss, 32, WAVE);
     const float rq = rsqrtf(ss / (float)D + a.eps);
 #pragma unroll
-    for (int t = 0; t < NDG; ++t)
+    for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q[4 * t + e] = q[4 * t + e] * rq * a.q_norm[16 * t + 4 * c + e];
-    // rotate-half pairs (d, d + D/2) sit in the same lane, groups t and t + D/32
+      for (int r = 0; r < 8; ++r) q[ds][r] = q[ds][r] * rq * a.q_norm[32 * ds + 8 * c + r];
+    // rotate-half pairs (d, d + D/2) sit in the same lane: chunks ds and ds + NDS/2
     const float* crow = a.rope_cos + (size_t)rpos * (D / 2);
     const float* srow = a.rope_sin + (size_t)rpos * (D / 2);
 #pragma unroll
-    for (int t = 0; t < NDG / 2; ++t)
+    for (int ds = 0; ds < NDS / 2; ++ds)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 16 * t + 4 * c + e;
+      for (int r = 0; r < 8; ++r) {
+        const int d = 32 * ds + 8 * c + r;
         const float cs = crow[d], sn = srow[d];
-        const float x0 = q[4 * t + e], x1 = q[4 * (t + NDG / 2) + e];
-        q[4 * t + e] = (x0 * cs - x1 * sn) * a.scale;
-        q[4 * (t + NDG / 2) + e] = (x1 * cs + x0 * sn) * a.scale;
+        const float x0 = q[ds][r], x1 = q[ds + NDS / 2][r];
+        q[ds][r] = (x0 * cs - x1 * sn) * a.scale;
+        q[ds + NDS / 2][r] = (x1 * cs + x0 * sn) * a.scale;
       }
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      uint2 h0, l0, h1, l1;
+      split4({q[ds][0], q[ds][1], q[ds][2], q[ds][3]}, h0, l0);
+      split4({q[ds][4], q[ds][5], q[ds][6], q[ds][7]}, h1, l1);
+      qh[ds] = as_bf16x8(h0, h1);
+      ql[ds] = as_bf16x8(l0, l1);
+    }
   }
 
   float m_i = -INFINITY, l_i = 0.f;  // softmax state of row i
-  f32x4 o[NDG];                       // o[t][r] = O[row 4 c + r][dim 16 t + i]
+  f32x4 o[NDT];                       // o[t][r] = O[row 4 c + r][dim 16 t + i]
 #pragma unroll
-  for (int t = 0; t < NDG; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float* kc = static_cast<const float*>(a.k_cache);
   const float* vc = static_cast<const float*>(a.v_cache);
   const uint16_t* kb = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vb = static_cast<const uint16_t*>(a.v_cache);
-  // a thread's 16-byte K and V pieces of a tile, loaded in batches of PB with every load of a batch
-  // issued before the first is used: keys past the tile's end read the last key (in bounds) and are
-  // zeroed after the loads, so no load sits behind a branch
-  constexpr int PT = KT * D / 4 / NT, PB = PT < 8 ? PT : 8;
-  static_assert(PT * NT * 4 == KT * D && PT % PB == 0, "tile pieces must divide evenly");
+  // A tile is staged as blocks of 4 keys x 4 dimensions: a thread loads its blocks' rows (every load
+  // of a batch issued before the first is used; keys past the tile's end read the last key, in
+  // bounds, and are zeroed after the loads), splits them, and writes K rows and transposed V rows
+  constexpr int NBLK = (KT / 4) * (D / 4);
+  constexpr int NB = (NBLK + NT - 1) / NT, NBB = NB < 2 ? NB : 2;
+  static_assert(NB % NBB == 0, "staging batches must divide evenly");
   for (int j0 = j_begin; j0 < j_end; j0 += KT) {
     const int nk = min(KT, j_end - j0);
     __syncthreads();  // the previous tile is no longer read (and, first, the offsets are in LDS)
 #pragma unroll
-    for (int u0 = 0; u0 < PT; u0 += PB) {
-      f32x4 kr[PB], vr[PB];
+    for (int u0 = 0; u0 < NB; u0 += NBB) {
+      f32x4 kr[NBB][4], vr[NBB][4];
 #pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        const int e = (tid + (u0 + u) * NT) * 4, j = e / D, d = e % D;
-        const size_t off = (size_t)rowoff[j0 - j_begin + min(j, nk - 1)] + d;
-        if constexpr (KVB) {
-          const uint2 k2 = *reinterpret_cast<const uint2*>(kb + off), v2 = *reinterpret_cast<const uint2*>(vb + off);
-          kr[u] = f32x4{__uint_as_float(k2.x << 16), __uint_as_float(k2.x & 0xffff0000u), __uint_as_float(k2.y << 16),
-                        __uint_as_float(k2.y & 0xffff0000u)};
-          vr[u] = f32x4{__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u), __uint_as_float(v2.y << 16),
-                        __uint_as_float(v2.y & 0xffff0000u)};
-        } else {
-          kr[u] = *reinterpret_cast<const f32x4*>(kc + off);
-          vr[u] = *reinterpret_cast<const f32x4*>(vc + off);
+      for (int u = 0; u < NBB; ++u) {
+        const int bb = tid + (u0 + u) * NT;
+        if (NBLK % NT == 0 || bb < NBLK) {
+          const int kg = bb / (D / 4), dg = bb % (D / 4);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const size_t off = (size_t)rowoff[j0 - j_begin + min(4 * kg + x, nk - 1)] + 4 * dg;
+            if constexpr (KVB) {
+              const uint2 k2 = *reinterpret_cast<const uint2*>(kb + off), v2 = *reinterpret_cast<const uint2*>(vb + off);
+              kr[u][x] = f32x4{__uint_as_float(k2.x << 16), __uint_as_float(k2.x & 0xffff0000u),
+                               __uint_as_float(k2.y << 16), __uint_as_float(k2.y & 0xffff0000u)};
+              vr[u][x] = f32x4{__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u),
+                               __uint_as_float(v2.y << 16), __uint_as_float(v2.y & 0xffff0000u)};
+            } else {
+              kr[u][x] = *reinterpret_cast<const f32x4*>(kc + off);
+              vr[u][x] = *reinterpret_cast<const f32x4*>(vc + off);
+            }
+          }
         }
       }
 #pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        const int e = (tid + (u0 + u) * NT) * 4, j = e / D, d = e % D;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};  // keys past the tile stay finite (and carry no weight)
-        *reinterpret_cast<f32x4*>(&ks[j * KSTR + d]) = j < nk ? kr[u] : z;
-        *reinterpret_cast<f32x4*>(&vs[j * KSTR + d]) = j < nk ? vr[u] : z;
+      for (int u = 0; u < NBB; ++u) {
+        const int bb = tid + (u0 + u) * NT;
+        if (NBLK % NT == 0 || bb < NBLK) {
+          const int kg = bb / (D / 4), dg = bb % (D / 4);
+          float kx[4][4], vx[4][4];  // [key x][dim y]; keys past the tile stay finite and weightless
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const bool live = 4 * kg + x < nk;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              kx[x][y] = live ? kr[u][x][y] : 0.f;
+              vx[x][y] = live ? vr[u][x][y] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            uint2 hh, ll;
+            split4(kx[x], hh, ll);
+            *reinterpret_cast<uint2*>(&kh[(4 * kg + x) * KS + 4 * dg]) = hh;
+            *reinterpret_cast<uint2*>(&kl[(4 * kg + x) * KS + 4 * dg]) = ll;
+          }
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            uint2 hh, ll;
+            split4({vx[0][y], vx[1][y], vx[2][y], vx[3][y]}, hh, ll);
+            *reinterpret_cast<uint2*>(&vh[(4 * dg + y) * VS + 4 * kg]) = hh;
+            *reinterpret_cast<uint2*>(&vl[(4 * dg + y) * VS + 4 * kg]) = ll;
+          }
+        }
       }
     }
     __syncthreads();
 
-    const int ngrp = min(KT / 16, (nk + 15) / 16);  // 16-key groups holding any key of the block
+    // S^T = K Q^T: st[kt][r] = score of row i against key 16 kt + 4 c + r
     f32x4 st[KT / 16];
 #pragma unroll
-    for (int kt = 0; kt < KT / 16; ++kt) {
-      st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (kt < ngrp) {
+    for (int kt = 0; kt < KT / 16; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < NDG; ++t) {
-          const f32x4 k4 = *reinterpret_cast<const f32x4*>(&ks[(kt * 16 + i) * KSTR + 16 * t + 4 * c]);
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.x, q[4 * t], st[kt], 0, 0, 0);
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.y, q[4 * t + 1], st[kt], 0, 0, 0);
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.z, q[4 * t + 2], st[kt], 0, 0, 0);
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.w, q[4 * t + 3], st[kt], 0, 0, 0);
-        }
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < KT / 16; ++kt) {
+        const int ko = (kt * 16 + i) * KS + 32 * ds + 8 * c;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kh[ko]);
+        const bf16x8 kb8 = *reinterpret_cast<const bf16x8*>(&kl[ko]);
+        st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[ds], st[kt], 0, 0, 0);
+        st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb8, qh[ds], st[kt], 0, 0, 0);
+        st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[ds], st[kt], 0, 0, 0);
       }
-    }
     // causal mask and online softmax of row i over this tile (lane (i, c) holds keys 16 kt + 4 c + r)
     float mx = -INFINITY;
 #pragma unroll
@@ -608,19 +671,24 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
 #pragma unroll
     for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * c + r, WAVE);
 #pragma unroll
-    for (int t = 0; t < NDG; ++t)
+    for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[t][r] *= cr[r];
-    // O += P V: step r of key group kt takes keys 16 kt + 4 c + r (A = st[kt][r] as held)
+    // O += P V over 32-key blocks m: lane (i, c) contracts keys 32 m + 4 c + r and 32 m + 16 + 4 c + r
 #pragma unroll
-    for (int kt = 0; kt < KT / 16; ++kt) {
-      if (kt < ngrp) {
+    for (int m = 0; m < KT / 32; ++m) {
+      uint2 p0h, p0l, p1h, p1l;
+      split4({st[2 * m][0], st[2 * m][1], st[2 * m][2], st[2 * m][3]}, p0h, p0l);
+      split4({st[2 * m + 1][0], st[2 * m + 1][1], st[2 * m + 1][2], st[2 * m + 1][3]}, p1h, p1l);
+      const bf16x8 pa = as_bf16x8(p0h, p1h), pb = as_bf16x8(p0l, p1l);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float* vrow = &vs[(kt * 16 + 4 * c + r) * KSTR + i];
-#pragma unroll
-          for (int t = 0; t < NDG; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(st[kt][r], vrow[16 * t], o[t], 0, 0, 0);
-        }
+      for (int t = 0; t < NDT; ++t) {
+        const int vo = (16 * t + i) * VS + 32 * m + 4 * c;
+        const bf16x8 va = as_bf16x8(*reinterpret_cast<const uint2*>(&vh[vo]), *reinterpret_cast<const uint2*>(&vh[vo + 16]));
+        const bf16x8 vb8 = as_bf16x8(*reinterpret_cast<const uint2*>(&vl[vo]), *reinterpret_cast<const uint2*>(&vl[vo + 16]));
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, va, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb8, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, va, o[t], 0, 0, 0);
       }
     }
   }
@@ -631,7 +699,7 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
       if (row - row0 < nrows) {
         float* po = a.part_o + (((size_t)sp * a.rows + row) * a.Hq + h) * D + i;
 #pragma unroll
-        for (int t = 0; t < NDG; ++t) po[16 * t] = o[t][r];
+        for (int t = 0; t < NDT; ++t) po[16 * t] = o[t][r];
       }
     }
     if (c == 0 && i < nrows) {
@@ -651,7 +719,7 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
       uint16_t* oh = a.out_hi + (size_t)row * a.ld_out + h * D + i;
       uint16_t* ol = a.out_lo + (size_t)row * a.ld_out + h * D + i;
 #pragma unroll
-      for (int t = 0; t < NDG; ++t) {
+      for (int t = 0; t < NDT; ++t) {
         const float y = o[t][r] * inv[r];
         const uint32_t hb = bf16_bits(y);
         oh[16 * t] = (uint16_t)hb;
