@@ -111,6 +111,54 @@ def multi_stream(args, w, log):
             "note": "same synthetic weights as the batch-1 line (shapes identical)"}
 
 
+def int8_weights(args, cfg, w, toks, forced, ref, log):
+    """Batch-1 frames/s with the layer matrices and heads as int8 plus per-row scales (the same
+    synthetic weights, quantised by the library at create), and the drift from bf16 on the same
+    teacher-forced frames (the GPU against itself: hidden cosine, logit error, agreeing picks)."""
+    import numpy as np
+    import torch
+
+    from dual_ar_codec_amd import metrics, s2ar
+
+    c8 = dict(cfg, weight_dtype="i8")
+    log("[bench] int8 weights: quantise + upload")
+    ctx = s2ar.Context(c8, w, max_streams=2)
+    ctx.prefill(0, toks)
+    ctx.decode_frames([0], 3)
+    ctx.release(0)
+    ctx.prefill(0, toks)
+    torch.cuda.synchronize()
+    steps = args.int8_steps
+    t0 = time.perf_counter()
+    ctx.decode_frames([0], steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    fps = steps / dt
+    ctx.prefill(1, toks)
+    got = [ctx.debug_frame(1, forced=f) for f in forced]
+    ctx.close()
+
+    def cos(a, b):
+        a, b = a.astype(np.float64).ravel(), b.astype(np.float64).ravel()
+        return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+    h_cos = min(cos(g["slow_h"], r["slow_h"]) for g, r in zip(got, ref))
+    fz_cos = min(cos(g["fast_z"], r["fast_z"]) for g, r in zip(got, ref))
+    lrel = max(float(np.max(np.abs(g["slow_logits"] - r["slow_logits"])) / np.max(np.abs(r["slow_logits"])))
+               for g, r in zip(got, ref))
+    agree = float(np.mean([np.mean(g["own_codes"] == r["own_codes"]) for g, r in zip(got, ref)]))
+    fb = metrics.int8_frame_bytes(c8, len(toks) + steps // 2)
+    gbps = fb["total"] * fps / 1e9
+    return {"workload": f"{cfg['name']}: {len(toks)}-token prompt, {steps} greedy frames, 1 stream",
+            "frames_per_s": round(fps, 2), "ms_per_frame": round(dt / steps * 1e3, 4),
+            "frame_bytes": fb["total"], "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "drift_vs_bf16": {"frames": len(forced), "min_cos_slow_h": round(h_cos, 6),
+                              "min_cos_fast_z": round(fz_cos, 6), "max_slow_logit_rel": round(lrel, 5),
+                              "own_pick_agreement": round(agree, 4)},
+            "note": "int8 layer matrices and heads, one fp32 scale per row; parity is checked against the "
+                    "oracle fed the same quantisation, drift against the bf16 context on the same forced codes"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +170,7 @@ def main():
     ap.add_argument("--prefill", type=int, default=1, help="also time a 1200-position voice-clone prefill")
     ap.add_argument("--multi-steps", type=int, default=20, help="batched 16-stream decode steps (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a 256 MiB copy (counter calibration)")
+    ap.add_argument("--int8-steps", type=int, default=40, help="batch-1 frames with int8 weights (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py drives one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
@@ -200,7 +249,15 @@ def main():
     roofline["stream_read_context"] = {"gbps": round(s_gbps, 1), "frac_of_peak": round(s_gbps / HBM_PEAK_GBPS, 4),
                                        "avg_launch_us": round(sms * 1e3, 2),
                                        "gemv_over_stream": round(k_gbps / s_gbps, 4)}
+    forced, ref = [], []
+    if args.int8_steps > 0:  # bf16 reference taps for the int8 drift: frames forced to this run's codes
+        forced = [np.ascontiguousarray(out[t, 0]) for t in range(3)]
+        ctx.prefill(1, toks)
+        ref = [ctx.debug_frame(1, forced=f) for f in forced]
+        ctx.release(1)
     ctx.close()
+
+    int8 = int8_weights(args, cfg, w, toks, forced, ref, log) if args.int8_steps > 0 else None
 
     multi = None
     if args.multi_steps > 0:
@@ -239,6 +296,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "multi_stream": multi,
+        "int8": int8,
     }
     print(json.dumps(line), flush=True)
 

@@ -41,6 +41,8 @@ struct LayerW {
   float* k_norm = nullptr;
   // tiled copies of the four matrices for the batched multi-stream GEMVs (k_mgemv layout)
   uint16_t *tqkv = nullptr, *to = nullptr, *tgu = nullptr, *tdown = nullptr;
+  // int8 weights: fp32 scale of every row of the four matrices (same row order)
+  float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sdown = nullptr;
 };
 
 struct Graph {
@@ -52,7 +54,8 @@ struct Graph {
 
 struct s2ar_ctx {
   s2ar_config cfg{};
-  bool bf16 = true;
+  bool bf16 = true;  // tables (embeddings, codebooks, gains) arrive as bf16
+  bool i8 = false;   // layer matrices and heads are stored as int8 with per-row scales
   int esz = 2;
   hipStream_t user_stream = nullptr;
   hipStream_t stream = nullptr;
@@ -66,6 +69,7 @@ struct s2ar_ctx {
   void* codebook = nullptr;
   void* fast_head = nullptr;
   uint16_t *slow_head_t = nullptr, *fast_head_t = nullptr;  // tiled copies (batched decode)
+  float *slow_head_s = nullptr, *fast_head_s = nullptr;      // int8 weights: row scales
   float* slow_final = nullptr;
   float* fast_final = nullptr;
   std::vector<LayerW> slow, fast;
@@ -190,11 +194,11 @@ int check_stack(const s2ar_stack& s, const char* name, int epc, std::string& why
 }
 
 int validate_config(const s2ar_config* c, std::string& why) {
-  if (c->weight_dtype != 0 && c->weight_dtype != 1) {
-    why = "weight_dtype must be 0 (fp32) or 1 (bf16)";
+  if (c->weight_dtype < 0 || c->weight_dtype > 2) {
+    why = "weight_dtype must be 0 (fp32), 1 (bf16) or 2 (bf16 tensors, int8 matrices)";
     return -1;
   }
-  const int epc = c->weight_dtype == 1 ? 8 : 4;
+  const int epc = c->weight_dtype == 0 ? 4 : 8;
   if (check_stack(c->slow, "slow", epc, why) || check_stack(c->fast, "fast", epc, why)) return -1;
   if (c->slow.hidden != c->fast.hidden) {
     why = "fast.hidden must equal slow.hidden (the Slow hidden feeds the Fast AR)";
@@ -310,7 +314,69 @@ int upload_gain(s2ar_ctx* c, const s2ar_tensor& t, int n, float** out) {
   return 0;
 }
 
+// Symmetric int8 per output row: s = max|w| / 127 and q = rint(w / s), both in fp32 on the host
+// (a row of zeros has s = 0 and q = 0); w is used as q * s.  Eight-bit weights halve the bytes a
+// batch-1 frame streams ("s2pro-native", Where it stands), with one scale per output channel
+// ("s2pro-native", The gate that says no).
+void quantize_rows_i8(const uint16_t* w, size_t rows, size_t cols, int8_t* q, float* s) {
+  for (size_t r = 0; r < rows; ++r) {
+    const uint16_t* row = w + r * cols;
+    float m = 0.f;
+    for (size_t k = 0; k < cols; ++k) m = std::fmax(m, std::fabs(bf16_bits_to_float(row[k])));
+    const float sc = m / 127.0f;
+    s[r] = sc;
+    for (size_t k = 0; k < cols; ++k) {
+      const float v = sc > 0.f ? std::rint(bf16_bits_to_float(row[k]) / sc) : 0.f;
+      q[r * cols + k] = (int8_t)std::fmin(127.f, std::fmax(-127.f, v));
+    }
+  }
+}
+
+// Upload row blocks of bf16 host matrices as one int8 matrix plus its row scales; block b's rows
+// land at rows first[b] + stride * i (stride 2 interleaves the gate and up rows).
+struct QBlock {
+  const void* src;
+  size_t rows, first, stride;
+};
+int upload_i8(s2ar_ctx* c, const std::vector<QBlock>& blocks, size_t total_rows, size_t cols, void** w, float** sc) {
+  std::vector<int8_t> q(total_rows * cols);
+  std::vector<float> s(total_rows);
+  std::vector<int8_t> qb;
+  std::vector<float> sb;
+  for (const QBlock& b : blocks) {
+    qb.resize(b.rows * cols);
+    sb.resize(b.rows);
+    quantize_rows_i8(static_cast<const uint16_t*>(b.src), b.rows, cols, qb.data(), sb.data());
+    for (size_t i = 0; i < b.rows; ++i) {
+      const size_t r = b.first + b.stride * i;
+      std::memcpy(q.data() + r * cols, qb.data() + i * cols, cols);
+      s[r] = sb[i];
+    }
+  }
+  if (int rc = dev_alloc(c, w, total_rows * cols)) return rc;
+  if (int rc = dev_alloc(c, sc, sizeof(float) * total_rows)) return rc;
+  HIP_TRY(c, hipMemcpy(*w, q.data(), total_rows * cols, hipMemcpyHostToDevice));
+  HIP_TRY(c, hipMemcpy(*sc, s.data(), sizeof(float) * total_rows, hipMemcpyHostToDevice));
+  return 0;
+}
+
+int upload_layer_i8(s2ar_ctx* c, const s2ar_stack& s, const s2ar_tensor* t, LayerW* L) {
+  const size_t H = s.hidden, qd = (size_t)s.n_q_heads * s.head_dim, kd = (size_t)s.n_kv_heads * s.head_dim,
+               F = s.ffn;
+  if (int rc = upload_gain(c, t[0], s.hidden, &L->attn_norm)) return rc;
+  if (int rc = upload_i8(c, {{t[1].host_ptr, qd, 0, 1}, {t[2].host_ptr, kd, qd, 1}, {t[3].host_ptr, kd, qd + kd, 1}},
+                         qd + 2 * kd, H, &L->wqkv, &L->sqkv))
+    return rc;
+  if (int rc = upload_gain(c, t[4], s.head_dim, &L->q_norm)) return rc;
+  if (int rc = upload_gain(c, t[5], s.head_dim, &L->k_norm)) return rc;
+  if (int rc = upload_i8(c, {{t[6].host_ptr, H, 0, 1}}, H, qd, &L->wo, &L->so)) return rc;
+  if (int rc = upload_gain(c, t[7], s.hidden, &L->mlp_norm)) return rc;
+  if (int rc = upload_i8(c, {{t[8].host_ptr, F, 0, 2}, {t[9].host_ptr, F, 1, 2}}, 2 * F, H, &L->wgu, &L->sgu)) return rc;
+  return upload_i8(c, {{t[10].host_ptr, H, 0, 1}}, H, F, &L->wdown, &L->sdown);
+}
+
 int upload_layer(s2ar_ctx* c, const s2ar_stack& s, const s2ar_tensor* t, LayerW* L) {
+  if (c->i8) return upload_layer_i8(c, s, t, L);
   const size_t e = c->esz;
   const size_t H = s.hidden, qd = (size_t)s.n_q_heads * s.head_dim, kd = (size_t)s.n_kv_heads * s.head_dim,
                F = s.ffn;
@@ -383,7 +449,8 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   s2ar_ctx* c = new (std::nothrow) s2ar_ctx();
   if (!c) return set_err(nullptr, S2AR_E_NOMEM, "out of host memory");
   c->cfg = *cfg;
-  c->bf16 = cfg->weight_dtype == 1;
+  c->bf16 = cfg->weight_dtype != 0;
+  c->i8 = cfg->weight_dtype == 2;
   c->esz = c->bf16 ? 2 : 4;
   c->user_stream = static_cast<hipStream_t>(hip_stream);
   auto fail = [&](int rc) {
@@ -421,15 +488,23 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   c->slow.resize(g.slow.n_layers);
   for (int l = 0; l < g.slow.n_layers; ++l, ti += 11) C_TRY(upload_layer(c, g.slow, t + ti, &c->slow[l]));
   C_TRY(upload_gain(c, t[ti++], H, &c->slow_final));
-  C_TRY(dev_alloc(c, &c->slow_head, (size_t)V * H * e));
-  C_HIP(hipMemcpy(c->slow_head, t[ti++].host_ptr, (size_t)V * H * e, hipMemcpyHostToDevice));
+  if (c->i8) {
+    C_TRY(upload_i8(c, {{t[ti++].host_ptr, (size_t)V, 0, 1}}, (size_t)V, H, &c->slow_head, &c->slow_head_s));
+  } else {
+    C_TRY(dev_alloc(c, &c->slow_head, (size_t)V * H * e));
+    C_HIP(hipMemcpy(c->slow_head, t[ti++].host_ptr, (size_t)V * H * e, hipMemcpyHostToDevice));
+  }
   C_TRY(dev_alloc(c, &c->codebook, (size_t)NC * K * H * e));
   C_HIP(hipMemcpy(c->codebook, t[ti++].host_ptr, (size_t)NC * K * H * e, hipMemcpyHostToDevice));
   c->fast.resize(g.fast.n_layers);
   for (int l = 0; l < g.fast.n_layers; ++l, ti += 11) C_TRY(upload_layer(c, g.fast, t + ti, &c->fast[l]));
   C_TRY(upload_gain(c, t[ti++], H, &c->fast_final));
-  C_TRY(dev_alloc(c, &c->fast_head, (size_t)K * H * e));
-  C_HIP(hipMemcpy(c->fast_head, t[ti++].host_ptr, (size_t)K * H * e, hipMemcpyHostToDevice));
+  if (c->i8) {
+    C_TRY(upload_i8(c, {{t[ti++].host_ptr, (size_t)K, 0, 1}}, (size_t)K, H, &c->fast_head, &c->fast_head_s));
+  } else {
+    C_TRY(dev_alloc(c, &c->fast_head, (size_t)K * H * e));
+    C_HIP(hipMemcpy(c->fast_head, t[ti++].host_ptr, (size_t)K * H * e, hipMemcpyHostToDevice));
+  }
   C_TRY(upload_rope(c, g.slow.head_dim, g.max_context, &c->rope_cos_s, &c->rope_sin_s));
   C_TRY(upload_rope(c, g.fast.head_dim, NC - 1, &c->rope_cos_f, &c->rope_sin_f));
 
@@ -510,7 +585,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   {
     const s2ar_stack& st = g.slow;
     const int qkvd_s = (st.n_q_heads + 2 * st.n_kv_heads) * st.head_dim, qd_s = st.n_q_heads * st.head_dim;
-    c->mfma_prefill = c->bf16 && qkvd_s % 128 == 0 && H % 128 == 0 && (2 * st.ffn) % 128 == 0 && H % 32 == 0 &&
+    c->mfma_prefill = c->bf16 && !c->i8 && qkvd_s % 128 == 0 && H % 128 == 0 && (2 * st.ffn) % 128 == 0 && H % 32 == 0 &&
                       qd_s % 32 == 0 && st.ffn % 32 == 0;
     if (c->mfma_prefill) {
       c->pch = std::min(g.max_context, 2048);
@@ -540,7 +615,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     auto k_ok = [](const s2ar_stack& st) {
       return st.hidden % 512 == 0 && (st.n_q_heads * st.head_dim) % 512 == 0 && st.ffn % 512 == 0;
     };
-    c->batched_ok = c->bf16 && g.max_streams > 1 && k_ok(g.slow) && k_ok(g.fast);
+    c->batched_ok = c->bf16 && !c->i8 && g.max_streams > 1 && k_ok(g.slow) && k_ok(g.fast);
     if (c->batched_ok) {
       const int MBt = 16;
       const int qkvd_max = std::max((g.slow.n_q_heads + 2 * g.slow.n_kv_heads) * g.slow.head_dim,
@@ -632,10 +707,11 @@ struct Enq {
     chk(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s));
   }
 
-  void gemv(int kind, const void* w, const float* x, const float* gain, float* y, int N, int K,
+  void gemv(int kind, const void* w, const float* wscale, const float* x, const float* gain, float* y, int N, int K,
             float* xnorm_out = nullptr, int lo = 0, int hi = 0, int* code_out = nullptr) {
     s2k::GemvArgs a{};
     a.w = w;
+    a.wscale = wscale;
     a.x = x;
     a.gain = gain;
     a.eps = (float)c->cfg.rms_eps;
@@ -684,7 +760,7 @@ struct Enq {
     const int qkvd = (st.n_q_heads + 2 * st.n_kv_heads) * D;
     for (int l = 0; l < st.n_layers; ++l) {
       const LayerW& L = W[l];
-      gemv(s2k::GEMV_NORM_STORE, L.wqkv, x, L.attn_norm, c->qkv, qkvd, H);
+      gemv(s2k::GEMV_NORM_STORE, L.wqkv, L.sqkv, x, L.attn_norm, c->qkv, qkvd, H);
       s2k::AttnArgs a{};
       a.qkv = c->qkv;
       a.q_norm = L.q_norm;
@@ -726,9 +802,9 @@ struct Enq {
       }
       chk(s2k::launch_attention(a, s));
       if (a.max_splits > 1) chk(s2k::launch_attention_combine(a, s));
-      gemv(s2k::GEMV_RESID, L.wo, c->att, nullptr, x, H, qd);
-      gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, x, L.mlp_norm, c->act, 2 * st.ffn, H);
-      gemv(s2k::GEMV_RESID, L.wdown, c->act, nullptr, x, H, st.ffn);
+      gemv(s2k::GEMV_RESID, L.wo, L.so, c->att, nullptr, x, H, qd);
+      gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, L.sgu, x, L.mlp_norm, c->act, 2 * st.ffn, H);
+      gemv(s2k::GEMV_RESID, L.wdown, L.sdown, c->act, nullptr, x, H, st.ffn);
       if (resid_tap) d2h(resid_tap + (size_t)l * H, x, sizeof(float) * H);
     }
   }
@@ -739,7 +815,7 @@ struct Enq {
   void slow_head(int slot, const TapPlan* tp) {
     const s2ar_config& g = c->cfg;
     const int H = g.slow.hidden, V = g.vocab_text + g.codebook_size;
-    gemv(s2k::GEMV_NORM_ARGMAX, c->slow_head, c->x, c->slow_final, c->slow_logits, V, H, c->d_h + (size_t)slot * H,
+    gemv(s2k::GEMV_NORM_ARGMAX, c->slow_head, c->slow_head_s, c->x, c->slow_final, c->slow_logits, V, H, c->d_h + (size_t)slot * H,
          g.vocab_text, V);
     finish(s2k::FIN_SLOW, 0, slot, g.vocab_text, V, xf_of(slot));
     if (tp && tp->slow_h) d2h(tp->slow_h, c->d_h + (size_t)slot * H, sizeof(float) * H);
@@ -762,7 +838,7 @@ struct Enq {
                                    H, 1, s));
       fast_pos_ptr = c->d_fast_pos + (size_t)(j - 1) * g.max_streams;
       layers(false, slot, xf, tp && tp->fast_resid ? tp->fast_resid + (size_t)(j - 1) * Lf * H : nullptr);
-      gemv(s2k::GEMV_NORM_ARGMAX, c->fast_head, xf, c->fast_final, c->fast_logits, K, H,
+      gemv(s2k::GEMV_NORM_ARGMAX, c->fast_head, c->fast_head_s, xf, c->fast_final, c->fast_logits, K, H,
            tp && tp->fast_z ? c->z : nullptr, 0, K);
       const int mode = tp ? s2k::FIN_CODE : (j < NC - 1 ? s2k::FIN_FAST_NEXT : s2k::FIN_FAST_LAST);
       finish(mode, j, slot, 0, K, j < NC - 1 ? xf : c->x);
@@ -1240,7 +1316,7 @@ int s2ar_create(const s2ar_config* cfg, const s2ar_tensor* tensors, int32_t n_te
   if (validate_config(cfg, why)) return set_err(nullptr, S2AR_E_ARG, why);
   if (n_tensors != n_tensors_for(cfg)) return set_err(nullptr, S2AR_E_ARG, "n_tensors does not match the config");
   const std::vector<int64_t> sizes = tensor_sizes(cfg);
-  const int64_t esz = cfg->weight_dtype == 1 ? 2 : 4;
+  const int64_t esz = cfg->weight_dtype == 0 ? 4 : 2;  // bf16 tensors for weight_dtype 1 and 2
   for (int i = 0; i < n_tensors; ++i) {
     if (!tensors[i].host_ptr) return set_err(nullptr, S2AR_E_ARG, "tensor " + std::to_string(i) + " is null");
     if (tensors[i].nbytes != sizes[i] * esz)
@@ -1537,12 +1613,12 @@ int s2ar_time_kernel(s2ar_ctx* c, int32_t which, int32_t iters, float* avg_ms, i
   if (which < 0 || which > 1 || iters < 1 || !avg_ms)
     return set_err(c, S2AR_E_ARG, "which must be 0 or 1, iters >= 1, avg_ms non-null");
   const s2ar_stack& st = c->cfg.slow;
-  const size_t wbytes = (size_t)2 * st.ffn * st.hidden * c->esz;
+  const size_t wbytes = (size_t)2 * st.ffn * st.hidden * (c->i8 ? 1 : c->esz);
   Enq q{c, c->stream};
   HIP_TRY(c, hipEventRecord(c->ev_t0, c->stream));
   for (int i = 0; i < iters; ++i) {
     const LayerW& L = c->slow[i % st.n_layers];
-    if (which == 0) q.gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, c->x, L.mlp_norm, c->act, 2 * st.ffn, st.hidden);
+    if (which == 0) q.gemv(s2k::GEMV_NORM_SWIGLU, L.wgu, L.sgu, c->x, L.mlp_norm, c->act, 2 * st.ffn, st.hidden);
     else q.chk(s2k::launch_stream_read(L.wgu, wbytes, c->d_sink, c->stream));
   }
   HIP_TRY(c, hipEventRecord(c->ev_t1, c->stream));
@@ -1552,7 +1628,9 @@ int s2ar_time_kernel(s2ar_ctx* c, int32_t which, int32_t iters, float* avg_ms, i
   HIP_TRY(c, hipEventElapsedTime(&ms, c->ev_t0, c->ev_t1));
   *avg_ms = ms / (float)iters;
   if (bytes_out)
-    *bytes_out = which == 0 ? (int64_t)wbytes + (int64_t)st.hidden * 4 * 2 + (int64_t)st.ffn * 4 : (int64_t)wbytes;
+    *bytes_out = which == 0 ? (int64_t)wbytes + (int64_t)st.hidden * 4 * 2 + (int64_t)st.ffn * 4 +
+                                  (c->i8 ? (int64_t)2 * st.ffn * 4 : 0)
+                            : (int64_t)wbytes;
   return S2AR_OK;
 }
 

@@ -18,7 +18,8 @@ enum GemvKind : int {
 int pad_k(int K);
 
 struct GemvArgs {
-  const void* w;          // weights (bf16 bits or fp32), [N][K]
+  const void* w;          // weights (bf16 bits, fp32, or int8 when wscale is set), [N][K]
+  const float* wscale;    // int8 weights: fp32 scale of each row [N]; nullptr for bf16 / fp32
   const float* x;         // input vector [pad_k(K)] (fp32, zero past K)
   const float* gain;      // RMSNorm gain [pad_k(K)] (fp32, zero past K) for the NORM kinds
   float eps;

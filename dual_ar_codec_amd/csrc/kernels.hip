@@ -25,6 +25,7 @@
 namespace s2k {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
@@ -86,15 +87,52 @@ __device__ __forceinline__ float dot_chunk(const u32x4 w, const float* x, float 
 
 __host__ __device__ constexpr int rows_per_wave(int kind) { return kind == GEMV_RESID ? 1 : 2; }
 
+// Weight formats of the GEMVs: fp32, bf16, or int8 with an fp32 scale per output row (the row's
+// dot product is taken on the integers and scaled once).  A lane's chunk is 16 bytes (fp32, bf16)
+// or 8 bytes (int8), so every format has 8 (bf16, int8) or 4 (fp32) elements per chunk.
+constexpr int WF_F32 = 0, WF_BF16 = 1, WF_I8 = 2;
+template <int WF>
+struct WFmt {
+  using CT = u32x4;
+  static constexpr int EPC = WF == WF_F32 ? 4 : 8;
+  static constexpr int ESZ = WF == WF_F32 ? 4 : 2;
+  static __device__ __forceinline__ float dot(const CT w, const float* x, float acc) {
+    return dot_chunk<WF == WF_BF16>(w, x, acc);
+  }
+};
+template <>
+struct WFmt<WF_I8> {
+  using CT = u32x2;
+  static constexpr int EPC = 8;
+  static constexpr int ESZ = 1;
+  // acc += <8 int8 weights (byte k of the chunk is element k), 8 inputs from LDS>, in element order
+  static __device__ __forceinline__ float dot(const CT w, const float* x, float acc) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(x);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(x + 4);
+    acc = fmaf((float)(int8_t)(w.x & 0xffu), a.x, acc);
+    acc = fmaf((float)(int8_t)((w.x >> 8) & 0xffu), a.y, acc);
+    acc = fmaf((float)(int8_t)((w.x >> 16) & 0xffu), a.z, acc);
+    acc = fmaf((float)(int8_t)(w.x >> 24), a.w, acc);
+    acc = fmaf((float)(int8_t)(w.y & 0xffu), b.x, acc);
+    acc = fmaf((float)(int8_t)((w.y >> 8) & 0xffu), b.y, acc);
+    acc = fmaf((float)(int8_t)((w.y >> 16) & 0xffu), b.z, acc);
+    acc = fmaf((float)(int8_t)(w.y >> 24), b.w, acc);
+    return acc;
+  }
+};
+
 // ---------------------------------------------------------------------------------------------
 // Weight-streaming GEMV.  Workgroup = 4 wavefronts; wavefront w of block b owns rows
 // (4b + w) * R ... + R - 1.  NCH > 0: K == NCH * 64 * elements-per-chunk and all weight loads of
 // the wavefront are issued up front; NCH == 0: any K divisible by the chunk width / 8, looped.
-template <bool BF16, int NCH, int KIND>
-__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
+// Int8 weights: each row's sum is multiplied by the row's scale before the epilogue.
+template <int WF, int NCH, int KIND>
+__device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
   extern __shared__ float xs[];
+  using F = WFmt<WF>;
+  using CT = typename F::CT;
   constexpr int R = rows_per_wave(KIND);
-  constexpr int EPC = BF16 ? 8 : 4;
+  constexpr int EPC = F::EPC;
   constexpr bool NORM = KIND != GEMV_RESID;
   __shared__ float red[GEMV_WAVES];
   __shared__ int bidx[GEMV_WAVES];
@@ -103,13 +141,16 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
   const int wid = threadIdx.x / WAVE;
   const int K = a.K;
   const int row0 = (blockIdx.x * GEMV_WAVES + wid) * R;
-  const size_t row_bytes = (size_t)K * (BF16 ? 2 : 4);
+  const size_t row_bytes = (size_t)K * F::ESZ;
+  float sc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) sc[r] = WF == WF_I8 ? a.wscale[min(row0 + r, a.N - 1)] : 1.f;
 
   // 1. loads: the input vector (and gain) first, then every weight chunk of this wavefront's
   //    rows.  vmcnt retires in issue order, so staging the input only waits for the input.
   constexpr int XL = NCH > 0 ? (NCH * WAVE * EPC + GEMV_THREADS * 4 - 1) / (GEMV_THREADS * 4) : 1;
   f32x4 xv[XL], gv[XL];
-  u32x4 wv[R][NCH > 0 ? NCH : 1];
+  CT wv[R][NCH > 0 ? NCH : 1];
   if constexpr (NCH > 0) {
 #pragma unroll
     for (int t = 0; t < XL; ++t) {  // x and gain are zero-padded to a multiple of 1024 floats
@@ -120,7 +161,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = min(row0 + r, a.N - 1);
-      const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.w) + (size_t)row * row_bytes);
+      const CT* wp = reinterpret_cast<const CT*>(static_cast<const char*>(a.w) + (size_t)row * row_bytes);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) wv[r][c] = __builtin_nontemporal_load(wp + c * WAVE + lane);
     }
@@ -186,7 +227,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
     for (int c = 0; c < NCH; ++c) {
       const float* xp = xs + (c * WAVE + lane) * EPC;
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = dot_chunk<BF16>(wv[r][c], xp, acc[r]);
+      for (int r = 0; r < R; ++r) acc[r] = F::dot(wv[r][c], xp, acc[r]);
     }
   } else {
     const int nch = (K / EPC + WAVE - 1) / WAVE;
@@ -197,14 +238,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int row = min(row0 + r, a.N - 1);
-          const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.w) + (size_t)row * row_bytes);
-          acc[r] = dot_chunk<BF16>(__builtin_nontemporal_load(wp + c * WAVE + lane), xp, acc[r]);
+          const CT* wp = reinterpret_cast<const CT*>(static_cast<const char*>(a.w) + (size_t)row * row_bytes);
+          acc[r] = F::dot(__builtin_nontemporal_load(wp + c * WAVE + lane), xp, acc[r]);
         }
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]) * sc[r];
 
   // 4. epilogue
   if constexpr (KIND == GEMV_NORM_STORE) {
@@ -253,6 +294,16 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
       a.am_idx[blockIdx.x] = i;
     }
   }
+}
+
+template <bool BF16, int NCH, int KIND>
+__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
+  gemv_impl<BF16 ? WF_BF16 : WF_F32, NCH, KIND>(a);
+}
+
+template <int NCH, int KIND>
+__global__ __launch_bounds__(GEMV_THREADS) void k_gemv_i8(const GemvArgs a) {
+  gemv_impl<WF_I8, NCH, KIND>(a);
 }
 
 int argmax_block_rows() { return GEMV_WAVES * rows_per_wave(GEMV_NORM_ARGMAX); }
@@ -341,10 +392,12 @@ hipError_t launch_finish(bool bf16, const FinishArgs& f, hipStream_t s) {
 // b, b + grid, ...  The next tile's weights are issued before the current tile is reduced
 // (register double buffer), and the input is staged in LDS once per block.  The greedy-pick
 // kind leaves one (max, argmax) per block, over all the rows the block visited.
-template <bool BF16, int NCH, int KIND, int R, int WPB>
-__global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
+template <int WF, int NCH, int KIND, int R, int WPB>
+__device__ __forceinline__ void gemv2_impl(const GemvArgs& a) {
   extern __shared__ float xs[];
-  constexpr int EPC = BF16 ? 8 : 4;
+  using F = WFmt<WF>;
+  using CT = typename F::CT;
+  constexpr int EPC = F::EPC;
   constexpr int NT = WPB * WAVE;
   constexpr int K = NCH * WAVE * EPC;
   constexpr int XL = (K + NT * 4 - 1) / (NT * 4);
@@ -357,7 +410,7 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
   const int n_tiles = (a.N + RPT - 1) / RPT;
   int tile = blockIdx.x;
   if (tile >= n_tiles) return;
-  constexpr size_t row_bytes = (size_t)K * (BF16 ? 2 : 4);
+  constexpr size_t row_bytes = (size_t)K * F::ESZ;
 
   f32x4 xv[XL], gv[XL];
 #pragma unroll
@@ -368,17 +421,19 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
       if constexpr (NORM) gv[t] = *reinterpret_cast<const f32x4*>(a.gain + k);
     }
   }
-  u32x4 wa[R][NCH], wb[R][NCH];
-  auto issue = [&](u32x4 (&wv)[R][NCH], int tl) {
+  CT wa[R][NCH], wb[R][NCH];
+  float sa[R], sb[R];  // int8: the rows' scales, loaded with their weights
+  auto issue = [&](CT (&wv)[R][NCH], float (&sv)[R], int tl) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = min(tl * RPT + wid * R + r, a.N - 1);
-      const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.w) + (size_t)row * row_bytes);
+      const CT* wp = reinterpret_cast<const CT*>(static_cast<const char*>(a.w) + (size_t)row * row_bytes);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) wv[r][c] = __builtin_nontemporal_load(wp + c * WAVE + lane);
+      sv[r] = WF == WF_I8 ? a.wscale[row] : 1.f;
     }
   };
-  issue(wa, tile);
+  issue(wa, sa, tile);
   __builtin_amdgcn_sched_barrier(0);
 
   float ss = 0.f;
@@ -420,7 +475,7 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
 
   float bv = -INFINITY;
   int bi = INT_MAX;
-  auto process = [&](u32x4 (&wv)[R][NCH], int tl) {
+  auto process = [&](CT (&wv)[R][NCH], const float (&sv)[R], int tl) {
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -428,10 +483,10 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
     for (int c = 0; c < NCH; ++c) {
       const float* xp = xs + (c * WAVE + lane) * EPC;
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = dot_chunk<BF16>(wv[r][c], xp, acc[r]);
+      for (int r = 0; r < R; ++r) acc[r] = F::dot(wv[r][c], xp, acc[r]);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+    for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]) * sv[r];
     const int row0 = tl * RPT + wid * R;
     if constexpr (KIND == GEMV_NORM_STORE) {
 #pragma unroll
@@ -462,12 +517,12 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
   };
   while (true) {
     const int t1 = tile + gridDim.x;
-    if (t1 < n_tiles) issue(wb, t1);
-    process(wa, tile);
+    if (t1 < n_tiles) issue(wb, sb, t1);
+    process(wa, sa, tile);
     if (t1 >= n_tiles) break;
     const int t2 = t1 + gridDim.x;
-    if (t2 < n_tiles) issue(wa, t2);
-    process(wb, t1);
+    if (t2 < n_tiles) issue(wa, sa, t2);
+    process(wb, sb, t1);
     if (t2 >= n_tiles) break;
     tile = t2;
   }
@@ -489,6 +544,16 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
       a.am_idx[blockIdx.x] = i;
     }
   }
+}
+
+template <bool BF16, int NCH, int KIND, int R, int WPB>
+__global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
+  gemv2_impl<BF16 ? WF_BF16 : WF_F32, NCH, KIND, R, WPB>(a);
+}
+
+template <int NCH, int KIND, int R, int WPB>
+__global__ __launch_bounds__(WPB * WAVE) void k_gemv2_i8(const GemvArgs a) {
+  gemv2_impl<WF_I8, NCH, KIND, R, WPB>(a);
 }
 
 int pad_k(int K) { return (K + 1023) / 1024 * 1024; }
@@ -526,6 +591,33 @@ static hipError_t gemv_dispatch(const GemvArgs& a, hipStream_t s) {
 #undef S2_NCH
 }
 
+template <int KIND>
+static hipError_t gemv_dispatch_i8(const GemvArgs& a, hipStream_t s) {
+  const dim3 grid(gemv_blocks(KIND, a.N)), block(GEMV_THREADS);
+  const size_t lds = (size_t)pad_k(a.K) * sizeof(float);
+  const int nch = (a.K % (WAVE * 8) == 0) ? a.K / (WAVE * 8) : -1;
+#define S2_NCH(n) \
+  case n:         \
+    hipLaunchKernelGGL((k_gemv_i8<n, KIND>), grid, block, lds, s, a); \
+    return hipGetLastError();
+  switch (nch) {
+    S2_NCH(1)
+    S2_NCH(2)
+    S2_NCH(3)
+    S2_NCH(4)
+    S2_NCH(5)
+    S2_NCH(6)
+    S2_NCH(8)
+    S2_NCH(12)
+    S2_NCH(16)
+    S2_NCH(19)
+    default:
+      hipLaunchKernelGGL((k_gemv_i8<0, KIND>), grid, block, lds, s, a);
+      return hipGetLastError();
+  }
+#undef S2_NCH
+}
+
 static int g_cus = 256;
 void set_device_cus(int n) { g_cus = n > 0 ? n : 256; }
 int device_cus() { return g_cus; }
@@ -541,7 +633,28 @@ static hipError_t gemv2_launch(const GemvArgs& a, int blocks_per_cu, hipStream_t
   return hipGetLastError();
 }
 
+template <int NCH, int KIND, int R, int WPB>
+static hipError_t gemv2_launch_i8(const GemvArgs& a, int blocks_per_cu, hipStream_t s) {
+  const int tiles = (a.N + R * WPB - 1) / (R * WPB);
+  const int grid = std::min(tiles, g_cus * blocks_per_cu);
+  hipLaunchKernelGGL((k_gemv2_i8<NCH, KIND, R, WPB>), dim3(grid), dim3(WPB * WAVE), (size_t)pad_k(a.K) * 4, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s) {
+  if (a.wscale) {  // int8 weights with per-row scales, the launch shapes of the bf16 kernels
+    if (a.K % 8) return hipErrorInvalidValue;
+    const int nch = a.K % (WAVE * 8) == 0 ? a.K / (WAVE * 8) : -1;
+    if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch_i8<5, GEMV_NORM_STORE, 1, 4>(a, 2, s);
+    if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch_i8<5, GEMV_NORM_SWIGLU, 2, 4>(a, 2, s);
+    switch (kind) {
+      case GEMV_NORM_STORE: return gemv_dispatch_i8<GEMV_NORM_STORE>(a, s);
+      case GEMV_RESID: return gemv_dispatch_i8<GEMV_RESID>(a, s);
+      case GEMV_NORM_SWIGLU: return gemv_dispatch_i8<GEMV_NORM_SWIGLU>(a, s);
+      case GEMV_NORM_ARGMAX: return gemv_dispatch_i8<GEMV_NORM_ARGMAX>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (bf16 && a.K % (WAVE * 8) == 0) {
     const int nch = a.K / (WAVE * 8);
     if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch<5, GEMV_NORM_STORE, 1, 4>(a, 2, s);

@@ -78,6 +78,22 @@ def frame_bytes(cfg, context_len: int) -> dict:
     return dict(weights=w, kv=kv, embed=embed, total=w + kv + embed)
 
 
+def int8_frame_bytes(cfg, context_len: int) -> dict:
+    """frame_bytes with the layer matrices and both heads stored as int8 plus one fp32 scale per
+    row (embeddings, codebooks and gains as in frame_bytes)."""
+    fb = frame_bytes(cfg, context_len)
+    s, f = cfg["slow"], cfg["fast"]
+
+    def rows(st):
+        H, D = st["hidden"], st["head_dim"]
+        return (st["n_q_heads"] + 2 * st["n_kv_heads"]) * D + H + 2 * st["ffn"] + H
+
+    p = params_per_frame(cfg)
+    scale_rows = s["n_layers"] * rows(s) + cfg["vocab_slow"] + N_FAST_STEPS * (f["n_layers"] * rows(f) + cfg["codebook_size"])
+    w = fb["weights"] - p * _esz(cfg) + p + 4 * scale_rows
+    return dict(fb, weights=w, total=w + fb["kv"] + fb["embed"])
+
+
 def gate_up_launch_bytes(cfg, stack: str = "slow") -> int:
     """Algorithmic bytes of one fused RMSNorm + gate/up + SwiGLU launch:
     both weight matrices, the gain, the fp32 input and the fp32 output."""

@@ -82,12 +82,16 @@ def lib():
     return _lib
 
 
+# "i8": bf16 tensors in; the library keeps the layer matrices and heads as int8 with row scales
+WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "i8": 2}
+
+
 def make_config(cfg: dict, max_streams: int | None = None) -> Config:
     def st(s):
         return Stack(s["n_layers"], s["hidden"], s["n_q_heads"], s["n_kv_heads"], s["head_dim"], s["ffn"])
 
     return Config(st(cfg["slow"]), st(cfg["fast"]), cfg["vocab_text"], cfg["n_codebooks"], cfg["codebook_size"],
-                  float(cfg["rope_theta"]), float(cfg["rms_eps"]), 1 if cfg["weight_dtype"] == "bf16" else 0,
+                  float(cfg["rope_theta"]), float(cfg["rms_eps"]), WEIGHT_DTYPES[cfg["weight_dtype"]],
                   int(cfg["rope_bf16"]), int(max_streams or cfg.get("n_streams", 1)), int(cfg["max_context"]),
                   int(cfg.get("page_size", 16)), 1 if cfg.get("kv_dtype", "f32") == "bf16" else 0)
 

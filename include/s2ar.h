@@ -58,7 +58,12 @@ typedef struct {
   int32_t codebook_size;  /* entries per codebook */
   double rope_theta;      /* RoPE base (1e6 for S2) */
   double rms_eps;         /* RMSNorm epsilon, inside the square root */
-  int32_t weight_dtype;   /* 0: fp32 weights, 1: bf16 weights */
+  int32_t weight_dtype;   /* 0: fp32 weights, 1: bf16 weights, 2: bf16 tensors with the layer matrices and
+                             both heads stored as int8 with one fp32 scale per output row (symmetric:
+                             s = max|w| / 127, q = rint(w / s), computed in fp32 at create; a zero row
+                             has s = 0); embeddings, codebooks and gains stay bf16.  Int8 contexts run
+                             prefill position by position and decode streams one at a time
+                             ("s2pro-native", Where it stands; The gate that says no). */
   int32_t rope_bf16;      /* 1: round the cos/sin table to bf16 (S2 page, Engineering Appendix) */
   int32_t max_streams;    /* concurrent decode streams (stream ids 0..max_streams-1) */
   int32_t max_context;    /* Slow positions per stream, prompt plus frames */
@@ -82,7 +87,7 @@ typedef struct {
  *   slow.final_norm[H], slow.head[vocab_text+codebook_size][H],
  *   codebook.embed[n_codebooks][codebook_size][H],
  *   per Fast layer: the same eleven, fast.final_norm[H], fast.head[codebook_size][H]
- * Matrices are row-major [out][in]; every tensor has weight_dtype elements and
+ * Matrices are row-major [out][in]; every tensor has fp32 (weight_dtype 0) or bf16 (1, 2) elements and
  * nbytes must equal its element count times the element size.
  * hip_stream: a hipStream_t (may be NULL = the legacy default stream).  The
  * library orders its work after the work already queued on it at each call.

@@ -72,6 +72,8 @@ def lib():
         L.orc_matvec_f32.argtypes = [vp, c_i32, c_i32, vp, c_i32, vp]
         L.orc_bf16_round.restype = c_dbl
         L.orc_bf16_round.argtypes = [c_dbl]
+        L.orc_quantize_rows_i8.argtypes = [vp, c_i64, c_i64, vp, vp]
+        L.orc_dequantize_rows_i8.argtypes = [vp, vp, c_i64, c_i64, vp]
         L.orc_get_counters.argtypes = [vp]
         L.orc_set_threads.argtypes = [c_i32]
         _lib = L
@@ -284,3 +286,21 @@ def matvec_f32(w, x):
 
 def bf16_round(v):
     return lib().orc_bf16_round(float(v))
+
+
+def quantize_rows_i8(w_bits):
+    """Symmetric per-row int8 of a bf16 matrix (uint16 bit patterns [rows][cols]) -> (q int8, s fp32)."""
+    w = np.ascontiguousarray(w_bits, np.uint16)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty(rows, np.float32)
+    lib().orc_quantize_rows_i8(_p(w), rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def dequantize_rows_i8(q, s):
+    q = np.ascontiguousarray(q, np.int8)
+    s = np.ascontiguousarray(s, np.float32)
+    out = np.empty(q.shape, np.float32)
+    lib().orc_dequantize_rows_i8(_p(q), _p(s), q.shape[0], q.shape[1], _p(out))
+    return out

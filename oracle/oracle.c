@@ -92,6 +92,35 @@ double orc_bf16_round(double v) {
   return (double)x.f;
 }
 
+static float bf16_bits_f32(uint16_t b) {
+  union { uint32_t u; float f; } x;
+  x.u = (uint32_t)b << 16;
+  return x.f;
+}
+
+void orc_quantize_rows_i8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* q, float* s) {
+  for (int64_t r = 0; r < rows; ++r) {
+    float m = 0.0f;
+    for (int64_t k = 0; k < cols; ++k) {
+      const float a = fabsf(bf16_bits_f32(w[r * cols + k]));
+      if (a > m) m = a;
+    }
+    const float sc = m / 127.0f;
+    s[r] = sc;
+    for (int64_t k = 0; k < cols; ++k) {
+      float v = sc > 0.0f ? rintf(bf16_bits_f32(w[r * cols + k]) / sc) : 0.0f;
+      if (v > 127.0f) v = 127.0f;
+      if (v < -127.0f) v = -127.0f;
+      q[r * cols + k] = (int8_t)v;
+    }
+  }
+}
+
+void orc_dequantize_rows_i8(const int8_t* q, const float* s, int64_t rows, int64_t cols, float* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < cols; ++k) out[r * cols + k] = (float)q[r * cols + k] * s[r];
+}
+
 /* RMSNorm: y = x / sqrt(mean(x^2) + eps) * g  (epsilon inside the root). */
 void orc_rmsnorm(const double* x, const double* g, int32_t n, double eps, double* y) {
   double ss = 0.0;

@@ -98,6 +98,15 @@ int32_t orc_argmax(const double* v, int32_t lo, int32_t hi, double* margin);
 void orc_matvec_f32(const float* w, int32_t n_rows, int32_t k, const double* x, int32_t n_vec, double* y);
 double orc_bf16_round(double v);
 
+/* Symmetric int8 weights with one scale per output row ("s2pro-native": Where it stands, eight-bit
+ * weights; The gate that says no, INT8 with per-channel weight scales).  Reading taken: per row,
+ * s = max_k |w_k| / 127 and q_k = rint(w_k / s), both in IEEE fp32 with round-to-nearest-even,
+ * q in [-127, 127]; a row of zeros has s = 0 and q = 0.  The model then uses q * s.
+ * w: bf16 bit patterns [rows][cols]; q: [rows][cols]; s: [rows]. */
+void orc_quantize_rows_i8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* q, float* s);
+/* out[r][k] = (float)q[r][k] * s[r], an fp32 product */
+void orc_dequantize_rows_i8(const int8_t* q, const float* s, int64_t rows, int64_t cols, float* out);
+
 /* Instrumented counters: [slow steps, fast steps, fast layer passes, codes emitted]. */
 void orc_get_counters(int64_t* out4);
 void orc_reset_counters(void);

@@ -60,6 +60,21 @@ class Report:
                     tokens_skipped=self.skipped)
 
 
+def int8_reference(cfg, weights):
+    """(cfg, weights) of the oracle's view of an int8-weight context built from bf16 weights: every
+    layer matrix and both heads quantised per row by the oracle's own quantiser and dequantised
+    (q * s in fp32); embeddings, codebooks and gains widened exactly from bf16."""
+    from dual_ar_codec_amd import synth
+    out = []
+    for (name, shape, kind), w in zip(synth.tensor_specs(cfg), weights):
+        f = (np.ascontiguousarray(w).astype(np.uint32) << 16).view(np.float32).reshape(shape)
+        if kind == "matrix" and name not in ("slow.embed", "codebook.embed"):
+            q, s = oracle.quantize_rows_i8(np.ascontiguousarray(w).reshape(shape[0], -1))
+            f = oracle.dequantize_rows_i8(q, s).reshape(shape)
+        out.append(np.ascontiguousarray(f, np.float32))
+    return dict(cfg, weight_dtype="f32"), out
+
+
 def oracle_run(cfg, weights, tokens, mask, codes, n_frames):
     """Oracle free-running decode with every tap; frame t = (fast taps, the Slow
     step that follows frame t)."""

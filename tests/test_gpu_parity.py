@@ -8,7 +8,7 @@ import pytest
 import oracle
 from dual_ar_codec_amd import s2ar, synth
 
-from parity_util import Report, compare_frames, oracle_run, remember_codebook
+from parity_util import Report, compare_frames, int8_reference, oracle_run, remember_codebook
 
 pytestmark = pytest.mark.gpu
 
@@ -177,6 +177,38 @@ def test_graph_replay_equals_debug_path_and_is_deterministic():
         if min(margins) <= 5e-2:
             break
         assert np.array_equal(runs[0][t], f["codes"]), f"frame {t}"
+
+
+def _int8_teacher_forced(name, n_frames):
+    cfg = synth.config(name)
+    _say(f"[parity] {name} int8: generating weights")
+    w = synth.make_weights(cfg)
+    ocfg, ow = int8_reference(cfg, w)
+    toks, _, _ = synth.make_prompt(cfg)
+    _say(f"[parity] {name} int8: oracle prefill {len(toks)} + {n_frames} frames")
+    frames = oracle_run(ocfg, ow, toks, None, None, n_frames)
+    del ow
+    gc.collect()
+    _say(f"[parity] {name} int8: GPU")
+    ctx = _ctx(dict(cfg, weight_dtype="i8"), w)
+    del w
+    gc.collect()
+    ctx.prefill(0, toks)
+    rep = compare_frames(ctx, 0, frames, cfg).finish()
+    _say(f"[parity] {name} int8: {rep}")
+    ctx.close()
+    return rep
+
+
+def test_int8_weights_mid_teacher_forced():
+    """Int8 layer matrices and heads with per-row scales (quantised by the library at create) against
+    the oracle fed the same quantisation (its own quantiser, dequantised): the bf16 acceptance bar."""
+    assert _int8_teacher_forced("mid", 8)["tokens_checked"] > 0
+
+
+@pytest.mark.timeout(1200)
+def test_int8_weights_full_teacher_forced():
+    assert _int8_teacher_forced("full", 2)["tokens_checked"] > 0
 
 
 def test_decode_frame_one_call_per_frame_matches_batched_call():

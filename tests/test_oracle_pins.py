@@ -496,3 +496,45 @@ def test_byte_model_reproduces_params_per_frame():
     fb = metrics.frame_bytes(cfg, 100)
     assert fb["weights"] > 15.5e9 and fb["kv"] == 294_912 * 101  # fp32 K and V, 36 layers x 8 heads x 128
     assert metrics.kv_bytes_per_position(dict(cfg, kv_dtype="bf16")) == 147_456
+
+
+# ------------------------------------------------ int8 weights with per-row scales
+
+def _bf16_bits(v):
+    """bf16 bit patterns of values that bf16 holds exactly."""
+    return (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_int8_rows_closed_form():
+    # max |w| = 2 maps to -127; 1 / (2/127) = 63.5 rounds to the even 64; 0.5 / (2/127) = 31.75 -> 32
+    q, s = oracle.quantize_rows_i8(_bf16_bits([[1.0, -2.0, 0.5, 0.0], [0.0, 0.0, 0.0, 0.0], [3.0, 3.0, -3.0, 1.5]]))
+    assert q[0].tolist() == [64, -127, 32, 0]
+    assert s[0] == np.float32(2.0) / np.float32(127.0) and abs(float(s[0]) * 127 - 2.0) < 1e-6
+    assert q[1].tolist() == [0, 0, 0, 0] and s[1] == 0.0  # a zero row: scale 0, no division
+    assert q[2].tolist() == [127, 127, -127, 64]          # 1.5 / (3/127) = 63.5 -> 64
+    deq = oracle.dequantize_rows_i8(q, s)
+    assert deq[1].tolist() == [0.0] * 4 and deq[0][1] == -np.float32(2.0) / np.float32(127.0) * 127
+
+
+def test_int8_rows_invariants():
+    r = np.random.default_rng(11)
+    w = (r.standard_normal((64, 300)) * 0.02).astype(np.float32)
+    w[5] *= 1000.0                       # rows of very different magnitude
+    w[9, :] = 0.0
+    bits = _bf16_bits(np.array([[oracle.bf16_round(v) for v in row] for row in w], np.float32))
+    wf = (bits.astype(np.uint32) << 16).view(np.float32)
+    q, s = oracle.quantize_rows_i8(bits)
+    deq = oracle.dequantize_rows_i8(q, s)
+    nz = np.any(wf != 0, axis=1)
+    # every non-zero row reaches +-127 at its largest element, and no element leaves [-127, 127]
+    assert np.all(np.max(np.abs(q[nz].astype(np.int32)), axis=1) == 127) and np.all(q[~nz] == 0)
+    # the rounding error of each weight is at most half a step (plus fp32 rounding of the product)
+    err = np.abs(deq.astype(np.float64) - wf.astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 1e-5) + 1e-30)
+    # the scale is the row's max |w| / 127 and does not depend on the other rows
+    assert np.allclose(s[nz] * 127.0, np.max(np.abs(wf[nz]), axis=1), rtol=1e-6)
+    q1, s1 = oracle.quantize_rows_i8(bits[5:6])
+    assert np.array_equal(q1[0], q[5]) and s1[0] == s[5]
+    # sign symmetry: -w quantises to -q with the same scale
+    qn, sn = oracle.quantize_rows_i8(bits ^ np.uint16(0x8000))
+    assert np.array_equal(qn.astype(np.int32), -q.astype(np.int32)) and np.array_equal(sn, s)
