@@ -251,7 +251,7 @@ def main():
                                        "gemv_over_stream": round(k_gbps / s_gbps, 4)}
     forced, ref = [], []
     if args.int8_steps > 0:  # bf16 reference taps for the int8 drift: frames forced to this run's codes
-        forced = [np.ascontiguousarray(out[t, 0]) for t in range(3)]
+        forced = [np.ascontiguousarray(out[t, 0]) for t in range(min(3, args.steps))]
         ctx.prefill(1, toks)
         ref = [ctx.debug_frame(1, forced=f) for f in forced]
         ctx.release(1)
