@@ -139,6 +139,7 @@ class Context:
         self._weights = None  # uploaded; the library keeps no host pointer
         if rc != S2AR_OK:
             raise S2arError(rc, s2ar_last_error(None))
+        self._destroy = lib().s2ar_destroy  # kept: module globals may be gone when __del__ runs at exit
         self.h = h
 
     def _check(self, rc):
@@ -147,7 +148,7 @@ class Context:
 
     def close(self):
         if getattr(self, "h", None):
-            lib().s2ar_destroy(self.h)
+            self._destroy(self.h)
             self.h = None
 
     def __del__(self):
