@@ -111,6 +111,37 @@ def multi_stream(args, w, log):
             "note": "same synthetic weights as the batch-1 line (shapes identical)"}
 
 
+def prefix_sharing(ctx, vc, vt, vm, vcodes):
+    """Time to first frame of the voice-clone prompt on a fresh stream, prefilled whole against
+    sharing the 1000-position reference-audio prefix with a stream that already holds it and
+    prefilling only the 200 text positions (streams 1 and 2, graphs captured beforehand)."""
+    import torch
+
+    n_pref = vc["prompt"]["n_vq"]
+    for s_ in (1, 2):  # capture each stream's frame graph outside the timed region
+        ctx.prefill(s_, vt[:64], vm[:64], vcodes[:64])
+        ctx.decode_frames([s_], 1)
+        ctx.release(s_)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ctx.prefill(1, vt, vm, vcodes)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ctx.decode_frames([1], 1)
+    t2 = time.perf_counter()
+    ctx.share_prefix(1, 2, n_pref)
+    ctx.prefill(2, vt[n_pref:], vm[n_pref:], vcodes[n_pref:])
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    ctx.decode_frames([2], 1)
+    t4 = time.perf_counter()
+    ctx.release(1)
+    ctx.release(2)
+    return {"shared_positions": n_pref, "own_positions": len(vt) - n_pref,
+            "full_prefill_ms": round((t1 - t0) * 1e3, 2), "full_first_frame_ms": round((t2 - t0) * 1e3, 2),
+            "shared_prefill_ms": round((t3 - t2) * 1e3, 2), "shared_first_frame_ms": round((t4 - t2) * 1e3, 2)}
+
+
 def int8_weights(args, cfg, w, toks, forced, ref, log):
     """Batch-1 frames/s with the layer matrices and heads as int8 plus per-row scales (the same
     synthetic weights, quantised by the library at create), and the drift from bf16 on the same
@@ -171,6 +202,8 @@ def main():
     ap.add_argument("--multi-steps", type=int, default=20, help="batched 16-stream decode steps (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a 256 MiB copy (counter calibration)")
     ap.add_argument("--int8-steps", type=int, default=40, help="batch-1 frames with int8 weights (0 = skip)")
+    ap.add_argument("--prefix-share", type=int, default=0,
+                    help="time to first frame of the voice-clone prompt with its 1000-position prefix shared")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py drives one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
@@ -186,7 +219,7 @@ def main():
     n_prompt = synth.prompt_lengths(cfg)[0]
     vc = synth.config("voice_clone") if args.prefill else None
     vc_len = synth.prompt_lengths(vc)[0] if vc else 0
-    need = max(n_prompt + max(args.steps, args.warmup) + 1, vc_len + 1)
+    need = max(n_prompt + max(args.steps, args.warmup) + 1, vc_len + 2)
     if need > cfg["max_context"]:
         cfg = synth.config(args.config, max_context=(need + 63) // 64 * 64)
     log(f"[bench] generating {cfg['name']} weights ({synth.weight_bytes(cfg) / 1e9:.2f} GB)")
@@ -194,7 +227,7 @@ def main():
     w = synth.make_weights(cfg)
     log(f"[bench] weights in {time.perf_counter() - t:.1f} s; uploading")
     toks, mask, codes = synth.make_prompt(cfg)
-    ctx = s2ar.Context(cfg, w, max_streams=2)
+    ctx = s2ar.Context(cfg, w, max_streams=3 if args.prefix_share else 2)
     log("[bench] prefill + warmup")
     ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
     if args.warmup:
@@ -234,6 +267,8 @@ def main():
                    "mfma_frac": round((lin + att) / pt / 1e12 / 2500.0, 4),
                    "note": "bf16 hi+lo split activations: 2 MFMA passes per algorithmic product"}
         ctx.release(1)
+        if args.prefix_share:
+            prefill["prefix_sharing"] = prefix_sharing(ctx, vc, vt, vm, vcodes)
 
     log("[bench] dominant kernel (fused RMSNorm + gate/up + SwiGLU GEMV)")
     ms, nbytes = ctx.time_kernel(0, args.kernel_iters)

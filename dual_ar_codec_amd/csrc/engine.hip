@@ -85,6 +85,7 @@ struct s2ar_ctx {
   int* d_fast_bt = nullptr;  // [max_streams]: stream s uses fast page s
   std::vector<int> free_pages;
   std::vector<std::vector<int>> stream_pages;
+  std::vector<int> page_refs;  // streams holding each page (shared prefixes hold a page several times)
 
   // per-stream device state
   int* d_pos = nullptr;       // [max_streams] next Slow position
@@ -546,6 +547,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     }
   }
   c->stream_pages.assign(g.max_streams, {});
+  c->page_refs.assign(c->n_pages, 0);
 
   // state
   C_TRY(dev_alloc(c, &c->d_pos, sizeof(int) * g.max_streams));
@@ -1199,6 +1201,7 @@ int ensure_pages(s2ar_ctx* c, int s, int upto) {
   while ((int)pages.size() < need) {
     const int p = c->free_pages.back();
     c->free_pages.pop_back();
+    c->page_refs[p] = 1;
     c->h_bt[s * c->bt_stride + (int)pages.size()] = p;
     pages.push_back(p);
   }
@@ -1592,12 +1595,52 @@ int s2ar_release_stream(s2ar_ctx* c, int32_t sid) {
   if (!c) return S2AR_E_ARG;
   if (sid < 0 || sid >= c->cfg.max_streams) return set_err(c, S2AR_E_RANGE, "stream id out of range");
   HIP_TRY(c, hipStreamSynchronize(c->stream));
-  for (int p : c->stream_pages[sid]) c->free_pages.push_back(p);
+  for (int p : c->stream_pages[sid])
+    if (--c->page_refs[p] == 0) c->free_pages.push_back(p);
   c->stream_pages[sid].clear();
   c->pos[sid] = 0;
   c->ready[sid] = 0;
   const int zero = 0;
   HIP_TRY(c, hipMemcpy(c->d_pos + sid, &zero, sizeof(int), hipMemcpyHostToDevice));
+  return S2AR_OK;
+}
+
+int s2ar_share_prefix(s2ar_ctx* c, int32_t src, int32_t dst, int32_t n) {
+  if (!c) return S2AR_E_ARG;
+  const int ms = c->cfg.max_streams;
+  if (src < 0 || src >= ms || dst < 0 || dst >= ms) return set_err(c, S2AR_E_RANGE, "stream id out of range");
+  if (src == dst) return set_err(c, S2AR_E_STATE, "a stream cannot share a prefix with itself");
+  if (c->pos[dst] != 0 || !c->stream_pages[dst].empty()) return set_err(c, S2AR_E_STATE, "destination stream is not empty");
+  if (n < 1 || n > c->pos[src]) return set_err(c, S2AR_E_RANGE, "n_positions must be in [1, position of the source]");
+  const int full = n / kPageSize, part = n % kPageSize;
+  if (part && c->free_pages.empty()) return set_err(c, S2AR_E_CAPACITY, "no free KV page");
+  if (int rc = order_after_user(c)) return rc;
+  const std::vector<int>& sp = c->stream_pages[src];
+  std::vector<int>& dp = c->stream_pages[dst];
+  int* bt = c->h_bt + dst * c->bt_stride;
+  for (int i = 0; i < full; ++i) {
+    ++c->page_refs[sp[i]];
+    dp.push_back(sp[i]);
+    bt[i] = sp[i];
+  }
+  if (part) {  // the partial last page: a private copy (its remaining slots are dst's to fill)
+    const int p = c->free_pages.back();
+    c->free_pages.pop_back();
+    c->page_refs[p] = 1;
+    dp.push_back(p);
+    bt[full] = p;
+    const size_t page_bytes = c->kv_layer / c->n_pages;  // [Hkv][16][D] of one layer
+    for (int l = 0; l < c->cfg.slow.n_layers; ++l)
+      for (char* pool : {c->kv_k, c->kv_v}) {
+        char* base = pool + (size_t)l * c->kv_layer;
+        HIP_TRY(c, hipMemcpyAsync(base + (size_t)p * page_bytes, base + (size_t)sp[full] * page_bytes, page_bytes,
+                                  hipMemcpyDeviceToDevice, c->stream));
+      }
+  }
+  HIP_TRY(c, hipMemcpyAsync(c->d_bt + dst * c->bt_stride, bt, sizeof(int) * dp.size(), hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(c, hipStreamSynchronize(c->stream));  // the pinned block-table row may change on the next call
+  c->pos[dst] = n;
+  c->ready[dst] = 0;
   return S2AR_OK;
 }
 

@@ -68,6 +68,7 @@ def lib():
         L.s2ar_decode_frame.argtypes = [vp, vp, i32, vp]
         L.s2ar_decode_frames.argtypes = [vp, vp, i32, i32, vp]
         L.s2ar_release_stream.argtypes = [vp, i32]
+        L.s2ar_share_prefix.argtypes = [vp, i32, i32, i32]
         L.s2ar_stream_position.argtypes = [vp, i32, ctypes.POINTER(i32)]
         L.s2ar_destroy.argtypes = [vp]
         L.s2ar_destroy.restype = None
@@ -180,6 +181,9 @@ class Context:
 
     def release(self, stream_id):
         self._check(lib().s2ar_release_stream(self.h, int(stream_id)))
+
+    def share_prefix(self, src_id, dst_id, n_positions):
+        self._check(lib().s2ar_share_prefix(self.h, int(src_id), int(dst_id), int(n_positions)))
 
     def position(self, stream_id):
         p = i32()

@@ -126,6 +126,20 @@ int s2ar_decode_frames(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n_strea
 /* Forget a stream's context and return its KV pages to the pool. */
 int s2ar_release_stream(s2ar_ctx* ctx, int32_t stream_id);
 
+/* Share the first n_positions cached positions of stream src_id with stream dst_id, so a common
+ * prefix (a reference-audio clip, a system prompt) is prefilled once and reused: radix prefix
+ * caching of shared prefixes ("SGLang Day-0 Support for FishAudio S2", Optimizations with SGLang
+ * Omni).  dst_id must be empty (never prefilled, or released).  Every KV page of src that lies
+ * wholly inside the prefix becomes a page of dst too (the pool counts its holders and frees it when
+ * the last one is released; positions only ever append, so no holder writes it again); the partial
+ * last page, if any, is copied into a fresh page of dst.  dst then holds n_positions positions but
+ * is not ready to decode: a prefill of at least one more position must follow (it produces the
+ * hidden state and the first code).  Ordered like the other calls on the context's stream.
+ * Errors: S2AR_E_RANGE (stream ids, or n_positions outside [1, position of src]), S2AR_E_STATE
+ * (src_id == dst_id, or dst not empty), S2AR_E_CAPACITY (no free page for the copy); on error nothing
+ * changes. */
+int s2ar_share_prefix(s2ar_ctx* ctx, int32_t src_id, int32_t dst_id, int32_t n_positions);
+
 /* Current Slow position (= context length) of a stream, or a negative code. */
 int s2ar_stream_position(const s2ar_ctx* ctx, int32_t stream_id, int32_t* pos_out);
 

@@ -179,6 +179,60 @@ def test_graph_replay_equals_debug_path_and_is_deterministic():
         assert np.array_equal(runs[0][t], f["codes"]), f"frame {t}"
 
 
+@pytest.mark.parametrize("n_shared", [64, 37])
+def test_shared_prefix_streams(n_shared):
+    """Two streams share the first n_shared positions of a VQ-masked prompt (whole pages by
+    reference, the partial last page copied when n_shared is not a multiple of 16), then each
+    prefills its own text.  Both match the oracle run on their full prompts, before and after the
+    other stream decodes, and the sharer keeps working after the source is released."""
+    cfg = synth.config("mid", max_context=256)
+    w = synth.make_weights(cfg)
+    r = np.random.default_rng(17)
+    n_vq, n_text = 70, 24
+    codes = r.integers(0, cfg["codebook_size"], (n_vq + n_text, 10)).astype(np.int32)
+    mask = np.zeros(n_vq + n_text, np.uint8)
+    mask[:n_vq] = 1
+    prompts = []
+    for s_ in range(2):
+        toks = r.integers(0, cfg["vocab_text"], n_vq + n_text).astype(np.int32)
+        toks[:n_shared] = prompts[0][0][:n_shared] if prompts else toks[:n_shared]
+        m, c = mask.copy(), codes.copy()
+        prompts.append((toks, m, c))
+    refs = [oracle_run(cfg, w, t, m, c, 3) for t, m, c in prompts]
+    ctx = _ctx(cfg, w, max_streams=2)
+    t0, m0, c0 = prompts[0]
+    ctx.prefill(0, t0, m0, c0)
+    ctx.share_prefix(0, 1, n_shared)
+    assert ctx.position(1) == n_shared
+    with pytest.raises(s2ar.S2arError):
+        ctx.decode_frame([1])  # not ready until its own positions are prefilled
+    t1, m1, c1 = prompts[1]
+    ctx.prefill(1, t1[n_shared:], m1[n_shared:], c1[n_shared:])
+    assert ctx.position(1) == len(t1)
+    rep1 = compare_frames(ctx, 1, refs[1][:2], cfg).finish()
+    rep0 = compare_frames(ctx, 0, refs[0], cfg).finish()
+    ctx.release(0)
+    rep1b = compare_frames(ctx, 1, refs[1][2:], cfg).finish()
+    _say(f"[parity] shared prefix {n_shared}: {rep0} {rep1} {rep1b}")
+    ctx.close()
+
+
+def test_shared_prefix_errors_leave_state_unchanged():
+    cfg = synth.config("tiny")
+    w = synth.make_weights(cfg)
+    toks, _, _ = synth.make_prompt(cfg)
+    ctx = _ctx(cfg, w, max_streams=3)
+    ctx.prefill(0, toks)
+    ctx.prefill(2, toks[:5])
+    for args in [(0, 0, 4), (0, 2, 4), (0, 1, 0), (0, 1, len(toks) + 1), (0, 7, 4), (-1, 1, 4)]:
+        with pytest.raises(s2ar.S2arError):
+            ctx.share_prefix(*args)
+    assert ctx.position(1) == 0 and ctx.position(2) == 5
+    ctx.share_prefix(0, 1, len(toks))  # the whole prompt: still needs one more position
+    ctx.prefill(1, toks[-1:])
+    ctx.close()
+
+
 def _int8_teacher_forced(name, n_frames):
     cfg = synth.config(name)
     _say(f"[parity] {name} int8: generating weights")
