@@ -74,6 +74,10 @@ def lib():
         L.orc_bf16_round.argtypes = [c_dbl]
         L.orc_quantize_rows_i8.argtypes = [vp, c_i64, c_i64, vp, vp]
         L.orc_dequantize_rows_i8.argtypes = [vp, vp, c_i64, c_i64, vp]
+        L.orc_f8_value.restype = c_dbl
+        L.orc_f8_value.argtypes = [ctypes.c_uint8]
+        L.orc_quantize_rows_f8.argtypes = [vp, c_i64, c_i64, vp, vp]
+        L.orc_dequantize_rows_f8.argtypes = [vp, vp, c_i64, c_i64, vp]
         L.orc_get_counters.argtypes = [vp]
         L.orc_set_threads.argtypes = [c_i32]
         _lib = L
@@ -303,4 +307,27 @@ def dequantize_rows_i8(q, s):
     s = np.ascontiguousarray(s, np.float32)
     out = np.empty(q.shape, np.float32)
     lib().orc_dequantize_rows_i8(_p(q), _p(s), q.shape[0], q.shape[1], _p(out))
+    return out
+
+
+def f8_value(b):
+    """Value of one OCP FP8 E4M3 byte."""
+    return lib().orc_f8_value(int(b) & 0xff)
+
+
+def quantize_rows_f8(w_bits):
+    """Per-row FP8 E4M3 of a bf16 matrix (uint16 bit patterns [rows][cols]) -> (q uint8, s fp32)."""
+    w = np.ascontiguousarray(w_bits, np.uint16)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty(rows, np.float32)
+    lib().orc_quantize_rows_f8(_p(w), rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def dequantize_rows_f8(q, s):
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.float32)
+    out = np.empty(q.shape, np.float32)
+    lib().orc_dequantize_rows_f8(_p(q), _p(s), q.shape[0], q.shape[1], _p(out))
     return out

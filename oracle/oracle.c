@@ -121,6 +121,54 @@ void orc_dequantize_rows_i8(const int8_t* q, const float* s, int64_t rows, int64
     for (int64_t k = 0; k < cols; ++k) out[r * cols + k] = (float)q[r * cols + k] * s[r];
 }
 
+/* Value of an OCP FP8 E4M3 ("e4m3fn") byte: sign in bit 7, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN (never produced here).
+ * Normal values are (8 + m) * 2^(e - 10). */
+double orc_f8_value(uint8_t b) {
+  const int e = (b >> 3) & 15, m = b & 7;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  if ((b & 0x7f) == 0x7f) v = NAN;
+  return (b & 0x80) ? -v : v;
+}
+
+/* Nearest E4M3 magnitude code (0x00..0x7e) to a |v| <= 448 by a scan of every finite magnitude in
+ * increasing order; a tie between two neighbours goes to the even code (even last mantissa bit). */
+static uint8_t f8_nearest_code(double a) {
+  uint8_t best = 0;
+  double bd = fabs(a);
+  for (int c = 1; c <= 0x7e; ++c) {
+    const double d = fabs(orc_f8_value((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = (uint8_t)c;
+    }
+  }
+  return best;
+}
+
+void orc_quantize_rows_f8(const uint16_t* w, int64_t rows, int64_t cols, uint8_t* q, float* s) {
+  for (int64_t r = 0; r < rows; ++r) {
+    float m = 0.0f;
+    for (int64_t k = 0; k < cols; ++k) {
+      const float a = fabsf(bf16_bits_f32(w[r * cols + k]));
+      if (a > m) m = a;
+    }
+    const float sc = m / 448.0f;
+    s[r] = sc;
+    for (int64_t k = 0; k < cols; ++k) {
+      float v = sc > 0.0f ? bf16_bits_f32(w[r * cols + k]) / sc : 0.0f;
+      if (v > 448.0f) v = 448.0f;
+      if (v < -448.0f) v = -448.0f;
+      q[r * cols + k] = (uint8_t)(f8_nearest_code(fabs((double)v)) | (v < 0.0f ? 0x80 : 0x00));
+    }
+  }
+}
+
+void orc_dequantize_rows_f8(const uint8_t* q, const float* s, int64_t rows, int64_t cols, float* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < cols; ++k) out[r * cols + k] = (float)orc_f8_value(q[r * cols + k]) * s[r];
+}
+
 /* RMSNorm: y = x / sqrt(mean(x^2) + eps) * g  (epsilon inside the root). */
 void orc_rmsnorm(const double* x, const double* g, int32_t n, double eps, double* y) {
   double ss = 0.0;

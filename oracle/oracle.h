@@ -107,6 +107,16 @@ void orc_quantize_rows_i8(const uint16_t* w, int64_t rows, int64_t cols, int8_t*
 /* out[r][k] = (float)q[r][k] * s[r], an fp32 product */
 void orc_dequantize_rows_i8(const int8_t* q, const float* s, int64_t rows, int64_t cols, float* out);
 
+/* FP8 weights, measured only ("s2pro-native", The gate that says no: FP8 runs about twice as fast
+ * as bf16 and fails the fidelity gate).  Format: OCP FP8 E4M3 (bias 7, largest finite 448, no
+ * infinities), the gfx950 matrix-core format.  Reading taken: one scale per output row, as for int8:
+ * s = max_k |w_k| / 448 in fp32, v_k = w_k / s in fp32, q_k = the nearest E4M3 value to v_k with ties
+ * to the even code; a row of zeros has s = 0 and q = 0.  The model then uses value(q) * s. */
+double orc_f8_value(uint8_t b);
+void orc_quantize_rows_f8(const uint16_t* w, int64_t rows, int64_t cols, uint8_t* q, float* s);
+/* out[r][k] = (float)value(q[r][k]) * s[r], an fp32 product */
+void orc_dequantize_rows_f8(const uint8_t* q, const float* s, int64_t rows, int64_t cols, float* out);
+
 /* Instrumented counters: [slow steps, fast steps, fast layer passes, codes emitted]. */
 void orc_get_counters(int64_t* out4);
 void orc_reset_counters(void);

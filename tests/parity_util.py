@@ -60,19 +60,25 @@ class Report:
                     tokens_skipped=self.skipped)
 
 
-def int8_reference(cfg, weights):
-    """(cfg, weights) of the oracle's view of an int8-weight context built from bf16 weights: every
-    layer matrix and both heads quantised per row by the oracle's own quantiser and dequantised
-    (q * s in fp32); embeddings, codebooks and gains widened exactly from bf16."""
+def quant_reference(cfg, weights, fmt="i8"):
+    """(cfg, weights) of the oracle's view of an 8-bit-weight context built from bf16 weights: every
+    layer matrix and both heads quantised per row by the oracle's own quantiser (int8 or FP8 E4M3)
+    and dequantised (value * s in fp32); embeddings, codebooks and gains widened exactly from bf16."""
     from dual_ar_codec_amd import synth
+    quant, dequant = ((oracle.quantize_rows_i8, oracle.dequantize_rows_i8) if fmt == "i8"
+                      else (oracle.quantize_rows_f8, oracle.dequantize_rows_f8))
     out = []
     for (name, shape, kind), w in zip(synth.tensor_specs(cfg), weights):
         f = (np.ascontiguousarray(w).astype(np.uint32) << 16).view(np.float32).reshape(shape)
         if kind == "matrix" and name not in ("slow.embed", "codebook.embed"):
-            q, s = oracle.quantize_rows_i8(np.ascontiguousarray(w).reshape(shape[0], -1))
-            f = oracle.dequantize_rows_i8(q, s).reshape(shape)
+            q, s = quant(np.ascontiguousarray(w).reshape(shape[0], -1))
+            f = dequant(q, s).reshape(shape)
         out.append(np.ascontiguousarray(f, np.float32))
     return dict(cfg, weight_dtype="f32"), out
+
+
+def int8_reference(cfg, weights):
+    return quant_reference(cfg, weights, "i8")
 
 
 def oracle_run(cfg, weights, tokens, mask, codes, n_frames):

@@ -538,3 +538,58 @@ def test_int8_rows_invariants():
     # sign symmetry: -w quantises to -q with the same scale
     qn, sn = oracle.quantize_rows_i8(bits ^ np.uint16(0x8000))
     assert np.array_equal(qn.astype(np.int32), -q.astype(np.int32)) and np.array_equal(sn, s)
+
+
+# ------------------------------------------------ FP8 E4M3 weights with per-row scales
+
+def test_f8_values_follow_the_e4m3_encoding():
+    # OCP FP8 E4M3: bias 7, 3 mantissa bits, subnormals m * 2^-9, largest finite 448, S.1111.111 NaN
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+            0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for b, v in want.items():
+        assert oracle.f8_value(b) == v, hex(b)
+    assert math.isnan(oracle.f8_value(0x7F)) and math.isnan(oracle.f8_value(0xFF))
+    # the finite magnitudes are strictly increasing in the code, so code order is value order
+    mags = [oracle.f8_value(b) for b in range(0x7F)]
+    assert all(a < b for a, b in zip(mags, mags[1:]))
+    # every E4M3 value has at most 4 significant bits, so bf16 (8) holds each one exactly
+    assert all(oracle.bf16_round(v) == v for v in mags)
+
+
+def test_f8_rows_exact_values_and_ties_to_even():
+    # max |w| = 448 gives s = 1, so representable values come back unchanged; halfway values go to
+    # the even code: 1.0625 lies between 1.0 (0x38) and 1.125 (0x39) -> 1.0; 1.1875 between 1.125
+    # and 1.25 (0x3A) -> 1.25; 2^-10 between 0 and 2^-9 -> 0; 3 * 2^-10 between 2^-9 and 2^-8 -> 2^-8
+    row = [448.0, -1.0, 0.5, 2.0 ** -9, 1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, -240.0, 0.0]
+    q, s = oracle.quantize_rows_f8(_bf16_bits([row, [0.0] * 10]))
+    assert s[0] == 1.0 and s[1] == 0.0 and q[1].tolist() == [0] * 10
+    deq = oracle.dequantize_rows_f8(q, s)
+    assert deq[0].tolist() == [448.0, -1.0, 0.5, 2.0 ** -9, 1.0, 1.25, 0.0, 2.0 ** -8, -240.0, 0.0]
+    assert q[0][0] == 0x7E and q[0][1] == 0xB8 and q[0][4] == 0x38 and q[0][5] == 0x3A
+
+
+def test_f8_rows_invariants():
+    r = np.random.default_rng(12)
+    w = (r.standard_normal((48, 260)) * 0.02).astype(np.float32)
+    w[3] *= 500.0
+    w[7, :] = 0.0
+    bits = _bf16_bits(np.array([[oracle.bf16_round(v) for v in row] for row in w], np.float32))
+    wf = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    q, s = oracle.quantize_rows_f8(bits)
+    deq = oracle.dequantize_rows_f8(q, s).astype(np.float64)
+    nz = np.any(wf != 0, axis=1)
+    # each non-zero row's largest element maps to +-448, and the scale is max |w| / 448
+    assert np.all(np.max(q[nz] & 0x7F, axis=1) == 0x7E)
+    assert np.allclose(s[nz].astype(np.float64) * 448.0, np.max(np.abs(wf[nz]), axis=1), rtol=1e-6)
+    # error within half a step of the E4M3 grid at the scaled magnitude (step 2^(floor(log2 v) - 3)
+    # for normals, 2^-9 below 2^-6), plus fp32 rounding of the quotient and the product
+    v = np.abs(wf[nz]) / s[nz][:, None]
+    step = np.where(v >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(v, 1e-300))) - 3), 2.0 ** -9)
+    err = np.abs(deq[nz] - wf[nz]) / s[nz][:, None]
+    assert np.all(err <= 0.5 * step * (1 + 1e-5) + 448.0 * 2.0 ** -23)
+    # sign symmetry and row independence
+    qn, sn = oracle.quantize_rows_f8(bits ^ np.uint16(0x8000))
+    nzc = (q & 0x7F) != 0
+    assert np.array_equal(qn[nzc], q[nzc] ^ 0x80) and np.array_equal(sn, s)
+    q1, s1 = oracle.quantize_rows_f8(bits[3:4])
+    assert np.array_equal(q1[0], q[3]) and s1[0] == s[3]
