@@ -25,7 +25,7 @@ class OrcStack(ctypes.Structure):
 class OrcConfig(ctypes.Structure):
     _fields_ = [("slow", OrcStack), ("fast", OrcStack), ("vocab_text", c_i32), ("n_codebooks", c_i32),
                 ("codebook_size", c_i32), ("rope_theta", c_dbl), ("rms_eps", c_dbl), ("weight_dtype", c_i32),
-                ("rope_bf16", c_i32), ("max_context", c_i32)]
+                ("rope_bf16", c_i32), ("max_context", c_i32), ("eos_id", c_i32)]
 
 
 def build(force: bool = False) -> str:
@@ -67,6 +67,8 @@ def lib():
         L.orc_attention.argtypes = [vp, vp, vp, c_i32, c_i32, c_i32, c_i32, vp, vp]
         L.orc_silu.restype = c_dbl
         L.orc_silu.argtypes = [c_dbl]
+        L.orc_slow_pick.restype = c_i32
+        L.orc_slow_pick.argtypes = [vp, c_i32, c_i32, c_i32, vp]
         L.orc_argmax.restype = c_i32
         L.orc_argmax.argtypes = [vp, c_i32, c_i32, vp]
         L.orc_matvec_f32.argtypes = [vp, c_i32, c_i32, vp, c_i32, vp]
@@ -94,7 +96,7 @@ def make_config(cfg: dict) -> OrcConfig:
 
     return OrcConfig(st(cfg["slow"]), st(cfg["fast"]), cfg["vocab_text"], cfg["n_codebooks"], cfg["codebook_size"],
                      float(cfg["rope_theta"]), float(cfg["rms_eps"]), 1 if cfg["weight_dtype"] == "bf16" else 0,
-                     int(cfg["rope_bf16"]), int(cfg["max_context"]))
+                     int(cfg["rope_bf16"]), int(cfg["max_context"]), int(cfg.get("eos_id", -1)))
 
 
 class Model:
@@ -269,6 +271,14 @@ def attention(q, k_cache, v_cache, n_q_heads, n_kv_heads, head_dim):
 
 def silu(z):
     return lib().orc_silu(float(z))
+
+
+def slow_pick(logits, vocab_text, codebook_size, eos_id=-1):
+    """(c0, margin): the Slow pick over the semantic ids plus the EOS id (c0 = -1 for EOS)."""
+    v = np.ascontiguousarray(logits, np.float64)
+    mg = np.zeros(1, np.float64)
+    c0 = lib().orc_slow_pick(_p(v), int(vocab_text), int(codebook_size), int(eos_id), _p(mg))
+    return int(c0), float(mg[0])
 
 
 def argmax(v, lo=0, hi=None):

@@ -131,22 +131,26 @@ double orc_f8_value(uint8_t b) {
   return (b & 0x80) ? -v : v;
 }
 
-/* Nearest E4M3 magnitude code (0x00..0x7e) to a |v| <= 448 by a scan of every finite magnitude in
- * increasing order; a tie between two neighbours goes to the even code (even last mantissa bit). */
-static uint8_t f8_nearest_code(double a) {
-  uint8_t best = 0;
-  double bd = fabs(a);
-  for (int c = 1; c <= 0x7e; ++c) {
-    const double d = fabs(orc_f8_value((uint8_t)c) - a);
-    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
-      bd = d;
-      best = (uint8_t)c;
-    }
+/* Nearest E4M3 magnitude code (0x00..0x7e) to an a in [0, 448]: the finite magnitudes increase with
+ * the code, so a bisection of the table of their values finds the neighbours below and above a; a
+ * tie between the two goes to the even code (even last mantissa bit). */
+static uint8_t f8_nearest_code(const double* tab, double a) {
+  int lo = 0, hi = 0x7e; /* invariant: tab[lo] <= a, and a <= tab[hi] once a <= 448 */
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (tab[mid] <= a) lo = mid;
+    else hi = mid;
   }
-  return best;
+  const double dl = a - tab[lo], dh = tab[hi] - a;
+  if (dl < dh) return (uint8_t)lo;
+  if (dh < dl) return (uint8_t)hi;
+  return (uint8_t)((lo & 1) == 0 ? lo : hi);
 }
 
 void orc_quantize_rows_f8(const uint16_t* w, int64_t rows, int64_t cols, uint8_t* q, float* s) {
+  double tab[0x7f]; /* every finite magnitude, indexed by its code */
+  for (int c = 0; c < 0x7f; ++c) tab[c] = orc_f8_value((uint8_t)c);
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
     float m = 0.0f;
     for (int64_t k = 0; k < cols; ++k) {
@@ -159,7 +163,7 @@ void orc_quantize_rows_f8(const uint16_t* w, int64_t rows, int64_t cols, uint8_t
       float v = sc > 0.0f ? bf16_bits_f32(w[r * cols + k]) / sc : 0.0f;
       if (v > 448.0f) v = 448.0f;
       if (v < -448.0f) v = -448.0f;
-      q[r * cols + k] = (uint8_t)(f8_nearest_code(fabs((double)v)) | (v < 0.0f ? 0x80 : 0x00));
+      q[r * cols + k] = (uint8_t)(f8_nearest_code(tab, fabs((double)v)) | (v < 0.0f ? 0x80 : 0x00));
     }
   }
 }
@@ -312,6 +316,7 @@ static void gains_to_f64(wt g, int32_t n, double* out) {
 orc_model* orc_model_new(const orc_config* cfg, const void* const* t, int32_t n_tensors) {
   if (n_tensors != orc_n_tensors(cfg)) return NULL;
   if (cfg->slow.hidden != cfg->fast.hidden) return NULL; /* h feeds the Fast AR unprojected */
+  if (cfg->eos_id < -1 || cfg->eos_id >= cfg->vocab_text) return NULL; /* a text id, or none */
   if (cfg->slow.n_q_heads % cfg->slow.n_kv_heads || cfg->fast.n_q_heads % cfg->fast.n_kv_heads) return NULL;
   if (cfg->slow.head_dim % 2 || cfg->fast.head_dim % 2 || cfg->n_codebooks < 2) return NULL;
   orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
@@ -467,15 +472,35 @@ static void stack_forward(const orc_model* m, const orc_stack* s, const layer_w*
   free(xn); free(q); free(k); free(v); free(o); free(t); free(g); free(u); free(gq); free(gk); free(tmp);
 }
 
-/* Final norm and Slow head on the residual x; constrained argmax over the
- * semantic ids [vocab_text, vocab_text + codebook_size). */
+int32_t orc_slow_pick(const double* logits, int32_t vocab_text, int32_t codebook_size, int32_t eos_id,
+                      double* margin) {
+  /* candidate ids in increasing order: the EOS id (if any), then the semantic ids */
+  const int32_t n = codebook_size + (eos_id >= 0 ? 1 : 0);
+  int32_t best = -2;
+  double bv = -INFINITY, second = -INFINITY;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t id = eos_id >= 0 ? (i == 0 ? eos_id : vocab_text + i - 1) : vocab_text + i;
+    const double v = logits[id];
+    if (best == -2 || v > bv) {
+      if (best != -2) second = bv;
+      best = id;
+      bv = v;
+    } else if (v > second) {
+      second = v;
+    }
+  }
+  if (margin) *margin = n > 1 ? bv - second : INFINITY;
+  return best == eos_id ? -1 : best - vocab_text;
+}
+
+/* Final norm and Slow head on the residual x, then the Slow pick (semantic ids, plus the EOS id
+ * when the model has one). */
 static void slow_head(const orc_model* m, const double* x, double* h, double* logits, int32_t* c0,
                       double* margin) {
   int32_t H = m->c.slow.hidden, V = m->c.vocab_text + m->c.codebook_size;
   rmsnorm_w(x, m->slow_final, 0, H, m->c.rms_eps, h);
   matvec(m->slow_head, 0, V, H, h, 1, logits);
-  int32_t best = orc_argmax(logits, m->c.vocab_text, V, margin);
-  *c0 = best - m->c.vocab_text;
+  *c0 = orc_slow_pick(logits, m->c.vocab_text, m->c.codebook_size, m->c.eos_id, margin);
 }
 
 int orc_prefill(const orc_model* m, orc_state* st, const int32_t* tokens, const uint8_t* mask,
@@ -585,6 +610,10 @@ int orc_generate(const orc_model* m, orc_state* st, const double* h0, int32_t c0
     if (t > 0) {
       rc = orc_slow_step_codes(m, st, codes_out + (size_t)(t - 1) * NC, NULL, h, NULL, &c0, NULL);
       if (rc) break;
+    }
+    if (c0 < 0) { /* EOS: the stream has ended */
+      for (size_t e = (size_t)t * NC; e < (size_t)n_frames * NC; ++e) codes_out[e] = -1;
+      break;
     }
     fr[0] = c0;
     orc_fast_loop(m, h, NULL, fr + 1, NULL, NULL, NULL, NULL);

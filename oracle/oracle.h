@@ -39,6 +39,7 @@ typedef struct {
   int32_t weight_dtype; /* 0: fp32 arrays, 1: bf16 bit patterns (uint16) */
   int32_t rope_bf16;    /* 1: cos/sin rounded to bf16 */
   int32_t max_context;
+  int32_t eos_id;       /* -1: no stop token; else a text id in [0, vocab_text) that ends the stream */
 } orc_config;
 
 typedef struct orc_model orc_model;
@@ -57,6 +58,17 @@ int32_t orc_state_pos(const orc_state* s);
 /* Input embeddings (fp64 [hidden]). */
 int orc_embed_token(const orc_model* m, int32_t token, double* x);
 int orc_embed_codes(const orc_model* m, const int32_t* codes /*[n_codebooks]*/, double* x);
+
+/* The Slow pick.  The pages constrain the Slow AR's greedy pick to the semantic ids ("SGLang Day-0
+ * Support for FishAudio S2", Background and Motivation) and speak of the model ending early on an EOS
+ * token (same page, Attention Backend Divergence Causing Early Stopping), so the EOS id must be a
+ * candidate too.  Reading taken: with eos_id >= 0 the candidates are eos_id and the semantic ids, the
+ * largest logit wins and a tie goes to the lowest id (the EOS id, a text id, is below every semantic
+ * id); the pick is reported as c0 = -1.  With eos_id = -1 only the semantic ids compete.  c0 is the
+ * semantic code (id - vocab_text) or -1; the margin is the winner minus the best other candidate.
+ * The outputs of prefill and of a Slow step below carry this pick. */
+int32_t orc_slow_pick(const double* logits, int32_t vocab_text, int32_t codebook_size, int32_t eos_id,
+                      double* margin);
 
 /* Prefill n positions (tokens, optional mask/codes).  The last position goes
  * through the final norm and the Slow head; outputs may be NULL. */
@@ -78,7 +90,9 @@ int orc_fast_loop(const orc_model* m, const double* h, const int32_t* forced, in
 
 /* Free-running greedy decode of n_frames after a prefill, in the pages' order:
  * frame 1 uses the prefill's (h, c0); frame t >= 2 first runs the Slow step on
- * frame t-1's ten codes.  codes_out: [n_frames][n_codebooks]. */
+ * frame t-1's ten codes.  codes_out: [n_frames][n_codebooks].  A Slow pick of the
+ * EOS id (c0 = -1) ends the stream: that frame and every later one are written as
+ * n_codebooks values of -1 and nothing more is computed. */
 int orc_generate(const orc_model* m, orc_state* st, const double* h0, int32_t c0, int32_t n_frames,
                  int32_t* codes_out);
 

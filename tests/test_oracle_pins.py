@@ -593,3 +593,62 @@ def test_f8_rows_invariants():
     assert np.array_equal(qn[nzc], q[nzc] ^ 0x80) and np.array_equal(sn, s)
     q1, s1 = oracle.quantize_rows_f8(bits[3:4])
     assert np.array_equal(q1[0], q[3]) and s1[0] == s[3]
+
+
+# ------------------------------------------------ stop token (EOS) in the Slow pick
+
+def test_slow_pick_with_stop_brute_force():
+    r = _rng(30)
+    Vt, K = 40, 24
+    for trial in range(300):
+        v = r.integers(-3, 4, Vt + K).astype(np.float64)  # many ties
+        eos = int(r.integers(-1, Vt))
+        c0, mg = oracle.slow_pick(v, Vt, K, eos)
+        cand = ([eos] if eos >= 0 else []) + list(range(Vt, Vt + K))
+        # the largest logit wins; among equal logits the lowest id
+        best = min(cand, key=lambda i: (-v[i], i))
+        assert c0 == (-1 if best == eos else best - Vt)
+        others = sorted((v[i] for i in cand if i != best), reverse=True)
+        assert mg == v[best] - others[0]
+        if eos < 0:  # no stop token: the plain constrained argmax
+            i, m2 = oracle.argmax(v, Vt, Vt + K)
+            assert c0 == i - Vt and mg == m2
+    # a tie between the EOS logit and the best semantic logit goes to EOS (the lower id)
+    v = np.zeros(Vt + K)
+    v[Vt + 5] = 2.0
+    v[7] = 2.0
+    assert oracle.slow_pick(v, Vt, K, 7) == (-1, 0.0)
+    v[7] = np.nextafter(2.0, 0.0)
+    assert oracle.slow_pick(v, Vt, K, 7)[0] == 5
+
+
+def test_generate_stops_at_the_first_eos_pick_and_keeps_earlier_frames():
+    """A stop id that wins at some Slow step ends the stream there; the frames before it are those
+    of the run without a stop id, and every frame from it on is -1."""
+    cfg = _micro(seed=31)
+    m, w = _model(cfg)
+    Vt, K, n_frames = cfg["vocab_text"], cfg["codebook_size"], 6
+    toks = _rng(31).integers(0, Vt, 5).astype(np.int32)
+    st = m.new_state()
+    pre = st.prefill(toks)
+    free = st.generate(pre["h"], pre["c0"], n_frames)
+    # the Slow logits of every frame's pick: prefill's, then each Slow step's on the free codes
+    st2 = m.new_state()
+    logits = [st2.prefill(toks)["logits"]]
+    for t in range(1, n_frames):
+        logits.append(st2.slow_step(free[t - 1])["logits"])
+    # stop id: the text id with the largest logit at frame 3's pick, where it beats every semantic id
+    eos = int(np.argmax(logits[3][:Vt]))
+    if logits[3][eos] < np.max(logits[3][Vt:Vt + K]):
+        pytest.skip("no text id beats the semantic ids at this seed")
+    stop = next(t for t in range(n_frames) if logits[t][eos] >= np.max(logits[t][Vt:Vt + K]))
+    assert stop <= 3
+    me = oracle.Model(dict(cfg, eos_id=eos), w)
+    st3 = me.new_state()
+    pre3 = st3.prefill(toks)
+    assert (pre3["c0"] == -1) == (stop == 0)
+    got = st3.generate(pre3["h"], pre3["c0"], n_frames)
+    assert np.array_equal(got[:stop], free[:stop])
+    assert np.all(got[stop:] == -1)
+    with pytest.raises(ValueError):
+        oracle.Model(dict(cfg, eos_id=Vt), w)  # a semantic id cannot be the stop id
