@@ -77,7 +77,7 @@ def multi_stream(args, w, log):
 
     from dual_ar_codec_amd import metrics, s2ar, synth
 
-    cfg = synth.config("multi_stream")
+    cfg = synth.config("multi_stream", kv_dtype="bf16")
     lens = synth.prompt_lengths(cfg)
     n = cfg["n_streams"]
     ctx = s2ar.Context(cfg, w, max_streams=n)
@@ -107,7 +107,7 @@ def multi_stream(args, w, log):
             "ms_per_step": round(step_s * 1e3, 3), "per_stream_rtf": round(metrics.rtf(1.0 / step_s), 5),
             "step_bytes": w_bytes + kv, "hbm_gbps": round((w_bytes + kv) / step_s / 1e9, 1),
             "hbm_frac": round((w_bytes + kv) / step_s / 1e9 / HBM_PEAK_GBPS, 4),
-            "prefill_s": round(tp, 2), "kv_dtype": "f32",
+            "prefill_s": round(tp, 2), "kv_dtype": "bf16",
             "note": "same synthetic weights as the batch-1 line (shapes identical)"}
 
 
@@ -142,24 +142,58 @@ def prefix_sharing(ctx, vc, vt, vm, vcodes):
             "shared_prefill_ms": round((t3 - t2) * 1e3, 2), "shared_first_frame_ms": round((t4 - t2) * 1e3, 2)}
 
 
-def int8_weights(args, cfg, w, toks, forced, ref, log):
-    """Batch-1 frames/s with the layer matrices and heads as int8 plus per-row scales (the same
-    synthetic weights, quantised by the library at create), and the drift from bf16 on the same
-    teacher-forced frames (the GPU against itself: hidden cosine, logit error, agreeing picks)."""
+def slice_head(steps, cfg, w, toks, log):
+    """Batch-1 frames/s with the semantic-slice Slow head (the 4096 semantic rows plus a stop row;
+    the stop id stands in as the last text id) on the same weights and prompt."""
+    import torch
+
+    from dual_ar_codec_amd import metrics, s2ar
+
+    cs = dict(cfg, head_slice=1, eos_id=cfg["vocab_text"] - 1)
+    log("[bench] semantic-slice head")
+    ctx = s2ar.Context(cs, w, max_streams=1)
+    ctx.prefill(0, toks)
+    ctx.decode_frames([0], 3)
+    ctx.release(0)
+    ctx.prefill(0, toks)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = ctx.decode_frames([0], steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ctx.close()
+    fps = steps / dt
+    H, K = cfg["slow"]["hidden"], cfg["codebook_size"]
+    fb = metrics.frame_bytes(cfg, len(toks) + steps // 2)
+    dropped = (cfg["vocab_slow"] - K - 1) * H * 2  # bf16 head rows not read
+    total = fb["total"] - dropped
+    gbps = total * fps / 1e9
+    return {"workload": f"{cfg['name']}: {len(toks)}-token prompt, {steps} greedy frames, 1 stream",
+            "frames_per_s": round(fps, 2), "ms_per_frame": round(dt / steps * 1e3, 4),
+            "frame_bytes": total, "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "stopped_at_frame": int(next((t for t in range(steps) if out[t, 0, 0] < 0), -1)),
+            "note": "Slow head reads 4097 rows instead of 155776; the picks are those of the full head"}
+
+
+def quant_weights(steps, fmt, cfg, w, toks, forced, ref, log):
+    """Batch-1 frames/s with the layer matrices and heads as 8-bit codes (fmt "i8": int8, "f8": FP8
+    E4M3) plus per-row scales (the same synthetic weights, quantised by the library at create), and
+    the drift from bf16 on the same teacher-forced frames (the GPU against itself: hidden cosine,
+    logit error, agreeing picks)."""
     import numpy as np
     import torch
 
     from dual_ar_codec_amd import metrics, s2ar
 
-    c8 = dict(cfg, weight_dtype="i8")
-    log("[bench] int8 weights: quantise + upload")
+    name = "int8" if fmt == "i8" else "FP8 E4M3"
+    c8 = dict(cfg, weight_dtype=fmt)
+    log(f"[bench] {name} weights: quantise + upload")
     ctx = s2ar.Context(c8, w, max_streams=2)
     ctx.prefill(0, toks)
     ctx.decode_frames([0], 3)
     ctx.release(0)
     ctx.prefill(0, toks)
     torch.cuda.synchronize()
-    steps = args.int8_steps
     t0 = time.perf_counter()
     ctx.decode_frames([0], steps)
     torch.cuda.synchronize()
@@ -186,7 +220,7 @@ def int8_weights(args, cfg, w, toks, forced, ref, log):
             "drift_vs_bf16": {"frames": len(forced), "min_cos_slow_h": round(h_cos, 6),
                               "min_cos_fast_z": round(fz_cos, 6), "max_slow_logit_rel": round(lrel, 5),
                               "own_pick_agreement": round(agree, 4)},
-            "note": "int8 layer matrices and heads, one fp32 scale per row; parity is checked against the "
+            "note": f"{name} layer matrices and heads, one fp32 scale per row; parity is checked against the "
                     "oracle fed the same quantisation, drift against the bf16 context on the same forced codes"}
 
 
@@ -202,6 +236,8 @@ def main():
     ap.add_argument("--multi-steps", type=int, default=20, help="batched 16-stream decode steps (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a 256 MiB copy (counter calibration)")
     ap.add_argument("--int8-steps", type=int, default=40, help="batch-1 frames with int8 weights (0 = skip)")
+    ap.add_argument("--fp8-steps", type=int, default=40, help="batch-1 frames with FP8 E4M3 weights (0 = skip)")
+    ap.add_argument("--slice-steps", type=int, default=60, help="batch-1 frames with the semantic-slice head (0 = skip)")
     ap.add_argument("--prefix-share", type=int, default=0,
                     help="time to first frame of the voice-clone prompt with its 1000-position prefix shared")
     args = ap.parse_args()
@@ -285,14 +321,16 @@ def main():
                                        "avg_launch_us": round(sms * 1e3, 2),
                                        "gemv_over_stream": round(k_gbps / s_gbps, 4)}
     forced, ref = [], []
-    if args.int8_steps > 0:  # bf16 reference taps for the int8 drift: frames forced to this run's codes
+    if args.int8_steps > 0 or args.fp8_steps > 0:  # bf16 taps for the 8-bit drift, forced to this run's codes
         forced = [np.ascontiguousarray(out[t, 0]) for t in range(min(3, args.steps))]
         ctx.prefill(1, toks)
         ref = [ctx.debug_frame(1, forced=f) for f in forced]
         ctx.release(1)
     ctx.close()
 
-    int8 = int8_weights(args, cfg, w, toks, forced, ref, log) if args.int8_steps > 0 else None
+    int8 = quant_weights(args.int8_steps, "i8", cfg, w, toks, forced, ref, log) if args.int8_steps > 0 else None
+    fp8 = quant_weights(args.fp8_steps, "f8", cfg, w, toks, forced, ref, log) if args.fp8_steps > 0 else None
+    sliced = slice_head(args.slice_steps, cfg, w, toks, log) if args.slice_steps > 0 else None
 
     multi = None
     if args.multi_steps > 0:
@@ -332,6 +370,8 @@ def main():
         "prefill": prefill,
         "multi_stream": multi,
         "int8": int8,
+        "fp8": fp8,
+        "semantic_slice_head": sliced,
     }
     print(json.dumps(line), flush=True)
 

@@ -580,6 +580,8 @@ __global__ __launch_bounds__(256) void k_finish_b(const FinishBArgs f) {
         i = bidx[w];
       }
     s_code = (i == INT_MAX) ? 0 : i - f.lo;
+    // the stop id is a text id, below every semantic id, so it also wins a tie
+    if (f.mode == FIN_SLOW && f.eos_at >= 0 && f.logits[(size_t)b * f.ld_logits + f.eos_at] >= v) s_code = -1;
   }
   __syncthreads();
   const int code = s_code;
@@ -592,7 +594,8 @@ __global__ __launch_bounds__(256) void k_finish_b(const FinishBArgs f) {
     if (e < f.H) {
       float acc = 0.f;
       for (int k = 0; k < f.NC; ++k) {
-        const int ck = (k == f.j) ? code : codes[k];
+        // c0 is -1 once the stream picked its stop id: the gather stays in bounds, the result is unused
+        const int ck = min(max((k == f.j) ? code : codes[k], 0), f.K - 1);
         acc += load_w<BF16>(f.codebook, ((size_t)k * f.K + ck) * f.H + e);
       }
       x[e] = acc;

@@ -55,7 +55,8 @@ struct Graph {
 struct s2ar_ctx {
   s2ar_config cfg{};
   bool bf16 = true;  // tables (embeddings, codebooks, gains) arrive as bf16
-  bool i8 = false;   // layer matrices and heads are stored as int8 with per-row scales
+  bool q8 = false;   // layer matrices and heads are stored as 8-bit codes with per-row scales
+  bool f8 = false;   // ... and those codes are FP8 E4M3 (else int8)
   int esz = 2;
   hipStream_t user_stream = nullptr;
   hipStream_t stream = nullptr;
@@ -96,6 +97,10 @@ struct s2ar_ctx {
   int* d_fast_pos = nullptr;  // [NC-1][max_streams] = j - 1
   std::vector<int> pos;
   std::vector<char> ready;
+  std::vector<char> ended;  // the stream's Slow pick was the stop id
+  // Slow head as stored: head_rows rows, the semantic ids at rows [head_lo, head_lo + K), and the
+  // stop id's logit at row head_eos (-1: none)
+  int head_rows = 0, head_lo = 0, head_eos = -1;
 
   // workspace (batch row 0), every input vector zero-padded to pad_k
   float *x = nullptr, *qkv = nullptr, *att = nullptr, *act = nullptr;
@@ -195,8 +200,8 @@ int check_stack(const s2ar_stack& s, const char* name, int epc, std::string& why
 }
 
 int validate_config(const s2ar_config* c, std::string& why) {
-  if (c->weight_dtype < 0 || c->weight_dtype > 2) {
-    why = "weight_dtype must be 0 (fp32), 1 (bf16) or 2 (bf16 tensors, int8 matrices)";
+  if (c->weight_dtype < 0 || c->weight_dtype > 3) {
+    why = "weight_dtype must be 0 (fp32), 1 (bf16), 2 (bf16 tensors, int8 matrices) or 3 (bf16 tensors, FP8 matrices)";
     return -1;
   }
   const int epc = c->weight_dtype == 0 ? 4 : 8;
@@ -223,6 +228,14 @@ int validate_config(const s2ar_config* c, std::string& why) {
   }
   if (c->kv_dtype != 0 && c->kv_dtype != 1) {
     why = "kv_dtype must be 0 (fp32) or 1 (bf16)";
+    return -1;
+  }
+  if (c->eos_id < -1 || c->eos_id >= c->vocab_text) {
+    why = "eos_id must be -1 (none) or a text id in [0, vocab_text)";
+    return -1;
+  }
+  if (c->head_slice != 0 && c->head_slice != 1) {
+    why = "head_slice must be 0 (full head) or 1 (semantic rows plus the eos_id row)";
     return -1;
   }
   if (!(c->rope_theta > 0.0) || !(c->rms_eps >= 0.0)) {
@@ -333,7 +346,40 @@ void quantize_rows_i8(const uint16_t* w, size_t rows, size_t cols, int8_t* q, fl
   }
 }
 
-// Upload row blocks of bf16 host matrices as one int8 matrix plus its row scales; block b's rows
+// OCP FP8 E4M3 byte nearest to v (|v| <= 448 after the clamp), ties to the even code: below 2^-6 the
+// grid is the subnormal step 2^-9; in [2^E, 2^(E+1)) it is 2^(E-3), and rint (round to nearest even
+// in the default rounding mode) of the value in those steps gives 8 + mantissa, where 16 carries
+// into the next exponent.  Scaling by powers of two is exact, so only rint rounds.
+uint8_t f32_to_e4m3(float v) {
+  const uint8_t sign = v < 0.f ? 0x80 : 0x00;
+  const float a = std::fmin(std::fabs(v), 448.0f);
+  if (a < 0.015625f) return sign | (uint8_t)std::rint(a * 512.0f);  // 8 lands on 0x08 = 2^-6
+  int x = 0;
+  std::frexp(a, &x);
+  int E = x - 1;
+  int q = (int)std::rint(std::ldexp(a, 3 - E));
+  if (q == 16) {
+    ++E;
+    q = 8;
+  }
+  return sign | (uint8_t)(((E + 7) << 3) | (q - 8));
+}
+
+// Per output row FP8: s = max|w| / 448 and q = E4M3(w / s), both in fp32 on the host; w is used as
+// value(q) * s ("s2pro-native", The gate that says no: FP8 weights, measured only).
+void quantize_rows_f8(const uint16_t* w, size_t rows, size_t cols, uint8_t* q, float* s) {
+  for (size_t r = 0; r < rows; ++r) {
+    const uint16_t* row = w + r * cols;
+    float m = 0.f;
+    for (size_t k = 0; k < cols; ++k) m = std::fmax(m, std::fabs(bf16_bits_to_float(row[k])));
+    const float sc = m / 448.0f;
+    s[r] = sc;
+    for (size_t k = 0; k < cols; ++k) q[r * cols + k] = sc > 0.f ? f32_to_e4m3(bf16_bits_to_float(row[k]) / sc) : 0;
+  }
+}
+
+// Upload row blocks of bf16 host matrices as one 8-bit matrix (int8 or FP8, as the context stores
+// them) plus its row scales; block b's rows
 // land at rows first[b] + stride * i (stride 2 interleaves the gate and up rows).
 struct QBlock {
   const void* src;
@@ -347,7 +393,11 @@ int upload_i8(s2ar_ctx* c, const std::vector<QBlock>& blocks, size_t total_rows,
   for (const QBlock& b : blocks) {
     qb.resize(b.rows * cols);
     sb.resize(b.rows);
-    quantize_rows_i8(static_cast<const uint16_t*>(b.src), b.rows, cols, qb.data(), sb.data());
+    if (c->f8)
+      quantize_rows_f8(static_cast<const uint16_t*>(b.src), b.rows, cols, reinterpret_cast<uint8_t*>(qb.data()),
+                       sb.data());
+    else
+      quantize_rows_i8(static_cast<const uint16_t*>(b.src), b.rows, cols, qb.data(), sb.data());
     for (size_t i = 0; i < b.rows; ++i) {
       const size_t r = b.first + b.stride * i;
       std::memcpy(q.data() + r * cols, qb.data() + i * cols, cols);
@@ -377,7 +427,7 @@ int upload_layer_i8(s2ar_ctx* c, const s2ar_stack& s, const s2ar_tensor* t, Laye
 }
 
 int upload_layer(s2ar_ctx* c, const s2ar_stack& s, const s2ar_tensor* t, LayerW* L) {
-  if (c->i8) return upload_layer_i8(c, s, t, L);
+  if (c->q8) return upload_layer_i8(c, s, t, L);
   const size_t e = c->esz;
   const size_t H = s.hidden, qd = (size_t)s.n_q_heads * s.head_dim, kd = (size_t)s.n_kv_heads * s.head_dim,
                F = s.ffn;
@@ -451,7 +501,8 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   if (!c) return set_err(nullptr, S2AR_E_NOMEM, "out of host memory");
   c->cfg = *cfg;
   c->bf16 = cfg->weight_dtype != 0;
-  c->i8 = cfg->weight_dtype == 2;
+  c->q8 = cfg->weight_dtype == 2 || cfg->weight_dtype == 3;
+  c->f8 = cfg->weight_dtype == 3;
   c->esz = c->bf16 ? 2 : 4;
   c->user_stream = static_cast<hipStream_t>(hip_stream);
   auto fail = [&](int rc) {
@@ -489,18 +540,41 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   c->slow.resize(g.slow.n_layers);
   for (int l = 0; l < g.slow.n_layers; ++l, ti += 11) C_TRY(upload_layer(c, g.slow, t + ti, &c->slow[l]));
   C_TRY(upload_gain(c, t[ti++], H, &c->slow_final));
-  if (c->i8) {
-    C_TRY(upload_i8(c, {{t[ti++].host_ptr, (size_t)V, 0, 1}}, (size_t)V, H, &c->slow_head, &c->slow_head_s));
-  } else {
-    C_TRY(dev_alloc(c, &c->slow_head, (size_t)V * H * e));
-    C_HIP(hipMemcpy(c->slow_head, t[ti++].host_ptr, (size_t)V * H * e, hipMemcpyHostToDevice));
+  // Slow head: every row, or the semantic slice (rows vocab_text.. of the tensor) followed by the
+  // stop id's row
+  const bool has_eos = g.eos_id >= 0;
+  c->head_rows = g.head_slice ? K + (has_eos ? 1 : 0) : (int)V;
+  c->head_lo = g.head_slice ? 0 : g.vocab_text;
+  c->head_eos = !has_eos ? -1 : (g.head_slice ? K : g.eos_id);
+  {
+    const char* hp = static_cast<const char*>(t[ti++].host_ptr);
+    const size_t rb = (size_t)H * e;  // bytes of one host row
+    if (c->q8) {
+      std::vector<QBlock> blocks;
+      if (g.head_slice) {
+        blocks.push_back({hp + (size_t)g.vocab_text * rb, (size_t)K, 0, 1});
+        if (has_eos) blocks.push_back({hp + (size_t)g.eos_id * rb, 1, (size_t)K, 1});
+      } else {
+        blocks.push_back({hp, (size_t)V, 0, 1});
+      }
+      C_TRY(upload_i8(c, blocks, (size_t)c->head_rows, H, &c->slow_head, &c->slow_head_s));
+    } else {
+      C_TRY(dev_alloc(c, &c->slow_head, (size_t)c->head_rows * rb));
+      char* dh = static_cast<char*>(c->slow_head);
+      if (g.head_slice) {
+        C_HIP(hipMemcpy(dh, hp + (size_t)g.vocab_text * rb, (size_t)K * rb, hipMemcpyHostToDevice));
+        if (has_eos) C_HIP(hipMemcpy(dh + (size_t)K * rb, hp + (size_t)g.eos_id * rb, rb, hipMemcpyHostToDevice));
+      } else {
+        C_HIP(hipMemcpy(dh, hp, (size_t)V * rb, hipMemcpyHostToDevice));
+      }
+    }
   }
   C_TRY(dev_alloc(c, &c->codebook, (size_t)NC * K * H * e));
   C_HIP(hipMemcpy(c->codebook, t[ti++].host_ptr, (size_t)NC * K * H * e, hipMemcpyHostToDevice));
   c->fast.resize(g.fast.n_layers);
   for (int l = 0; l < g.fast.n_layers; ++l, ti += 11) C_TRY(upload_layer(c, g.fast, t + ti, &c->fast[l]));
   C_TRY(upload_gain(c, t[ti++], H, &c->fast_final));
-  if (c->i8) {
+  if (c->q8) {
     C_TRY(upload_i8(c, {{t[ti++].host_ptr, (size_t)K, 0, 1}}, (size_t)K, H, &c->fast_head, &c->fast_head_s));
   } else {
     C_TRY(dev_alloc(c, &c->fast_head, (size_t)K * H * e));
@@ -557,6 +631,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   C_TRY(dev_alloc(c, &c->d_sink, sizeof(uint32_t)));
   c->pos.assign(g.max_streams, 0);
   c->ready.assign(g.max_streams, 0);
+  c->ended.assign(g.max_streams, 0);
 
   // workspace
   const int qkvd = (g.slow.n_q_heads + 2 * g.slow.n_kv_heads) * g.slow.head_dim;
@@ -587,7 +662,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   {
     const s2ar_stack& st = g.slow;
     const int qkvd_s = (st.n_q_heads + 2 * st.n_kv_heads) * st.head_dim, qd_s = st.n_q_heads * st.head_dim;
-    c->mfma_prefill = c->bf16 && !c->i8 && qkvd_s % 128 == 0 && H % 128 == 0 && (2 * st.ffn) % 128 == 0 && H % 32 == 0 &&
+    c->mfma_prefill = c->bf16 && !c->q8 && qkvd_s % 128 == 0 && H % 128 == 0 && (2 * st.ffn) % 128 == 0 && H % 32 == 0 &&
                       qd_s % 32 == 0 && st.ffn % 32 == 0;
     if (c->mfma_prefill) {
       c->pch = std::min(g.max_context, 2048);
@@ -617,7 +692,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     auto k_ok = [](const s2ar_stack& st) {
       return st.hidden % 512 == 0 && (st.n_q_heads * st.head_dim) % 512 == 0 && st.ffn % 512 == 0;
     };
-    c->batched_ok = c->bf16 && !c->i8 && g.max_streams > 1 && k_ok(g.slow) && k_ok(g.fast);
+    c->batched_ok = c->bf16 && !c->q8 && g.max_streams > 1 && k_ok(g.slow) && k_ok(g.fast);
     if (c->batched_ok) {
       const int MBt = 16;
       const int qkvd_max = std::max((g.slow.n_q_heads + 2 * g.slow.n_kv_heads) * g.slow.head_dim,
@@ -657,7 +732,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
           jobs.push_back({L.wdown, st.hidden, st.ffn, &L.tdown});
         }
       }
-      jobs.push_back({c->slow_head, (int)V, H, &c->slow_head_t});
+      jobs.push_back({c->slow_head, c->head_rows, H, &c->slow_head_t});
       jobs.push_back({c->fast_head, K, H, &c->fast_head_t});
       for (const TileJob& j : jobs) C_TRY(dev_alloc(c, j.dst, sizeof(uint16_t) * s2k::tiled_weight_elems(j.N, j.K)));
       C_HIP(hipDeviceSynchronize());
@@ -714,6 +789,7 @@ struct Enq {
     s2k::GemvArgs a{};
     a.w = w;
     a.wscale = wscale;
+    a.w_f8 = c->f8 ? 1 : 0;
     a.x = x;
     a.gain = gain;
     a.eps = (float)c->cfg.rms_eps;
@@ -751,6 +827,8 @@ struct Enq {
     f.H = g.slow.hidden;
     f.K = g.codebook_size;
     f.NC = g.n_codebooks;
+    f.logits = c->slow_logits;
+    f.eos_at = mode == s2k::FIN_SLOW ? c->head_eos : -1;
     chk(s2k::launch_finish(c->bf16, f, s));
   }
 
@@ -817,11 +895,19 @@ struct Enq {
   void slow_head(int slot, const TapPlan* tp) {
     const s2ar_config& g = c->cfg;
     const int H = g.slow.hidden, V = g.vocab_text + g.codebook_size;
-    gemv(s2k::GEMV_NORM_ARGMAX, c->slow_head, c->slow_head_s, c->x, c->slow_final, c->slow_logits, V, H, c->d_h + (size_t)slot * H,
-         g.vocab_text, V);
-    finish(s2k::FIN_SLOW, 0, slot, g.vocab_text, V, xf_of(slot));
+    const int lo = c->head_lo, K = g.codebook_size;
+    gemv(s2k::GEMV_NORM_ARGMAX, c->slow_head, c->slow_head_s, c->x, c->slow_final, c->slow_logits, c->head_rows, H,
+         c->d_h + (size_t)slot * H, lo, lo + K);
+    finish(s2k::FIN_SLOW, 0, slot, lo, lo + K, xf_of(slot));
     if (tp && tp->slow_h) d2h(tp->slow_h, c->d_h + (size_t)slot * H, sizeof(float) * H);
-    if (tp && tp->slow_logits) d2h(tp->slow_logits, c->slow_logits, sizeof(float) * V);
+    if (tp && tp->slow_logits) {
+      if (g.head_slice) {  // the tap keeps full-vocabulary indexing; the rows not computed stay NaN
+        d2h(tp->slow_logits + g.vocab_text, c->slow_logits, sizeof(float) * K);
+        if (g.eos_id >= 0) d2h(tp->slow_logits + g.eos_id, c->slow_logits + K, sizeof(float));
+      } else {
+        d2h(tp->slow_logits, c->slow_logits, sizeof(float) * V);
+      }
+    }
     if (tp && tp->next_c0) d2h(tp->next_c0, c->d_codes + (size_t)slot * g.n_codebooks, sizeof(int));
   }
 
@@ -1126,6 +1212,9 @@ struct Enq {
     f.H = g.slow.hidden;
     f.K = g.codebook_size;
     f.NC = g.n_codebooks;
+    f.logits = c->blogits;
+    f.ld_logits = c->head_rows;
+    f.eos_at = mode == s2k::FIN_SLOW ? c->head_eos : -1;
     chk(s2k::launch_finish_b(c->bf16, f, M, s));
   }
 
@@ -1166,11 +1255,19 @@ struct Enq {
       chk(s2k::launch_embed_codes(c->bf16, c->codebook, K, H, NC, slots, c->d_codes, c->d_snap, c->bx, ldx, M, s));
     int pending = layers_b(true, M, slots, c->bx);
     norm_b(c->bx, pending, H, M, c->slow_final);
-    mgemv(s2k::MG_ARGMAX, c->slow_head_t, c->bxn, ldx, c->blogits, V, V, H, M, g.vocab_text, V);
-    finish_b(s2k::FIN_SLOW, 0, M, slots, g.vocab_text, V, c->bxf);
+    const int NH = c->head_rows, lo = c->head_lo;
+    mgemv(s2k::MG_ARGMAX, c->slow_head_t, c->bxn, ldx, c->blogits, NH, NH, H, M, lo, lo + K);
+    finish_b(s2k::FIN_SLOW, 0, M, slots, lo, lo + K, c->bxf);
     if (btp)
       for (int b = 0; b < M; ++b) {
-        if (btp[b].slow_logits) d2h(btp[b].slow_logits, c->blogits + (size_t)b * V, sizeof(float) * V);
+        if (btp[b].slow_logits) {
+          if (g.head_slice) {  // full-vocabulary indexing; the rows not computed stay NaN
+            d2h(btp[b].slow_logits + g.vocab_text, c->blogits + (size_t)b * NH, sizeof(float) * K);
+            if (g.eos_id >= 0) d2h(btp[b].slow_logits + g.eos_id, c->blogits + (size_t)b * NH + K, sizeof(float));
+          } else {
+            d2h(btp[b].slow_logits, c->blogits + (size_t)b * V, sizeof(float) * V);
+          }
+        }
         if (btp[b].slow_h) d2h(btp[b].slow_h, c->d_h + (size_t)bslots_host[b] * H, sizeof(float) * H);
         if (btp[b].next_c0) d2h(btp[b].next_c0, code_ptr(b, 0), sizeof(int));
       }
@@ -1220,6 +1317,8 @@ int check_streams(s2ar_ctx* c, const int32_t* ids, int32_t n, int frames) {
   }
   for (int i = 0; i < n; ++i)
     if (!c->ready[ids[i]]) return set_err(c, S2AR_E_STATE, "stream has not been prefilled");
+  for (int i = 0; i < n; ++i)
+    if (c->ended[ids[i]]) return set_err(c, S2AR_E_STATE, "stream has ended (its Slow pick was the stop id)");
   for (int i = 0; i < n; ++i)
     if (c->pos[ids[i]] + frames > c->cfg.max_context)
       return set_err(c, S2AR_E_CAPACITY, "context would exceed max_context");
@@ -1319,7 +1418,7 @@ int s2ar_create(const s2ar_config* cfg, const s2ar_tensor* tensors, int32_t n_te
   if (validate_config(cfg, why)) return set_err(nullptr, S2AR_E_ARG, why);
   if (n_tensors != n_tensors_for(cfg)) return set_err(nullptr, S2AR_E_ARG, "n_tensors does not match the config");
   const std::vector<int64_t> sizes = tensor_sizes(cfg);
-  const int64_t esz = cfg->weight_dtype == 0 ? 4 : 2;  // bf16 tensors for weight_dtype 1 and 2
+  const int64_t esz = cfg->weight_dtype == 0 ? 4 : 2;  // bf16 tensors for weight_dtype 1, 2 and 3
   for (int i = 0; i < n_tensors; ++i) {
     if (!tensors[i].host_ptr) return set_err(nullptr, S2AR_E_ARG, "tensor " + std::to_string(i) + " is null");
     if (tensors[i].nbytes != sizes[i] * esz)
@@ -1390,7 +1489,20 @@ int s2ar_prefill(s2ar_ctx* c, int32_t sid, const int32_t* tokens, const uint8_t*
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   c->pos[sid] += n;
   c->ready[sid] = 1;
+  c->ended[sid] = 0;  // the new positions end with a fresh Slow pick
   return S2AR_OK;
+}
+
+// A frame whose semantic code is -1 is the stream's stop: it and every later frame of the call come
+// out as -1 (the device kept running the stream's graph, on clamped codes), and the stream ends.
+void mark_stops(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_frames, int32_t* codes_out) {
+  const int NC = c->cfg.n_codebooks;
+  for (int i = 0; i < n; ++i)
+    for (int f = 0; f < n_frames; ++f) {
+      int32_t* row = codes_out + ((size_t)f * n + i) * NC;
+      if (row[0] < 0) c->ended[ids[i]] = 1;
+      if (c->ended[ids[i]]) std::fill(row, row + NC, -1);
+    }
 }
 
 int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_frames, int32_t* codes_out) {
@@ -1428,6 +1540,7 @@ int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_fra
       done += chunk;
     }
     for (int i = 0; i < n; ++i) c->pos[ids[i]] += n_frames;
+    mark_stops(c, ids, n, n_frames, codes_out);
     return S2AR_OK;
   }
   std::vector<Graph*> gs(n);
@@ -1453,6 +1566,7 @@ int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_fra
     done += chunk;
   }
   for (int i = 0; i < n; ++i) c->pos[ids[i]] += n_frames;
+  mark_stops(c, ids, n, n_frames, codes_out);
   return S2AR_OK;
 }
 
@@ -1491,6 +1605,7 @@ int s2ar_debug_frame(s2ar_ctx* c, int32_t sid, const int32_t* forced, s2ar_taps*
     std::memcpy(c->h_small + 2 * NC, forced, sizeof(int) * NC);
     tp.forced = c->h_small + 2 * NC;
   }
+  if (g.head_slice) std::fill(tp.slow_logits, tp.slow_logits + V, NAN);
   if (int rc = order_after_user(c)) return rc;
   if (int rc = ensure_pages(c, sid, c->pos[sid] + 1)) return rc;
   Enq q{c, c->stream};
@@ -1511,7 +1626,8 @@ int s2ar_debug_frame(s2ar_ctx* c, int32_t sid, const int32_t* forced, s2ar_taps*
   if (T.own_codes) std::memcpy(T.own_codes, tp.own, sizeof(int) * NC);
   if (T.next_c0) *T.next_c0 = *tp.next_c0;
   bool finite = true;
-  for (int i = 0; i < V && finite; ++i) finite = std::isfinite(tp.slow_logits[i]);
+  for (int i = g.head_slice ? g.vocab_text : 0; i < V && finite; ++i) finite = std::isfinite(tp.slow_logits[i]);
+  if (g.eos_id >= 0) finite = finite && std::isfinite(tp.slow_logits[g.eos_id]);
   for (int i = 0; i < (NC - 1) * K && finite; ++i) finite = std::isfinite(tp.fast_logits[i]);
   if (!finite) return set_err(c, S2AR_E_NUMERIC, "non-finite logits");
   return S2AR_OK;
@@ -1543,6 +1659,7 @@ int s2ar_debug_frame_batch(s2ar_ctx* c, const int32_t* ids, int32_t n, const int
     bt[b].slow_h = f;
     f += H;
     bt[b].slow_logits = f;
+    if (g.head_slice) std::fill(f, f + V, NAN);  // rows the semantic-slice head does not compute
     f += V;
     bt[b].fast_resid = f;
     f += (size_t)(NC - 1) * g.fast.n_layers * H;
@@ -1600,6 +1717,7 @@ int s2ar_release_stream(s2ar_ctx* c, int32_t sid) {
   c->stream_pages[sid].clear();
   c->pos[sid] = 0;
   c->ready[sid] = 0;
+  c->ended[sid] = 0;
   const int zero = 0;
   HIP_TRY(c, hipMemcpy(c->d_pos + sid, &zero, sizeof(int), hipMemcpyHostToDevice));
   return S2AR_OK;
@@ -1641,6 +1759,7 @@ int s2ar_share_prefix(s2ar_ctx* c, int32_t src, int32_t dst, int32_t n) {
   HIP_TRY(c, hipStreamSynchronize(c->stream));  // the pinned block-table row may change on the next call
   c->pos[dst] = n;
   c->ready[dst] = 0;
+  c->ended[dst] = 0;
   return S2AR_OK;
 }
 
@@ -1656,7 +1775,7 @@ int s2ar_time_kernel(s2ar_ctx* c, int32_t which, int32_t iters, float* avg_ms, i
   if (which < 0 || which > 1 || iters < 1 || !avg_ms)
     return set_err(c, S2AR_E_ARG, "which must be 0 or 1, iters >= 1, avg_ms non-null");
   const s2ar_stack& st = c->cfg.slow;
-  const size_t wbytes = (size_t)2 * st.ffn * st.hidden * (c->i8 ? 1 : c->esz);
+  const size_t wbytes = (size_t)2 * st.ffn * st.hidden * (c->q8 ? 1 : c->esz);
   Enq q{c, c->stream};
   HIP_TRY(c, hipEventRecord(c->ev_t0, c->stream));
   for (int i = 0; i < iters; ++i) {
@@ -1672,7 +1791,7 @@ int s2ar_time_kernel(s2ar_ctx* c, int32_t which, int32_t iters, float* avg_ms, i
   *avg_ms = ms / (float)iters;
   if (bytes_out)
     *bytes_out = which == 0 ? (int64_t)wbytes + (int64_t)st.hidden * 4 * 2 + (int64_t)st.ffn * 4 +
-                                  (c->i8 ? (int64_t)2 * st.ffn * 4 : 0)
+                                  (c->q8 ? (int64_t)2 * st.ffn * 4 : 0)
                             : (int64_t)wbytes;
   return S2AR_OK;
 }

@@ -18,8 +18,9 @@ enum GemvKind : int {
 int pad_k(int K);
 
 struct GemvArgs {
-  const void* w;          // weights (bf16 bits, fp32, or int8 when wscale is set), [N][K]
-  const float* wscale;    // int8 weights: fp32 scale of each row [N]; nullptr for bf16 / fp32
+  const void* w;          // weights (bf16 bits, fp32, or 8-bit codes when wscale is set), [N][K]
+  const float* wscale;    // 8-bit weights: fp32 scale of each row [N]; nullptr for bf16 / fp32
+  int w_f8;               // 8-bit weights: 0 = int8, 1 = OCP FP8 E4M3 bytes
   const float* x;         // input vector [pad_k(K)] (fp32, zero past K)
   const float* gain;      // RMSNorm gain [pad_k(K)] (fp32, zero past K) for the NORM kinds
   float eps;
@@ -90,6 +91,10 @@ struct FinishArgs {
   const float* h;        // FIN_SLOW: the final-normed Slow hidden
   float* x;              // next input vector [H]
   int H, K, NC;
+  // FIN_SLOW with a stop id: logits[eos_at] is its logit; if it is >= the best semantic logit the
+  // pick is the stop (code -1).  eos_at < 0: no stop id.
+  const float* logits;
+  int eos_at;
 };
 hipError_t launch_finish(bool bf16, const FinishArgs& f, hipStream_t s);
 void set_device_cus(int n);
@@ -260,6 +265,9 @@ struct FinishBArgs {
   float* xf_slot;          // FIN_SLOW: also write h into the single-stream Fast residual of the slot
   int ld_xf_slot;
   int H, K, NC;
+  const float* logits;     // FIN_SLOW with a stop id: row b's logits at logits + b * ld_logits
+  int ld_logits;
+  int eos_at;              // index of the stop id's logit in a row (< 0: no stop id)
 };
 hipError_t launch_finish_b(bool bf16, const FinishBArgs& f, int M, hipStream_t s);
 hipError_t launch_gather_h(const float* h, const int* slots, int H, float* x, int ldx, int M, hipStream_t s);

@@ -90,7 +90,7 @@ __host__ __device__ constexpr int rows_per_wave(int kind) { return kind == GEMV_
 // Weight formats of the GEMVs: fp32, bf16, or int8 with an fp32 scale per output row (the row's
 // dot product is taken on the integers and scaled once).  A lane's chunk is 16 bytes (fp32, bf16)
 // or 8 bytes (int8), so every format has 8 (bf16, int8) or 4 (fp32) elements per chunk.
-constexpr int WF_F32 = 0, WF_BF16 = 1, WF_I8 = 2;
+constexpr int WF_F32 = 0, WF_BF16 = 1, WF_I8 = 2, WF_F8 = 3;
 template <int WF>
 struct WFmt {
   using CT = u32x4;
@@ -121,6 +121,32 @@ struct WFmt<WF_I8> {
   }
 };
 
+// OCP FP8 E4M3 bytes (gfx950's matrix-core FP8 format), decoded exactly to fp32 two at a time by the
+// hardware conversion; byte k of the chunk is element k.
+template <>
+struct WFmt<WF_F8> {
+  using CT = u32x2;
+  static constexpr int EPC = 8;
+  static constexpr int ESZ = 1;
+  static __device__ __forceinline__ float dot(const CT w, const float* x, float acc) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(x);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(x + 4);
+    const auto w01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const auto w23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const auto w45 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const auto w67 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    acc = fmaf(w01[0], a.x, acc);
+    acc = fmaf(w01[1], a.y, acc);
+    acc = fmaf(w23[0], a.z, acc);
+    acc = fmaf(w23[1], a.w, acc);
+    acc = fmaf(w45[0], b.x, acc);
+    acc = fmaf(w45[1], b.y, acc);
+    acc = fmaf(w67[0], b.z, acc);
+    acc = fmaf(w67[1], b.w, acc);
+    return acc;
+  }
+};
+
 // ---------------------------------------------------------------------------------------------
 // Weight-streaming GEMV.  Workgroup = 4 wavefronts; wavefront w of block b owns rows
 // (4b + w) * R ... + R - 1.  NCH > 0: K == NCH * 64 * elements-per-chunk and all weight loads of
@@ -144,7 +170,7 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
   const size_t row_bytes = (size_t)K * F::ESZ;
   float sc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) sc[r] = WF == WF_I8 ? a.wscale[min(row0 + r, a.N - 1)] : 1.f;
+  for (int r = 0; r < R; ++r) sc[r] = (WF == WF_I8 || WF == WF_F8) ? a.wscale[min(row0 + r, a.N - 1)] : 1.f;
 
   // 1. loads: the input vector (and gain) first, then every weight chunk of this wavefront's
   //    rows.  vmcnt retires in issue order, so staging the input only waits for the input.
@@ -301,9 +327,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
   gemv_impl<BF16 ? WF_BF16 : WF_F32, NCH, KIND>(a);
 }
 
-template <int NCH, int KIND>
-__global__ __launch_bounds__(GEMV_THREADS) void k_gemv_i8(const GemvArgs a) {
-  gemv_impl<WF_I8, NCH, KIND>(a);
+template <int WF, int NCH, int KIND>
+__global__ __launch_bounds__(GEMV_THREADS) void k_gemv_q(const GemvArgs a) {
+  gemv_impl<WF, NCH, KIND>(a);
 }
 
 int argmax_block_rows() { return GEMV_WAVES * rows_per_wave(GEMV_NORM_ARGMAX); }
@@ -353,6 +379,8 @@ __global__ __launch_bounds__(256) void k_finish(const FinishArgs f) {
         i = bidx[w];
       }
     s_code = (i == INT_MAX) ? 0 : i - f.lo;  // all-NaN logits: code 0 (the debug path flags it)
+    // the stop id is a text id, below every semantic id, so it also wins a tie
+    if (f.mode == FIN_SLOW && f.eos_at >= 0 && f.logits[f.eos_at] >= v) s_code = -1;
   }
   __syncthreads();
   // every block found the same pick; block b handles elements [256 b, 256 b + 256) of the next
@@ -365,7 +393,8 @@ __global__ __launch_bounds__(256) void k_finish(const FinishArgs f) {
     if (e < f.H) {
       float acc = 0.f;
       for (int k = 0; k < f.NC; ++k) {
-        const int ck = (k == f.j) ? code : f.codes[k];
+        // c0 is -1 once the stream picked its stop id: the gather stays in bounds, the result is unused
+        const int ck = min(max((k == f.j) ? code : f.codes[k], 0), f.K - 1);
         acc += load_w<BF16>(f.codebook, ((size_t)k * f.K + ck) * f.H + e);
       }
       f.x[e] = acc;
@@ -430,7 +459,7 @@ __device__ __forceinline__ void gemv2_impl(const GemvArgs& a) {
       const CT* wp = reinterpret_cast<const CT*>(static_cast<const char*>(a.w) + (size_t)row * row_bytes);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) wv[r][c] = __builtin_nontemporal_load(wp + c * WAVE + lane);
-      sv[r] = WF == WF_I8 ? a.wscale[row] : 1.f;
+      sv[r] = (WF == WF_I8 || WF == WF_F8) ? a.wscale[row] : 1.f;
     }
   };
   issue(wa, sa, tile);
@@ -551,9 +580,9 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2(const GemvArgs a) {
   gemv2_impl<BF16 ? WF_BF16 : WF_F32, NCH, KIND, R, WPB>(a);
 }
 
-template <int NCH, int KIND, int R, int WPB>
-__global__ __launch_bounds__(WPB * WAVE) void k_gemv2_i8(const GemvArgs a) {
-  gemv2_impl<WF_I8, NCH, KIND, R, WPB>(a);
+template <int WF, int NCH, int KIND, int R, int WPB>
+__global__ __launch_bounds__(WPB * WAVE) void k_gemv2_q(const GemvArgs a) {
+  gemv2_impl<WF, NCH, KIND, R, WPB>(a);
 }
 
 int pad_k(int K) { return (K + 1023) / 1024 * 1024; }
@@ -591,14 +620,14 @@ static hipError_t gemv_dispatch(const GemvArgs& a, hipStream_t s) {
 #undef S2_NCH
 }
 
-template <int KIND>
-static hipError_t gemv_dispatch_i8(const GemvArgs& a, hipStream_t s) {
+template <int WF, int KIND>
+static hipError_t gemv_dispatch_q(const GemvArgs& a, hipStream_t s) {
   const dim3 grid(gemv_blocks(KIND, a.N)), block(GEMV_THREADS);
   const size_t lds = (size_t)pad_k(a.K) * sizeof(float);
   const int nch = (a.K % (WAVE * 8) == 0) ? a.K / (WAVE * 8) : -1;
 #define S2_NCH(n) \
   case n:         \
-    hipLaunchKernelGGL((k_gemv_i8<n, KIND>), grid, block, lds, s, a); \
+    hipLaunchKernelGGL((k_gemv_q<WF, n, KIND>), grid, block, lds, s, a); \
     return hipGetLastError();
   switch (nch) {
     S2_NCH(1)
@@ -612,7 +641,7 @@ static hipError_t gemv_dispatch_i8(const GemvArgs& a, hipStream_t s) {
     S2_NCH(16)
     S2_NCH(19)
     default:
-      hipLaunchKernelGGL((k_gemv_i8<0, KIND>), grid, block, lds, s, a);
+      hipLaunchKernelGGL((k_gemv_q<WF, 0, KIND>), grid, block, lds, s, a);
       return hipGetLastError();
   }
 #undef S2_NCH
@@ -633,27 +662,33 @@ static hipError_t gemv2_launch(const GemvArgs& a, int blocks_per_cu, hipStream_t
   return hipGetLastError();
 }
 
-template <int NCH, int KIND, int R, int WPB>
-static hipError_t gemv2_launch_i8(const GemvArgs& a, int blocks_per_cu, hipStream_t s) {
+template <int WF, int NCH, int KIND, int R, int WPB>
+static hipError_t gemv2_launch_q(const GemvArgs& a, int blocks_per_cu, hipStream_t s) {
   const int tiles = (a.N + R * WPB - 1) / (R * WPB);
   const int grid = std::min(tiles, g_cus * blocks_per_cu);
-  hipLaunchKernelGGL((k_gemv2_i8<NCH, KIND, R, WPB>), dim3(grid), dim3(WPB * WAVE), (size_t)pad_k(a.K) * 4, s, a);
+  hipLaunchKernelGGL((k_gemv2_q<WF, NCH, KIND, R, WPB>), dim3(grid), dim3(WPB * WAVE), (size_t)pad_k(a.K) * 4, s, a);
   return hipGetLastError();
 }
 
+// 8-bit weights with per-row scales (int8 or FP8 E4M3), the launch shapes of the bf16 kernels
+template <int WF>
+static hipError_t launch_gemv_q(int kind, const GemvArgs& a, hipStream_t s) {
+  const int nch = a.K % (WAVE * 8) == 0 ? a.K / (WAVE * 8) : -1;
+  if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch_q<WF, 5, GEMV_NORM_STORE, 1, 4>(a, 2, s);
+  if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch_q<WF, 5, GEMV_NORM_SWIGLU, 2, 4>(a, 2, s);
+  switch (kind) {
+    case GEMV_NORM_STORE: return gemv_dispatch_q<WF, GEMV_NORM_STORE>(a, s);
+    case GEMV_RESID: return gemv_dispatch_q<WF, GEMV_RESID>(a, s);
+    case GEMV_NORM_SWIGLU: return gemv_dispatch_q<WF, GEMV_NORM_SWIGLU>(a, s);
+    case GEMV_NORM_ARGMAX: return gemv_dispatch_q<WF, GEMV_NORM_ARGMAX>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s) {
-  if (a.wscale) {  // int8 weights with per-row scales, the launch shapes of the bf16 kernels
+  if (a.wscale) {
     if (a.K % 8) return hipErrorInvalidValue;
-    const int nch = a.K % (WAVE * 8) == 0 ? a.K / (WAVE * 8) : -1;
-    if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch_i8<5, GEMV_NORM_STORE, 1, 4>(a, 2, s);
-    if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch_i8<5, GEMV_NORM_SWIGLU, 2, 4>(a, 2, s);
-    switch (kind) {
-      case GEMV_NORM_STORE: return gemv_dispatch_i8<GEMV_NORM_STORE>(a, s);
-      case GEMV_RESID: return gemv_dispatch_i8<GEMV_RESID>(a, s);
-      case GEMV_NORM_SWIGLU: return gemv_dispatch_i8<GEMV_NORM_SWIGLU>(a, s);
-      case GEMV_NORM_ARGMAX: return gemv_dispatch_i8<GEMV_NORM_ARGMAX>(a, s);
-    }
-    return hipErrorInvalidValue;
+    return a.w_f8 ? launch_gemv_q<WF_F8>(kind, a, s) : launch_gemv_q<WF_I8>(kind, a, s);
   }
   if (bf16 && a.K % (WAVE * 8) == 0) {
     const int nch = a.K / (WAVE * 8);
@@ -963,7 +998,7 @@ __global__ __launch_bounds__(256) void k_embed_codes(const void* cb, int K, int 
   if (blockIdx.x == 0 && threadIdx.x < NC) codes_snap[(size_t)slot * NC + threadIdx.x] = cd[threadIdx.x];
   if (i >= H) return;
   float acc = 0.f;
-  for (int k = 0; k < NC; ++k) acc += load_w<BF16>(cb, ((size_t)k * K + cd[k]) * H + i);
+  for (int k = 0; k < NC; ++k) acc += load_w<BF16>(cb, ((size_t)k * K + min(max(cd[k], 0), K - 1)) * H + i);
   x[(size_t)b * ldx + i] = acc;
 }
 

@@ -79,7 +79,7 @@ def frame_bytes(cfg, context_len: int) -> dict:
 
 
 def int8_frame_bytes(cfg, context_len: int) -> dict:
-    """frame_bytes with the layer matrices and both heads stored as int8 plus one fp32 scale per
+    """frame_bytes with the layer matrices and both heads stored as 8-bit codes (int8 or FP8) plus one fp32 scale per
     row (embeddings, codebooks and gains as in frame_bytes)."""
     fb = frame_bytes(cfg, context_len)
     s, f = cfg["slow"], cfg["fast"]

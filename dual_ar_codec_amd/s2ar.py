@@ -41,7 +41,7 @@ class Config(ctypes.Structure):
     _fields_ = [("slow", Stack), ("fast", Stack), ("vocab_text", i32), ("n_codebooks", i32),
                 ("codebook_size", i32), ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double),
                 ("weight_dtype", i32), ("rope_bf16", i32), ("max_streams", i32), ("max_context", i32),
-                ("page_size", i32), ("kv_dtype", i32)]
+                ("page_size", i32), ("kv_dtype", i32), ("eos_id", i32), ("head_slice", i32)]
 
 
 class Tensor(ctypes.Structure):
@@ -83,8 +83,9 @@ def lib():
     return _lib
 
 
-# "i8": bf16 tensors in; the library keeps the layer matrices and heads as int8 with row scales
-WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "i8": 2}
+# "i8" / "f8": bf16 tensors in; the library keeps the layer matrices and heads as int8 / FP8 E4M3
+# codes with row scales
+WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "i8": 2, "f8": 3}
 
 
 def make_config(cfg: dict, max_streams: int | None = None) -> Config:
@@ -94,7 +95,8 @@ def make_config(cfg: dict, max_streams: int | None = None) -> Config:
     return Config(st(cfg["slow"]), st(cfg["fast"]), cfg["vocab_text"], cfg["n_codebooks"], cfg["codebook_size"],
                   float(cfg["rope_theta"]), float(cfg["rms_eps"]), WEIGHT_DTYPES[cfg["weight_dtype"]],
                   int(cfg["rope_bf16"]), int(max_streams or cfg.get("n_streams", 1)), int(cfg["max_context"]),
-                  int(cfg.get("page_size", 16)), 1 if cfg.get("kv_dtype", "f32") == "bf16" else 0)
+                  int(cfg.get("page_size", 16)), 1 if cfg.get("kv_dtype", "f32") == "bf16" else 0,
+                  int(cfg.get("eos_id", -1)), int(cfg.get("head_slice", 0)))
 
 
 def _p(a):

@@ -63,12 +63,28 @@ typedef struct {
                              s = max|w| / 127, q = rint(w / s), computed in fp32 at create; a zero row
                              has s = 0); embeddings, codebooks and gains stay bf16.  Int8 contexts run
                              prefill position by position and decode streams one at a time
-                             ("s2pro-native", Where it stands; The gate that says no). */
+                             ("s2pro-native", Where it stands; The gate that says no); 3: as 2 with
+                             OCP FP8 E4M3 codes instead of int8 (s = max|w| / 448, q = the E4M3 value
+                             nearest w / s, ties to the even code), measured only: the same page
+                             reports FP8 weights as fast but failing its fidelity gate. */
   int32_t rope_bf16;      /* 1: round the cos/sin table to bf16 (S2 page, Engineering Appendix) */
   int32_t max_streams;    /* concurrent decode streams (stream ids 0..max_streams-1) */
   int32_t max_context;    /* Slow positions per stream, prompt plus frames */
   int32_t page_size;      /* KV positions per page; must be 16 */
   int32_t kv_dtype;       /* KV cache element: 0 = fp32 (default), 1 = bf16 (half the KV bytes) */
+  int32_t eos_id;         /* -1: no stop token (decode exactly the frames asked for); else a text id in
+                             [0, vocab_text) that also competes in the Slow pick, winning ties (it is
+                             below every semantic id).  A stream whose pick is that id has ended: its
+                             frame, and every later frame of the same call, comes out as n_codebooks
+                             values of -1, and a further decode of it is S2AR_E_STATE until a prefill
+                             appends to it or it is released ("SGLang Day-0 Support for FishAudio S2",
+                             Background and Motivation: constrained decoding; Attention Backend
+                             Divergence Causing Early Stopping: the model ends on an EOS token). */
+  int32_t head_slice;     /* 0: the Slow head computes every row (text and semantic ids), as the pages
+                             count a frame's weights; 1: only the codebook_size semantic rows and the
+                             eos_id row are kept on the device and computed (the text rows can never be
+                             picked), a semantic slice of the head.  The picks are identical; the
+                             debug taps then hold those rows' logits only (the others NaN). */
 } s2ar_config;
 
 /* One weight tensor in host memory: fp32, or bf16 bit patterns (uint16). */
@@ -87,7 +103,7 @@ typedef struct {
  *   slow.final_norm[H], slow.head[vocab_text+codebook_size][H],
  *   codebook.embed[n_codebooks][codebook_size][H],
  *   per Fast layer: the same eleven, fast.final_norm[H], fast.head[codebook_size][H]
- * Matrices are row-major [out][in]; every tensor has fp32 (weight_dtype 0) or bf16 (1, 2) elements and
+ * Matrices are row-major [out][in]; every tensor has fp32 (weight_dtype 0) or bf16 (1, 2, 3) elements and
  * nbytes must equal its element count times the element size.
  * hip_stream: a hipStream_t (may be NULL = the legacy default stream).  The
  * library orders its work after the work already queued on it at each call.

@@ -81,21 +81,42 @@ def int8_reference(cfg, weights):
     return quant_reference(cfg, weights, "i8")
 
 
-def oracle_run(cfg, weights, tokens, mask, codes, n_frames):
+def oracle_run(cfg, weights, tokens, mask, codes, n_frames, prefill_out=None):
     """Oracle free-running decode with every tap; frame t = (fast taps, the Slow
-    step that follows frame t)."""
+    step that follows frame t).  With a stop id the run ends at the frame whose
+    following Slow pick is the stop (its slow["c0"] is -1); a stop at the prefill's
+    pick gives no frames (prefill_out, a dict, receives the prefill's outputs)."""
     m = oracle.Model(cfg, weights)
     st = m.new_state()
     pre = st.prefill(tokens, mask, codes)
+    if prefill_out is not None:
+        prefill_out.update(pre)
     h, c0, c0m = pre["h"], pre["c0"], pre["margin"]
     frames = []
     for _ in range(n_frames):
+        if c0 < 0:
+            break
         fl = m.fast_loop(h, taps=True)
         codes_t = np.concatenate([[c0], fl["codes"]]).astype(np.int32)
         nxt = st.slow_step(codes_t, taps=True)
         frames.append(dict(codes=codes_t, c0_margin=c0m, fast=fl, slow=nxt))
         h, c0, c0m = nxt["h"], nxt["c0"], nxt["margin"]
     return frames
+
+
+def slow_rows(cfg):
+    """Indices of the Slow logits the GPU computes: all, or the semantic slice plus the stop id."""
+    Vt, K, eos = cfg["vocab_text"], cfg["codebook_size"], cfg.get("eos_id", -1)
+    if not cfg.get("head_slice", 0):
+        return np.arange(Vt + K)
+    return np.concatenate([[eos] if eos >= 0 else [], np.arange(Vt, Vt + K)]).astype(np.int64)
+
+
+def own_slow_pick(logits, cfg):
+    """The Slow pick rule applied to the GPU's own logits (the kernel's pick must equal it)."""
+    Vt, K, eos = cfg["vocab_text"], cfg["codebook_size"], cfg.get("eos_id", -1)
+    b = int(np.argmax(logits[Vt:Vt + K]))
+    return -1 if eos >= 0 and logits[eos] >= logits[Vt + b] else b
 
 
 def compare_frames(ctx, stream, frames, cfg, report=None, gather_check=True):
@@ -119,9 +140,10 @@ def compare_frames(ctx, stream, frames, cfg, report=None, gather_check=True):
         for l in range(cfg["slow"]["n_layers"]):
             r.cos(f"frame {t} slow layer {l}", g["slow_resid"][l], s["resid"][l])
         r.cos(f"frame {t} slow h", g["slow_h"], s["h"])
-        r.logits(f"frame {t} slow logits", g["slow_logits"], s["logits"])
+        rows = slow_rows(cfg)
+        r.logits(f"frame {t} slow logits", g["slow_logits"][rows], s["logits"][rows])
         r.token(f"frame {t} next c0", int(g["next_c0"]), int(s["c0"]), s["margin"])
-        assert int(g["next_c0"]) == int(np.argmax(g["slow_logits"][Vt:Vt + K]))
+        assert int(g["next_c0"]) == own_slow_pick(g["slow_logits"], cfg)
         if gather_check:
             if cb is None:
                 cb = codebook_f32(cfg, ctx)

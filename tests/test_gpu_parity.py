@@ -8,7 +8,8 @@ import pytest
 import oracle
 from dual_ar_codec_amd import s2ar, synth
 
-from parity_util import Report, compare_frames, int8_reference, oracle_run, remember_codebook
+from parity_util import (Report, compare_frames, oracle_run, own_slow_pick, quant_reference, remember_codebook,
+                         slow_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -233,23 +234,23 @@ def test_shared_prefix_errors_leave_state_unchanged():
     ctx.close()
 
 
-def _int8_teacher_forced(name, n_frames):
+def _int8_teacher_forced(name, n_frames, fmt="i8"):
     cfg = synth.config(name)
-    _say(f"[parity] {name} int8: generating weights")
+    _say(f"[parity] {name} {fmt}: generating weights")
     w = synth.make_weights(cfg)
-    ocfg, ow = int8_reference(cfg, w)
+    ocfg, ow = quant_reference(cfg, w, fmt)
     toks, _, _ = synth.make_prompt(cfg)
-    _say(f"[parity] {name} int8: oracle prefill {len(toks)} + {n_frames} frames")
+    _say(f"[parity] {name} {fmt}: oracle prefill {len(toks)} + {n_frames} frames")
     frames = oracle_run(ocfg, ow, toks, None, None, n_frames)
     del ow
     gc.collect()
-    _say(f"[parity] {name} int8: GPU")
-    ctx = _ctx(dict(cfg, weight_dtype="i8"), w)
+    _say(f"[parity] {name} {fmt}: GPU")
+    ctx = _ctx(dict(cfg, weight_dtype=fmt), w)
     del w
     gc.collect()
     ctx.prefill(0, toks)
     rep = compare_frames(ctx, 0, frames, cfg).finish()
-    _say(f"[parity] {name} int8: {rep}")
+    _say(f"[parity] {name} {fmt}: {rep}")
     ctx.close()
     return rep
 
@@ -263,6 +264,17 @@ def test_int8_weights_mid_teacher_forced():
 @pytest.mark.timeout(1200)
 def test_int8_weights_full_teacher_forced():
     assert _int8_teacher_forced("full", 2)["tokens_checked"] > 0
+
+
+def test_fp8_weights_mid_teacher_forced():
+    """FP8 E4M3 layer matrices and heads with per-row scales, decoded by gfx950's hardware
+    conversion, against the oracle fed its own E4M3 quantisation: the bf16 acceptance bar."""
+    assert _int8_teacher_forced("mid", 8, "f8")["tokens_checked"] > 0
+
+
+@pytest.mark.timeout(1200)
+def test_fp8_weights_full_teacher_forced():
+    assert _int8_teacher_forced("full", 2, "f8")["tokens_checked"] > 0
 
 
 def test_decode_frame_one_call_per_frame_matches_batched_call():
@@ -356,9 +368,10 @@ def _compare_batch(ctx, ids, per_stream, cfg, rep):
             for l in range(cfg["slow"]["n_layers"]):
                 rep.cos(f"{tag} slow layer {l}", g["slow_resid"][l], f["slow"]["resid"][l])
             rep.cos(f"{tag} slow h", g["slow_h"], f["slow"]["h"])
-            rep.logits(f"{tag} slow logits", g["slow_logits"], f["slow"]["logits"])
+            rows = slow_rows(cfg)
+            rep.logits(f"{tag} slow logits", g["slow_logits"][rows], f["slow"]["logits"][rows])
             rep.token(f"{tag} next c0", int(g["next_c0"]), int(f["slow"]["c0"]), f["slow"]["margin"])
-            assert int(g["next_c0"]) == int(np.argmax(g["slow_logits"][Vt:Vt + K]))
+            assert int(g["next_c0"]) == own_slow_pick(g["slow_logits"], cfg)
     return rep
 
 
@@ -366,9 +379,11 @@ def _ragged_prompts(cfg, lens, seed):
     return [synth.uniform_ints(seed, 900 + i, n, 0, cfg["vocab_text"]) for i, n in enumerate(lens)]
 
 
-def test_batched_multi_stream_teacher_forced_mid_ragged():
-    """Batched decode kernels (matrix-core GEMVs over several streams, ragged paged attention)."""
-    cfg = synth.config("mid", max_context=640)
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])
+def test_batched_multi_stream_teacher_forced_mid_ragged(kv_dtype):
+    """Batched decode kernels (matrix-core GEMVs over several streams, ragged paged attention),
+    with an fp32 and a bf16 KV cache."""
+    cfg = synth.config("mid", max_context=640, kv_dtype=kv_dtype)
     w = synth.make_weights(cfg)
     lens = [64, 17, 300, 130, 5]
     prompts = _ragged_prompts(cfg, lens, 31)
@@ -378,7 +393,7 @@ def test_batched_multi_stream_teacher_forced_mid_ragged():
     for s_, p in zip(ids, prompts):
         ctx.prefill(s_, p)
     rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
-    _say(f"[parity] batched mid: {rep}")
+    _say(f"[parity] batched mid, {kv_dtype} KV: {rep}")
     ctx.close()
 
 
@@ -431,3 +446,99 @@ def test_batched_graph_equals_eager_batched_frame():
             runs.append(ctx.decode_frames(ids, 6))
         ctx.close()
     assert np.array_equal(runs[0], runs[1])
+
+
+# ----------------------------------------------------- semantic-slice head and the stop id
+
+def _stop_setup(cfg, w, toks, n_frames=6):
+    """A stop id (a text id) and the oracle's run with it: the text id with the largest logit at one
+    of the oracle's early Slow picks, chosen so that the run stops after at least one frame and the
+    stop pick's margin decides it.  Returns (eos, frames, all_margins_decide)."""
+    free = oracle_run(cfg, w, toks, None, None, 4)
+    Vt = cfg["vocab_text"]
+    for at in (2, 1, 3, 0):
+        eos = int(np.argmax(free[at]["slow"]["logits"][:Vt]))
+        ce = dict(cfg, eos_id=eos)
+        pre = {}
+        frames = oracle_run(ce, w, toks, None, None, n_frames, prefill_out=pre)
+        if pre["c0"] < 0 or not frames or frames[-1]["slow"]["c0"] != -1:
+            continue
+        if frames[-1]["slow"]["margin"] <= 5e-2:
+            continue
+        margins = [f["c0_margin"] for f in frames] + [m for f in frames for m in f["fast"]["margins"]]
+        return eos, frames, min(margins) > 5e-2
+    pytest.skip("no early text id stops this run by a deciding margin")
+
+
+@pytest.mark.parametrize("head_slice", [0, 1])
+def test_stop_id_teacher_forced(head_slice):
+    """The Slow pick with a stop id (full head, and the semantic-slice head that keeps only the
+    semantic rows plus the stop row): every frame matches the oracle run with the same stop id, and
+    the stop pick itself comes out as -1."""
+    cfg = synth.config("mid", head_slice=head_slice)
+    w = synth.make_weights(cfg)
+    toks, _, _ = synth.make_prompt(cfg)
+    eos, frames, _ = _stop_setup(cfg, w, toks)
+    ce = dict(cfg, eos_id=eos)
+    ctx = _ctx(ce, w)
+    ctx.prefill(0, toks)
+    rep = compare_frames(ctx, 0, frames, ce).finish()
+    _say(f"[parity] stop id {eos}, head_slice {head_slice}: {len(frames)} frames then the stop; {rep}")
+    # the oracle's stop is the GPU's too: the next frame comes out as the stop, then the stream has ended
+    assert np.all(ctx.decode_frames([0], 1) == -1)
+    with pytest.raises(s2ar.S2arError):
+        ctx.decode_frames([0], 1)
+    ctx.close()
+
+
+def test_semantic_slice_head_batched_teacher_forced():
+    """The batched Slow head over the semantic slice plus a stop row, three ragged streams."""
+    cfg = synth.config("mid", max_context=640, head_slice=1, eos_id=5)
+    w = synth.make_weights(cfg)
+    prompts = _ragged_prompts(cfg, [64, 17, 130], 34)
+    per_stream = _oracle_frames_per_stream(cfg, w, prompts, 3)
+    ctx = _ctx(cfg, w, max_streams=3)
+    ids = [2, 0, 1]
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    n = min(len(f) for f in per_stream)
+    rep = _compare_batch(ctx, ids, [f[:n] for f in per_stream], cfg, Report()).finish()
+    _say(f"[parity] batched slice head: {rep}")
+    ctx.close()
+
+
+@pytest.mark.parametrize("batched", [False, True])
+def test_stop_id_ends_free_running_stream(batched):
+    """decode_frames with a stop id: the stream's frames up to the stop are the oracle's, the stop
+    frame and every later frame of the call are -1, a further decode is refused, and a prefill that
+    appends to the stream lets it decode again."""
+    cfg = synth.config("mid", max_context=640, head_slice=1 if batched else 0)
+    w = synth.make_weights(cfg)
+    toks, _, _ = synth.make_prompt(cfg)
+    eos, frames, decided = _stop_setup(cfg, w, toks)
+    ce = dict(cfg, eos_id=eos)
+    stop = len(frames)
+    ctx = _ctx(ce, w, max_streams=3)
+    ctx.prefill(0, toks)
+    ids = [0]
+    if batched:
+        for s_, p in zip((1, 2), _ragged_prompts(cfg, [40, 90], 35)):
+            ctx.prefill(s_, p)
+        ids = [1, 0, 2]
+    out = ctx.decode_frames(ids, stop + 3)
+    rows = out[:, ids.index(0)]
+    if decided:
+        assert np.array_equal(rows[:stop], np.stack([f["codes"] for f in frames]))
+        assert np.all(rows[stop:] == -1)
+    for s_ in range(len(ids)):  # once a stream's frame is -1, so is every later frame of the call
+        r = out[:, s_, 0]
+        first = int(np.argmax(r < 0)) if np.any(r < 0) else len(r)
+        assert np.all(out[first:, s_] == -1) and np.all(out[:first, s_] >= 0)
+    with pytest.raises(s2ar.S2arError):
+        ctx.decode_frames([0], 1)
+    live = [s_ for i, s_ in enumerate(ids) if s_ != 0 and np.all(out[:, i] >= 0)]
+    if live:
+        assert ctx.decode_frames(live, 1).shape == (1, len(live), 10)
+    ctx.prefill(0, toks[:3])
+    assert ctx.decode_frames([0], 1).shape == (1, 1, 10)
+    ctx.close()
