@@ -858,9 +858,10 @@ struct Enq {
       a.part_o = c->att_o;
       a.kv_bf16 = c->cfg.kv_dtype == 1;
       a.split = kAttnSplit;
-      a.fixed_slot = -1;
+      a.fixed_slot = slot;  // a frame graph belongs to one stream: no slot lookup on the device
       a.row_pos = nullptr;
       a.append = 1;
+      a.const_pos = is_slow ? -1 : fast_step - 1;
       if (is_slow) {
         a.rope_cos = c->rope_cos_s;
         a.rope_sin = c->rope_sin_s;
@@ -889,6 +890,7 @@ struct Enq {
     }
   }
   const int* fast_pos_ptr = nullptr;
+  int fast_step = 1;  // the Fast step j whose layers are being enqueued (position j - 1)
 
   // Slow final norm + head + constrained argmax -> codes[slot][0] and h[slot]; the finisher
   // also copies h into the Fast input and advances the stream's position
@@ -925,6 +927,7 @@ struct Enq {
         chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, c->d_slot_ids + slot, c->d_codes, j, xf,
                                    H, 1, s));
       fast_pos_ptr = c->d_fast_pos + (size_t)(j - 1) * g.max_streams;
+      fast_step = j;
       layers(false, slot, xf, tp && tp->fast_resid ? tp->fast_resid + (size_t)(j - 1) * Lf * H : nullptr);
       gemv(s2k::GEMV_NORM_ARGMAX, c->fast_head, c->fast_head_s, xf, c->fast_final, c->fast_logits, K, H,
            tp && tp->fast_z ? c->z : nullptr, 0, K);
@@ -1151,6 +1154,7 @@ struct Enq {
       a.fixed_slot = -1;
       a.row_pos = nullptr;
       a.append = 1;
+      a.const_pos = is_slow ? -1 : fast_step - 1;  // every stream's Fast step j sits at position j - 1
       if (is_slow) {
         a.rope_cos = c->rope_cos_s;
         a.rope_sin = c->rope_sin_s;
@@ -1236,6 +1240,7 @@ struct Enq {
       if (btp && j > 1)  // eager frame: the input honours forced codes
         chk(s2k::launch_fast_input(c->bf16, c->codebook, c->d_h, K, H, NC, slots, c->d_codes, j, c->bxf, ldx, M, s));
       tap_step = j - 1;
+      fast_step = j;
       int pending = layers_b(false, M, slots, c->bxf);
       fold_b(c->bxf, pending, H, M);
       mgemv(s2k::MG_ARGMAX, c->fast_head_t, c->bxf, ldx, c->blogits, K, K, H, M, 0, K, c->fast_final);

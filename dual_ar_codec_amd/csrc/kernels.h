@@ -68,6 +68,9 @@ struct AttnArgs {
   const float* qkv_part;
   int qkv_S;
   int qkv_ldp;
+  // >= 0: every row's position is this constant (the Fast AR's step j sits at position j - 1), and
+  // `pos` is not read
+  int const_pos;
 };
 // Attention of the new position over its context; a context longer than `split` is cut into
 // splits whose partial results launch_attention_combine merges (needed only when

@@ -750,41 +750,56 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
   using T = typename KV::T;
   constexpr int CH = WAVE;                   // positions per chunk, one per lane in the scores
   constexpr int NT = G * WAVE;               // threads
-  constexpr int KSTR = KVB ? D + 2 : D + 1;  // padded K row: consecutive lanes hit consecutive banks
+  constexpr int KSTR = KVB ? D + 8 : D + 4;  // K row padded by one 16-byte piece: 16-byte aligned rows
+                                             // whose 16-byte reads by consecutive lanes spread over the banks
   constexpr int PER = D / WAVE;
   constexpr int EP16 = 16 / sizeof(T);       // elements per 16-byte piece
   constexpr int CPR = D / EP16;              // 16-byte pieces per row
   constexpr int PIECES = CH * CPR / NT;      // K (and V) pieces per thread per chunk
   constexpr int MAXSPLIT = 256;
+  constexpr int MAXPG = MAXSPLIT / 16;       // pages of one split (page size 16)
   static_assert(CH * CPR % NT == 0, "tile pieces must divide evenly");
-  __shared__ float q_s[G][D];
+  __shared__ __attribute__((aligned(16))) float q_s[G][D];
   __shared__ float kn_s[D];
   __shared__ float vn_s[D];
   __shared__ __attribute__((aligned(16))) T k_s[CH * KSTR];
   __shared__ __attribute__((aligned(16))) T v_s[CH * D];
   __shared__ float p_s[G][CH];
   __shared__ int rowoff_s[MAXSPLIT];
+  __shared__ int page_s[MAXPG];
 
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
   const int slot = a.fixed_slot >= 0 ? a.fixed_slot : a.slots[b];
-  const int pos = a.row_pos ? a.row_pos[b] : a.pos[slot];
+  const int s0 = sp * a.split;
+  // The position and the page-table entries of this split's (at most 16) pages do not depend on
+  // each other: both loads go out together, so the cache offsets cost one round trip after the
+  // slot.  Entries past the stream's last page are read (in bounds of the table) but never used.
+  const int pg0 = s0 / a.page_size;
+  int pg = 0;
+  if (threadIdx.x < MAXPG && pg0 + (int)threadIdx.x < a.bt_stride)
+    pg = a.block_table[slot * a.bt_stride + pg0 + threadIdx.x];
+  // a single q|k|v row (batch 1) is read before the position too: its q head is needed whatever
+  // the position is (split partials, summed below, wait for the early exit instead)
+  constexpr int PERQ = D / WAVE;
+  float qv[PERQ];
+  if (a.qkv_S == 0) {
+    const float* qrow = a.qkv + (size_t)b * (a.Hq + 2 * a.Hkv) * D + (size_t)(g * G + w) * D;
+#pragma unroll
+    for (int i = 0; i < PERQ; ++i) qv[i] = qrow[lane + i * WAVE];
+  }
+  const int pos = a.const_pos >= 0 ? a.const_pos : (a.row_pos ? a.row_pos[b] : a.pos[slot]);
   const int ctx = pos + 1;
   const int nsplit = (ctx + a.split - 1) / a.split;
   if (sp >= nsplit) return;
-  const int s0 = sp * a.split, s1 = min(s0 + a.split, ctx);
+  const int s1 = min(s0 + a.split, ctx);
   const bool has_new = a.append && pos >= s0 && pos < s1;
   const int h = g * G + w;
   const float* qkv = a.qkv + (size_t)b * (a.Hq + 2 * a.Hkv) * D;
   T* kc = static_cast<T*>(a.k_cache);
   T* vc = static_cast<T*>(a.v_cache);
+  if (threadIdx.x < MAXPG) page_s[threadIdx.x] = pg;
 
-  // cache offsets of every position of the split: one page-table round trip
-  for (int t = threadIdx.x; t < s1 - s0; t += NT) {
-    const int jj = s0 + t;
-    const int page = a.block_table[slot * a.bt_stride + jj / a.page_size];
-    rowoff_s[t] = (int)((((size_t)page * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
-  }
   // this wave's q head (and, for wave 0 of the split holding pos, the new k and v)
   // element n of this row's q | k | v vector (summing the split partials in split order)
   auto qkv_at = [&](int n) -> float {
@@ -802,9 +817,10 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     }
     return v;
   };
-  float qv[PER], kv[PER], vv[PER];
+  float kv[PER], vv[PER];
+  if (a.qkv_S != 0)
 #pragma unroll
-  for (int i = 0; i < PER; ++i) qv[i] = qkv_at(h * D + lane + i * WAVE);
+    for (int i = 0; i < PER; ++i) qv[i] = qkv_at(h * D + lane + i * WAVE);
   const bool mk = has_new && w == 0;
   if (mk) {
 #pragma unroll
@@ -812,6 +828,12 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
       kv[i] = qkv_at((a.Hq + g) * D + lane + i * WAVE);
       vv[i] = qkv_at((a.Hq + a.Hkv + g) * D + lane + i * WAVE);
     }
+  }
+  __syncthreads();
+  // cache offsets of every position of the split
+  for (int t = threadIdx.x; t < s1 - s0; t += NT) {
+    const int jj = s0 + t;
+    rowoff_s[t] = (int)((((size_t)page_s[jj / a.page_size - pg0] * a.Hkv + g) * a.page_size + jj % a.page_size) * D);
   }
   __syncthreads();
 
@@ -852,7 +874,7 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) kv[i] = kv[i] * rk * a.k_norm[lane + i * WAVE];
       rope_lane<D>(kv, crow, srow, lane);
-      const int page = a.block_table[slot * a.bt_stride + pos / a.page_size];
+      const int page = page_s[pos / a.page_size - pg0];
       const size_t off = (((size_t)page * a.Hkv + g) * a.page_size + pos % a.page_size) * D;
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
@@ -865,9 +887,15 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     }
   }
 
-  float m_run = -INFINITY, l_run = 0.f, o_run[PER];
+  // Scores: lane j dots q with key j, reading the key row 16 bytes at a time into four partial sums
+  // (added in a fixed order).  Weighted sum: the lanes split into KG key groups x DG groups of eight
+  // dimensions; lane (kg, dg) accumulates keys kg, kg + KG, ... over its eight dimensions (one
+  // 16-byte V read per key for bf16), and the key groups are added by a butterfly at the end.
+  constexpr int DG = D / 8, KG = WAVE / DG;
+  const int dg = lane % DG, kg = lane / DG;
+  float m_run = -INFINITY, l_run = 0.f, o8[8];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) o_run[i] = 0.f;
+  for (int e = 0; e < 8; ++e) o8[e] = 0.f;
   for (int j0 = s0; j0 < s1; j0 += CH) {
     const int nv = min(CH, s1 - j0);
     const int jn = has_new ? pos - j0 : -1;  // row of the new position in this chunk (if any)
@@ -875,11 +903,7 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     for (int u = 0; u < PIECES; ++u) {
       const int pi = threadIdx.x + u * NT, j = pi / CPR, q = pi % CPR;
       if (j < nv && j != jn) {
-        uint32_t* kd = reinterpret_cast<uint32_t*>(k_s + j * KSTR + q * EP16);
-        kd[0] = kt[u].x;
-        kd[1] = kt[u].y;
-        kd[2] = kt[u].z;
-        kd[3] = kt[u].w;
+        *reinterpret_cast<u32x4*>(k_s + j * KSTR + q * EP16) = kt[u];
         *reinterpret_cast<u32x4*>(v_s + j * D + q * EP16) = vt[u];
       }
     }
@@ -896,10 +920,35 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     float s = -INFINITY;
     if (lane < nv) {
       const T* kr = k_s + lane * KSTR;
-      float acc = 0.f;
-#pragma unroll 16
-      for (int d = 0; d < D; ++d) acc = fmaf(q_s[w][d], KV::ld(kr, d), acc);
-      s = acc;
+      const float* qr = q_s[w];
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / EP16; ++c) {
+        const u32x4 kp = *reinterpret_cast<const u32x4*>(kr + c * EP16);
+        if constexpr (KVB) {
+          const f32x4 qa = *reinterpret_cast<const f32x4*>(qr + c * 8);
+          const f32x4 qb = *reinterpret_cast<const f32x4*>(qr + c * 8 + 4);
+          float t = acc[c & 3];
+          t = fmaf(qa.x, bf_lo(kp.x), t);
+          t = fmaf(qa.y, bf_hi(kp.x), t);
+          t = fmaf(qa.z, bf_lo(kp.y), t);
+          t = fmaf(qa.w, bf_hi(kp.y), t);
+          t = fmaf(qb.x, bf_lo(kp.z), t);
+          t = fmaf(qb.y, bf_hi(kp.z), t);
+          t = fmaf(qb.z, bf_lo(kp.w), t);
+          t = fmaf(qb.w, bf_hi(kp.w), t);
+          acc[c & 3] = t;
+        } else {
+          const f32x4 qa = *reinterpret_cast<const f32x4*>(qr + c * 4);
+          float t = acc[c & 3];
+          t = fmaf(qa.x, __uint_as_float(kp.x), t);
+          t = fmaf(qa.y, __uint_as_float(kp.y), t);
+          t = fmaf(qa.z, __uint_as_float(kp.z), t);
+          t = fmaf(qa.w, __uint_as_float(kp.w), t);
+          acc[c & 3] = t;
+        }
+      }
+      s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
     const float m_new = fmaxf(m_run, wave_max(s));
     const float p = (lane < nv) ? expf(s - m_new) : 0.f;
@@ -908,22 +957,49 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     p_s[w][lane] = p;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o_run[i] *= corr;
-#pragma unroll 8
-    for (int j = 0; j < nv; ++j) {
+    for (int e = 0; e < 8; ++e) o8[e] *= corr;
+    for (int j = kg; j < nv; j += KG) {
       const float pj = p_s[w][j];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) o_run[i] = fmaf(pj, KV::ld(v_s, (size_t)j * D + lane + i * WAVE), o_run[i]);
+      const T* vr = v_s + (size_t)j * D + dg * 8;
+      if constexpr (KVB) {
+        const u32x4 vp = *reinterpret_cast<const u32x4*>(vr);
+        o8[0] = fmaf(pj, bf_lo(vp.x), o8[0]);
+        o8[1] = fmaf(pj, bf_hi(vp.x), o8[1]);
+        o8[2] = fmaf(pj, bf_lo(vp.y), o8[2]);
+        o8[3] = fmaf(pj, bf_hi(vp.y), o8[3]);
+        o8[4] = fmaf(pj, bf_lo(vp.z), o8[4]);
+        o8[5] = fmaf(pj, bf_hi(vp.z), o8[5]);
+        o8[6] = fmaf(pj, bf_lo(vp.w), o8[6]);
+        o8[7] = fmaf(pj, bf_hi(vp.w), o8[7]);
+      } else {
+        const f32x4 va = *reinterpret_cast<const f32x4*>(vr);
+        const f32x4 vb = *reinterpret_cast<const f32x4*>(vr + 4);
+        o8[0] = fmaf(pj, va.x, o8[0]);
+        o8[1] = fmaf(pj, va.y, o8[1]);
+        o8[2] = fmaf(pj, va.z, o8[2]);
+        o8[3] = fmaf(pj, va.w, o8[3]);
+        o8[4] = fmaf(pj, vb.x, o8[4]);
+        o8[5] = fmaf(pj, vb.y, o8[5]);
+        o8[6] = fmaf(pj, vb.z, o8[6]);
+        o8[7] = fmaf(pj, vb.w, o8[7]);
+      }
     }
     m_run = m_new;
     __syncthreads();
   }
+  // add the key groups (a fixed butterfly: every lane of a dimension group ends with the same sum)
+#pragma unroll
+  for (int o = DG; o < WAVE; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o8[e] += __shfl_xor(o8[e], o, WAVE);
 
   if (nsplit == 1) {
-    float* out = a.out + ((size_t)b * a.Hq + h) * D;
-    const float inv = 1.0f / l_run;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) out[lane + i * WAVE] = o_run[i] * inv;
+    if (kg == 0) {
+      float* out = a.out + ((size_t)b * a.Hq + h) * D + dg * 8;
+      const float inv = 1.0f / l_run;
+      *reinterpret_cast<f32x4*>(out) = f32x4{o8[0] * inv, o8[1] * inv, o8[2] * inv, o8[3] * inv};
+      *reinterpret_cast<f32x4*>(out + 4) = f32x4{o8[4] * inv, o8[5] * inv, o8[6] * inv, o8[7] * inv};
+    }
     return;
   }
   const size_t pi = ((size_t)b * a.Hq + h) * a.max_splits + sp;
@@ -931,8 +1007,11 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     a.part_ml[pi * 2] = m_run;
     a.part_ml[pi * 2 + 1] = l_run;
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) a.part_o[pi * D + lane + i * WAVE] = o_run[i];
+  if (kg == 0) {
+    float* po = a.part_o + pi * D + dg * 8;
+    *reinterpret_cast<f32x4*>(po) = f32x4{o8[0], o8[1], o8[2], o8[3]};
+    *reinterpret_cast<f32x4*>(po + 4) = f32x4{o8[4], o8[5], o8[6], o8[7]};
+  }
 }
 
 // Merge the splits of every q head in split order.  grid = (Hq, M), one wavefront each.
@@ -940,7 +1019,8 @@ template <int D>
 __global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
   constexpr int PER = D / WAVE;
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int pos = a.row_pos ? a.row_pos[b] : a.pos[a.fixed_slot >= 0 ? a.fixed_slot : a.slots[b]];
+  const int pos = a.const_pos >= 0 ? a.const_pos
+                                   : (a.row_pos ? a.row_pos[b] : a.pos[a.fixed_slot >= 0 ? a.fixed_slot : a.slots[b]]);
   const int nsplit = (pos + 1 + a.split - 1) / a.split;
   if (nsplit == 1) return;  // the attention kernel wrote the output itself
   const size_t base = ((size_t)b * a.Hq + h) * a.max_splits;
@@ -962,7 +1042,7 @@ __global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.split > 256 || a.split % 64) return hipErrorInvalidValue;
+  if (a.split > 256 || a.split % 64 || a.page_size != 16) return hipErrorInvalidValue;
   const int G = a.Hq / a.Hkv;
   const dim3 grid(a.max_splits, a.Hkv, a.M);
 #define S2_ATT(DD, GG)                                                                         \
