@@ -800,33 +800,54 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
   T* vc = static_cast<T*>(a.v_cache);
   if (threadIdx.x < MAXPG) page_s[threadIdx.x] = pg;
 
-  // this wave's q head (and, for wave 0 of the split holding pos, the new k and v)
-  // element n of this row's q | k | v vector (summing the split partials in split order)
-  auto qkv_at = [&](int n) -> float {
-    if (a.qkv_S == 0) return qkv[n];
-    const float* p = a.qkv_part + (size_t)b * a.qkv_ldp + n;
-    const size_t st = (size_t)16 * a.qkv_ldp;
-    float v = 0.f;
-    for (int s0 = 0; s0 < a.qkv_S; s0 += 8) {  // eight loads in flight at a time
-      float t[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = (s0 + u < a.qkv_S) ? p[(s0 + u) * st] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < a.qkv_S) v += t[u];
+  // this wave's q head (and, for wave 0 of the split holding pos, the new k and v): elements
+  // n[i] of this row's q | k | v vector, each the sum of the split partials in split order; every
+  // partial of every element is loaded before the first add
+  auto qkv_sum = [&](const int* n, float* out, int cnt) {
+    if (a.qkv_S == 0) {
+      for (int i = 0; i < cnt; ++i) out[i] = qkv[n[i]];
+      return;
     }
-    return v;
+    const float* p = a.qkv_part + (size_t)b * a.qkv_ldp;
+    const size_t st = (size_t)16 * a.qkv_ldp;
+    for (int i = 0; i < cnt; ++i) out[i] = 0.f;
+    for (int s0 = 0; s0 < a.qkv_S; s0 += 8) {
+      float t[2 * PER][8];
+#pragma unroll
+      for (int i = 0; i < 2 * PER; ++i)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[i][u] = (i < cnt && s0 + u < a.qkv_S) ? p[(s0 + u) * st + n[i]] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 2 * PER; ++i)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i < cnt && s0 + u < a.qkv_S) out[i] += t[i][u];
+    }
   };
   float kv[PER], vv[PER];
-  if (a.qkv_S != 0)
+  if (a.qkv_S != 0) {
+    int n[2 * PER];
+    float o[2 * PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) qv[i] = qkv_at(h * D + lane + i * WAVE);
+    for (int i = 0; i < PER; ++i) n[i] = h * D + lane + i * WAVE;
+    qkv_sum(n, o, PER);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) qv[i] = o[i];
+  }
   const bool mk = has_new && w == 0;
   if (mk) {
+    int n[2 * PER];
+    float o[2 * PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      kv[i] = qkv_at((a.Hq + g) * D + lane + i * WAVE);
-      vv[i] = qkv_at((a.Hq + a.Hkv + g) * D + lane + i * WAVE);
+      n[i] = (a.Hq + g) * D + lane + i * WAVE;
+      n[PER + i] = (a.Hq + a.Hkv + g) * D + lane + i * WAVE;
+    }
+    qkv_sum(n, o, 2 * PER);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      kv[i] = o[i];
+      vv[i] = o[PER + i];
     }
   }
   __syncthreads();
