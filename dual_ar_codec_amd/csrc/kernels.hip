@@ -1045,16 +1045,40 @@ __global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
   const int nsplit = (pos + 1 + a.split - 1) / a.split;
   if (nsplit == 1) return;  // the attention kernel wrote the output itself
   const size_t base = ((size_t)b * a.Hq + h) * a.max_splits;
+  // the splits' (max, sum) are read one split per lane, 64 at a time, and each split's weight is
+  // passed from its lane; the sums still run in split order, so the loads of up to eight splits'
+  // outputs go out together instead of one dependent round trip per split
   float M = -INFINITY;
-  for (int c = 0; c < nsplit; ++c) M = fmaxf(M, a.part_ml[(base + c) * 2]);
+  for (int c0 = 0; c0 < nsplit; c0 += WAVE)
+    if (c0 + lane < nsplit) M = fmaxf(M, a.part_ml[(base + c0 + lane) * 2]);
+  M = wave_max(M);
   float L = 0.f, acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int c = 0; c < nsplit; ++c) {
-    const float e = expf(a.part_ml[(base + c) * 2] - M);
-    L = fmaf(e, a.part_ml[(base + c) * 2 + 1], L);
+  for (int c0 = 0; c0 < nsplit; c0 += WAVE) {
+    const int cn = min(WAVE, nsplit - c0);
+    float e = 0.f, l = 0.f;
+    if (lane < cn) {
+      e = expf(a.part_ml[(base + c0 + lane) * 2] - M);
+      l = a.part_ml[(base + c0 + lane) * 2 + 1];
+    }
+    for (int u0 = 0; u0 < cn; u0 += 8) {
+      float t[8][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = fmaf(e, a.part_o[(base + c) * D + lane + i * WAVE], acc[i]);
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          t[u][i] = (u0 + u < cn) ? a.part_o[(base + c0 + u0 + u) * D + lane + i * WAVE] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float eu = __shfl(e, u0 + u, WAVE), lu = __shfl(l, u0 + u, WAVE);
+        if (u0 + u < cn) {
+          L = fmaf(eu, lu, L);
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] = fmaf(eu, t[u][i], acc[i]);
+        }
+      }
+    }
   }
   float* out = a.out + ((size_t)b * a.Hq + h) * D;
   const float inv = 1.0f / L;
