@@ -285,9 +285,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.N % 128 || g.K % 32 || g.M < 1) return hipErrorInvalidValue;
-  // long prompts: the 8-wavefront kernel, with the largest tile that still fills the CUs
+  // the 8-wavefront kernel for every prompt length (rows past M repeat the last row and are not
+  // stored): at 64..200 rows it ran the full-shape prefill in 14-15 ms against 25-30 ms for the
+  // 4-wavefront kernel, which remains for K not divisible by 64
   if (g.epi == GEMM_SWIGLU ? (!g.c_hi || !g.c_lo) : !g.c) return hipErrorInvalidValue;
-  if (g.K % 64 == 0 && g.M >= 256) {
+  if (g.K % 64 == 0) {
     // Measured at P = 1200 on the full shape (copy-only stage loaders): the wide gate/up + SwiGLU
     // product runs best on 128 x 256 tiles (64 x 128 per wavefront; its store and add forms would
     // spill), the other shapes on 64 x 256 tiles, both with 8 wavefronts.
