@@ -116,6 +116,9 @@ struct s2ar_ctx {
 
   // batched prefill (MFMA): chunk of up to pch prompt rows
   int pch = 0;
+  // split-K partials of the prefill GEMMs of short prompts
+  float* pgemm_part = nullptr;
+  size_t pgemm_part_floats = 0;
   bool mfma_prefill = false;
   float *px = nullptr, *pqkv = nullptr;
   // prefill attention key splits: unnormalised outputs and row states of the splits
@@ -679,6 +682,8 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
       C_TRY(dev_alloc(c, &c->pattl, sizeof(uint16_t) * (size_t)c->pch * qd_s));
       C_TRY(dev_alloc(c, &c->pacth, sizeof(uint16_t) * (size_t)c->pch * st.ffn));
       C_TRY(dev_alloc(c, &c->pactl, sizeof(uint16_t) * (size_t)c->pch * st.ffn));
+      c->pgemm_part_floats = (size_t)4 * 256 * std::max(std::max(qkvd_s, 2 * st.ffn), H);
+      C_TRY(dev_alloc(c, &c->pgemm_part, sizeof(float) * c->pgemm_part_floats));
       std::vector<int> iota(g.max_context);
       for (int i = 0; i < g.max_context; ++i) iota[i] = i;
       C_TRY(dev_alloc(c, &c->d_iota, sizeof(int) * g.max_context));
@@ -979,6 +984,8 @@ struct Enq {
       ga.N = N;
       ga.K = K;
       ga.epi = epi;
+      ga.part = c->pgemm_part;
+      ga.part_floats = c->pgemm_part_floats;
       chk(s2k::launch_gemm(ga, s));
     };
     for (int l = 0; l < st.n_layers; ++l) {

@@ -119,6 +119,11 @@ struct GemmArgs {
   int ldc;
   int M, N, K;
   int epi;
+  // split-K workspace for short prompts ([splits][M][N] fp32 partials, part_floats capacity);
+  // nullptr: never split.  `split` is set by the launcher.
+  float* part;
+  size_t part_floats;
+  int split;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 // RMSNorm of M rows and the bf16 split of the result: hi/lo planes of x[m] * (scale[m] * gain),

@@ -168,10 +168,16 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / WN, wn = wv % WN;
   const int mt = (g.M + BM - 1) / BM, ntiles = mt * (g.N / BN);
-  const int xcd = blockIdx.x & 7, per = ntiles >> 3, rem = ntiles & 7;
-  const int tile = xcd * per + min(xcd, rem) + (int)(blockIdx.x >> 3);
+  int tile, ks = 0;
+  if (g.split > 1) {  // split K: block b takes slice b % split of tile b / split
+    tile = (int)blockIdx.x / g.split;
+    ks = (int)blockIdx.x % g.split;
+  } else {
+    const int xcd = blockIdx.x & 7, per = ntiles >> 3, rem = ntiles & 7;
+    tile = xcd * per + min(xcd, rem) + (int)(blockIdx.x >> 3);
+  }
   const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
-  const int nk = g.K / BK;
+  const int nk = g.K / BK / max(g.split, 1), kbeg = ks * nk;  // this block's stages
   (void)NT;
 
   // A rows of this thread: a_row0 + 8 i, columns 8 (lane % 8) .. + 7 of the stage, both planes
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   u32x4 ah0[AI], al0[AI], ah1[AI], al1[AI];
   u32x4 wr0[WI], wr1[WI];
   auto load = [&](int kt, u32x4 (&ah)[AI], u32x4 (&al)[AI], u32x4 (&wr)[WI]) {
-    const int k = min(kt, nk - 1) * BK;  // past the end: reload the last stage (never computed)
+    const int k = (kbeg + min(kt, nk - 1)) * BK;  // past the end: reload the last stage (never computed)
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       ah[i] = *reinterpret_cast<const u32x4*>(g.a_hi + a_off[i] + k);
@@ -258,6 +264,21 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   }
 
   // epilogue: lane holds rows 4 (lane/16) + r, column lane % 16 of each 16 x 16 tile
+  if (g.split > 1) {  // the slice's partial sums; k_gemm_split_reduce adds the slices and applies EPI
+    float* part = g.part + (size_t)ks * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+          if (m < g.M) part[(size_t)m * g.N + n] = acc[i][j][r];
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -283,6 +304,59 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
     }
 }
 
+// Sum of the K slices of a split GEMM, in slice order, and the GEMM's epilogue.  Thread (m, e):
+// column e (GEMM_STORE, GEMM_ADD) or the SwiGLU pair (2e, 2e + 1) of row m.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_split_reduce(const GemmArgs g) {
+  const int m = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const size_t slice = (size_t)g.M * g.N;
+  const float* p = g.part + (size_t)m * g.N;
+  if constexpr (EPI == GEMM_SWIGLU) {
+    if (2 * e + 1 >= g.N) return;
+    float gt = 0.f, up = 0.f;
+    for (int k = 0; k < g.split; ++k) {
+      gt += p[k * slice + 2 * e];
+      up += p[k * slice + 2 * e + 1];
+    }
+    const float y = gt / (1.0f + expf(-gt)) * up;
+    const uint32_t h = bf16_bits(y);
+    g.c_hi[(size_t)m * g.ldc + e] = (uint16_t)h;
+    g.c_lo[(size_t)m * g.ldc + e] = (uint16_t)bf16_bits(y - __uint_as_float(h << 16));
+  } else {
+    if (e >= g.N) return;
+    float v = 0.f;
+    for (int k = 0; k < g.split; ++k) v += p[k * slice + e];
+    if constexpr (EPI == GEMM_ADD) g.c[(size_t)m * g.ldc + e] += v;
+    else g.c[(size_t)m * g.ldc + e] = v;
+  }
+}
+
+// K slices for a GEMM whose tiles alone would leave the CUs idle (prompts of up to 512 rows): the
+// fewest of 2, 4 or 8 that give at least two blocks per CU, each slice a whole number of 64-wide
+// stages.  Full-shape prefill, unsplit -> split: 64 rows 13.9 -> 6.0 ms, 200 rows 14.6 -> 10.1,
+// 512 rows 18.0 -> 16.1; at 1200 rows splitting the O and down products cost 1.5 ms.
+static int gemm_splits(const GemmArgs& g, int ntiles) {
+  if (!g.part || g.M > 512) return 1;
+  int S = 1;
+  while (S < 8 && ntiles * S < 2 * device_cus() && (g.K / 64) % (2 * S) == 0 &&
+         (size_t)2 * S * g.M * g.N <= g.part_floats)
+    S *= 2;
+  return S;
+}
+
+template <int BM, int BN, int EPI>
+static hipError_t gemm2_launch(GemmArgs g, hipStream_t s) {
+  const int ntiles = (g.M + BM - 1) / BM * (g.N / BN);
+  g.split = gemm_splits(g, ntiles);
+  hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI>), dim3(ntiles * g.split), dim3(512), 0, s, g);
+  if (g.split > 1) {
+    const int cols = EPI == GEMM_SWIGLU ? g.N / 2 : g.N;
+    hipLaunchKernelGGL(k_gemm_split_reduce<EPI>, dim3((cols + 255) / 256, g.M), dim3(256), 0, s, g);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.N % 128 || g.K % 32 || g.M < 1) return hipErrorInvalidValue;
   // the 8-wavefront kernel for every prompt length (rows past M repeat the last row and are not
@@ -293,23 +367,15 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     // Measured at P = 1200 on the full shape (copy-only stage loaders): the wide gate/up + SwiGLU
     // product runs best on 128 x 256 tiles (64 x 128 per wavefront; its store and add forms would
     // spill), the other shapes on 64 x 256 tiles, both with 8 wavefronts.
-    const int mt128 = (g.M + 127) / 128, mt64 = (g.M + 63) / 64;
-    if (g.epi == GEMM_SWIGLU && g.N % 256 == 0 && g.N >= 16384) {
-      hipLaunchKernelGGL((k_gemm2<128, 256, 8, 2, GEMM_SWIGLU>), dim3(mt128 * (g.N / 256)), dim3(512), 0, s, g);
-      return hipGetLastError();
-    }
+    if (g.epi == GEMM_SWIGLU && g.N % 256 == 0 && g.N >= 16384) return gemm2_launch<128, 256, GEMM_SWIGLU>(g, s);
     if (g.N % 256 == 0) {
-      const dim3 grid(mt64 * (g.N / 256));
-      if (g.epi == GEMM_STORE) hipLaunchKernelGGL((k_gemm2<64, 256, 8, 2, GEMM_STORE>), grid, dim3(512), 0, s, g);
-      else if (g.epi == GEMM_ADD) hipLaunchKernelGGL((k_gemm2<64, 256, 8, 2, GEMM_ADD>), grid, dim3(512), 0, s, g);
-      else hipLaunchKernelGGL((k_gemm2<64, 256, 8, 2, GEMM_SWIGLU>), grid, dim3(512), 0, s, g);
-      return hipGetLastError();
+      if (g.epi == GEMM_STORE) return gemm2_launch<64, 256, GEMM_STORE>(g, s);
+      if (g.epi == GEMM_ADD) return gemm2_launch<64, 256, GEMM_ADD>(g, s);
+      return gemm2_launch<64, 256, GEMM_SWIGLU>(g, s);
     }
-    const dim3 grid(mt128 * (g.N / 128));
-    if (g.epi == GEMM_STORE) hipLaunchKernelGGL((k_gemm2<128, 128, 8, 2, GEMM_STORE>), grid, dim3(512), 0, s, g);
-    else if (g.epi == GEMM_ADD) hipLaunchKernelGGL((k_gemm2<128, 128, 8, 2, GEMM_ADD>), grid, dim3(512), 0, s, g);
-    else hipLaunchKernelGGL((k_gemm2<128, 128, 8, 2, GEMM_SWIGLU>), grid, dim3(512), 0, s, g);
-    return hipGetLastError();
+    if (g.epi == GEMM_STORE) return gemm2_launch<128, 128, GEMM_STORE>(g, s);
+    if (g.epi == GEMM_ADD) return gemm2_launch<128, 128, GEMM_ADD>(g, s);
+    return gemm2_launch<128, 128, GEMM_SWIGLU>(g, s);
   }
   const bool small = (long)((g.M + 127) / 128) * (g.N / 128) < 2L * device_cus();
   const int BM = small ? 64 : 128;
