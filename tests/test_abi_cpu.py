@@ -75,6 +75,9 @@ def _cfg(**over):
     ({"max_context": 0}, "max_context"),
     ({"slow.ffn": 770}, "multiples of 4"),
     ({"rope_theta": -1.0}, "rope_theta"),
+    ({"eos_id": 4096}, "eos_id"),        # a semantic id (tiny: 4096 text ids) cannot be the stop id
+    ({"eos_id": -2}, "eos_id"),
+    ({"head_slice": 2}, "head_slice"),
 ])
 def test_config_validation(L, over, needle):
     cfg = _cfg(**over)
@@ -82,6 +85,14 @@ def test_config_validation(L, over, needle):
     rc, h = s2ar.s2ar_create(s2ar.make_config(cfg), w, None)
     assert rc == -1 and h is None
     assert needle in s2ar.s2ar_last_error(None)
+
+
+@pytest.mark.parametrize("field,value,needle", [("weight_dtype", 4, "weight_dtype"), ("kv_dtype", 2, "kv_dtype")])
+def test_raw_config_fields_out_of_range(L, field, value, needle):
+    c = s2ar.make_config(_cfg())
+    setattr(c, field, value)
+    rc, h = s2ar.s2ar_create(c, [np.zeros(1, np.float32)], None)
+    assert rc == -1 and h is None and needle in s2ar.s2ar_last_error(None)
 
 
 def test_tensor_validation(L):
