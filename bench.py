@@ -284,6 +284,13 @@ def main():
     ctx_mid = n_prompt + args.steps // 2
     fb = metrics.frame_bytes(cfg, ctx_mid)
     gbps = fb["total"] * fps / 1e9
+    # the same frames again, each graph replay between its own pair of HIP events
+    ctx.release(0)
+    ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
+    fms = np.sort(ctx.time_frames(0, args.steps).astype(np.float64))
+    frame_events = {"frames": args.steps, "median_ms": round(float(np.median(fms)), 4),
+                    "p10_ms": round(float(np.percentile(fms, 10)), 4), "p90_ms": round(float(np.percentile(fms, 90)), 4),
+                    "min_ms": round(float(fms[0]), 4), "max_ms": round(float(fms[-1]), 4)}
 
     prefill = None
     if vc is not None:
@@ -368,6 +375,7 @@ def main():
         "frame_bytes": fb["total"],
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "frame_events": frame_events,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill": prefill,

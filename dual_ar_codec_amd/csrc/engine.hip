@@ -1782,6 +1782,33 @@ int s2ar_stream_position(const s2ar_ctx* c, int32_t sid, int32_t* pos_out) {
   return S2AR_OK;
 }
 
+int s2ar_time_frames(s2ar_ctx* c, int32_t sid, int32_t n_frames, float* ms_out) {
+  if (!c) return S2AR_E_ARG;
+  if (!ms_out || n_frames < 1 || n_frames > 4096)
+    return set_err(c, S2AR_E_ARG, "ms_out must be non-null and n_frames in [1, 4096]");
+  if (int rc = check_streams(c, &sid, 1, n_frames)) return rc;
+  int rc = 0;
+  Graph* gr = frame_graph(c, sid, &rc);
+  if (!gr) return rc;
+  if ((rc = order_after_user(c))) return rc;
+  if ((rc = ensure_pages(c, sid, c->pos[sid] + n_frames))) return rc;
+  std::vector<hipEvent_t> ev(2 * (size_t)n_frames, nullptr);
+  hipError_t e = hipSuccess;
+  for (size_t i = 0; i < ev.size() && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+  for (int f = 0; f < n_frames && e == hipSuccess; ++f) {
+    e = hipEventRecord(ev[2 * f], c->stream);
+    if (e == hipSuccess) e = hipGraphLaunch(gr->exec, c->stream);
+    if (e == hipSuccess) e = hipEventRecord(ev[2 * f + 1], c->stream);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  for (int f = 0; f < n_frames && e == hipSuccess; ++f) e = hipEventElapsedTime(&ms_out[f], ev[2 * f], ev[2 * f + 1]);
+  for (hipEvent_t x : ev)
+    if (x) hipEventDestroy(x);
+  if (e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("time frames: ") + hipGetErrorString(e));
+  c->pos[sid] += n_frames;
+  return S2AR_OK;
+}
+
 int s2ar_time_kernel(s2ar_ctx* c, int32_t which, int32_t iters, float* avg_ms, int64_t* bytes_out) {
   if (!c) return S2AR_E_ARG;
   if (which < 0 || which > 1 || iters < 1 || !avg_ms)

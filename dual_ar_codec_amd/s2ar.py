@@ -22,7 +22,7 @@ ERRORS = {-1: "S2AR_E_ARG", -2: "S2AR_E_RANGE", -3: "S2AR_E_CAPACITY", -4: "S2AR
 
 SYMBOLS = ("s2ar_create", "s2ar_prefill", "s2ar_decode_frame", "s2ar_decode_frames", "s2ar_release_stream",
            "s2ar_stream_position", "s2ar_destroy", "s2ar_last_error", "s2ar_error_name", "s2ar_debug_frame",
-           "s2ar_time_kernel", "s2ar_debug_frame_batch")
+           "s2ar_time_kernel", "s2ar_debug_frame_batch", "s2ar_share_prefix", "s2ar_time_frames")
 
 i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 
@@ -79,6 +79,7 @@ def lib():
         L.s2ar_debug_frame.argtypes = [vp, i32, vp, ctypes.POINTER(Taps)]
         L.s2ar_time_kernel.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i64)]
         L.s2ar_debug_frame_batch.argtypes = [vp, vp, i32, vp, ctypes.POINTER(Taps)]
+        L.s2ar_time_frames.argtypes = [vp, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -225,6 +226,12 @@ class Context:
         for o in outs:
             o["next_c0"] = int(o["next_c0"][0])
         return outs
+
+    def time_frames(self, stream_id, n_frames):
+        """Per-frame graph-replay durations (ms) of n_frames frames of one stream, from HIP events."""
+        out = np.zeros(int(n_frames), np.float32)
+        self._check(lib().s2ar_time_frames(self.h, int(stream_id), int(n_frames), _p(out)))
+        return out
 
     def time_kernel(self, which=0, iters=100):
         ms = ctypes.c_float()

@@ -206,6 +206,14 @@ int s2ar_debug_frame_batch(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n, 
  * one launch.  S2AR_E_ARG for another which, iters < 1 or a null avg_ms. */
 int s2ar_time_kernel(s2ar_ctx* ctx, int32_t which, int32_t iters, float* avg_ms, int64_t* bytes_out);
 
+/* Decode n_frames frames of one stream as decode_frames does (one frame-graph replay each, back to
+ * back on the context's stream) with a HIP event pair around every replay, and write each
+ * replay's duration in ms to ms_out[n_frames] (caller-owned host memory).  The stream advances by
+ * n_frames positions; the frames' codes are not returned (a stop id is not tracked here).
+ * Errors as decode_frames for one stream, and S2AR_E_ARG for a null ms_out or n_frames outside
+ * [1, 4096]. */
+int s2ar_time_frames(s2ar_ctx* ctx, int32_t stream_id, int32_t n_frames, float* ms_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,8 @@ def test_null_and_noop_calls(L):
     assert L.s2ar_prefill(None, 0, None, None, None, 1) == -1
     assert L.s2ar_decode_frame(None, None, 1, None) == -1
     assert L.s2ar_debug_frame(None, 0, None, None) == -1
+    assert L.s2ar_time_frames(None, 0, 1, None) == -1
+    assert L.s2ar_share_prefix(None, 0, 1, 1) == -1
     out = ctypes.c_void_p()
     assert L.s2ar_create(None, None, 0, None, ctypes.byref(out)) == -1
     assert out.value is None

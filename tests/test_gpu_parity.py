@@ -326,6 +326,24 @@ def test_errors_leave_state_unchanged():
     ctx.close()
 
 
+def test_time_frames_per_replay_events():
+    """s2ar_time_frames: one positive duration per frame, the stream advances like decode_frames, and
+    the next frame's codes equal a decode_frames run over the same frames."""
+    cfg = synth.config("tiny")
+    w = synth.make_weights(cfg)
+    toks, _, _ = synth.make_prompt(cfg)
+    ctx = _ctx(cfg, w, max_streams=2)
+    ctx.prefill(0, toks)
+    ctx.prefill(1, toks)
+    ms = ctx.time_frames(0, 3)
+    assert ms.shape == (3,) and np.all(ms > 0) and ctx.position(0) == len(toks) + 3
+    ctx.decode_frames([1], 3)
+    assert np.array_equal(ctx.decode_frames([0], 1), ctx.decode_frames([1], 1))
+    with pytest.raises(s2ar.S2arError):
+        ctx.time_frames(0, 0)
+    ctx.close()
+
+
 def test_time_kernel_gemv_and_stream_read():
     """The bench's timing entry: the gate/up GEMV and the plain streaming read of the same weights."""
     cfg = synth.config("mid")
