@@ -177,6 +177,37 @@ def slice_head(steps, cfg, w, toks, log):
             "note": "Slow head reads 4097 rows instead of 155776; the picks are those of the full head"}
 
 
+def mid_workload(log):
+    """The mid Dual-AR (8 + 2 layers, hidden 1024, bf16): its 64-token prompt, then its 32 greedy
+    frames timed as one call.  Its Fast working set (56.6 MB per step) fits in the 256 MB last-level
+    cache, so its GB/s is effective, not HBM: a probe of the per-launch overhead of a frame graph."""
+    import torch
+
+    from dual_ar_codec_amd import metrics, s2ar, synth
+
+    cfg = synth.config("mid")
+    w = synth.make_weights(cfg)
+    toks, _, _ = synth.make_prompt(cfg)
+    ctx = s2ar.Context(cfg, w, max_streams=1)
+    ctx.prefill(0, toks)
+    ctx.decode_frames([0], 3)
+    ctx.release(0)
+    ctx.prefill(0, toks)
+    n = cfg["frames"]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ctx.decode_frames([0], n)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ctx.close()
+    fb = metrics.frame_bytes(cfg, len(toks) + n // 2)
+    log(f"[bench] mid: {n / dt:.1f} frames/s")
+    return {"workload": f"mid: {len(toks)}-token prompt, {n} greedy frames, 1 stream",
+            "frames_per_s": round(n / dt, 1), "ms_per_frame": round(dt / n * 1e3, 4),
+            "frame_bytes": fb["total"], "effective_gbps": round(fb["total"] * n / dt / 1e9, 1),
+            "note": "the Fast working set fits in the last-level cache: effective GB/s, not a roofline claim"}
+
+
 def quant_weights(steps, fmt, cfg, w, toks, forced, ref, log):
     """Batch-1 frames/s with the layer matrices and heads as 8-bit codes (fmt "i8": int8, "f8": FP8
     E4M3) plus per-row scales (the same synthetic weights, quantised by the library at create), and
@@ -240,6 +271,7 @@ def main():
     ap.add_argument("--int8-steps", type=int, default=40, help="batch-1 frames with int8 weights (0 = skip)")
     ap.add_argument("--fp8-steps", type=int, default=40, help="batch-1 frames with FP8 E4M3 weights (0 = skip)")
     ap.add_argument("--slice-steps", type=int, default=60, help="batch-1 frames with the semantic-slice head (0 = skip)")
+    ap.add_argument("--mid", type=int, default=1, help="also time the mid workload (32 frames)")
     ap.add_argument("--prefix-share", type=int, default=1,
                     help="time to first frame of the voice-clone prompt with its 1000-position prefix shared")
     args = ap.parse_args()
@@ -340,6 +372,7 @@ def main():
     int8 = quant_weights(args.int8_steps, "i8", cfg, w, toks, forced, ref, log) if args.int8_steps > 0 else None
     fp8 = quant_weights(args.fp8_steps, "f8", cfg, w, toks, forced, ref, log) if args.fp8_steps > 0 else None
     sliced = slice_head(args.slice_steps, cfg, w, toks, log) if args.slice_steps > 0 else None
+    mid = mid_workload(log) if args.mid else None
 
     multi = multi_bf16 = None
     if args.multi_steps > 0:
@@ -360,6 +393,11 @@ def main():
     if args.cpu_budget > 0:
         log(f"[bench] CPU oracle baseline ({args.cpu_budget:.0f} s budget)")
         cpu = cpu_baseline(cfg, w, args.cpu_budget)
+        import oracle
+        oracle.set_threads(1)  # the same oracle on one core, a shorter sample
+        one = cpu_baseline(cfg, w, args.cpu_budget / 2)
+        oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+        cpu["single_thread"] = {"value": one["value"], "cores": 1, "sample": one["sample"]}
 
     line = {
         "metric": "frames/s at batch 1 (full S2 shape), with codebook tok/s, HBM GB/s and RTF",
@@ -384,6 +422,7 @@ def main():
         "int8": int8,
         "fp8": fp8,
         "semantic_slice_head": sliced,
+        "mid": mid,
     }
     print(json.dumps(line), flush=True)
 
