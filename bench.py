@@ -289,7 +289,8 @@ def main():
     n_prompt = synth.prompt_lengths(cfg)[0]
     vc = synth.config("voice_clone") if args.prefill else None
     vc_len = synth.prompt_lengths(vc)[0] if vc else 0
-    need = max(n_prompt + max(args.steps, args.warmup) + 1, vc_len + 2)
+    vc_frames = vc["frames"] if vc else 0
+    need = max(n_prompt + max(args.steps, args.warmup) + 1, vc_len + vc_frames + 2)
     if need > cfg["max_context"]:
         cfg = synth.config(args.config, max_context=(need + 63) // 64 * 64)
     log(f"[bench] generating {cfg['name']} weights ({synth.weight_bytes(cfg) / 1e9:.2f} GB)")
@@ -329,7 +330,8 @@ def main():
         # voice-clone prompt (1000 VQ positions + 200 text positions) on a second stream: the
         # prefill's projections run as MFMA GEMMs
         vt, vm, vcodes = synth.make_prompt(vc)
-        ctx.prefill(1, vt[:64], vm[:64], vcodes[:64])  # warm-up
+        ctx.prefill(1, vt[:64], vm[:64], vcodes[:64])  # warm-up; the decode captures stream 1's frame graph
+        ctx.decode_frames([1], 1)
         ctx.release(1)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -343,6 +345,15 @@ def main():
                    "tflop_s": round((lin + att) / pt / 1e12, 1), "peak_tflop_s": 2500.0,
                    "mfma_frac": round((lin + att) / pt / 1e12 / 2500.0, 4),
                    "note": "bf16 hi+lo split activations: 2 MFMA passes per algorithmic product"}
+        # the voice-clone workload's decode: 200 frames at contexts 1201..1400
+        t0 = time.perf_counter()
+        ctx.decode_frames([1], vc_frames)
+        torch.cuda.synchronize()
+        dt_vc = time.perf_counter() - t0
+        fb_vc = metrics.frame_bytes(cfg, vc_len + vc_frames // 2)
+        prefill["decode"] = {"frames": vc_frames, "frames_per_s": round(vc_frames / dt_vc, 2),
+                             "ms_per_frame": round(dt_vc / vc_frames * 1e3, 4), "frame_bytes": fb_vc["total"],
+                             "hbm_frac": round(fb_vc["total"] * vc_frames / dt_vc / 1e9 / HBM_PEAK_GBPS, 4)}
         ctx.release(1)
         if args.prefix_share:
             prefill["prefix_sharing"] = prefix_sharing(ctx, vc, vt, vm, vcodes)
