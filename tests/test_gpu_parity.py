@@ -83,6 +83,17 @@ def test_voice_clone_prefill_teacher_forced():
     assert rep["tokens_checked"] > 5
 
 
+def test_attention_merge_over_more_than_64_splits():
+    """A 4200-position context at batch 1: 66 attention splits of 64 positions, so the split merge
+    takes its (max, sum) pairs in two rounds of 64 lanes."""
+    cfg = synth.config("tiny", max_context=4288)
+    toks = synth.uniform_ints(78, 0, 4200, 0, cfg["vocab_text"])
+    mask = np.zeros(len(toks), np.uint8)
+    codes = np.zeros((len(toks), cfg["n_codebooks"]), np.int32)
+    rep = _teacher_forced("tiny", n_frames=2, prompt=(toks, mask, codes), max_context=4288)
+    assert rep["tokens_checked"] > 5
+
+
 def test_prefill_longer_than_one_row_block():
     """A 2100-position prompt at the mid shape: the matrix-core prefill runs it as two row blocks
     (2048 + 52), the second attending over the first block's cached keys."""
