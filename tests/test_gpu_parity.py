@@ -277,6 +277,23 @@ def test_int8_weights_full_teacher_forced():
     assert _int8_teacher_forced("full", 2)["tokens_checked"] > 0
 
 
+def test_int8_semantic_slice_head_with_stop_id_mid():
+    """The semantic-slice head built from quantised rows (the semantic rows plus the stop row, each
+    with its own scale) against the oracle's full head on the same int8 quantisation."""
+    cfg = synth.config("mid", head_slice=1, eos_id=7)
+    w = synth.make_weights(cfg)
+    ocfg, ow = quant_reference(cfg, w, "i8")
+    toks, _, _ = synth.make_prompt(cfg)
+    frames = oracle_run(ocfg, ow, toks, None, None, 4)
+    del ow
+    ctx = _ctx(dict(cfg, weight_dtype="i8"), w)
+    ctx.prefill(0, toks)
+    rep = compare_frames(ctx, 0, frames, cfg).finish()
+    _say(f"[parity] mid int8, slice head, stop id 7: {rep}")
+    ctx.close()
+    assert rep["tokens_checked"] > 0
+
+
 def test_fp8_weights_mid_teacher_forced():
     """FP8 E4M3 layer matrices and heads with per-row scales, decoded by gfx950's hardware
     conversion, against the oracle fed its own E4M3 quantisation: the bf16 acceptance bar."""
