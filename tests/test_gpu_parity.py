@@ -476,6 +476,51 @@ def test_batched_multi_stream_teacher_forced_full_shape():
     ctx.close()
 
 
+@pytest.mark.timeout(900)
+def test_batched_kernels_at_the_multi_stream_contexts_match_the_batch1_path():
+    """The 16-stream workload at its real shapes and contexts (full S2 shape, 920..3948 positions):
+    too long for the fp64 oracle, so the batched kernels are held to the batch-1 path, which the
+    oracle pins at the full shape.  Streams 16 and 17 repeat the shortest and the longest prompt;
+    one batched frame of streams 0..15 and one batch-1 frame of each repeat, forced with the same
+    codes, must agree to the acceptance bar."""
+    cfg = synth.config("multi_stream")
+    lens = synth.prompt_lengths(cfg)
+    w = synth.make_weights(cfg)
+    ctx = _ctx(cfg, w, max_streams=18)
+    del w
+    gc.collect()
+    prompts = [synth.make_prompt(cfg, i)[0] for i in range(16)]
+    for i, p in enumerate(prompts):
+        ctx.prefill(i, p)
+    lo, hi = int(np.argmin(lens)), int(np.argmax(lens))
+    ctx.prefill(16, prompts[lo])
+    ctx.prefill(17, prompts[hi])
+    forced = synth.uniform_ints(44, 0, 16 * 10, 0, cfg["codebook_size"]).reshape(16, 10).astype(np.int32)
+    outs = ctx.debug_frame_batch(list(range(16)), forced)
+    K, Vt = cfg["codebook_size"], cfg["vocab_text"]
+    rep = Report()
+    for src, rep_id in ((lo, 16), (hi, 17)):
+        one = ctx.debug_frame(rep_id, forced=forced[src])
+        b = outs[src]
+        tag = f"stream {src} ({lens[src]} positions)"
+        for l in range(cfg["slow"]["n_layers"]):
+            rep.cos(f"{tag} slow layer {l}", b["slow_resid"][l], one["slow_resid"][l].astype(np.float64))
+        rep.cos(f"{tag} slow h", b["slow_h"], one["slow_h"].astype(np.float64))
+        rep.logits(f"{tag} slow logits", b["slow_logits"], one["slow_logits"].astype(np.float64))
+        srt = np.sort(one["slow_logits"][Vt:Vt + K].astype(np.float64))
+        rep.token(f"{tag} next c0", int(b["next_c0"]), int(one["next_c0"]), srt[-1] - srt[-2])
+        for j in range(9):
+            for l in range(cfg["fast"]["n_layers"]):
+                rep.cos(f"{tag} fast step {j + 1} layer {l}", b["fast_resid"][j, l], one["fast_resid"][j, l].astype(np.float64))
+            fl = one["fast_logits"][j].astype(np.float64)
+            rep.logits(f"{tag} fast step {j + 1} logits", b["fast_logits"][j], fl)
+            srt = np.sort(fl)
+            rep.token(f"{tag} c{j + 1}", int(b["own_codes"][j + 1]), int(one["own_codes"][j + 1]), srt[-1] - srt[-2])
+    r = rep.finish()
+    _say(f"[parity] batched vs batch-1 at contexts {min(lens)}..{max(lens)}: {r}")
+    ctx.close()
+
+
 def test_batched_graph_equals_eager_batched_frame():
     cfg = synth.config("mid", max_context=256)
     w = synth.make_weights(cfg)
