@@ -191,6 +191,39 @@ def test_graph_replay_equals_debug_path_and_is_deterministic():
         assert np.array_equal(runs[0][t], f["codes"]), f"frame {t}"
 
 
+@pytest.mark.timeout(900)
+def test_full_workload_graph_replay_in_the_bench_configuration():
+    """The timed workload as bench.py runs it (full shape, 41-token prompt, context capacity 1408 and
+    three stream slots, so the split merges are live): 60 graph-replayed frames, the first 8 equal
+    to the eager path bit for bit and the free-running frames equal to the oracle's up to the first
+    decision with a thin margin."""
+    cfg = synth.config("full", max_context=1408)
+    w = synth.make_weights(cfg)
+    toks, _, _ = synth.make_prompt(cfg)
+    ctx = _ctx(cfg, w, max_streams=3)
+    ctx.prefill(0, toks)
+    graph = ctx.decode_frames([0], 60)[:, 0]
+    assert np.all((graph >= 0) & (graph < cfg["codebook_size"]))
+    ctx.prefill(1, toks)
+    eager = np.stack([ctx.debug_frame(1)["own_codes"] for _ in range(8)])
+    assert np.array_equal(eager, graph[:8]), "graph replay and the eager path disagree"
+    ctx.close()
+    frames = oracle_run(cfg, w, toks, None, None, 4)
+    checked = 0  # picks in decode order (c0, c1 .. c9 of frame 0, then frame 1 ..) up to a thin margin
+    done = False
+    for t, f in enumerate(frames):
+        for k, m in enumerate([f["c0_margin"], *f["fast"]["margins"]]):
+            if m <= 5e-2:
+                done = True
+                break
+            assert graph[t][k] == f["codes"][k], f"frame {t} code {k}"
+            checked += 1
+        if done:
+            break
+    assert checked > 0
+    _say(f"[parity] full workload, bench configuration: {checked} free-running picks equal to the oracle's")
+
+
 @pytest.mark.parametrize("n_shared", [64, 37])
 def test_shared_prefix_streams(n_shared):
     """Two streams share the first n_shared positions of a VQ-masked prompt (whole pages by
