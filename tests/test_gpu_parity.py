@@ -262,6 +262,26 @@ def test_shared_prefix_streams(n_shared):
     ctx.close()
 
 
+def test_shared_prefix_streams_batched():
+    """Two streams sharing the first 37 positions (two whole pages by reference and a copied partial
+    page) decode together through the batched kernels and match the oracle on their full prompts."""
+    cfg = synth.config("mid", max_context=256)
+    w = synth.make_weights(cfg)
+    r = np.random.default_rng(19)
+    n, n_shared = 90, 37
+    base = r.integers(0, cfg["vocab_text"], n).astype(np.int32)
+    other = r.integers(0, cfg["vocab_text"], n).astype(np.int32)
+    other[:n_shared] = base[:n_shared]
+    refs = [oracle_run(cfg, w, t, None, None, 3) for t in (base, other)]
+    ctx = _ctx(cfg, w, max_streams=2)
+    ctx.prefill(0, base)
+    ctx.share_prefix(0, 1, n_shared)
+    ctx.prefill(1, other[n_shared:])
+    rep = _compare_batch(ctx, [0, 1], refs, cfg, Report()).finish()
+    _say(f"[parity] shared prefix, batched: {rep}")
+    ctx.close()
+
+
 def test_shared_prefix_errors_leave_state_unchanged():
     cfg = synth.config("tiny")
     w = synth.make_weights(cfg)
