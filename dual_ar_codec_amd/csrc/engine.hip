@@ -29,6 +29,20 @@ constexpr int kMaxStreams = 256;
 // context positions per batch-1 attention workgroup: at the voice-clone contexts (1201..1400) 64
 // decodes 254.8 frames/s against 249.2 for 128 and 237.0 for 256; at a context of 100 the three agree
 constexpr int kAttnSplit = 64;
+// a Slow context of at most kShortCtx positions is attended by one workgroup per KV head (one split
+// of kShortCtx positions), so its frame needs no split merge launch at all
+constexpr int kShortCtx = 128;
+
+// Slow attention split of a frame whose Slow step attends over ctx positions: (positions per
+// workgroup, splits).  Every path (captured graphs, eager frames) uses this one rule, so they agree
+// bit for bit.
+struct SlowSplit {
+  int split, nsplit;
+};
+SlowSplit slow_split_for(int ctx) {
+  if (ctx <= kShortCtx) return {kShortCtx, 1};
+  return {kAttnSplit, (ctx + kAttnSplit - 1) / kAttnSplit};
+}
 // prefill attention: at most this many 64-key tiles per workgroup (longer causal ranges are split)
 constexpr int kPrefillAttnTiles = 8;
 
@@ -63,7 +77,7 @@ struct s2ar_ctx {
   hipStream_t user_stream = nullptr;
   hipStream_t stream = nullptr;
   hipEvent_t ev_order = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
-  std::vector<void*> dev_allocs;
+  std::vector<std::pair<void*, size_t>> dev_allocs;  // every device block and its size
   std::vector<void*> host_allocs;
 
   // weights
@@ -142,7 +156,7 @@ struct s2ar_ctx {
   size_t h_taps_floats = 0;
   int* h_small = nullptr;  // small int staging (forced codes, own picks)
 
-  std::map<int, Graph> graphs;  // per stream id
+  std::map<int, Graph> graphs;  // per (stream id, attention bucket)
 
   // batched multi-stream decode (up to 16 streams per launch, MFMA GEMVs)
   bool batched_ok = false;
@@ -243,6 +257,10 @@ int validate_config(const s2ar_config* c, std::string& why) {
     why = "head_slice must be 0 (full head) or 1 (semantic rows plus the eos_id row)";
     return -1;
   }
+  if ((c->dev_alloc == nullptr) != (c->dev_free == nullptr)) {
+    why = "dev_alloc and dev_free must both be set or both be NULL";
+    return -1;
+  }
   if (!(c->rope_theta > 0.0) || !(c->rms_eps >= 0.0)) {
     why = "rope_theta must be > 0 and rms_eps >= 0";
     return -1;
@@ -297,14 +315,24 @@ float round_to_bf16(float f) {
   return f;
 }
 
+// One zeroed device block, from the caller's allocator when the config names one, else hipMalloc.
 template <typename T>
 int dev_alloc(s2ar_ctx* c, T** p, size_t bytes) {
   void* q = nullptr;
-  hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
-  if (e != hipSuccess) return set_err(c, e == hipErrorOutOfMemory ? S2AR_E_NOMEM : S2AR_E_DEVICE,
-                                      std::string("hipMalloc: ") + hipGetErrorString(e));
-  c->dev_allocs.push_back(q);
-  e = hipMemset(q, 0, bytes ? bytes : 16);
+  bytes = bytes ? bytes : 16;
+  if (c->cfg.dev_alloc) {
+    q = c->cfg.dev_alloc((uint64_t)bytes, c->cfg.alloc_user);
+    if (!q) return set_err(c, S2AR_E_NOMEM, "dev_alloc returned NULL for " + std::to_string(bytes) + " bytes");
+    c->dev_allocs.push_back({q, bytes});
+    if (reinterpret_cast<uintptr_t>(q) % 256)
+      return set_err(c, S2AR_E_ARG, "dev_alloc returned a pointer not aligned to 256 bytes");
+  } else {
+    hipError_t e = hipMalloc(&q, bytes);
+    if (e != hipSuccess) return set_err(c, e == hipErrorOutOfMemory ? S2AR_E_NOMEM : S2AR_E_DEVICE,
+                                        std::string("hipMalloc: ") + hipGetErrorString(e));
+    c->dev_allocs.push_back({q, bytes});
+  }
+  hipError_t e = hipMemset(q, 0, bytes);
   if (e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("hipMemset: ") + hipGetErrorString(e));
   *p = static_cast<T*>(q);
   return 0;
@@ -492,7 +520,10 @@ void free_ctx(s2ar_ctx* c) {
     if (kv.second.g.exec) hipGraphExecDestroy(kv.second.g.exec);
     if (kv.second.g.g) hipGraphDestroy(kv.second.g.g);
   }
-  for (void* p : c->dev_allocs) hipFree(p);
+  for (const auto& b : c->dev_allocs) {
+    if (c->cfg.dev_free) c->cfg.dev_free(b.first, (uint64_t)b.second, c->cfg.alloc_user);
+    else hipFree(b.first);
+  }
   for (void* p : c->host_allocs) hipHostFree(p);
   if (c->ev_order) hipEventDestroy(c->ev_order);
   if (c->ev_t0) hipEventDestroy(c->ev_t0);
@@ -626,6 +657,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     }
   }
   c->stream_pages.assign(g.max_streams, {});
+  for (auto& sp : c->stream_pages) sp.reserve(c->bt_stride);  // appends never reallocate
   c->page_refs.assign(c->n_pages, 0);
 
   // state
@@ -781,6 +813,23 @@ struct Enq {
   s2ar_ctx* c;
   hipStream_t s;
   hipError_t e = hipSuccess;
+  // scratch of the frame's kernels: greedy-pick partials and Slow attention split partials
+  float* ws_am_val = c->am_val;
+  int* ws_am_idx = c->am_idx;
+  float* ws_att_ml = c->att_ml;
+  float* ws_att_o = c->att_o;
+  // Slow attention: positions per workgroup and grid extent along the context (splits past the
+  // stream's context exit at once); a merge launch follows when slow_max_splits > 1
+  int slow_split = kAttnSplit;
+  int slow_max_splits = c->max_splits;
+  // the split rule of a frame whose Slow step attends over ctx positions; exact: a grid of exactly
+  // the splits needed (eager frames), else the context's capacity (a captured graph serves every
+  // context of its bucket)
+  void set_slow_ctx(int ctx, bool exact) {
+    const SlowSplit ss = slow_split_for(ctx);
+    slow_split = ss.split;
+    slow_max_splits = ss.nsplit == 1 ? 1 : (exact ? ss.nsplit : c->max_splits);
+  }
   void chk(hipError_t r) {
     if (e == hipSuccess && r != hipSuccess) e = r;
   }
@@ -806,8 +855,8 @@ struct Enq {
     a.K = K;
     a.am_lo = lo;
     a.am_hi = hi;
-    a.am_val = c->am_val;
-    a.am_idx = c->am_idx;
+    a.am_val = ws_am_val;
+    a.am_idx = ws_am_idx;
     chk(s2k::launch_gemv(kind, c->bf16, a, s));
   }
 
@@ -818,8 +867,8 @@ struct Enq {
     const s2ar_config& g = c->cfg;
     const int rb = s2k::argmax_block_rows();
     s2k::FinishArgs f{};
-    f.am_val = c->am_val;
-    f.am_idx = c->am_idx;
+    f.am_val = ws_am_val;
+    f.am_idx = ws_am_idx;
     f.b0 = lo / rb;
     f.b1 = (hi - 1) / rb;
     f.lo = lo;
@@ -861,10 +910,10 @@ struct Enq {
       a.eps = (float)c->cfg.rms_eps;
       a.scale = (float)(1.0 / std::sqrt((double)D));
       a.out = c->att;
-      a.part_ml = c->att_ml;
-      a.part_o = c->att_o;
+      a.part_ml = ws_att_ml;
+      a.part_o = ws_att_o;
       a.kv_bf16 = c->cfg.kv_dtype == 1;
-      a.split = kAttnSplit;
+      a.split = is_slow ? slow_split : kAttnSplit;
       a.fixed_slot = slot;  // a frame graph belongs to one stream: no slot lookup on the device
       a.row_pos = nullptr;
       a.append = 1;
@@ -877,7 +926,7 @@ struct Enq {
         a.v_cache = c->kv_v + (size_t)l * c->kv_layer;
         a.block_table = c->d_bt;
         a.bt_stride = c->bt_stride;
-        a.max_splits = c->max_splits;
+        a.max_splits = slow_max_splits;
       } else {
         a.rope_cos = c->rope_cos_f;
         a.rope_sin = c->rope_sin_f;
@@ -1345,8 +1394,13 @@ int check_streams(s2ar_ctx* c, const int32_t* ids, int32_t n, int frames) {
   return 0;
 }
 
-Graph* frame_graph(s2ar_ctx* c, int slot, int* rc) {
-  auto it = c->graphs.find(slot);
+// Frame graphs of a stream: one for frames whose Slow context fits one attention workgroup
+// (bucket 0, no split merge) and one for longer contexts (bucket 1).
+int frame_bucket(int ctx) { return slow_split_for(ctx).nsplit == 1 ? 0 : 1; }
+
+Graph* frame_graph(s2ar_ctx* c, int slot, int bucket, int* rc) {
+  const int key = slot * 2 + bucket;
+  auto it = c->graphs.find(key);
   if (it != c->graphs.end()) return &it->second;
   Graph g;
   hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal);
@@ -1355,6 +1409,7 @@ Graph* frame_graph(s2ar_ctx* c, int slot, int* rc) {
     return nullptr;
   }
   Enq q{c, c->stream};
+  q.set_slow_ctx(bucket == 0 ? 1 : c->cfg.max_context, false);
   q.frame(slot, nullptr);
   e = hipStreamEndCapture(c->stream, &g.g);
   if (q.e != hipSuccess || e != hipSuccess) {
@@ -1368,7 +1423,7 @@ Graph* frame_graph(s2ar_ctx* c, int slot, int* rc) {
     *rc = set_err(c, S2AR_E_DEVICE, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
     return nullptr;
   }
-  return &(c->graphs[slot] = g);
+  return &(c->graphs[key] = g);
 }
 
 s2ar_ctx::BatchGraph* batch_graph(s2ar_ctx* c, const std::vector<int>& ids, int* rc) {
@@ -1507,16 +1562,33 @@ int s2ar_prefill(s2ar_ctx* c, int32_t sid, const int32_t* tokens, const uint8_t*
   return S2AR_OK;
 }
 
-// A frame whose semantic code is -1 is the stream's stop: it and every later frame of the call come
-// out as -1 (the device kept running the stream's graph, on clamped codes), and the stream ends.
-void mark_stops(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_frames, int32_t* codes_out) {
+// Advance the streams by the call's frames.  A frame whose semantic code is -1 is the stream's stop:
+// it and every later frame of the call come out as -1 and the stream ends.  The device kept running
+// the stream's graph after the stop, appending a Slow position per frame built from clamped codes;
+// frame f of the call appended position p0 + f, and the stop pick of frame f came from the position
+// before it, so the stream is rewound to p0 + f on the host and the device: its cache then holds
+// exactly the positions the model decoded, and a later prefill appends after them.
+int finish_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_frames, int32_t* codes_out) {
   const int NC = c->cfg.n_codebooks;
-  for (int i = 0; i < n; ++i)
+  for (int i = 0; i < n; ++i) {
+    const int p0 = c->pos[ids[i]];
+    int stop = -1;
     for (int f = 0; f < n_frames; ++f) {
       int32_t* row = codes_out + ((size_t)f * n + i) * NC;
-      if (row[0] < 0) c->ended[ids[i]] = 1;
-      if (c->ended[ids[i]]) std::fill(row, row + NC, -1);
+      if (stop < 0 && row[0] < 0) stop = f;
+      if (stop >= 0) std::fill(row, row + NC, -1);
     }
+    if (stop < 0) {
+      c->pos[ids[i]] = p0 + n_frames;
+    } else {
+      c->ended[ids[i]] = 1;
+      c->pos[ids[i]] = p0 + stop;
+      c->h_pos_stage[0] = p0 + stop;
+      HIP_TRY(c, hipMemcpyAsync(c->d_pos + ids[i], c->h_pos_stage, sizeof(int), hipMemcpyHostToDevice, c->stream));
+      HIP_TRY(c, hipStreamSynchronize(c->stream));  // the pinned staging is reused
+    }
+  }
+  return S2AR_OK;
 }
 
 int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_frames, int32_t* codes_out) {
@@ -1553,16 +1625,16 @@ int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_fra
                       sizeof(int) * NC);
       done += chunk;
     }
-    for (int i = 0; i < n; ++i) c->pos[ids[i]] += n_frames;
-    mark_stops(c, ids, n, n_frames, codes_out);
-    return S2AR_OK;
+    return finish_frames(c, ids, n, n_frames, codes_out);
   }
-  std::vector<Graph*> gs(n);
-  for (int i = 0; i < n; ++i) {
-    int rc = 0;
-    gs[i] = frame_graph(c, ids[i], &rc);
-    if (!gs[i]) return rc;
-  }
+  // the graphs of every bucket the call's frames reach, captured before any work is queued
+  std::vector<Graph*> gs(2 * (size_t)n, nullptr);
+  for (int i = 0; i < n; ++i)
+    for (int b = frame_bucket(c->pos[ids[i]] + 1); b <= frame_bucket(c->pos[ids[i]] + n_frames); ++b) {
+      int rc = 0;
+      gs[2 * i + b] = frame_graph(c, ids[i], b, &rc);
+      if (!gs[2 * i + b]) return rc;
+    }
   if (int rc = order_after_user(c)) return rc;
   for (int i = 0; i < n; ++i)
     if (int rc = ensure_pages(c, ids[i], c->pos[ids[i]] + n_frames)) return rc;
@@ -1571,7 +1643,9 @@ int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_fra
     const int chunk = std::min(n_frames - done, c->h_codes_frames * c->cfg.max_streams / n);
     for (int f = 0; f < chunk; ++f)
       for (int i = 0; i < n; ++i) {
-        HIP_TRY(c, hipGraphLaunch(gs[i]->exec, c->stream));
+        // frame done + f of stream i: its Slow step attends over pos + done + f + 1 positions
+        const Graph* gr = gs[2 * i + frame_bucket(c->pos[ids[i]] + done + f + 1)];
+        HIP_TRY(c, hipGraphLaunch(gr->exec, c->stream));
         HIP_TRY(c, hipMemcpyAsync(c->h_codes + ((size_t)f * n + i) * NC, c->d_snap + (size_t)ids[i] * NC,
                                   sizeof(int) * NC, hipMemcpyDeviceToHost, c->stream));
       }
@@ -1579,9 +1653,7 @@ int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_fra
     std::memcpy(codes_out + (size_t)done * n * NC, c->h_codes, sizeof(int) * (size_t)chunk * n * NC);
     done += chunk;
   }
-  for (int i = 0; i < n; ++i) c->pos[ids[i]] += n_frames;
-  mark_stops(c, ids, n, n_frames, codes_out);
-  return S2AR_OK;
+  return finish_frames(c, ids, n, n_frames, codes_out);
 }
 
 int s2ar_decode_frame(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t* codes_out) {
@@ -1623,6 +1695,7 @@ int s2ar_debug_frame(s2ar_ctx* c, int32_t sid, const int32_t* forced, s2ar_taps*
   if (int rc = order_after_user(c)) return rc;
   if (int rc = ensure_pages(c, sid, c->pos[sid] + 1)) return rc;
   Enq q{c, c->stream};
+  q.set_slow_ctx(c->pos[sid] + 1, true);
   q.frame(sid, &tp);
   if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("debug frame: ") + hipGetErrorString(q.e));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
@@ -1770,7 +1843,10 @@ int s2ar_share_prefix(s2ar_ctx* c, int32_t src, int32_t dst, int32_t n) {
       }
   }
   HIP_TRY(c, hipMemcpyAsync(c->d_bt + dst * c->bt_stride, bt, sizeof(int) * dp.size(), hipMemcpyHostToDevice, c->stream));
-  HIP_TRY(c, hipStreamSynchronize(c->stream));  // the pinned block-table row may change on the next call
+  // the device position too: the next prefill (position by position, or its last row) appends at n
+  c->h_pos_stage[0] = n;
+  HIP_TRY(c, hipMemcpyAsync(c->d_pos + dst, c->h_pos_stage, sizeof(int), hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(c, hipStreamSynchronize(c->stream));  // the pinned staging may change on the next call
   c->pos[dst] = n;
   c->ready[dst] = 0;
   c->ended[dst] = 0;
@@ -1788,16 +1864,20 @@ int s2ar_time_frames(s2ar_ctx* c, int32_t sid, int32_t n_frames, float* ms_out) 
   if (!c) return S2AR_E_ARG;
   if (!ms_out || n_frames < 1 || n_frames > 4096)
     return set_err(c, S2AR_E_ARG, "ms_out must be non-null and n_frames in [1, 4096]");
+  if (c->cfg.eos_id >= 0)
+    return set_err(c, S2AR_E_ARG, "time_frames returns no codes, so it cannot see a stop: use a context without eos_id");
   if (int rc = check_streams(c, &sid, 1, n_frames)) return rc;
   int rc = 0;
-  Graph* gr = frame_graph(c, sid, &rc);
-  if (!gr) return rc;
+  Graph* grs[2] = {nullptr, nullptr};
+  for (int b = frame_bucket(c->pos[sid] + 1); b <= frame_bucket(c->pos[sid] + n_frames); ++b)
+    if (!(grs[b] = frame_graph(c, sid, b, &rc))) return rc;
   if ((rc = order_after_user(c))) return rc;
   if ((rc = ensure_pages(c, sid, c->pos[sid] + n_frames))) return rc;
   std::vector<hipEvent_t> ev(2 * (size_t)n_frames, nullptr);
   hipError_t e = hipSuccess;
   for (size_t i = 0; i < ev.size() && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
   for (int f = 0; f < n_frames && e == hipSuccess; ++f) {
+    const Graph* gr = grs[frame_bucket(c->pos[sid] + f + 1)];
     e = hipEventRecord(ev[2 * f], c->stream);
     if (e == hipSuccess) e = hipGraphLaunch(gr->exec, c->stream);
     if (e == hipSuccess) e = hipEventRecord(ev[2 * f + 1], c->stream);

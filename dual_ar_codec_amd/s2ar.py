@@ -37,11 +37,18 @@ class Stack(ctypes.Structure):
     _fields_ = [(n, i32) for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn")]
 
 
+# device-memory callbacks of s2ar_config: void* dev_alloc(uint64 bytes, void* user),
+# void dev_free(void* ptr, uint64 bytes, void* user)
+DEV_ALLOC = ctypes.CFUNCTYPE(vp, ctypes.c_uint64, vp)
+DEV_FREE = ctypes.CFUNCTYPE(None, vp, ctypes.c_uint64, vp)
+
+
 class Config(ctypes.Structure):
     _fields_ = [("slow", Stack), ("fast", Stack), ("vocab_text", i32), ("n_codebooks", i32),
                 ("codebook_size", i32), ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double),
                 ("weight_dtype", i32), ("rope_bf16", i32), ("max_streams", i32), ("max_context", i32),
-                ("page_size", i32), ("kv_dtype", i32), ("eos_id", i32), ("head_slice", i32)]
+                ("page_size", i32), ("kv_dtype", i32), ("eos_id", i32), ("head_slice", i32),
+                ("dev_alloc", DEV_ALLOC), ("dev_free", DEV_FREE), ("alloc_user", vp)]
 
 
 class Tensor(ctypes.Structure):
@@ -127,10 +134,31 @@ def s2ar_last_error(ctx=None) -> str:
     return lib().s2ar_last_error(ctx).decode()
 
 
-class Context:
-    """One s2ar context: weights resident in HBM, per-stream KV pages and state."""
+def torch_allocator():
+    """(alloc, free) over PyTorch's caching allocator on the current device and stream: the
+    context's device memory then belongs to torch's pool."""
+    import torch
 
-    def __init__(self, cfg: dict, weights: list, max_streams: int | None = None, hip_stream="torch"):
+    dev = torch.cuda.current_device()
+    stream = torch.cuda.current_stream()
+
+    def alloc(nbytes):
+        return torch.cuda.caching_allocator_alloc(int(nbytes), dev, stream)
+
+    def free(ptr, nbytes):
+        torch.cuda.caching_allocator_delete(ptr)
+
+    return alloc, free
+
+
+class Context:
+    """One s2ar context: weights resident in HBM, per-stream KV pages and state.
+
+    allocator: None (the library's hipMalloc), "torch" (PyTorch's caching allocator) or a pair
+    (alloc(nbytes) -> device pointer int or 0, free(ptr, nbytes)) of Python callables."""
+
+    def __init__(self, cfg: dict, weights: list, max_streams: int | None = None, hip_stream="torch",
+                 allocator=None):
         self.cfg = cfg
         self.NC = cfg["n_codebooks"]
         self.H = cfg["slow"]["hidden"]
@@ -138,6 +166,12 @@ class Context:
         self.K = cfg["codebook_size"]
         self._weights = [np.ascontiguousarray(w) for w in weights]
         self.ccfg = make_config(cfg, max_streams)
+        if allocator is not None:
+            alloc, free = torch_allocator() if allocator == "torch" else allocator
+            # the callbacks must outlive the context: the library calls dev_free in s2ar_destroy
+            self._cb = (DEV_ALLOC(lambda nbytes, user: alloc(nbytes) or None),
+                        DEV_FREE(lambda ptr, nbytes, user: free(ptr, nbytes)))
+            self.ccfg.dev_alloc, self.ccfg.dev_free = self._cb
         stream = current_stream_handle() if hip_stream == "torch" else hip_stream
         rc, h = s2ar_create(self.ccfg, self._weights, stream)
         self._weights = None  # uploaded; the library keeps no host pointer

@@ -77,7 +77,9 @@ typedef struct {
                              below every semantic id).  A stream whose pick is that id has ended: its
                              frame, and every later frame of the same call, comes out as n_codebooks
                              values of -1, and a further decode of it is S2AR_E_STATE until a prefill
-                             appends to it or it is released ("SGLang Day-0 Support for FishAudio S2",
+                             appends to it or it is released.  The stream's position is then the one
+                             after the Slow step that picked the stop: the frames that follow the stop in
+                             the call leave nothing in its context ("SGLang Day-0 Support for FishAudio S2",
                              Background and Motivation: constrained decoding; Attention Backend
                              Divergence Causing Early Stopping: the model ends on an EOS token). */
   int32_t head_slice;     /* 0: the Slow head computes every row (text and semantic ids), as the pages
@@ -85,6 +87,16 @@ typedef struct {
                              eos_id row are kept on the device and computed (the text rows can never be
                              picked), a semantic slice of the head.  The picks are identical; the
                              debug taps then hold those rows' logits only (the others NaN). */
+  /* Device memory source, optional: both NULL = hipMalloc / hipFree.  Otherwise every device
+   * allocation of the context comes from dev_alloc(bytes, alloc_user), which returns memory of the
+   * current device aligned to 256 bytes, or NULL (the call that needed it then fails with
+   * S2AR_E_NOMEM and changes nothing); every block goes back through dev_free(ptr, bytes,
+   * alloc_user), in s2ar_destroy or when s2ar_create fails.  It lets the caller's caching allocator
+   * (PyTorch's, for one) own the device memory, while the library keeps using it only on its own
+   * stream; the library zeroes each block it takes.  Setting only one of the two is S2AR_E_ARG. */
+  void* (*dev_alloc)(uint64_t bytes, void* alloc_user);
+  void (*dev_free)(void* ptr, uint64_t bytes, void* alloc_user);
+  void* alloc_user;
 } s2ar_config;
 
 /* One weight tensor in host memory: fp32, or bf16 bit patterns (uint16). */
@@ -209,9 +221,9 @@ int s2ar_time_kernel(s2ar_ctx* ctx, int32_t which, int32_t iters, float* avg_ms,
 /* Decode n_frames frames of one stream as decode_frames does (one frame-graph replay each, back to
  * back on the context's stream) with a HIP event pair around every replay, and write each
  * replay's duration in ms to ms_out[n_frames] (caller-owned host memory).  The stream advances by
- * n_frames positions; the frames' codes are not returned (a stop id is not tracked here).
- * Errors as decode_frames for one stream, and S2AR_E_ARG for a null ms_out or n_frames outside
- * [1, 4096]. */
+ * n_frames positions; the frames' codes are not returned, so a context with a stop id (eos_id >= 0)
+ * is refused.  Errors as decode_frames for one stream, and S2AR_E_ARG for a null ms_out, n_frames
+ * outside [1, 4096] or eos_id >= 0. */
 int s2ar_time_frames(s2ar_ctx* ctx, int32_t stream_id, int32_t n_frames, float* ms_out);
 
 #ifdef __cplusplus

@@ -130,3 +130,41 @@ def test_product_path_never_imports_the_oracle():
         for f in files:
             if f.endswith((".py", ".hip", ".h", ".c", ".cpp")):
                 assert not pat.search(open(os.path.join(dirpath, f)).read()), f
+
+
+def test_allocator_callbacks_must_come_in_pairs(L):
+    """dev_alloc without dev_free (or the reverse) is rejected before any device work, and no
+    callback runs."""
+    calls = []
+    alloc = s2ar.DEV_ALLOC(lambda nbytes, user: calls.append(nbytes) or None)
+    free = s2ar.DEV_FREE(lambda ptr, nbytes, user: calls.append(-1))
+    for set_alloc, set_free in ((True, False), (False, True)):
+        c = s2ar.make_config(_cfg())
+        if set_alloc:
+            c.dev_alloc = alloc
+        if set_free:
+            c.dev_free = free
+        rc, h = s2ar.s2ar_create(c, [np.zeros(1, np.float32)], None)
+        assert rc == -1 and h is None and "dev_alloc and dev_free" in s2ar.s2ar_last_error(None)
+    assert calls == []
+
+
+def test_config_struct_matches_the_header():
+    """The binding's Config mirrors s2ar_config field for field (names in header order)."""
+    txt = open(os.path.join(ROOT, "include", "s2ar.h")).read()
+    body = txt[txt.index("typedef struct {\n  s2ar_stack slow, fast;"):txt.index("} s2ar_config;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl or decl.startswith("typedef"):
+            if decl.startswith("typedef struct {"):
+                decl = decl[len("typedef struct {"):].strip()
+            else:
+                continue
+        m = re.search(r"\(\*\s*(\w+)\)", decl)
+        if m:
+            names.append(m.group(1))
+            continue
+        names += [n.strip().lstrip("*") for n in decl.split(None, 1)[1].split(",")]
+    assert names == [n for n, _ in s2ar.Config._fields_]
