@@ -14,13 +14,25 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "kernels.h"
 #include "s2ar.h"
 
+// Scratch of s2ar_decode_frames_noalloc: the greedy-pick partials and the Slow attention split
+// partials of one frame, in a fixed array of every device the library runs on (each device holds
+// its own copy until the process ends).  Host code never passes `scratch` itself to a kernel (on
+// the host it only names the symbol): the device address comes from hipGetSymbolAddress, once per
+// device, at context creation.
+static __device__ __align__(256) unsigned char scratch[S2AR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void* g_scratch_addr[kMaxDevices] = {};
 
 thread_local std::string g_create_error;
 
@@ -157,6 +169,7 @@ struct s2ar_ctx {
   int* h_small = nullptr;  // small int staging (forced codes, own picks)
 
   std::map<int, Graph> graphs;  // per (stream id, attention bucket)
+  unsigned char* scratch_dev = nullptr;  // this device's copy of `scratch`
 
   // batched multi-stream decode (up to 16 streams per launch, MFMA GEMVs)
   bool batched_ok = false;
@@ -560,6 +573,18 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     C_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     s2k::set_device_cus(cus);
   }
+  {  // the device address of this device's scratch array, looked up once per device
+    int dev = 0;
+    C_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(set_err(c, S2AR_E_DEVICE, "device ordinal beyond 63"));
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+      void* ptr = nullptr;
+      C_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+      g_scratch_addr[dev] = ptr;
+    }
+    c->scratch_dev = static_cast<unsigned char*>(g_scratch_addr[dev]);
+  }
   C_HIP(hipEventCreateWithFlags(&c->ev_order, hipEventDisableTiming));
   C_HIP(hipEventCreate(&c->ev_t0));
   C_HIP(hipEventCreate(&c->ev_t1));
@@ -813,7 +838,8 @@ struct Enq {
   s2ar_ctx* c;
   hipStream_t s;
   hipError_t e = hipSuccess;
-  // scratch of the frame's kernels: greedy-pick partials and Slow attention split partials
+  // scratch of the frame's kernels: greedy-pick partials and Slow attention split partials (the
+  // context's workspace, or the file-scope scratch array of the allocation-free entry point)
   float* ws_am_val = c->am_val;
   int* ws_am_idx = c->am_idx;
   float* ws_att_ml = c->att_ml;
@@ -1658,6 +1684,48 @@ int s2ar_decode_frames(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t n_fra
 
 int s2ar_decode_frame(s2ar_ctx* c, const int32_t* ids, int32_t n, int32_t* codes_out) {
   return s2ar_decode_frames(c, ids, n, 1, codes_out);
+}
+
+int s2ar_decode_frames_noalloc(s2ar_ctx* c, int32_t sid, int32_t n_frames, int32_t* codes_out) {
+  if (!c) return S2AR_E_ARG;
+  if (!codes_out || n_frames < 1) return set_err(c, S2AR_E_ARG, "codes_out must be non-null and n_frames >= 1");
+  if (int rc = check_streams(c, &sid, 1, n_frames)) return rc;
+  const s2ar_config& g = c->cfg;
+  const int NC = g.n_codebooks;
+  // scratch layout: pick partials (values, then indices), then the Slow attention split partials
+  // of the call's longest frame ((max, sum) pairs, then outputs), each 256-byte aligned
+  auto up256 = [](size_t b) { return (b + 255) / 256 * 256; };
+  const size_t nb = (size_t)std::max(s2k::gemv_blocks(s2k::GEMV_NORM_ARGMAX, c->head_rows),
+                                     s2k::gemv_blocks(s2k::GEMV_NORM_ARGMAX, g.codebook_size));
+  const int hq = g.slow.n_q_heads, D = g.slow.head_dim;
+  const int max_nsplit = slow_split_for(c->pos[sid] + n_frames).nsplit;
+  const size_t am_bytes = up256(sizeof(float) * nb), ml_bytes = up256(sizeof(float) * 2 * hq * max_nsplit);
+  const size_t need = 2 * am_bytes + ml_bytes + up256(sizeof(float) * (size_t)hq * max_nsplit * D);
+  if (need > S2AR_NOALLOC_SCRATCH_BYTES)
+    return set_err(c, S2AR_E_CAPACITY, "frame scratch of " + std::to_string(need) + " bytes exceeds the " +
+                                           std::to_string(S2AR_NOALLOC_SCRATCH_BYTES) + "-byte scratch array");
+  if (int rc = order_after_user(c)) return rc;
+  if (int rc = ensure_pages(c, sid, c->pos[sid] + n_frames)) return rc;
+  unsigned char* sc = c->scratch_dev;
+  int done = 0;
+  while (done < n_frames) {
+    const int chunk = std::min(n_frames - done, c->h_codes_frames);
+    Enq q{c, c->stream};
+    q.ws_am_val = reinterpret_cast<float*>(sc);
+    q.ws_am_idx = reinterpret_cast<int*>(sc + am_bytes);
+    q.ws_att_ml = reinterpret_cast<float*>(sc + 2 * am_bytes);
+    q.ws_att_o = reinterpret_cast<float*>(sc + 2 * am_bytes + ml_bytes);
+    for (int f = 0; f < chunk && q.e == hipSuccess; ++f) {
+      q.set_slow_ctx(c->pos[sid] + done + f + 1, true);
+      q.frame(sid, nullptr);
+      q.d2h(c->h_codes + (size_t)f * NC, c->d_snap + (size_t)sid * NC, sizeof(int) * NC);
+    }
+    if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("noalloc frame: ") + hipGetErrorString(q.e));
+    HIP_TRY(c, hipStreamSynchronize(c->stream));
+    std::memcpy(codes_out + (size_t)done * NC, c->h_codes, sizeof(int) * (size_t)chunk * NC);
+    done += chunk;
+  }
+  return finish_frames(c, &sid, 1, n_frames, codes_out);
 }
 
 int s2ar_debug_frame(s2ar_ctx* c, int32_t sid, const int32_t* forced, s2ar_taps* taps) {

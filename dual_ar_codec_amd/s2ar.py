@@ -22,7 +22,8 @@ ERRORS = {-1: "S2AR_E_ARG", -2: "S2AR_E_RANGE", -3: "S2AR_E_CAPACITY", -4: "S2AR
 
 SYMBOLS = ("s2ar_create", "s2ar_prefill", "s2ar_decode_frame", "s2ar_decode_frames", "s2ar_release_stream",
            "s2ar_stream_position", "s2ar_destroy", "s2ar_last_error", "s2ar_error_name", "s2ar_debug_frame",
-           "s2ar_time_kernel", "s2ar_debug_frame_batch", "s2ar_share_prefix", "s2ar_time_frames")
+           "s2ar_time_kernel", "s2ar_debug_frame_batch", "s2ar_share_prefix", "s2ar_time_frames",
+           "s2ar_decode_frames_noalloc")
 
 i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 
@@ -87,6 +88,7 @@ def lib():
         L.s2ar_time_kernel.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i64)]
         L.s2ar_debug_frame_batch.argtypes = [vp, vp, i32, vp, ctypes.POINTER(Taps)]
         L.s2ar_time_frames.argtypes = [vp, i32, i32, vp]
+        L.s2ar_decode_frames_noalloc.argtypes = [vp, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -214,6 +216,12 @@ class Context:
         ids = np.ascontiguousarray(np.atleast_1d(stream_ids), np.int32)
         out = np.zeros((n_frames, len(ids), self.NC), np.int32)
         self._check(lib().s2ar_decode_frames(self.h, _p(ids), len(ids), int(n_frames), _p(out)))
+        return out
+
+    def decode_frames_noalloc(self, stream_id, n_frames):
+        """n_frames frames of one stream through the allocation-free entry point."""
+        out = np.zeros((int(n_frames), self.NC), np.int32)
+        self._check(lib().s2ar_decode_frames_noalloc(self.h, int(stream_id), int(n_frames), _p(out)))
         return out
 
     def release(self, stream_id):

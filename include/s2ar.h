@@ -151,6 +151,27 @@ int s2ar_decode_frame(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n_stream
 int s2ar_decode_frames(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n_streams, int32_t n_frames,
                        int32_t* codes_out);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Decodes n_frames frames of one stream exactly as
+ * s2ar_decode_frames does for that stream (the same kernels, the same codes bit for bit), but
+ * enqueues each frame's kernels directly instead of replaying a captured graph (instantiating one
+ * allocates), and keeps the frame's scratch -- the greedy-pick partials and the Slow attention
+ * split partials -- in a fixed device array of S2AR_NOALLOC_SCRATCH_BYTES bytes instead of the
+ * context's workspace.  It calls no hipMalloc, hipFree or other allocating routine; weights, KV
+ * pages and per-stream state are the context's, allocated at s2ar_create.
+ * codes_out: [n_frames][n_codebooks], caller-owned host memory.  Errors as s2ar_decode_frames, and
+ * S2AR_E_CAPACITY when the frame's scratch (about 156 KB of pick partials plus
+ * n_q_heads * (head_dim + 2) * 4 bytes per 64 context positions: contexts up to about 15,000
+ * positions at the S2 shape) exceeds the array.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (every
+ * scratch word a frame reads is written earlier in the same frame, so nothing needs clearing):
+ * calls that overlap on one GPU (from several threads, or on several contexts' streams) race and
+ * must be serialised by the caller.
+ */
+#define S2AR_NOALLOC_SCRATCH_BYTES (4u << 20)
+int s2ar_decode_frames_noalloc(s2ar_ctx* ctx, int32_t stream_id, int32_t n_frames, int32_t* codes_out);
+
 /* Forget a stream's context and return its KV pages to the pool. */
 int s2ar_release_stream(s2ar_ctx* ctx, int32_t stream_id);
 
