@@ -108,9 +108,12 @@ def multi_stream(args, w, log, kv_dtype="f32"):
             "step_bytes": w_bytes + kv, "hbm_gbps": round((w_bytes + kv) / step_s / 1e9, 1),
             "hbm_frac": round((w_bytes + kv) / step_s / 1e9 / HBM_PEAK_GBPS, 4),
             "prefill_s": round(tp, 2), "kv_dtype": kv_dtype,
-            "note": "same synthetic weights as the batch-1 line (shapes identical)" + (
-                "" if kv_dtype == "f32" else "; a bf16 KV cache halves the KV bytes but misses the 0.9999 "
-                "hidden-cosine bar at full shape (about 1 - 1.2e-4), so this line is context only")}
+            "note": "same synthetic weights as the batch-1 line (shapes identical); " + {
+                "k_bf16": "bf16 keys and fp32 values: a quarter fewer KV bytes than fp32, inside the parity bar",
+                "f32": "fp32 keys and values",
+                "bf16": "bf16 keys and values halve the KV bytes but miss the 0.9999 hidden-cosine bar at full "
+                        "shape (the fp64 oracle itself drifts 1 - 1.2e-4 with its cache rounded to bf16), so this "
+                        "line is context only"}[kv_dtype]}
 
 
 def prefix_sharing(ctx, vc, vt, vm, vcodes):
@@ -390,9 +393,10 @@ def main():
     sliced = slice_head(args.slice_steps, cfg, w, toks, log) if args.slice_steps > 0 else None
     mid = mid_workload(log) if args.mid else None
 
-    multi = multi_bf16 = None
+    multi = multi_f32 = multi_bf16 = None
     if args.multi_steps > 0:
-        multi = multi_stream(args, w, log)
+        multi = multi_stream(args, w, log, "k_bf16")
+        multi_f32 = multi_stream(args, w, log, "f32")
         multi_bf16 = multi_stream(args, w, log, "bf16")
 
     if args.copy_probe:
@@ -434,6 +438,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "multi_stream": multi,
+        "multi_stream_f32_kv": multi_f32,
         "multi_stream_bf16_kv": multi_bf16,
         "int8": int8,
         "fp8": fp8,

@@ -20,11 +20,23 @@ HIPCC_FLAGS = [
 ]
 
 
-def build_hip(out: str = LIB) -> str:
+def build_hip(out: str = LIB, defines=()) -> str:
+    """Compile the sources in parallel (one hipcc per file) and link libs2ar.so."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    tag = "".join("_" + d for d in defines)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", tag + ".o"))
+        cmd = [hipcc, *[f for f in HIPCC_FLAGS if f != "-shared"], "-c", *[f"-D{d}" for d in defines],
+               "-I", os.path.join(ROOT, "include"), "-o", obj, os.path.join(CSRC, src)]
+        procs.append(subprocess.Popen(cmd))
+        objs.append(obj)
+    if any(p.wait() for p in procs):
+        raise RuntimeError("hipcc failed")
     tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
-    subprocess.check_call(cmd)
+    subprocess.check_call([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, out)
     return out
 

@@ -106,8 +106,9 @@ struct s2ar_ctx {
 
   // KV pools (fp32 or bf16): slow [layers][n_pages][Hkv][page][D]; fast [layers][max_streams][Hkv][page][D]
   char *kv_k = nullptr, *kv_v = nullptr, *fkv_k = nullptr, *fkv_v = nullptr;
-  size_t kv_layer = 0, fkv_layer = 0;  // bytes per layer
-  int kv_esz = 4;
+  // bytes per layer of the key and value pools (Slow and Fast), and their element sizes
+  size_t kv_layer_k = 0, kv_layer_v = 0, fkv_layer_k = 0, fkv_layer_v = 0;
+  int k_bf16 = 0, v_bf16 = 0;
   int n_pages = 0, bt_stride = 0;
   int* d_bt = nullptr;       // [max_streams][bt_stride]
   int* h_bt = nullptr;       // pinned mirror
@@ -258,8 +259,8 @@ int validate_config(const s2ar_config* c, std::string& why) {
     why = "max_streams must be in [1, 256] and max_context in [1, 2^20]";
     return -1;
   }
-  if (c->kv_dtype != 0 && c->kv_dtype != 1) {
-    why = "kv_dtype must be 0 (fp32) or 1 (bf16)";
+  if (c->kv_dtype < 0 || c->kv_dtype > 3) {
+    why = "kv_dtype must be 0 (fp32), 1 (bf16), 2 (bf16 keys, fp32 values) or 3 (fp32 keys, bf16 values)";
     return -1;
   }
   if (c->eos_id < -1 || c->eos_id >= c->vocab_text) {
@@ -647,13 +648,20 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   // KV pools
   c->bt_stride = (g.max_context + kPageSize - 1) / kPageSize;
   c->n_pages = c->bt_stride * g.max_streams;
-  c->kv_esz = g.kv_dtype == 1 ? 2 : 4;
-  c->kv_layer = (size_t)c->n_pages * g.slow.n_kv_heads * kPageSize * g.slow.head_dim * c->kv_esz;
-  c->fkv_layer = (size_t)g.max_streams * g.fast.n_kv_heads * kPageSize * g.fast.head_dim * c->kv_esz;
-  C_TRY(dev_alloc(c, &c->kv_k, c->kv_layer * g.slow.n_layers));
-  C_TRY(dev_alloc(c, &c->kv_v, c->kv_layer * g.slow.n_layers));
-  C_TRY(dev_alloc(c, &c->fkv_k, c->fkv_layer * g.fast.n_layers));
-  C_TRY(dev_alloc(c, &c->fkv_v, c->fkv_layer * g.fast.n_layers));
+  c->k_bf16 = g.kv_dtype == 1 || g.kv_dtype == 2;
+  c->v_bf16 = g.kv_dtype == 1 || g.kv_dtype == 3;
+  {
+    const size_t slow_elems = (size_t)c->n_pages * g.slow.n_kv_heads * kPageSize * g.slow.head_dim;
+    const size_t fast_elems = (size_t)g.max_streams * g.fast.n_kv_heads * kPageSize * g.fast.head_dim;
+    c->kv_layer_k = slow_elems * (c->k_bf16 ? 2 : 4);
+    c->kv_layer_v = slow_elems * (c->v_bf16 ? 2 : 4);
+    c->fkv_layer_k = fast_elems * (c->k_bf16 ? 2 : 4);
+    c->fkv_layer_v = fast_elems * (c->v_bf16 ? 2 : 4);
+  }
+  C_TRY(dev_alloc(c, &c->kv_k, c->kv_layer_k * g.slow.n_layers));
+  C_TRY(dev_alloc(c, &c->kv_v, c->kv_layer_v * g.slow.n_layers));
+  C_TRY(dev_alloc(c, &c->fkv_k, c->fkv_layer_k * g.fast.n_layers));
+  C_TRY(dev_alloc(c, &c->fkv_v, c->fkv_layer_v * g.fast.n_layers));
   C_TRY(dev_alloc(c, &c->d_bt, sizeof(int) * c->n_pages));
   C_TRY(host_alloc(c, &c->h_bt, sizeof(int) * c->n_pages));
   {
@@ -938,7 +946,8 @@ struct Enq {
       a.out = c->att;
       a.part_ml = ws_att_ml;
       a.part_o = ws_att_o;
-      a.kv_bf16 = c->cfg.kv_dtype == 1;
+      a.k_bf16 = c->k_bf16;
+      a.v_bf16 = c->v_bf16;
       a.split = is_slow ? slow_split : kAttnSplit;
       a.fixed_slot = slot;  // a frame graph belongs to one stream: no slot lookup on the device
       a.row_pos = nullptr;
@@ -948,8 +957,8 @@ struct Enq {
         a.rope_cos = c->rope_cos_s;
         a.rope_sin = c->rope_sin_s;
         a.pos = c->d_pos;
-        a.k_cache = c->kv_k + (size_t)l * c->kv_layer;
-        a.v_cache = c->kv_v + (size_t)l * c->kv_layer;
+        a.k_cache = c->kv_k + (size_t)l * c->kv_layer_k;
+        a.v_cache = c->kv_v + (size_t)l * c->kv_layer_v;
         a.block_table = c->d_bt;
         a.bt_stride = c->bt_stride;
         a.max_splits = slow_max_splits;
@@ -957,8 +966,8 @@ struct Enq {
         a.rope_cos = c->rope_cos_f;
         a.rope_sin = c->rope_sin_f;
         a.pos = fast_pos_ptr;
-        a.k_cache = c->fkv_k + (size_t)l * c->fkv_layer;
-        a.v_cache = c->fkv_v + (size_t)l * c->fkv_layer;
+        a.k_cache = c->fkv_k + (size_t)l * c->fkv_layer_k;
+        a.v_cache = c->fkv_v + (size_t)l * c->fkv_layer_v;
         a.block_table = c->d_fast_bt;
         a.bt_stride = 1;
         a.max_splits = 1;
@@ -1075,9 +1084,10 @@ struct Enq {
       kv.k_norm = L.k_norm;
       kv.rope_cos = c->rope_cos_s;
       kv.rope_sin = c->rope_sin_s;
-      kv.k_cache = c->kv_k + (size_t)l * c->kv_layer;
-      kv.v_cache = c->kv_v + (size_t)l * c->kv_layer;
-      kv.kv_bf16 = g.kv_dtype == 1;
+      kv.k_cache = c->kv_k + (size_t)l * c->kv_layer_k;
+      kv.v_cache = c->kv_v + (size_t)l * c->kv_layer_v;
+      kv.k_bf16 = c->k_bf16;
+      kv.v_bf16 = c->v_bf16;
       kv.block_table = c->d_bt + (size_t)slot * c->bt_stride;
       kv.page_size = kPageSize;
       kv.pos0 = pos0;
@@ -1094,7 +1104,8 @@ struct Enq {
       pa.rope_sin = c->rope_sin_s;
       pa.k_cache = kv.k_cache;
       pa.v_cache = kv.v_cache;
-      pa.kv_bf16 = kv.kv_bf16;
+      pa.k_bf16 = kv.k_bf16;
+      pa.v_bf16 = kv.v_bf16;
       pa.block_table = kv.block_table;
       pa.page_size = kPageSize;
       pa.out_hi = c->patth;
@@ -1233,7 +1244,8 @@ struct Enq {
       a.out = c->batt;
       a.part_ml = c->batt_ml;
       a.part_o = c->batt_o;
-      a.kv_bf16 = g.kv_dtype == 1;
+      a.k_bf16 = c->k_bf16;
+      a.v_bf16 = c->v_bf16;
       a.split = c->attn_split_b;
       a.fixed_slot = -1;
       a.row_pos = nullptr;
@@ -1243,8 +1255,8 @@ struct Enq {
         a.rope_cos = c->rope_cos_s;
         a.rope_sin = c->rope_sin_s;
         a.pos = c->d_pos;
-        a.k_cache = c->kv_k + (size_t)l * c->kv_layer;
-        a.v_cache = c->kv_v + (size_t)l * c->kv_layer;
+        a.k_cache = c->kv_k + (size_t)l * c->kv_layer_k;
+        a.v_cache = c->kv_v + (size_t)l * c->kv_layer_v;
         a.block_table = c->d_bt;
         a.bt_stride = c->bt_stride;
         a.max_splits = c->max_splits_b;
@@ -1252,8 +1264,8 @@ struct Enq {
         a.rope_cos = c->rope_cos_f;
         a.rope_sin = c->rope_sin_f;
         a.pos = fast_pos_ptr;
-        a.k_cache = c->fkv_k + (size_t)l * c->fkv_layer;
-        a.v_cache = c->fkv_v + (size_t)l * c->fkv_layer;
+        a.k_cache = c->fkv_k + (size_t)l * c->fkv_layer_k;
+        a.v_cache = c->fkv_v + (size_t)l * c->fkv_layer_v;
         a.block_table = c->d_fast_bt;
         a.bt_stride = 1;
         a.max_splits = 1;
@@ -1902,10 +1914,11 @@ int s2ar_share_prefix(s2ar_ctx* c, int32_t src, int32_t dst, int32_t n) {
     c->page_refs[p] = 1;
     dp.push_back(p);
     bt[full] = p;
-    const size_t page_bytes = c->kv_layer / c->n_pages;  // [Hkv][16][D] of one layer
     for (int l = 0; l < c->cfg.slow.n_layers; ++l)
-      for (char* pool : {c->kv_k, c->kv_v}) {
-        char* base = pool + (size_t)l * c->kv_layer;
+      for (int kv = 0; kv < 2; ++kv) {
+        const size_t layer = kv ? c->kv_layer_v : c->kv_layer_k;
+        const size_t page_bytes = layer / c->n_pages;  // [Hkv][16][D] of one layer
+        char* base = (kv ? c->kv_v : c->kv_k) + (size_t)l * layer;
         HIP_TRY(c, hipMemcpyAsync(base + (size_t)p * page_bytes, base + (size_t)sp[full] * page_bytes, page_bytes,
                                   hipMemcpyDeviceToDevice, c->stream));
       }

@@ -47,7 +47,7 @@ struct AttnArgs {
   const int* pos;          // [slots] position of the new token (context = pos + 1)
   void* k_cache;           // [pages][Hkv][page_size][D], fp32 or bf16 bits (one layer)
   void* v_cache;
-  int kv_bf16;             // 1: caches hold bf16, 0: fp32
+  int k_bf16, v_bf16;      // element of the key / value cache: 1 bf16 bits, 0 fp32
   const int* block_table;  // [slots][bt_stride]
   int bt_stride;
   float* out;              // [M][Hq D]
@@ -139,7 +139,7 @@ struct PrefillKvArgs {
   const float* rope_sin;
   void* k_cache;           // one layer of the paged pool
   void* v_cache;
-  int kv_bf16;
+  int k_bf16, v_bf16;      // element of the key / value cache: 1 bf16 bits, 0 fp32
   const int* block_table;  // the stream's row of the block table
   int page_size;
   int pos0;                // position of row 0
@@ -158,7 +158,7 @@ struct PrefillAttnArgs {
   const float* rope_sin;
   const void* k_cache;     // one layer of the paged pool
   const void* v_cache;
-  int kv_bf16;
+  int k_bf16, v_bf16;      // element of the key / value cache: 1 bf16 bits, 0 fp32
   const int* block_table;  // the stream's row of the block table
   int page_size;
   uint16_t* out_hi;        // [rows][ld_out] attention output as bf16 high and low planes (the

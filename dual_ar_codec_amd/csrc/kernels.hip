@@ -152,7 +152,7 @@ struct WFmt<WF_F8> {
 // (4b + w) * R ... + R - 1.  NCH > 0: K == NCH * 64 * elements-per-chunk and all weight loads of
 // the wavefront are issued up front; NCH == 0: any K divisible by the chunk width / 8, looped.
 // Int8 weights: each row's sum is multiplied by the row's scale before the epilogue.
-template <int WF, int NCH, int KIND>
+template <int WF, int NCH, int KIND, int WPB = GEMV_WAVES>
 __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
   extern __shared__ float xs[];
   using F = WFmt<WF>;
@@ -160,13 +160,14 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
   constexpr int R = rows_per_wave(KIND);
   constexpr int EPC = F::EPC;
   constexpr bool NORM = KIND != GEMV_RESID;
-  __shared__ float red[GEMV_WAVES];
-  __shared__ int bidx[GEMV_WAVES];
+  constexpr int NT = WPB * WAVE;
+  __shared__ float red[WPB];
+  __shared__ int bidx[WPB];
 
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x / WAVE;
   const int K = a.K;
-  const int row0 = (blockIdx.x * GEMV_WAVES + wid) * R;
+  const int row0 = (blockIdx.x * WPB + wid) * R;
   const size_t row_bytes = (size_t)K * F::ESZ;
   float sc[R];
 #pragma unroll
@@ -174,13 +175,13 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
 
   // 1. loads: the input vector (and gain) first, then every weight chunk of this wavefront's
   //    rows.  vmcnt retires in issue order, so staging the input only waits for the input.
-  constexpr int XL = NCH > 0 ? (NCH * WAVE * EPC + GEMV_THREADS * 4 - 1) / (GEMV_THREADS * 4) : 1;
+  constexpr int XL = NCH > 0 ? (NCH * WAVE * EPC + NT * 4 - 1) / (NT * 4) : 1;
   f32x4 xv[XL], gv[XL];
   CT wv[R][NCH > 0 ? NCH : 1];
   if constexpr (NCH > 0) {
 #pragma unroll
     for (int t = 0; t < XL; ++t) {  // x and gain are zero-padded to a multiple of 1024 floats
-      const int k = (t * GEMV_THREADS + threadIdx.x) * 4;
+      const int k = (t * NT + threadIdx.x) * 4;
       xv[t] = *reinterpret_cast<const f32x4*>(a.x + k);
       if constexpr (NORM) gv[t] = *reinterpret_cast<const f32x4*>(a.gain + k);
     }
@@ -199,7 +200,7 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
   if constexpr (NCH > 0) {
 #pragma unroll
     for (int t = 0; t < XL; ++t) {
-      const int k = (t * GEMV_THREADS + threadIdx.x) * 4;
+      const int k = (t * NT + threadIdx.x) * 4;
       const f32x4 v = xv[t];
       *reinterpret_cast<f32x4*>(xs + k) = v;
       ss = fmaf(v.x, v.x, ss);
@@ -208,7 +209,7 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
       ss = fmaf(v.w, v.w, ss);
     }
   } else {
-    for (int k = threadIdx.x * 4; k < K; k += GEMV_THREADS * 4) {
+    for (int k = threadIdx.x * 4; k < K; k += NT * 4) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(a.x + k);
       *reinterpret_cast<f32x4*>(xs + k) = v;
       ss = fmaf(v.x, v.x, ss);
@@ -223,7 +224,7 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < GEMV_WAVES; ++w) tot += red[w];
+    for (int w = 0; w < WPB; ++w) tot += red[w];
     const float scale = rsqrtf(tot / (float)K + a.eps);
     const bool keep = blockIdx.x == 0 && a.xnorm_out != nullptr;
     auto norm4 = [&](int k, f32x4 g) {
@@ -237,9 +238,9 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
     };
     if constexpr (NCH > 0) {
 #pragma unroll
-      for (int t = 0; t < XL; ++t) norm4((t * GEMV_THREADS + threadIdx.x) * 4, gv[t]);
+      for (int t = 0; t < XL; ++t) norm4((t * NT + threadIdx.x) * 4, gv[t]);
     } else {
-      for (int k = threadIdx.x * 4; k < K; k += GEMV_THREADS * 4) norm4(k, *reinterpret_cast<const f32x4*>(a.gain + k));
+      for (int k = threadIdx.x * 4; k < K; k += NT * 4) norm4(k, *reinterpret_cast<const f32x4*>(a.gain + k));
     }
   }
   __syncthreads();
@@ -311,7 +312,7 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
     if (threadIdx.x == 0) {
       float v = red[0];
       int i = bidx[0];
-      for (int w = 1; w < GEMV_WAVES; ++w)
+      for (int w = 1; w < WPB; ++w)
         if (red[w] > v) {
           v = red[w];
           i = bidx[w];
@@ -322,9 +323,9 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
   }
 }
 
-template <bool BF16, int NCH, int KIND>
-__global__ __launch_bounds__(GEMV_THREADS) void k_gemv(const GemvArgs a) {
-  gemv_impl<BF16 ? WF_BF16 : WF_F32, NCH, KIND>(a);
+template <bool BF16, int NCH, int KIND, int WPB = GEMV_WAVES>
+__global__ __launch_bounds__(WPB * WAVE) void k_gemv(const GemvArgs a) {
+  gemv_impl<BF16 ? WF_BF16 : WF_F32, NCH, KIND, WPB>(a);
 }
 
 template <int WF, int NCH, int KIND>
@@ -694,6 +695,16 @@ hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s) {
     const int nch = a.K / (WAVE * 8);
     if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch<5, GEMV_NORM_STORE, 1, 4>(a, 2, s);
     if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch<5, GEMV_NORM_SWIGLU, 2, 4>(a, 2, s);
+    // residual projections of 2560 rows (O, down at the S2 shape): blocks of 5 wavefronts, one row
+    // each, so the 512 blocks sit exactly two per CU (4-wavefront blocks leave 2.5 per CU, and the
+    // CUs holding three set the launch's length: 267.3 -> 271.9 frames/s at the S2 shape)
+    if (kind == GEMV_RESID && a.N % (5 * g_cus) == 0 && (nch == 8 || nch == 19)) {
+      const dim3 grid(a.N / 5), block(5 * WAVE);
+      const size_t lds = (size_t)pad_k(a.K) * sizeof(float);
+      if (nch == 8) hipLaunchKernelGGL((k_gemv<true, 8, GEMV_RESID, 5>), grid, block, lds, s, a);
+      else hipLaunchKernelGGL((k_gemv<true, 19, GEMV_RESID, 5>), grid, block, lds, s, a);
+      return hipGetLastError();
+    }
   }
   switch (kind) {
     case GEMV_NORM_STORE: return bf16 ? gemv_dispatch<true, GEMV_NORM_STORE>(a, s) : gemv_dispatch<false, GEMV_NORM_STORE>(a, s);
@@ -744,26 +755,31 @@ __device__ __forceinline__ void rope_lane(float (&v)[D / WAVE], const float* cro
   }
 }
 
-template <int D, int G, bool KVB>
+template <int D, int G, bool KB, bool VB>
 __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
-  using KV = KvT<KVB>;
-  using T = typename KV::T;
+  using KK = KvT<KB>;
+  using VV = KvT<VB>;
+  using TK = typename KK::T;
+  using TV = typename VV::T;
   constexpr int CH = WAVE;                   // positions per chunk, one per lane in the scores
   constexpr int NT = G * WAVE;               // threads
-  constexpr int KSTR = KVB ? D + 8 : D + 4;  // K row padded by one 16-byte piece: 16-byte aligned rows
+  constexpr int KSTR = KB ? D + 8 : D + 4;   // K row padded by one 16-byte piece: 16-byte aligned rows
                                              // whose 16-byte reads by consecutive lanes spread over the banks
   constexpr int PER = D / WAVE;
-  constexpr int EP16 = 16 / sizeof(T);       // elements per 16-byte piece
-  constexpr int CPR = D / EP16;              // 16-byte pieces per row
-  constexpr int PIECES = CH * CPR / NT;      // K (and V) pieces per thread per chunk
+  constexpr int EPK = 16 / sizeof(TK);       // elements per 16-byte piece of a key / value row
+  constexpr int EPV = 16 / sizeof(TV);
+  constexpr int CPRK = D / EPK;              // 16-byte pieces per key / value row
+  constexpr int CPRV = D / EPV;
+  constexpr int PK = CH * CPRK / NT;         // key / value pieces per thread per chunk
+  constexpr int PV = CH * CPRV / NT;
   constexpr int MAXSPLIT = 256;
   constexpr int MAXPG = MAXSPLIT / 16;       // pages of one split (page size 16)
-  static_assert(CH * CPR % NT == 0, "tile pieces must divide evenly");
+  static_assert(CH * CPRK % NT == 0 && CH * CPRV % NT == 0, "tile pieces must divide evenly");
   __shared__ __attribute__((aligned(16))) float q_s[G][D];
   __shared__ float kn_s[D];
   __shared__ float vn_s[D];
-  __shared__ __attribute__((aligned(16))) T k_s[CH * KSTR];
-  __shared__ __attribute__((aligned(16))) T v_s[CH * D];
+  __shared__ __attribute__((aligned(16))) TK k_s[CH * KSTR];
+  __shared__ __attribute__((aligned(16))) TV v_s[CH * D];
   __shared__ float p_s[G][CH];
   __shared__ int rowoff_s[MAXSPLIT];
   __shared__ int page_s[MAXPG];
@@ -796,8 +812,8 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
   const bool has_new = a.append && pos >= s0 && pos < s1;
   const int h = g * G + w;
   const float* qkv = a.qkv + (size_t)b * (a.Hq + 2 * a.Hkv) * D;
-  T* kc = static_cast<T*>(a.k_cache);
-  T* vc = static_cast<T*>(a.v_cache);
+  TK* kc = static_cast<TK*>(a.k_cache);
+  TV* vc = static_cast<TV*>(a.v_cache);
   if (threadIdx.x < MAXPG) page_s[threadIdx.x] = pg;
 
   // this wave's q head (and, for wave 0 of the split holding pos, the new k and v): elements
@@ -860,18 +876,19 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
 
   // K and V pieces of one chunk: issued a chunk ahead, so the loads of chunk c + 1 are in flight
   // while chunk c is scored and accumulated
-  u32x4 kt[PIECES], vt[PIECES];
+  u32x4 kt[PK], vt[PV];
   auto issue = [&](int j0) {
     const int nv = min(CH, s1 - j0);
     const int jn = has_new ? pos - j0 : -1;  // the new position is not in the cache yet
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-      const int pi = threadIdx.x + u * NT, j = pi / CPR, q = pi % CPR;
-      if (j < nv && j != jn) {
-        const int off = rowoff_s[j0 - s0 + j] + q * EP16;
-        kt[u] = *reinterpret_cast<const u32x4*>(kc + off);
-        vt[u] = *reinterpret_cast<const u32x4*>(vc + off);
-      }
+    for (int u = 0; u < PK; ++u) {
+      const int pi = threadIdx.x + u * NT, j = pi / CPRK, q = pi % CPRK;
+      if (j < nv && j != jn) kt[u] = *reinterpret_cast<const u32x4*>(kc + rowoff_s[j0 - s0 + j] + q * EPK);
+    }
+#pragma unroll
+    for (int u = 0; u < PV; ++u) {
+      const int pi = threadIdx.x + u * NT, j = pi / CPRV, q = pi % CPRV;
+      if (j < nv && j != jn) vt[u] = *reinterpret_cast<const u32x4*>(vc + rowoff_s[j0 - s0 + j] + q * EPV);
     }
   };
   issue(s0);
@@ -900,10 +917,10 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int d = lane + i * WAVE;
-        kn_s[d] = KV::round(kv[i]);
-        vn_s[d] = KV::round(vv[i]);
-        kc[off + d] = KV::cvt(kv[i]);  // append the new position to the paged cache
-        vc[off + d] = KV::cvt(vv[i]);
+        kn_s[d] = KK::round(kv[i]);
+        vn_s[d] = VV::round(vv[i]);
+        kc[off + d] = KK::cvt(kv[i]);  // append the new position to the paged cache
+        vc[off + d] = VV::cvt(vv[i]);
       }
     }
   }
@@ -921,32 +938,34 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     const int nv = min(CH, s1 - j0);
     const int jn = has_new ? pos - j0 : -1;  // row of the new position in this chunk (if any)
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-      const int pi = threadIdx.x + u * NT, j = pi / CPR, q = pi % CPR;
-      if (j < nv && j != jn) {
-        *reinterpret_cast<u32x4*>(k_s + j * KSTR + q * EP16) = kt[u];
-        *reinterpret_cast<u32x4*>(v_s + j * D + q * EP16) = vt[u];
-      }
+    for (int u = 0; u < PK; ++u) {
+      const int pi = threadIdx.x + u * NT, j = pi / CPRK, q = pi % CPRK;
+      if (j < nv && j != jn) *reinterpret_cast<u32x4*>(k_s + j * KSTR + q * EPK) = kt[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PV; ++u) {
+      const int pi = threadIdx.x + u * NT, j = pi / CPRV, q = pi % CPRV;
+      if (j < nv && j != jn) *reinterpret_cast<u32x4*>(v_s + j * D + q * EPV) = vt[u];
     }
     if (mk && jn >= 0 && jn < nv)
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int d = lane + i * WAVE;
-        k_s[jn * KSTR + d] = KV::cvt(kn_s[d]);
-        v_s[jn * D + d] = KV::cvt(vn_s[d]);
+        k_s[jn * KSTR + d] = KK::cvt(kn_s[d]);
+        v_s[jn * D + d] = VV::cvt(vn_s[d]);
       }
     __syncthreads();
     if (j0 + CH < s1) issue(j0 + CH);
 
     float s = -INFINITY;
     if (lane < nv) {
-      const T* kr = k_s + lane * KSTR;
+      const TK* kr = k_s + lane * KSTR;
       const float* qr = q_s[w];
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < D / EP16; ++c) {
-        const u32x4 kp = *reinterpret_cast<const u32x4*>(kr + c * EP16);
-        if constexpr (KVB) {
+      for (int c = 0; c < D / EPK; ++c) {
+        const u32x4 kp = *reinterpret_cast<const u32x4*>(kr + c * EPK);
+        if constexpr (KB) {
           const f32x4 qa = *reinterpret_cast<const f32x4*>(qr + c * 8);
           const f32x4 qb = *reinterpret_cast<const f32x4*>(qr + c * 8 + 4);
           float t = acc[c & 3];
@@ -981,8 +1000,8 @@ __global__ __launch_bounds__(G * WAVE) void k_attn(const AttnArgs a) {
     for (int e = 0; e < 8; ++e) o8[e] *= corr;
     for (int j = kg; j < nv; j += KG) {
       const float pj = p_s[w][j];
-      const T* vr = v_s + (size_t)j * D + dg * 8;
-      if constexpr (KVB) {
+      const TV* vr = v_s + (size_t)j * D + dg * 8;
+      if constexpr (VB) {
         const u32x4 vp = *reinterpret_cast<const u32x4*>(vr);
         o8[0] = fmaf(pj, bf_lo(vp.x), o8[0]);
         o8[1] = fmaf(pj, bf_hi(vp.x), o8[1]);
@@ -1090,11 +1109,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.split > 256 || a.split % 64 || a.page_size != 16) return hipErrorInvalidValue;
   const int G = a.Hq / a.Hkv;
   const dim3 grid(a.max_splits, a.Hkv, a.M);
-#define S2_ATT(DD, GG)                                                                         \
-  if (a.D == DD && G == GG) {                                                                  \
-    if (a.kv_bf16) hipLaunchKernelGGL((k_attn<DD, GG, true>), grid, dim3(GG * WAVE), 0, s, a);  \
-    else hipLaunchKernelGGL((k_attn<DD, GG, false>), grid, dim3(GG * WAVE), 0, s, a);           \
-    return hipGetLastError();                                                                  \
+#define S2_ATT(DD, GG)                                                                                   \
+  if (a.D == DD && G == GG) {                                                                            \
+    if (a.k_bf16 && a.v_bf16) hipLaunchKernelGGL((k_attn<DD, GG, true, true>), grid, dim3(GG * WAVE), 0, s, a);        \
+    else if (a.k_bf16) hipLaunchKernelGGL((k_attn<DD, GG, true, false>), grid, dim3(GG * WAVE), 0, s, a);              \
+    else if (a.v_bf16) hipLaunchKernelGGL((k_attn<DD, GG, false, true>), grid, dim3(GG * WAVE), 0, s, a);              \
+    else hipLaunchKernelGGL((k_attn<DD, GG, false, false>), grid, dim3(GG * WAVE), 0, s, a);                           \
+    return hipGetLastError();                                                                            \
   }
   S2_ATT(64, 1) S2_ATT(64, 2) S2_ATT(64, 4) S2_ATT(64, 8)
   S2_ATT(128, 1) S2_ATT(128, 2) S2_ATT(128, 4) S2_ATT(128, 8)

@@ -428,7 +428,7 @@ hipError_t launch_norm_split(const float* x, int ld, int H, float eps, const flo
 // ---------------------------------------------------------------------------------------------
 // Append the keys and values of prompt rows to the paged cache: per (row, KV head) one
 // wavefront applies the per-head RMSNorm and RoPE to k at position pos0 + row.
-template <int D, bool KVB>
+template <int D, bool KB, bool VB>
 __global__ __launch_bounds__(64) void k_prefill_append(const PrefillKvArgs a) {
   constexpr int PER = D / WAVE;
   const int g = blockIdx.x, row = blockIdx.y, lane = threadIdx.x;
@@ -462,14 +462,18 @@ __global__ __launch_bounds__(64) void k_prefill_append(const PrefillKvArgs a) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int d = lane + i * WAVE;
-    if constexpr (KVB) {
-      uint32_t ku = __float_as_uint(kv[i]), vu = __float_as_uint(vv[i]);
+    if constexpr (KB) {
+      uint32_t ku = __float_as_uint(kv[i]);
       ku += 0x7fffu + ((ku >> 16) & 1u);
-      vu += 0x7fffu + ((vu >> 16) & 1u);
       static_cast<uint16_t*>(a.k_cache)[off + d] = (uint16_t)(ku >> 16);
-      static_cast<uint16_t*>(a.v_cache)[off + d] = (uint16_t)(vu >> 16);
     } else {
       static_cast<float*>(a.k_cache)[off + d] = kv[i];
+    }
+    if constexpr (VB) {
+      uint32_t vu = __float_as_uint(vv[i]);
+      vu += 0x7fffu + ((vu >> 16) & 1u);
+      static_cast<uint16_t*>(a.v_cache)[off + d] = (uint16_t)(vu >> 16);
+    } else {
       static_cast<float*>(a.v_cache)[off + d] = vv[i];
     }
   }
@@ -477,16 +481,17 @@ __global__ __launch_bounds__(64) void k_prefill_append(const PrefillKvArgs a) {
 
 hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s) {
   const dim3 grid(a.Hkv, rows);
-  if (a.D == 128) {
-    if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_append<128, true>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((k_prefill_append<128, false>), grid, dim3(64), 0, s, a);
-  } else if (a.D == 64) {
-    if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_append<64, true>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((k_prefill_append<64, false>), grid, dim3(64), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
+#define S2_APP(DD)                                                                                     \
+  if (a.D == DD) {                                                                                     \
+    if (a.k_bf16 && a.v_bf16) hipLaunchKernelGGL((k_prefill_append<DD, true, true>), grid, dim3(64), 0, s, a); \
+    else if (a.k_bf16) hipLaunchKernelGGL((k_prefill_append<DD, true, false>), grid, dim3(64), 0, s, a);    \
+    else if (a.v_bf16) hipLaunchKernelGGL((k_prefill_append<DD, false, true>), grid, dim3(64), 0, s, a);    \
+    else hipLaunchKernelGGL((k_prefill_append<DD, false, false>), grid, dim3(64), 0, s, a);                 \
+    return hipGetLastError();                                                                          \
   }
-  return hipGetLastError();
+  S2_APP(128) S2_APP(64)
+#undef S2_APP
+  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -530,7 +535,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint2 a, uint2 b) {
   return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
-template <int D, int G, bool KVB>
+template <int D, int G, bool KB, bool VB>
 __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a) {
   constexpr int QR = PA_QR, KT = PA_KT, NT = 64 * G, NDS = D / 32, NDT = D / 16;
   constexpr int KS = D + 8;    // bf16 row stride of the K planes [key][dim]
@@ -644,14 +649,18 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const size_t off = (size_t)rowoff[j0 - j_begin + min(4 * kg + x, nk - 1)] + 4 * dg;
-            if constexpr (KVB) {
-              const uint2 k2 = *reinterpret_cast<const uint2*>(kb + off), v2 = *reinterpret_cast<const uint2*>(vb + off);
+            if constexpr (KB) {
+              const uint2 k2 = *reinterpret_cast<const uint2*>(kb + off);
               kr[u][x] = f32x4{__uint_as_float(k2.x << 16), __uint_as_float(k2.x & 0xffff0000u),
                                __uint_as_float(k2.y << 16), __uint_as_float(k2.y & 0xffff0000u)};
+            } else {
+              kr[u][x] = *reinterpret_cast<const f32x4*>(kc + off);
+            }
+            if constexpr (VB) {
+              const uint2 v2 = *reinterpret_cast<const uint2*>(vb + off);
               vr[u][x] = f32x4{__uint_as_float(v2.x << 16), __uint_as_float(v2.x & 0xffff0000u),
                                __uint_as_float(v2.y << 16), __uint_as_float(v2.y & 0xffff0000u)};
             } else {
-              kr[u][x] = *reinterpret_cast<const f32x4*>(kc + off);
               vr[u][x] = *reinterpret_cast<const f32x4*>(vc + off);
             }
           }
@@ -850,6 +859,14 @@ __global__ __launch_bounds__(256) void k_prefill_attn_combine(const PrefillAttnA
   }
 }
 
+template <int D, int G>
+static void launch_pa_kernel(const PrefillAttnArgs& a, dim3 grid, hipStream_t s) {
+  if (a.k_bf16 && a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, true>), grid, dim3(64 * G), 0, s, a);
+  else if (a.k_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, false>), grid, dim3(64 * G), 0, s, a);
+  else if (a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, false, true>), grid, dim3(64 * G), 0, s, a);
+  else hipLaunchKernelGGL((k_prefill_attn<D, G, false, false>), grid, dim3(64 * G), 0, s, a);
+}
+
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int nb = (a.rows + PA_QR - 1) / PA_QR;
@@ -858,28 +875,14 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   for (int rb = 0; rb < nb; ++rb) blocks += pa_splits(rb, a.rows, a.pos0, a.tps);
   if (blocks > nb && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;
   const dim3 grid(blocks, a.Hkv);
-  if (blocks > nb) {  // some row block has several splits: attention, then the merge
-    hipError_t e = hipSuccess;
-#define S2_PA(DD, GG)                                                                                 \
-    if (a.D == DD && G == GG) {                                                                       \
-      if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_attn<DD, GG, true>), grid, dim3(64 * GG), 0, s, a); \
-      else hipLaunchKernelGGL((k_prefill_attn<DD, GG, false>), grid, dim3(64 * GG), 0, s, a);          \
-      e = hipGetLastError();                                                                          \
-      if (e != hipSuccess) return e;                                                                  \
-      hipLaunchKernelGGL(k_prefill_attn_combine<DD>, dim3(nb, a.Hq), dim3(256), 0, s, a);             \
-      return hipGetLastError();                                                                       \
-    }
-    S2_PA(64, 1) S2_PA(64, 2) S2_PA(64, 4) S2_PA(64, 8)
-    S2_PA(128, 1) S2_PA(128, 2) S2_PA(128, 4) S2_PA(128, 8)
-#undef S2_PA
-    (void)e;
-    return hipErrorInvalidValue;
-  }
-#define S2_PA(DD, GG)                                                                                 \
-  if (a.D == DD && G == GG) {                                                                         \
-    if (a.kv_bf16) hipLaunchKernelGGL((k_prefill_attn<DD, GG, true>), grid, dim3(64 * GG), 0, s, a);   \
-    else hipLaunchKernelGGL((k_prefill_attn<DD, GG, false>), grid, dim3(64 * GG), 0, s, a);            \
-    return hipGetLastError();                                                                         \
+  // some row block has several splits: the attention, then the merge
+#define S2_PA(DD, GG)                                                                     \
+  if (a.D == DD && G == GG) {                                                             \
+    launch_pa_kernel<DD, GG>(a, grid, s);                                                 \
+    hipError_t e = hipGetLastError();                                                     \
+    if (e != hipSuccess || blocks == nb) return e;                                        \
+    hipLaunchKernelGGL(k_prefill_attn_combine<DD>, dim3(nb, a.Hq), dim3(256), 0, s, a);   \
+    return hipGetLastError();                                                             \
   }
   S2_PA(64, 1) S2_PA(64, 2) S2_PA(64, 4) S2_PA(64, 8)
   S2_PA(128, 1) S2_PA(128, 2) S2_PA(128, 4) S2_PA(128, 8)

@@ -55,10 +55,13 @@ def params_per_frame(cfg, head_rows: int | None = None) -> int:
 
 
 def kv_bytes_per_position(cfg) -> int:
-    """K and V of one Slow position over all layers (fp32 cache by default, bf16 optional)."""
+    """K and V of one Slow position over all layers: fp32 by default; "bf16" both halves, "k_bf16"
+    bf16 keys with fp32 values, "v_bf16" fp32 keys with bf16 values."""
     s = cfg["slow"]
-    esz = 2 if cfg.get("kv_dtype", "f32") == "bf16" else 4
-    return s["n_layers"] * 2 * s["n_kv_heads"] * s["head_dim"] * esz
+    kv = cfg.get("kv_dtype", "f32")
+    k_esz = 2 if kv in ("bf16", "k_bf16") else 4
+    v_esz = 2 if kv in ("bf16", "v_bf16") else 4
+    return s["n_layers"] * s["n_kv_heads"] * s["head_dim"] * (k_esz + v_esz)
 
 
 def frame_bytes(cfg, context_len: int) -> dict:

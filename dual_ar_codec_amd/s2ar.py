@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libs2ar.so")
+# S2AR_LIB names another build of the same library (an alternative build to compare against)
+LIB_PATH = os.environ.get("S2AR_LIB") or os.path.join(_HERE, "libs2ar.so")
 
 S2AR_OK = 0
 ERRORS = {-1: "S2AR_E_ARG", -2: "S2AR_E_RANGE", -3: "S2AR_E_CAPACITY", -4: "S2AR_E_STATE",
@@ -96,6 +97,8 @@ def lib():
 # "i8" / "f8": bf16 tensors in; the library keeps the layer matrices and heads as int8 / FP8 E4M3
 # codes with row scales
 WEIGHT_DTYPES = {"f32": 0, "bf16": 1, "i8": 2, "f8": 3}
+# KV cache elements: both fp32, both bf16, bf16 keys with fp32 values, fp32 keys with bf16 values
+KV_DTYPES = {"f32": 0, "bf16": 1, "k_bf16": 2, "v_bf16": 3}
 
 
 def make_config(cfg: dict, max_streams: int | None = None) -> Config:
@@ -105,7 +108,7 @@ def make_config(cfg: dict, max_streams: int | None = None) -> Config:
     return Config(st(cfg["slow"]), st(cfg["fast"]), cfg["vocab_text"], cfg["n_codebooks"], cfg["codebook_size"],
                   float(cfg["rope_theta"]), float(cfg["rms_eps"]), WEIGHT_DTYPES[cfg["weight_dtype"]],
                   int(cfg["rope_bf16"]), int(max_streams or cfg.get("n_streams", 1)), int(cfg["max_context"]),
-                  int(cfg.get("page_size", 16)), 1 if cfg.get("kv_dtype", "f32") == "bf16" else 0,
+                  int(cfg.get("page_size", 16)), KV_DTYPES[cfg.get("kv_dtype", "f32")],
                   int(cfg.get("eos_id", -1)), int(cfg.get("head_slice", 0)))
 
 

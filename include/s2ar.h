@@ -71,7 +71,10 @@ typedef struct {
   int32_t max_streams;    /* concurrent decode streams (stream ids 0..max_streams-1) */
   int32_t max_context;    /* Slow positions per stream, prompt plus frames */
   int32_t page_size;      /* KV positions per page; must be 16 */
-  int32_t kv_dtype;       /* KV cache element: 0 = fp32 (default), 1 = bf16 (half the KV bytes) */
+  int32_t kv_dtype;       /* KV cache elements: 0 = fp32 keys and values (default); 1 = bf16 keys and values
+                             (half the KV bytes); 2 = bf16 keys, fp32 values; 3 = fp32 keys, bf16 values
+                             (a quarter fewer KV bytes).  bf16 entries are the fp32 values rounded to
+                             nearest even when appended. */
   int32_t eos_id;         /* -1: no stop token (decode exactly the frames asked for); else a text id in
                              [0, vocab_text) that also competes in the Slow pick, winning ties (it is
                              below every semantic id).  A stream whose pick is that id has ended: its

@@ -89,7 +89,8 @@ def test_config_validation(L, over, needle):
     assert needle in s2ar.s2ar_last_error(None)
 
 
-@pytest.mark.parametrize("field,value,needle", [("weight_dtype", 4, "weight_dtype"), ("kv_dtype", 2, "kv_dtype")])
+@pytest.mark.parametrize("field,value,needle", [("weight_dtype", 4, "weight_dtype"), ("kv_dtype", 4, "kv_dtype"),
+                                               ("kv_dtype", -1, "kv_dtype")])
 def test_raw_config_fields_out_of_range(L, field, value, needle):
     c = s2ar.make_config(_cfg())
     setattr(c, field, value)

@@ -89,17 +89,19 @@ def test_batched_decode_at_the_sixteen_stream_contexts_against_the_oracle():
     other = other.reshape(n_frames, 16, 10).astype(np.int32)
     forced = [np.stack([per_stream[i][t]["codes"] if per_stream[i] is not None else other[t, i] for i in range(16)])
               for t in range(n_frames)]
-    _say("[multi] GPU: prefill 16 streams + a repeat of the longest")
-    ctx = s2ar.Context(cfg, w, max_streams=17)
-    remember_codebook(ctx, cfg, w)
-    del w
-    gc.collect()
-    for i, p in enumerate(prompts):
-        ctx.prefill(i, p)
-    ctx.prefill(16, prompts[hi])
-    ids = list(range(16))
-    rep = _compare_batch(ctx, ids, per_stream, forced, cfg, Report()).finish()
-    _say(f"[multi] batched at contexts {min(lens)}..{max(lens)}, oracle on {checked}: {rep}")
-    rep1 = compare_frames(ctx, 16, per_stream[hi], cfg).finish()
-    _say(f"[multi] batch-1 at {lens[hi]} positions: {rep1}")
-    ctx.close()
+    # the fp32 KV cache, and bf16 keys with fp32 values (the 16-stream workload's cache in bench.py)
+    for kv in ("f32", "k_bf16"):
+        ckv = dict(cfg, kv_dtype=kv)
+        _say(f"[multi] GPU, {kv} KV: prefill 16 streams + a repeat of the longest")
+        ctx = s2ar.Context(ckv, w, max_streams=17)
+        remember_codebook(ctx, ckv, w)
+        for i, p in enumerate(prompts):
+            ctx.prefill(i, p)
+        ctx.prefill(16, prompts[hi])
+        ids = list(range(16))
+        rep = _compare_batch(ctx, ids, per_stream, forced, ckv, Report()).finish()
+        _say(f"[multi] {kv} KV, batched at contexts {min(lens)}..{max(lens)}, oracle on {checked}: {rep}")
+        rep1 = compare_frames(ctx, 16, per_stream[hi], ckv).finish()
+        _say(f"[multi] {kv} KV, batch-1 at {lens[hi]} positions: {rep1}")
+        ctx.close()
+        gc.collect()

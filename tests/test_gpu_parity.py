@@ -136,6 +136,31 @@ def test_prefill_in_two_calls_matches_one_prefill():
     ctx.close()
 
 
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("kv", ["k_bf16", "v_bf16"])
+def test_full_mixed_kv_cache_teacher_forced(kv):
+    """bf16 keys with fp32 values, and fp32 keys with bf16 values, at the full S2 shape: each keeps a
+    quarter fewer KV bytes than fp32 and stays inside the acceptance bar (both halves in bf16 do not:
+    the oracle itself, with its keys and values rounded to bf16, drifts 1 - cos = 1.2e-4)."""
+    rep = _teacher_forced("full", n_frames=3, kv_dtype=kv)
+    assert rep["tokens_checked"] > 0
+
+
+@pytest.mark.parametrize("kv", ["k_bf16", "v_bf16"])
+def test_batched_mixed_kv_cache_mid_ragged(kv):
+    cfg = synth.config("mid", max_context=640, kv_dtype=kv)
+    w = synth.make_weights(cfg)
+    prompts = _ragged_prompts(cfg, [64, 17, 300, 130, 5], 31)
+    per_stream = _oracle_frames_per_stream(cfg, w, prompts, 3)
+    ctx = _ctx(cfg, w, max_streams=6)
+    ids = [0, 2, 3, 4, 5]
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
+    _say(f"[parity] batched mid, {kv} KV: {rep}")
+    ctx.close()
+
+
 def test_mid_bf16_kv_cache_teacher_forced():
     """The optional bf16 KV cache (half the KV bytes) on the mid shape."""
     rep = _teacher_forced("mid", n_frames=8, kv_dtype="bf16")
