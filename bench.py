@@ -70,14 +70,14 @@ def measured_traffic():
         return None
 
 
-def multi_stream(args, w, log, kv_dtype="f32"):
+def multi_stream(args, w, log, kv_dtype="f32", weight_dtype="bf16"):
     """16 streams with ragged contexts (256..4096 random text positions, pages of 16 handed out in
     a scrambled order), then batched decode steps: one step = one frame for every stream."""
     import torch
 
     from dual_ar_codec_amd import metrics, s2ar, synth
 
-    cfg = synth.config("multi_stream", kv_dtype=kv_dtype)
+    cfg = synth.config("multi_stream", kv_dtype=kv_dtype, weight_dtype=weight_dtype)
     lens = synth.prompt_lengths(cfg)
     n = cfg["n_streams"]
     ctx = s2ar.Context(cfg, w, max_streams=n)
@@ -99,7 +99,7 @@ def multi_stream(args, w, log, kv_dtype="f32"):
     dt = time.perf_counter() - t0
     assert out.shape == (steps, n, 10)
     ctx.close()
-    w_bytes = metrics.frame_bytes(cfg, 0)["weights"]
+    w_bytes = (metrics.int8_frame_bytes(cfg, 0) if weight_dtype in ("i8", "f8") else metrics.frame_bytes(cfg, 0))["weights"]
     kv = sum(metrics.kv_bytes_per_position(cfg) * (L + 2 + steps // 2 + 1) for L in lens)
     step_s = dt / steps
     return {"workload": f"{n} streams, contexts {min(lens)}..{max(lens)} (sum {sum(lens)}), {steps} batched steps",
@@ -107,7 +107,7 @@ def multi_stream(args, w, log, kv_dtype="f32"):
             "ms_per_step": round(step_s * 1e3, 3), "per_stream_rtf": round(metrics.rtf(1.0 / step_s), 5),
             "step_bytes": w_bytes + kv, "hbm_gbps": round((w_bytes + kv) / step_s / 1e9, 1),
             "hbm_frac": round((w_bytes + kv) / step_s / 1e9 / HBM_PEAK_GBPS, 4),
-            "prefill_s": round(tp, 2), "kv_dtype": kv_dtype,
+            "prefill_s": round(tp, 2), "kv_dtype": kv_dtype, "weight_dtype": weight_dtype,
             "note": "same synthetic weights as the batch-1 line (shapes identical); " + {
                 "k_bf16": "bf16 keys and fp32 values: a quarter fewer KV bytes than fp32, inside the parity bar",
                 "f32": "fp32 keys and values",
@@ -393,11 +393,12 @@ def main():
     sliced = slice_head(args.slice_steps, cfg, w, toks, log) if args.slice_steps > 0 else None
     mid = mid_workload(log) if args.mid else None
 
-    multi = multi_f32 = multi_bf16 = None
+    multi = multi_f32 = multi_bf16 = multi_i8 = None
     if args.multi_steps > 0:
         multi = multi_stream(args, w, log, "k_bf16")
         multi_f32 = multi_stream(args, w, log, "f32")
         multi_bf16 = multi_stream(args, w, log, "bf16")
+        multi_i8 = multi_stream(args, w, log, "k_bf16", "i8")
 
     if args.copy_probe:
         # a plain 256 MiB device copy, the reference for scaling HBM byte counters
@@ -440,6 +441,7 @@ def main():
         "multi_stream": multi,
         "multi_stream_f32_kv": multi_f32,
         "multi_stream_bf16_kv": multi_bf16,
+        "multi_stream_int8": multi_i8,
         "int8": int8,
         "fp8": fp8,
         "semantic_slice_head": sliced,

@@ -65,6 +65,45 @@ __device__ __forceinline__ float load_w(const void* p, size_t i) {
   else return static_cast<const float*>(p)[i];
 }
 
+// two fp32 values with at most 8 significant bits (int8 or E4M3 codes) as a bf16 pair, exactly
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// 16 consecutive 8-bit codes (int8, or OCP FP8 E4M3 decoded by the hardware conversion) as two
+// bf16x8 MFMA operands: codes 0..7 and 8..15
+template <int WF>
+__device__ __forceinline__ void decode8(const u32x4 p, bf16x8& a, bf16x8& b) {
+  uint32_t o[8];
+  const uint32_t wd[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (WF == W_I8) {
+      o[2 * q] = pack_bf16_exact((float)(int8_t)(wd[q] & 0xffu), (float)(int8_t)((wd[q] >> 8) & 0xffu));
+      o[2 * q + 1] = pack_bf16_exact((float)(int8_t)((wd[q] >> 16) & 0xffu), (float)(int8_t)(wd[q] >> 24));
+    } else {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], true);
+      o[2 * q] = pack_bf16_exact(lo[0], lo[1]);
+      o[2 * q + 1] = pack_bf16_exact(hi[0], hi[1]);
+    }
+  }
+  a = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+  b = __builtin_bit_cast(bf16x8, u32x4{o[4], o[5], o[6], o[7]});
+}
+
+// weight pieces of one 128-K slice as the four MFMA steps' A operands
+template <int WF, int NP>
+__device__ __forceinline__ void slice_operands(const u32x4 (&wb)[NP], bf16x8 (&wf)[4]) {
+  if constexpr (WF == W_BF16) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) wf[st] = __builtin_bit_cast(bf16x8, wb[st]);
+  } else {
+    decode8<WF>(wb[0], wf[0], wf[1]);
+    decode8<WF>(wb[1], wf[2], wf[3]);
+  }
+}
+
 }  // namespace
 
 int mgemv_tiles(int N) { return (N + 63) / 64; }
@@ -88,8 +127,10 @@ __device__ __forceinline__ void lds_barrier() {
 // loads (clamped addresses): during task t each thread first loads its share of task t+1's
 // activations, then, slice by slice, task t+1's weights, so waiting for the activations never
 // drains the weight stream.
-template <int EPI>
+template <int EPI, int WF>
 __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
+  constexpr int NP = WF == W_BF16 ? 4 : 2;        // 16-byte weight pieces per lane and 128-K slice
+  constexpr int BLK = WF == W_BF16 ? 4096 : 2048;  // bytes of one 16-row x 128-K block
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][MB * XROW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
@@ -116,14 +157,14 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int lane_off = lane * 16;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.w), (short)0, (int)((size_t)ntiles * 64 * a.K * 2), kBufferWord3);
-  auto wtile = [&](int tile, int k) { return ((tile * 4 + wu) * ksl + k / KS) * 4096; };
+      const_cast<void*>(a.w), (short)0, (int)((size_t)ntiles * 64 * a.K * (BLK / 2048)), kBufferWord3);
+  auto wtile = [&](int tile, int k) { return ((tile * 4 + wu) * ksl + k / KS) * BLK; };
   auto wld = [&](int base, int piece) {
     return __builtin_amdgcn_raw_buffer_load_b128(wrs, lane_off, base + piece * 1024, kNonTemporal);
   };
 
   f32x4 xr[8];
-  u32x4 wb[CS][4];
+  u32x4 wb[CS][NP];
   {
     int tile;
     const int k = task_k(t0, tile);
@@ -134,7 +175,7 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
 #pragma unroll
     for (int sl = 0; sl < CS; ++sl)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) wb[sl][t] = wld(wr, sl * 4 + t);
+      for (int t = 0; t < NP; ++t) wb[sl][t] = wld(wr, sl * NP + t);
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -169,22 +210,23 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
       const int nwr = wtile(ntile, nk);
 #pragma unroll
       for (int sl = 0; sl < CS; ++sl) {
+        bf16x8 wf[4];
+        slice_operands<WF>(wb[sl], wf);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           // MFMA slot group g of step st holds k = 32 g + 8 st .. + 8 of the slice (same map for A and B)
           const int kl = sl * KS + 32 * g + 8 * st;
           const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&xs[0][i * XROW + kl]);
           const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&xs[1][i * XROW + kl]);
-          const bf16x8 wf = __builtin_bit_cast(bf16x8, wb[sl][st]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], xl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], xh, acc, 0, 0, 0);
         }
         if constexpr (LOAD) {
           // keep the reload of wb[sl] after its last use (see k_mgemv_s)
           __builtin_amdgcn_sched_barrier(0);
           asm volatile("" : "+a"(acc)::"memory");
 #pragma unroll
-          for (int st = 0; st < 4; ++st) wb[sl][st] = wld(nwr, sl * 4 + st);
+          for (int st = 0; st < NP; ++st) wb[sl][st] = wld(nwr, sl * NP + st);
         }
       }
     }
@@ -193,6 +235,11 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
       // item done: lane holds D[row 4 g + r][stream i], r = 0..3
       const int split = it / ntiles, tile = it - split * ntiles;
       const int n0 = tile * 64 + w * 16 + 4 * g;
+      if constexpr (WF != W_BF16) {  // 8-bit codes: the rows' scales (rows past N read zero padding)
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(a.wscale + n0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] *= sc[r];
+      }
       if (EPI == MG_ARGMAX && a.S == 1) {
         float bv = -INFINITY;
         int bi = INT_MAX;
@@ -250,7 +297,10 @@ __global__ __launch_bounds__(256) void k_mgemv(const MgemvArgs a) {
 // inner loop is straight-line: four slices of MFMA on the weight ring, the next item's weights
 // loaded slice by slice, and an unconditional 16-byte store of the item's partial sums into
 // part[split][16][ldp] (rows past M or N hold values nobody reads).
+template <int WF>
 __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
+  constexpr int NP = WF == W_BF16 ? 4 : 2;        // 16-byte weight pieces per lane and 128-K slice
+  constexpr int BLK = WF == W_BF16 ? 4096 : 2048;  // bytes of one 16-row x 128-K block
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][MB * XROW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
@@ -267,21 +317,21 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int lane_off = lane * 16;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.w), (short)0, (int)((size_t)ntiles * 64 * a.K * 2), kBufferWord3);
+      const_cast<void*>(a.w), (short)0, (int)((size_t)ntiles * 64 * a.K * (BLK / 2048)), kBufferWord3);
   auto wtile = [&](int it) {
     const int split = it / ntiles, tile = it - split * ntiles;
-    return ((tile * 4 + wu) * ksl + split * CS) * 4096;
+    return ((tile * 4 + wu) * ksl + split * CS) * BLK;
   };
   auto wld = [&](int base, int piece) {
     return __builtin_amdgcn_raw_buffer_load_b128(wrs, lane_off, base + piece * 1024, kNonTemporal);
   };
-  u32x4 wb[CS][4];
+  u32x4 wb[CS][NP];
   {
     const int wr = wtile(it0);
 #pragma unroll
     for (int sl = 0; sl < CS; ++sl)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) wb[sl][t] = wld(wr, sl * 4 + t);
+      for (int t = 0; t < NP; ++t) wb[sl][t] = wld(wr, sl * NP + t);
   }
   const int xr_row = tid >> 4, xr_col = (tid & 15) * 32;
   const int xr_m = min(xr_row, a.M - 1);
@@ -325,18 +375,23 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
     auto item = [&](auto load_next) {
       constexpr bool LOAD = decltype(load_next)::value;
       const int nwr = wtile(LOAD ? it + 1 : it);
+      const int tile = it - split * ntiles;
+      f32x4 sc = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (WF != W_BF16)  // 8-bit codes: the rows' scales (rows past N read zero padding)
+        sc = *reinterpret_cast<const f32x4*>(a.wscale + tile * 64 + w * 16 + 4 * g);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int sl = 0; sl < CS; ++sl) {
+        bf16x8 wf[4];
+        slice_operands<WF>(wb[sl], wf);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           // MFMA slot group g of step st holds k = 32 g + 8 st .. + 8 of the slice (same map for A and B)
           const int kl = sl * KS + 32 * g + 8 * st;
           const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&xs[0][i * XROW + kl]);
           const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&xs[1][i * XROW + kl]);
-          const bf16x8 wf = __builtin_bit_cast(bf16x8, wb[sl][st]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xl, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], xl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], xh, acc, 0, 0, 0);
         }
         if constexpr (LOAD) {
           // keep the reload of wb[sl] after its last use, so it lands in the same registers: the
@@ -345,11 +400,13 @@ __global__ __launch_bounds__(256) void k_mgemv_s(const MgemvArgs a) {
           __builtin_amdgcn_sched_barrier(0);
           asm volatile("" : "+a"(acc)::"memory");
 #pragma unroll
-          for (int st = 0; st < 4; ++st) wb[sl][st] = wld(nwr, sl * 4 + st);
+          for (int st = 0; st < NP; ++st) wb[sl][st] = wld(nwr, sl * NP + st);
         }
       }
+      if constexpr (WF != W_BF16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] *= sc[r];
       // lane holds D[row 4 g + r][stream i] of the item's tile
-      const int tile = it - split * ntiles;
       *reinterpret_cast<f32x4*>(a.part + ((size_t)split * MB + i) * ldp + tile * 64 + w * 16 + 4 * g) = acc;
     };
     // the loop itself has no branch (a branch between the two item forms inside it would make
@@ -385,6 +442,32 @@ __global__ __launch_bounds__(256) void k_tile_weights(const uint16_t* src, uint1
 }
 
 size_t tiled_weight_elems(int N, int K) { return (size_t)mgemv_tiles(N) * 64 * K; }
+
+// 8-bit codes: 16-byte piece o of the tiled copy holds the codes W[16 t + i][128 s + 32 g + 16 h ..
+// + 16] for lane l = i + 16 g (o = ((t * K / 128 + s) * 2 + h) * 64 + l): MFMA steps 2h and 2h + 1
+__global__ __launch_bounds__(256) void k_tile_weights8(const uint8_t* src, uint8_t* dst, int N, int K,
+                                                       size_t units) {
+  const int ksl = K / KS;
+  for (size_t o = blockIdx.x * (size_t)256 + threadIdx.x; o < units; o += (size_t)gridDim.x * 256) {
+    const int lane = (int)(o & 63), h = (int)((o >> 6) & 1);
+    const size_t rest = o >> 7;
+    const int sl = (int)(rest % ksl);
+    const size_t t16 = rest / ksl;
+    const size_t n = t16 * 16 + (lane & 15);
+    const int k = sl * KS + 32 * (lane >> 4) + 16 * h;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < (size_t)N) v = *reinterpret_cast<const u32x4*>(src + n * K + k);
+    *reinterpret_cast<u32x4*>(dst + o * 16) = v;
+  }
+}
+
+hipError_t launch_tile_weights8(const uint8_t* src, uint8_t* dst, int N, int K, hipStream_t s) {
+  if (K % KS) return hipErrorInvalidValue;
+  const size_t units = tiled_weight_elems(N, K) / 16;
+  hipLaunchKernelGGL(k_tile_weights8, dim3((unsigned)std::min<size_t>((units + 255) / 256, 65536)), dim3(256), 0, s,
+                     src, dst, N, K, units);
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_weights(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t s) {
   if (K % KS) return hipErrorInvalidValue;
@@ -517,11 +600,17 @@ hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s) {
   const dim3 grid((items + a.ipb - 1) / a.ipb);
   const bool split_form = a.S == a.K / KC;  // one 512-wide chunk per item: k_mgemv_s
   if (a.ssq && !split_form) return hipErrorInvalidValue;  // the input norm lives in k_mgemv_s only
-  if (tiled_weight_elems(a.N, a.K) * 2 > (size_t)INT_MAX) return hipErrorInvalidValue;  // buffer-resource range
+  const size_t esz = a.w_fmt == W_BF16 ? 2 : 1;
+  if (tiled_weight_elems(a.N, a.K) * esz > (size_t)INT_MAX) return hipErrorInvalidValue;  // buffer-resource range
+  if (a.w_fmt != W_BF16 && (a.w_fmt != W_I8 && a.w_fmt != W_F8 || !a.wscale)) return hipErrorInvalidValue;
+#define S2_MGW(E, WF)                                                                                  \
+  if (split_form) hipLaunchKernelGGL(k_mgemv_s<WF>, grid, dim3(256), 0, s, a);                         \
+  else hipLaunchKernelGGL((k_mgemv<E, WF>), grid, dim3(256), 0, s, a);
 #define S2_MG(E)                                                                                      \
   case E:                                                                                             \
-    if (split_form) hipLaunchKernelGGL(k_mgemv_s, grid, dim3(256), 0, s, a);                           \
-    else hipLaunchKernelGGL(k_mgemv<E>, grid, dim3(256), 0, s, a);                                     \
+    if (a.w_fmt == W_BF16) { S2_MGW(E, W_BF16) }                                                      \
+    else if (a.w_fmt == W_I8) { S2_MGW(E, W_I8) }                                                     \
+    else { S2_MGW(E, W_F8) }                                                                          \
     if ((a.S > 1 || split_form) && E != MG_ADD)                                                       \
       hipLaunchKernelGGL(k_mgemv_reduce<E>, dim3((a.N + 255) / 256, a.M), dim3(256), 0, s, a);        \
     break;
@@ -534,6 +623,7 @@ hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s) {
       return hipErrorInvalidValue;
   }
 #undef S2_MG
+#undef S2_MGW
   return hipGetLastError();
 }
 

@@ -67,8 +67,9 @@ struct LayerW {
   float* mlp_norm = nullptr;
   float* q_norm = nullptr;
   float* k_norm = nullptr;
-  // tiled copies of the four matrices for the batched multi-stream GEMVs (k_mgemv layout)
-  uint16_t *tqkv = nullptr, *to = nullptr, *tgu = nullptr, *tdown = nullptr;
+  // tiled copies of the four matrices for the batched multi-stream GEMVs (k_mgemv layout: bf16, or
+  // the 8-bit codes of an int8 / FP8 context)
+  void *tqkv = nullptr, *to = nullptr, *tgu = nullptr, *tdown = nullptr;
   // int8 weights: fp32 scale of every row of the four matrices (same row order)
   float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sdown = nullptr;
 };
@@ -97,7 +98,7 @@ struct s2ar_ctx {
   void* slow_head = nullptr;
   void* codebook = nullptr;
   void* fast_head = nullptr;
-  uint16_t *slow_head_t = nullptr, *fast_head_t = nullptr;  // tiled copies (batched decode)
+  void *slow_head_t = nullptr, *fast_head_t = nullptr;  // tiled copies (batched decode)
   float *slow_head_s = nullptr, *fast_head_s = nullptr;      // int8 weights: row scales
   float* slow_final = nullptr;
   float* fast_final = nullptr;
@@ -452,7 +453,8 @@ int upload_i8(s2ar_ctx* c, const std::vector<QBlock>& blocks, size_t total_rows,
     }
   }
   if (int rc = dev_alloc(c, w, total_rows * cols)) return rc;
-  if (int rc = dev_alloc(c, sc, sizeof(float) * total_rows)) return rc;
+  // scales zero-padded to whole 64-row tiles: the batched kernels read them four rows at a time
+  if (int rc = dev_alloc(c, sc, sizeof(float) * ((total_rows + 63) / 64 * 64))) return rc;
   HIP_TRY(c, hipMemcpy(*w, q.data(), total_rows * cols, hipMemcpyHostToDevice));
   HIP_TRY(c, hipMemcpy(*sc, s.data(), sizeof(float) * total_rows, hipMemcpyHostToDevice));
   return 0;
@@ -732,8 +734,10 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
   {
     const s2ar_stack& st = g.slow;
     const int qkvd_s = (st.n_q_heads + 2 * st.n_kv_heads) * st.head_dim, qd_s = st.n_q_heads * st.head_dim;
-    c->mfma_prefill = c->bf16 && !c->q8 && qkvd_s % 128 == 0 && H % 128 == 0 && (2 * st.ffn) % 128 == 0 && H % 32 == 0 &&
-                      qd_s % 32 == 0 && st.ffn % 32 == 0;
+    // 8-bit weights need every K a multiple of 64 (the 8-wavefront GEMM only)
+    const int kmul = c->q8 ? 64 : 32;
+    c->mfma_prefill = c->bf16 && qkvd_s % 128 == 0 && H % 128 == 0 && (2 * st.ffn) % 128 == 0 && H % kmul == 0 &&
+                      qd_s % kmul == 0 && st.ffn % kmul == 0;
     if (c->mfma_prefill) {
       c->pch = std::min(g.max_context, 2048);
       C_TRY(dev_alloc(c, &c->px, sizeof(float) * (size_t)c->pch * H));
@@ -764,7 +768,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
     auto k_ok = [](const s2ar_stack& st) {
       return st.hidden % 512 == 0 && (st.n_q_heads * st.head_dim) % 512 == 0 && st.ffn % 512 == 0;
     };
-    c->batched_ok = c->bf16 && !c->q8 && g.max_streams > 1 && k_ok(g.slow) && k_ok(g.fast);
+    c->batched_ok = c->bf16 && g.max_streams > 1 && k_ok(g.slow) && k_ok(g.fast);
     if (c->batched_ok) {
       const int MBt = 16;
       const int qkvd_max = std::max((g.slow.n_q_heads + 2 * g.slow.n_kv_heads) * g.slow.head_dim,
@@ -790,7 +794,7 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
       struct TileJob {
         const void* src;
         int N, K;
-        uint16_t** dst;
+        void** dst;
       };
       std::vector<TileJob> jobs;
       for (int pass = 0; pass < 2; ++pass) {
@@ -806,10 +810,17 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
       }
       jobs.push_back({c->slow_head, c->head_rows, H, &c->slow_head_t});
       jobs.push_back({c->fast_head, K, H, &c->fast_head_t});
-      for (const TileJob& j : jobs) C_TRY(dev_alloc(c, j.dst, sizeof(uint16_t) * s2k::tiled_weight_elems(j.N, j.K)));
+      const size_t wesz = c->q8 ? 1 : 2;  // bytes per tiled element
+      for (const TileJob& j : jobs) C_TRY(dev_alloc(c, j.dst, wesz * s2k::tiled_weight_elems(j.N, j.K)));
       C_HIP(hipDeviceSynchronize());
-      for (const TileJob& j : jobs)
-        C_HIP(s2k::launch_tile_weights(static_cast<const uint16_t*>(j.src), *j.dst, j.N, j.K, c->stream));
+      for (const TileJob& j : jobs) {
+        if (c->q8)
+          C_HIP(s2k::launch_tile_weights8(static_cast<const uint8_t*>(j.src), static_cast<uint8_t*>(*j.dst), j.N, j.K,
+                                          c->stream));
+        else
+          C_HIP(s2k::launch_tile_weights(static_cast<const uint16_t*>(j.src), static_cast<uint16_t*>(*j.dst), j.N, j.K,
+                                         c->stream));
+      }
       C_HIP(hipStreamSynchronize(c->stream));
       c->max_splits_b = (g.max_context + c->attn_split_b - 1) / c->attn_split_b;
       C_TRY(dev_alloc(c, &c->batt_ml, sizeof(float) * 2 * MBt * hq * c->max_splits_b));
@@ -1055,13 +1066,15 @@ struct Enq {
     const float eps = (float)g.rms_eps;
     chk(s2k::launch_embed_rows(c->bf16, c->embed, c->codebook, g.codebook_size, H, g.n_codebooks, c->d_tokens,
                                has_mask ? c->d_mask : nullptr, c->d_pcodes, p0, rows, c->px, H, s));
-    auto gemm = [&](const uint16_t* a_hi, const uint16_t* a_lo, int lda, const void* w, float* out, uint16_t* out_hi,
-                    uint16_t* out_lo, int ldc, int N, int K, int epi) {
+    auto gemm = [&](const uint16_t* a_hi, const uint16_t* a_lo, int lda, const void* w, const float* wscale, float* out,
+                    uint16_t* out_hi, uint16_t* out_lo, int ldc, int N, int K, int epi) {
       s2k::GemmArgs ga{};
       ga.a_hi = a_hi;
       ga.a_lo = a_lo;
       ga.lda = lda;
-      ga.w = static_cast<const uint16_t*>(w);
+      ga.w = w;
+      ga.wscale = wscale;
+      ga.w_fmt = !c->q8 ? s2k::W_BF16 : (c->f8 ? s2k::W_F8 : s2k::W_I8);
       ga.c = out;
       ga.c_hi = out_hi;
       ga.c_lo = out_lo;
@@ -1077,7 +1090,7 @@ struct Enq {
     for (int l = 0; l < st.n_layers; ++l) {
       const LayerW& L = c->slow[l];
       chk(s2k::launch_norm_split(c->px, H, H, eps, L.attn_norm, c->pxh, c->pxl, H, rows, s));
-      gemm(c->pxh, c->pxl, H, L.wqkv, c->pqkv, nullptr, nullptr, qkvd, qkvd, H, s2k::GEMM_STORE);
+      gemm(c->pxh, c->pxl, H, L.wqkv, L.sqkv, c->pqkv, nullptr, nullptr, qkvd, qkvd, H, s2k::GEMM_STORE);
       s2k::PrefillKvArgs kv{};
       kv.qkv = c->pqkv;
       kv.ld = qkvd;
@@ -1122,10 +1135,10 @@ struct Enq {
       pa.part_o = c->patt_o;
       pa.part_ml = c->patt_ml;
       chk(s2k::launch_prefill_attn(pa, s));
-      gemm(c->patth, c->pattl, qd, L.wo, c->px, nullptr, nullptr, H, H, qd, s2k::GEMM_ADD);
+      gemm(c->patth, c->pattl, qd, L.wo, L.so, c->px, nullptr, nullptr, H, H, qd, s2k::GEMM_ADD);
       chk(s2k::launch_norm_split(c->px, H, H, eps, L.mlp_norm, c->pxh, c->pxl, H, rows, s));
-      gemm(c->pxh, c->pxl, H, L.wgu, nullptr, c->pacth, c->pactl, F, 2 * F, H, s2k::GEMM_SWIGLU);
-      gemm(c->pacth, c->pactl, F, L.wdown, c->px, nullptr, nullptr, H, H, F, s2k::GEMM_ADD);
+      gemm(c->pxh, c->pxl, H, L.wgu, L.sgu, nullptr, c->pacth, c->pactl, F, 2 * F, H, s2k::GEMM_SWIGLU);
+      gemm(c->pacth, c->pactl, F, L.wdown, L.sdown, c->px, nullptr, nullptr, H, H, F, s2k::GEMM_ADD);
     }
   }
 
@@ -1143,12 +1156,14 @@ struct Enq {
   // next norm_b to fold into the residual
   // norm_gain != nullptr: the input rows are RMS-normalised on the fly with the sums of squares
   // that fold_b left in bssq
-  int mgemv(int epi, const void* w, const float* x, int ldx, float* out, int ldo, int N, int K, int M, int lo = 0,
-            int hi = 0, const float* norm_gain = nullptr) {
+  int mgemv(int epi, const void* w, const float* wscale, const float* x, int ldx, float* out, int ldo, int N, int K,
+            int M, int lo = 0, int hi = 0, const float* norm_gain = nullptr) {
     s2k::MgemvArgs a{};
     a.x = x;
     a.ldx = ldx;
-    a.w = static_cast<const uint16_t*>(w);
+    a.w = w;
+    a.wscale = wscale;
+    a.w_fmt = !c->q8 ? s2k::W_BF16 : (c->f8 ? s2k::W_F8 : s2k::W_I8);
     a.out = out;
     a.ldo = ldo;
     a.part = c->bpart;
@@ -1225,7 +1240,7 @@ struct Enq {
       const LayerW& L = W[l];
       fold_b(xres, pending, H, M);
       // q, k, v stay as split-K partials; the attention kernel sums them as it loads them
-      const int qkv_S = mgemv(s2k::MG_ADD, L.tqkv, xres, ldx, nullptr, 0, qkvd, H, M, 0, 0, L.attn_norm);
+      const int qkv_S = mgemv(s2k::MG_ADD, L.tqkv, L.sqkv, xres, ldx, nullptr, 0, qkvd, H, M, 0, 0, L.attn_norm);
       s2k::AttnArgs a{};
       a.qkv = c->bqkv;
       a.qkv_part = c->bpart;
@@ -1272,10 +1287,10 @@ struct Enq {
       }
       chk(s2k::launch_attention(a, s));
       if (a.max_splits > 1) chk(s2k::launch_attention_combine(a, s));
-      pending = mgemv(s2k::MG_ADD, L.to, c->batt, qd, nullptr, 0, H, qd, M);
+      pending = mgemv(s2k::MG_ADD, L.to, L.so, c->batt, qd, nullptr, 0, H, qd, M);
       fold_b(xres, pending, H, M);
-      mgemv(s2k::MG_SWIGLU, L.tgu, xres, ldx, c->bact, F, 2 * F, H, M, 0, 0, L.mlp_norm);
-      pending = mgemv(s2k::MG_ADD, L.tdown, c->bact, F, nullptr, 0, H, F, M);
+      mgemv(s2k::MG_SWIGLU, L.tgu, L.sgu, xres, ldx, c->bact, F, 2 * F, H, M, 0, 0, L.mlp_norm);
+      pending = mgemv(s2k::MG_ADD, L.tdown, L.sdown, c->bact, F, nullptr, 0, H, F, M);
       if (btp) {
         norm_b(xres, pending, H, M, nullptr);
         for (int b = 0; b < M; ++b) {
@@ -1339,7 +1354,7 @@ struct Enq {
       fast_step = j;
       int pending = layers_b(false, M, slots, c->bxf);
       fold_b(c->bxf, pending, H, M);
-      mgemv(s2k::MG_ARGMAX, c->fast_head_t, c->bxf, ldx, c->blogits, K, K, H, M, 0, K, c->fast_final);
+      mgemv(s2k::MG_ARGMAX, c->fast_head_t, c->fast_head_s, c->bxf, ldx, c->blogits, K, K, H, M, 0, K, c->fast_final);
       if (btp) {
         finish_b(s2k::FIN_CODE, j, M, slots, 0, K, c->bxf);
         for (int b = 0; b < M; ++b) {
@@ -1357,7 +1372,7 @@ struct Enq {
     int pending = layers_b(true, M, slots, c->bx);
     norm_b(c->bx, pending, H, M, c->slow_final);
     const int NH = c->head_rows, lo = c->head_lo;
-    mgemv(s2k::MG_ARGMAX, c->slow_head_t, c->bxn, ldx, c->blogits, NH, NH, H, M, lo, lo + K);
+    mgemv(s2k::MG_ARGMAX, c->slow_head_t, c->slow_head_s, c->bxn, ldx, c->blogits, NH, NH, H, M, lo, lo + K);
     finish_b(s2k::FIN_SLOW, 0, M, slots, lo, lo + K, c->bxf);
     if (btp)
       for (int b = 0; b < M; ++b) {
@@ -1802,7 +1817,7 @@ int s2ar_debug_frame(s2ar_ctx* c, int32_t sid, const int32_t* forced, s2ar_taps*
 
 int s2ar_debug_frame_batch(s2ar_ctx* c, const int32_t* ids, int32_t n, const int32_t* forced, s2ar_taps* taps) {
   if (!c) return S2AR_E_ARG;
-  if (!c->batched_ok) return set_err(c, S2AR_E_ARG, "batched decode needs bf16 weights and K dims divisible by 128");
+  if (!c->batched_ok) return set_err(c, S2AR_E_ARG, "batched decode needs bf16 tables and K dims divisible by 512");
   if (n > 16) return set_err(c, S2AR_E_ARG, "at most 16 streams per batched debug frame");
   if (int rc = check_streams(c, ids, n, 1)) return rc;
   const s2ar_config& g = c->cfg;

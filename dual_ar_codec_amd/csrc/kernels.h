@@ -103,6 +103,10 @@ hipError_t launch_finish(bool bf16, const FinishArgs& f, hipStream_t s);
 void set_device_cus(int n);
 int device_cus();
 
+// weight formats of the matrix-core kernels: bf16, or 8-bit codes (int8, OCP FP8 E4M3) with an fp32
+// scale per output row; the codes are exact in bf16, so the MFMA sees them unrounded
+enum WeightFmt : int { W_BF16 = 0, W_I8 = 1, W_F8 = 2 };
+
 // ---- prefill (prefill.hip) ----
 enum GemmEpi : int { GEMM_STORE = 0, GEMM_ADD = 1, GEMM_SWIGLU = 2 };
 // C[M][N] (=, +=) bf16(A[M][K] * a_scale[m] * a_gain[k]) . W[N][K]^T with fp32 accumulation on the
@@ -112,7 +116,9 @@ struct GemmArgs {
   const uint16_t* a_hi;    // [M][lda] activations as bf16 high parts
   const uint16_t* a_lo;    // [M][lda] and bf16 low parts (x - hi, rounded): x = hi + lo + O(2^-17 |x|)
   int lda;
-  const uint16_t* w;       // [N][K] bf16 weights
+  const void* w;           // [N][K] weights: bf16, or 8-bit codes (w_fmt) with a scale per row
+  const float* wscale;     // 8-bit weights: [N] row scales
+  int w_fmt;               // W_BF16, W_I8 or W_F8
   float* c;                // [M][ldc] fp32 output (GEMM_STORE, GEMM_ADD)
   uint16_t* c_hi;          // GEMM_SWIGLU: [M][ldc] silu(g) u as bf16 high and low planes
   uint16_t* c_lo;
@@ -209,7 +215,10 @@ enum MgemvEpi : int { MG_STORE = 0, MG_ADD = 1, MG_SWIGLU = 2, MG_ARGMAX = 3 };
 struct MgemvArgs {
   const float* x;          // [M][ldx] fp32 batch rows (normalised where a norm precedes)
   int ldx;
-  const uint16_t* w;       // bf16 [N][K] in the tiled layout of launch_tile_weights
+  const void* w;           // [N][K] in the tiled layout of launch_tile_weights (bf16) or
+                           // launch_tile_weights8 (8-bit codes)
+  const float* wscale;     // 8-bit weights: fp32 scale of each row, readable up to mgemv_tiles(N) * 64
+  int w_fmt;               // W_BF16, W_I8 or W_F8
   float* out;              // [M][ldo]
   int ldo;
   float* part;             // [S][M][N] split partials (S > 1, and always for MG_ADD)
@@ -232,6 +241,9 @@ hipError_t launch_mgemv(const MgemvArgs& a, hipStream_t s);
 // blocks of 4 KB, rows zero-padded to a multiple of 64; tiled_weight_elems(N, K) elements.
 size_t tiled_weight_elems(int N, int K);
 hipError_t launch_tile_weights(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t s);
+// The same tiling for 8-bit codes: 16-row x 128-K blocks of 2 KB in which each 16-byte piece is 16
+// consecutive codes of one row; tiled_weight_elems(N, K) bytes.
+hipError_t launch_tile_weights8(const uint8_t* src, uint8_t* dst, int N, int K, hipStream_t s);
 
 // x[j] += sum_s part[s][j] (split order, when S > 0); xn[j] = RMSNorm(x[j]) * gain.  M rows.
 struct NormRowsArgs {

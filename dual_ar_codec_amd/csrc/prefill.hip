@@ -11,9 +11,12 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace s2k {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -31,6 +34,32 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
   return v;
+}
+
+// eight 8-bit weight codes (int8, or OCP FP8 E4M3 through the hardware conversion) as eight bf16,
+// exactly (a code has at most 8 significant bits)
+template <int WF>
+__device__ __forceinline__ u32x4 widen8(const u32x2 p) {
+  uint32_t o[4];
+  const uint32_t wd[2] = {p.x, p.y};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    float f[4];
+    if constexpr (WF == W_I8) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[b] = (float)(int8_t)((wd[q] >> (8 * b)) & 0xffu);
+    } else {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], true);
+      f[0] = lo[0];
+      f[1] = lo[1];
+      f[2] = hi[0];
+      f[3] = hi[1];
+    }
+    o[2 * q] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+    o[2 * q + 1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
 }
 
 }  // namespace
@@ -63,7 +92,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
   const uint16_t* al_src = g.a_lo + (size_t)a_m * g.lda + a_k;
   // W: thread t loads 32 bytes of row t/2 at k (t%2)*16
   const int w_row = tid >> 1, w_k = (tid & 1) * 16;
-  const uint16_t* w_src = g.w + (size_t)(n0 + w_row) * g.K + w_k;
+  const uint16_t* w_src = static_cast<const uint16_t*>(g.w) + (size_t)(n0 + w_row) * g.K + w_k;
 
   u32x4 ahr[AE / 8], alr[AE / 8];
   u32x4 wr[2];
@@ -153,8 +182,11 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
 // stages before its compute.  Tiles are numbered with M fastest, and the blocks of one XCD
 // (block ids round-robin over the 8 XCDs) take a contiguous range of tiles, so the blocks that
 // share a weight column sit on one XCD and reuse it from that XCD's L2.
-template <int BM, int BN, int NW, int WM, int EPI>
+template <int BM, int BN, int NW, int WM, int EPI, int WF = W_BF16>
 __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
+  // WF: bf16 weights, or 8-bit codes loaded 8 bytes per lane, widened to bf16 when staged in LDS and
+  // scaled per output column (weight row) in the epilogue
+  using WR = typename std::conditional<WF == W_BF16, u32x4, u32x2>::type;
   // LDS row stride (bf16): 64 + 16.  Measured on the 1200-position prefill: 64 (no pad) 31.1 ms,
   // 72 26.5 ms, 80 25.9 ms; 80 fills the 160 KB of LDS exactly with the 128 x 256 tiles.
   constexpr int NT = NW * 64, WN = NW / WM, BK = 64, LS = BK + 16;
@@ -190,11 +222,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   for (int i = 0; i < AI; ++i) a_off[i] = (size_t)min(m0 + a_row0 + 8 * i, g.M - 1) * g.lda + r_k;
   // W rows: w_row0 + 8 i
   const int w_row0 = wv * (BN / NW) + (lane >> 3);
-  const uint16_t* w_src = g.w + (size_t)(n0 + w_row0) * g.K + r_k;
+  const size_t w_off = (size_t)(n0 + w_row0) * g.K + r_k;  // element (= byte for 8-bit codes) offset
 
   u32x4 ah0[AI], al0[AI], ah1[AI], al1[AI];
-  u32x4 wr0[WI], wr1[WI];
-  auto load = [&](int kt, u32x4 (&ah)[AI], u32x4 (&al)[AI], u32x4 (&wr)[WI]) {
+  WR wr0[WI], wr1[WI];
+  auto load = [&](int kt, u32x4 (&ah)[AI], u32x4 (&al)[AI], WR (&wr)[WI]) {
     const int k = (kbeg + min(kt, nk - 1)) * BK;  // past the end: reload the last stage (never computed)
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
@@ -202,10 +234,16 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
       al[i] = *reinterpret_cast<const u32x4*>(g.a_lo + a_off[i] + k);
     }
 #pragma unroll
-    for (int i = 0; i < WI; ++i)
-      wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w_src + (size_t)8 * i * g.K + k));
+    for (int i = 0; i < WI; ++i) {
+      if constexpr (WF == W_BF16)
+        wr[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.w) + w_off + (size_t)8 * i * g.K + k));
+      else
+        wr[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(g.w) + w_off + (size_t)8 * i * g.K + k));
+    }
   };
-  auto stash = [&](int st, const u32x4 (&ah)[AI], const u32x4 (&al)[AI], const u32x4 (&wr)[WI]) {
+  auto stash = [&](int st, const u32x4 (&ah)[AI], const u32x4 (&al)[AI], const WR (&wr)[WI]) {
     uint16_t* sh = lds + st * STAGE;
     uint16_t* sl = sh + BM * LS;
     uint16_t* sw = sl + BM * LS;
@@ -215,7 +253,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
       *reinterpret_cast<u32x4*>(sl + (a_row0 + 8 * i) * LS + r_k) = al[i];
     }
 #pragma unroll
-    for (int i = 0; i < WI; ++i) *reinterpret_cast<u32x4*>(sw + (w_row0 + 8 * i) * LS + r_k) = wr[i];
+    for (int i = 0; i < WI; ++i) {
+      if constexpr (WF == W_BF16) *reinterpret_cast<u32x4*>(sw + (w_row0 + 8 * i) * LS + r_k) = wr[i];
+      else *reinterpret_cast<u32x4*>(sw + (w_row0 + 8 * i) * LS + r_k) = widen8<WF>(wr[i]);
+    }
   };
 
   f32x4 acc[TM][TN];
@@ -265,6 +306,16 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
     __syncthreads();
   }
 
+  if constexpr (WF != W_BF16) {  // 8-bit codes: scale each column by its weight row's scale
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float sc = g.wscale[n0 + wn * (BN / WN) + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] *= sc;
+    }
+  }
   // epilogue: lane holds rows 4 (lane/16) + r, column lane % 16 of each 16 x 16 tile
   if (g.split > 1) {  // the slice's partial sums; k_gemm_split_reduce adds the slices and applies EPI
     float* part = g.part + (size_t)ks * g.M * g.N;
@@ -351,7 +402,10 @@ template <int BM, int BN, int EPI>
 static hipError_t gemm2_launch(GemmArgs g, hipStream_t s) {
   const int ntiles = (g.M + BM - 1) / BM * (g.N / BN);
   g.split = gemm_splits(g, ntiles);
-  hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI>), dim3(ntiles * g.split), dim3(512), 0, s, g);
+  const dim3 grid(ntiles * g.split), block(512);
+  if (g.w_fmt == W_I8) hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_I8>), grid, block, 0, s, g);
+  else if (g.w_fmt == W_F8) hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_F8>), grid, block, 0, s, g);
+  else hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI>), grid, block, 0, s, g);
   if (g.split > 1) {
     const int cols = EPI == GEMM_SWIGLU ? g.N / 2 : g.N;
     hipLaunchKernelGGL(k_gemm_split_reduce<EPI>, dim3((cols + 255) / 256, g.M), dim3(256), 0, s, g);
@@ -361,6 +415,7 @@ static hipError_t gemm2_launch(GemmArgs g, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.N % 128 || g.K % 32 || g.M < 1) return hipErrorInvalidValue;
+  if (g.w_fmt != W_BF16 && (g.K % 64 || !g.wscale)) return hipErrorInvalidValue;  // 8-bit: k_gemm2 only
   // the 8-wavefront kernel for every prompt length (rows past M repeat the last row and are not
   // stored): at 64..200 rows it ran the full-shape prefill in 14-15 ms against 25-30 ms for the
   // 4-wavefront kernel, which remains for K not divisible by 64

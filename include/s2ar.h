@@ -61,9 +61,9 @@ typedef struct {
   int32_t weight_dtype;   /* 0: fp32 weights, 1: bf16 weights, 2: bf16 tensors with the layer matrices and
                              both heads stored as int8 with one fp32 scale per output row (symmetric:
                              s = max|w| / 127, q = rint(w / s), computed in fp32 at create; a zero row
-                             has s = 0); embeddings, codebooks and gains stay bf16.  Int8 contexts run
-                             prefill position by position and decode streams one at a time
-                             ("s2pro-native", Where it stands; The gate that says no); 3: as 2 with
+                             has s = 0); embeddings, codebooks and gains stay bf16.  Prefill and
+                             batched decode run the 8-bit codes on the matrix cores as they do bf16
+                             weights ("s2pro-native", Where it stands; The gate that says no); 3: as 2 with
                              OCP FP8 E4M3 codes instead of int8 (s = max|w| / 448, q = the E4M3 value
                              nearest w / s, ties to the even code), measured only: the same page
                              reports FP8 weights as fast but failing its fidelity gate. */
@@ -229,7 +229,7 @@ int s2ar_debug_frame(s2ar_ctx* ctx, int32_t stream_id, const int32_t* forced_cod
 
 /* The batched multi-stream frame (the kernels s2ar_decode_frame uses for 2..16 streams), run
  * without the captured graph: forced_codes [n][n_codebooks] or NULL, taps [n] (fast_z and
- * slow_embed are not filled).  Needs bf16 weights and every K dimension divisible by 512
+ * slow_embed are not filled).  Needs weight_dtype 1, 2 or 3 and every K dimension divisible by 512
  * (S2AR_E_ARG otherwise); n <= 16. */
 int s2ar_debug_frame_batch(s2ar_ctx* ctx, const int32_t* stream_ids, int32_t n, const int32_t* forced_codes,
                            s2ar_taps* taps);

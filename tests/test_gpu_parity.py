@@ -323,25 +323,89 @@ def test_shared_prefix_errors_leave_state_unchanged():
     ctx.close()
 
 
-def _int8_teacher_forced(name, n_frames, fmt="i8"):
-    cfg = synth.config(name)
+def _int8_teacher_forced(name, n_frames, fmt="i8", prompt=None, **over):
+    cfg = synth.config(name, **over)
     _say(f"[parity] {name} {fmt}: generating weights")
     w = synth.make_weights(cfg)
     ocfg, ow = quant_reference(cfg, w, fmt)
-    toks, _, _ = synth.make_prompt(cfg)
+    toks, mask, codes = prompt if prompt is not None else synth.make_prompt(cfg)
+    mk, cd = (mask, codes) if mask.any() else (None, None)
     _say(f"[parity] {name} {fmt}: oracle prefill {len(toks)} + {n_frames} frames")
-    frames = oracle_run(ocfg, ow, toks, None, None, n_frames)
+    frames = oracle_run(ocfg, ow, toks, mk, cd, n_frames)
     del ow
     gc.collect()
     _say(f"[parity] {name} {fmt}: GPU")
     ctx = _ctx(dict(cfg, weight_dtype=fmt), w)
     del w
     gc.collect()
-    ctx.prefill(0, toks)
+    ctx.prefill(0, toks, mk, cd)
     rep = compare_frames(ctx, 0, frames, cfg).finish()
     _say(f"[parity] {name} {fmt}: {rep}")
     ctx.close()
     return rep
+
+
+def test_int8_vq_prompt_prefill_on_the_matrix_cores_mid():
+    """A 300-position VQ-masked prompt (200 VQ positions, then text) prefilled with int8 weights: the
+    matrix-core GEMMs widen the codes to bf16 in LDS and scale each output column."""
+    cfg = synth.config("mid", max_context=384)
+    r = np.random.default_rng(71)
+    n = 300
+    toks = r.integers(0, cfg["vocab_text"], n).astype(np.int32)
+    codes = r.integers(0, cfg["codebook_size"], (n, 10)).astype(np.int32)
+    mask = np.zeros(n, np.uint8)
+    mask[:200] = 1
+    for fmt in ("i8", "f8"):
+        rep = _int8_teacher_forced("mid", 3, fmt, prompt=(toks, mask, codes), max_context=384)
+        assert rep["tokens_checked"] > 0
+
+
+@pytest.mark.timeout(1500)
+def test_int8_voice_clone_prefill_teacher_forced():
+    """The 1200-position voice-clone prompt (1000 VQ + 200 text) at the full S2 shape with int8 weights,
+    prefilled on the matrix cores in one row block, then 2 frames against the oracle on the same
+    quantisation."""
+    assert _int8_teacher_forced("voice_clone", 2)["tokens_checked"] > 0
+
+
+@pytest.mark.parametrize("fmt", ["i8", "f8"])
+def test_int8_weights_batched_mid_ragged(fmt):
+    """8-bit weights through the batched kernels (tiled 8-bit copies, widened to bf16 for the matrix
+    cores, row scales on the partial sums) for five ragged streams."""
+    cfg = synth.config("mid", max_context=640)
+    w = synth.make_weights(cfg)
+    ocfg, ow = quant_reference(cfg, w, fmt)
+    prompts = _ragged_prompts(cfg, [64, 17, 300, 130, 5], 31)
+    per_stream = _oracle_frames_per_stream(ocfg, ow, prompts, 3)
+    del ow
+    ctx = _ctx(dict(cfg, weight_dtype=fmt), w, max_streams=6)
+    ids = [0, 2, 3, 4, 5]
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
+    _say(f"[parity] batched mid, {fmt} weights: {rep}")
+    ctx.close()
+
+
+@pytest.mark.timeout(1500)
+def test_int8_weights_batched_full_shape():
+    """Int8 weights, batched decode at the full S2 shape (three streams, bf16 keys)."""
+    cfg = synth.config("multi_stream", max_context=256, kv_dtype="k_bf16")
+    w = synth.make_weights(cfg)
+    ocfg, ow = quant_reference(cfg, w, "i8")
+    prompts = _ragged_prompts(cfg, [41, 9, 70], 32)
+    per_stream = _oracle_frames_per_stream(ocfg, ow, prompts, 2)
+    del ow
+    gc.collect()
+    ctx = _ctx(dict(cfg, weight_dtype="i8"), w, max_streams=4)
+    del w
+    gc.collect()
+    ids = [1, 0, 3]
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
+    _say(f"[parity] batched full, int8 weights: {rep}")
+    ctx.close()
 
 
 def test_int8_weights_mid_teacher_forced():
