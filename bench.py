@@ -270,6 +270,8 @@ def main():
     ap.add_argument("--kernel-iters", type=int, default=144)
     ap.add_argument("--prefill", type=int, default=1, help="also time a 1200-position voice-clone prefill")
     ap.add_argument("--multi-steps", type=int, default=20, help="batched 16-stream decode steps (0 = skip)")
+    ap.add_argument("--multi-lines", default="k_bf16,f32,bf16,int8",
+                    help="which 16-stream lines to run: k_bf16 (the workload's), f32, bf16, int8")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a 256 MiB copy (counter calibration)")
     ap.add_argument("--int8-steps", type=int, default=40, help="batch-1 frames with int8 weights (0 = skip)")
     ap.add_argument("--fp8-steps", type=int, default=40, help="batch-1 frames with FP8 E4M3 weights (0 = skip)")
@@ -394,10 +396,14 @@ def main():
     mid = mid_workload(log) if args.mid else None
 
     multi = multi_f32 = multi_bf16 = multi_i8 = None
-    if args.multi_steps > 0:
+    lines = args.multi_lines.split(",") if args.multi_steps > 0 else []
+    if "k_bf16" in lines:
         multi = multi_stream(args, w, log, "k_bf16")
+    if "f32" in lines:
         multi_f32 = multi_stream(args, w, log, "f32")
+    if "bf16" in lines:
         multi_bf16 = multi_stream(args, w, log, "bf16")
+    if "int8" in lines:
         multi_i8 = multi_stream(args, w, log, "k_bf16", "i8")
 
     if args.copy_probe:
