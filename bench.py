@@ -277,6 +277,9 @@ def main():
     ap.add_argument("--fp8-steps", type=int, default=40, help="batch-1 frames with FP8 E4M3 weights (0 = skip)")
     ap.add_argument("--slice-steps", type=int, default=60, help="batch-1 frames with the semantic-slice head (0 = skip)")
     ap.add_argument("--mid", type=int, default=1, help="also time the mid workload (32 frames)")
+    ap.add_argument("--counter-pass", type=int, default=0,
+                    help="for rocprofv3 --pmc passes: prefill, 2 frames enqueued without graphs, the gate/up and "
+                         "streaming-read launches (--kernel-iters each) and the 256 MiB copy probe, then exit")
     ap.add_argument("--prefix-share", type=int, default=1,
                     help="time to first frame of the voice-clone prompt with its 1000-position prefix shared")
     args = ap.parse_args()
@@ -304,6 +307,20 @@ def main():
     log(f"[bench] weights in {time.perf_counter() - t:.1f} s; uploading")
     toks, mask, codes = synth.make_prompt(cfg)
     ctx = s2ar.Context(cfg, w, max_streams=3 if args.prefix_share else 2)
+    if args.counter_pass:
+        ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
+        out = ctx.decode_frames_noalloc(0, 2)
+        ms, nbytes = ctx.time_kernel(0, args.kernel_iters)
+        sms, sbytes = ctx.time_kernel(1, args.kernel_iters)
+        ctx.close()
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_pass": True, "frames": out.tolist(), "gate_up_us": round(ms * 1e3, 2),
+                          "gate_up_bytes": nbytes, "stream_us": round(sms * 1e3, 2), "copy_bytes": 256 << 20}))
+        return
     log("[bench] prefill + warmup")
     ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
     if args.warmup:
