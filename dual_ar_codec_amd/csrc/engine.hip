@@ -143,6 +143,7 @@ struct s2ar_ctx {
   // batched decode: positions per attention workgroup (16 streams of 920..3948 positions measured
   // 9.80 ms per step at 192, 10.20 at 256, 10.52 at 128)
   int attn_split_b = 192, max_splits_b = 0;
+  bool attn_long = false;  // batched Slow attention through launch_attention_long (256-key splits)
 
   // batched prefill (MFMA): chunk of up to pch prompt rows
   int pch = 0;
@@ -822,6 +823,11 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
                                          c->stream));
       }
       C_HIP(hipStreamSynchronize(c->stream));
+#ifndef S2AR_ATTN_LONG
+#define S2AR_ATTN_LONG 1
+#endif
+      c->attn_long = S2AR_ATTN_LONG && s2k::attention_long_supports(g.slow.head_dim, g.slow.n_q_heads, g.slow.n_kv_heads);
+      if (c->attn_long) c->attn_split_b = 256;
       c->max_splits_b = (g.max_context + c->attn_split_b - 1) / c->attn_split_b;
       C_TRY(dev_alloc(c, &c->batt_ml, sizeof(float) * 2 * MBt * hq * c->max_splits_b));
       C_TRY(dev_alloc(c, &c->batt_o, sizeof(float) * (size_t)MBt * hq * c->max_splits_b * dmax));
@@ -1285,7 +1291,7 @@ struct Enq {
         a.bt_stride = 1;
         a.max_splits = 1;
       }
-      chk(s2k::launch_attention(a, s));
+      chk(is_slow && c->attn_long ? s2k::launch_attention_long(a, s) : s2k::launch_attention(a, s));
       if (a.max_splits > 1) chk(s2k::launch_attention_combine(a, s));
       pending = mgemv(s2k::MG_ADD, L.to, L.so, c->batt, qd, nullptr, 0, H, qd, M);
       fold_b(xres, pending, H, M);

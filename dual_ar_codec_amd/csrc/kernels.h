@@ -77,6 +77,11 @@ struct AttnArgs {
 // max_splits > 1; it does nothing for contexts that fit one split).
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t s);
+// The same attention for long contexts of many streams (the batched step): splits of 256 keys
+// (a.split must be 256), four wavefronts of 64 keys each reading the key and value rows straight
+// from the cache; split partials merge with launch_attention_combine as above.
+hipError_t launch_attention_long(const AttnArgs& a, hipStream_t s);
+bool attention_long_supports(int D, int Hq, int Hkv);  // head_dim 64 or 128, 1, 2 or 4 q heads per KV head
 
 // Second pass of the greedy pick over per-block maxima of blocks [b0, b1] (ties to the lowest
 // index), followed by the step's bookkeeping (see FinishMode).

@@ -1105,6 +1105,375 @@ __global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
   for (int i = 0; i < PER; ++i) out[lane + i * WAVE] = acc[i] * inv;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Decode attention over long paged contexts (the batched multi-stream step).  grid = (splits of
+// LONG_SPLIT keys, Hkv, M), block = 4 wavefronts; wavefront w takes keys s0 + 64 w .. + 63 of its
+// split.  Nothing is staged in LDS: every load reads cache rows straight into registers, LPK
+// adjacent lanes covering one row 16 bytes each, so a load instruction reads KPI whole rows (one
+// contiguous run of a page).
+//   Scores: lane (r, c) holds the q slice of its 16-byte column c for the G heads of the KV group
+// (read once from LDS) and forms partial dot products; a reduce-scatter over the LPK lanes of a
+// row (halving exchanges, one shuffle per retained value) leaves lane (r, c) with the whole score
+// of key KPI c + r.  The loads go in groups of four, the next group in flight while one is used.
+//   Weighted sum: lane (rv, cv) accumulates dimensions cv EPV .. + EPV of the keys KPV i + rv,
+// the weights read from LDS, then the KPV key lanes are added by shuffles.
+//   Each wavefront keeps one softmax state per head over its 64 keys; the four wavefronts' (max,
+// sum, output) merge in LDS in wavefront order.
+constexpr int LONG_SPLIT = 256;
+constexpr int kBufWord3 = 0x00020000;  // fourth descriptor word of a raw (untyped) gfx9 buffer
+constexpr int kNonTemp = 2;            // nontemporal cache policy of a buffer load
+
+template <int D, int G, bool KB, bool VB>
+__global__ __launch_bounds__(256, 4) void k_attn_long(const AttnArgs a) {
+  using KK = KvT<KB>;
+  using VV = KvT<VB>;
+  using TK = typename KK::T;
+  using TV = typename VV::T;
+  constexpr int NW = 4, CH = WAVE, PER = D / WAVE, PS = 16;
+  constexpr int EPK = 16 / sizeof(TK), LPK = D / EPK, KPI = WAVE / LPK, NI = LPK;
+  constexpr int QK = 4, RK = NI / QK;  // key loads per group, groups
+  constexpr int EPV = 16 / sizeof(TV), LPV = D / EPV, KPV = WAVE / LPV, NIV = LPV;
+  constexpr int QV = 4, RV = NIV / QV;
+  static_assert(KPI <= PS && PS % KPI == 0 && KPV <= PS && PS % KPV == 0, "load rows inside one page");
+  static_assert(RK >= 1 && RV >= 1 && G <= NW, "shape");
+  __shared__ __attribute__((aligned(16))) float q_s[G][D];
+  __shared__ __attribute__((aligned(16))) float kn_s[D];
+  __shared__ __attribute__((aligned(16))) float vn_s[D];
+  __shared__ __attribute__((aligned(16))) float p_s[NW][CH][G];
+  __shared__ float m_s[NW][G], l_s[NW][G];
+  __shared__ __attribute__((aligned(16))) float o_s[NW][G][D];
+
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int r = lane / LPK, c = lane % LPK;
+  const int rv = lane / LPV, cv = lane % LPV;
+  // values the whole block shares, read by vector loads (the kernel writes global memory): marked
+  // wave-uniform so that the buffer resources built from them stay in scalar registers
+  const int slot = __builtin_amdgcn_readfirstlane(a.fixed_slot >= 0 ? a.fixed_slot : a.slots[b]);
+  const int s0 = sp * LONG_SPLIT, k0 = s0 + CH * w;
+  // this wavefront's four page-table entries (read in bounds of the table, used below ctx only)
+  int pgw[CH / PS];
+#pragma unroll
+  for (int q = 0; q < CH / PS; ++q) {
+    const int pi = k0 / PS + q;
+    pgw[q] = __builtin_amdgcn_readfirstlane(pi < a.bt_stride ? a.block_table[slot * a.bt_stride + pi] : 0);
+  }
+  const int pos = __builtin_amdgcn_readfirstlane(a.const_pos >= 0 ? a.const_pos : (a.row_pos ? a.row_pos[b] : a.pos[slot]));
+  const int ctx = pos + 1;
+  const int nsplit = (ctx + LONG_SPLIT - 1) / LONG_SPLIT;
+  if (sp >= nsplit) return;
+  const int s1 = min(s0 + LONG_SPLIT, ctx);
+  const bool has_new = a.append && pos >= s0 && pos < s1;
+  const int nk = max(0, min(CH, s1 - k0));   // keys of this wavefront
+  const int jn = has_new ? pos - k0 : -1;    // the new position, relative to k0
+  TK* kc = static_cast<TK*>(a.k_cache);
+  TV* vc = static_cast<TV*>(a.v_cache);
+  // One buffer resource per page of this wavefront: the page's 16 rows of this KV head, cut at
+  // the end of the split's cached keys (the new position, appended by this kernel, is not read
+  // back), so loads past it return zeros without touching memory.
+  const int e1 = has_new ? pos : s1;
+  __amdgpu_buffer_rsrc_t kr_[CH / PS], vr_[CH / PS];
+#pragma unroll
+  for (int q = 0; q < CH / PS; ++q) {
+    const int rows = max(0, min(PS, e1 - (k0 + q * PS)));
+    const size_t base = ((size_t)(rows > 0 ? pgw[q] : 0) * a.Hkv + g) * PS * D;
+    kr_[q] = __builtin_amdgcn_make_buffer_rsrc(kc + base, (short)0, rows * D * (int)sizeof(TK), kBufWord3);
+    vr_[q] = __builtin_amdgcn_make_buffer_rsrc(vc + base, (short)0, rows * D * (int)sizeof(TV), kBufWord3);
+  }
+  // lane byte offsets inside a page; the whole offset goes in the vector operand (the scalar
+  // offset is left 0), which is what the range check covers
+  const int koff = (r * D + c * EPK) * (int)sizeof(TK), voff = (rv * D + cv * EPV) * (int)sizeof(TV);
+  // key loads: group j holds instructions j, j + RK, j + 2 RK, j + 3 RK; instruction i reads rows
+  // KPI i .. KPI i + KPI - 1 of the wavefront's keys
+  auto kload = [&](u32x4 (&buf)[QK], int j) {
+#pragma unroll
+    for (int t = 0; t < QK; ++t) {
+      const int k = KPI * (j + RK * t);
+      buf[t] = __builtin_amdgcn_raw_buffer_load_b128(kr_[k / PS], koff + (k % PS) * D * (int)sizeof(TK), 0, kNonTemp);
+    }
+  };
+  u32x4 kb[2][QK];
+  kload(kb[0], 0);
+  if constexpr (RK > 1) kload(kb[1], 1);
+
+  // element n of this batch row's q | k | v vector: the qkv row, or the sum of the split-K partials
+  // in split order
+  auto qkv_elem = [&](int n, float (&out)[PER]) {
+    if (a.qkv_S == 0) {
+      const float* qrow = a.qkv + (size_t)b * (a.Hq + 2 * a.Hkv) * D;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) out[i] = qrow[n + i * WAVE];
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[i] = 0.f;
+    const float* p = a.qkv_part + (size_t)b * a.qkv_ldp;
+    const size_t st = (size_t)16 * a.qkv_ldp;
+    for (int s8 = 0; s8 < a.qkv_S; s8 += 8) {
+      float t[PER][8];
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[i][u] = (s8 + u < a.qkv_S) ? p[(s8 + u) * st + n + i * WAVE] : 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s8 + u < a.qkv_S) out[i] += t[i][u];
+    }
+  };
+  const float* crow = a.rope_cos + (size_t)pos * (D / 2);
+  const float* srow = a.rope_sin + (size_t)pos * (D / 2);
+  if (w < G) {  // q head g G + w: QK-norm, RoPE, scale
+    float qv[PER];
+    qkv_elem((g * G + w) * D + lane, qv);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ss = fmaf(qv[i], qv[i], ss);
+    const float rq = rsqrtf(wave_sum(ss) / (float)D + a.eps);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) qv[i] = qv[i] * rq * a.q_norm[lane + i * WAVE];
+    rope_lane<D>(qv, crow, srow, lane);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) q_s[w][lane + i * WAVE] = qv[i] * a.scale;
+  }
+  if (has_new && w == NW - 1) {  // the new key (QK-norm, RoPE) and value, appended to the cache
+    float kv[PER], vv[PER];
+    qkv_elem((a.Hq + g) * D + lane, kv);
+    qkv_elem((a.Hq + a.Hkv + g) * D + lane, vv);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ss = fmaf(kv[i], kv[i], ss);
+    const float rk = rsqrtf(wave_sum(ss) / (float)D + a.eps);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) kv[i] = kv[i] * rk * a.k_norm[lane + i * WAVE];
+    rope_lane<D>(kv, crow, srow, lane);
+    const size_t off = (((size_t)a.block_table[slot * a.bt_stride + pos / PS] * a.Hkv + g) * PS + pos % PS) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int d = lane + i * WAVE;
+      kn_s[d] = KK::round(kv[i]);
+      vn_s[d] = VV::round(vv[i]);
+      kc[off + d] = KK::cvt(kv[i]);
+      vc[off + d] = VV::cvt(vv[i]);
+    }
+  }
+  __syncthreads();
+
+  // ---- scores
+  float qf[G][EPK];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPK; e += 4) {
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(&q_s[h][c * EPK + e]);
+      qf[h][e] = q4.x;
+      qf[h][e + 1] = q4.y;
+      qf[h][e + 2] = q4.z;
+      qf[h][e + 3] = q4.w;
+    }
+  float ret[RK][G];
+#pragma unroll
+  for (int j = 0; j < RK; ++j) {
+    float v[QK][G];
+#pragma unroll
+    for (int t = 0; t < QK; ++t) {
+      float kx[EPK];
+      const u32x4 kr = kb[j & 1][t];
+      if constexpr (KB) {
+        kx[0] = bf_lo(kr.x); kx[1] = bf_hi(kr.x); kx[2] = bf_lo(kr.y); kx[3] = bf_hi(kr.y);
+        kx[4] = bf_lo(kr.z); kx[5] = bf_hi(kr.z); kx[6] = bf_lo(kr.w); kx[7] = bf_hi(kr.w);
+      } else {
+        kx[0] = __uint_as_float(kr.x); kx[1] = __uint_as_float(kr.y);
+        kx[2] = __uint_as_float(kr.z); kx[3] = __uint_as_float(kr.w);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPK; ++e) acc = fmaf(qf[h][e], kx[e], acc);
+        v[t][h] = acc;
+      }
+    }
+    if (j + 2 < RK) kload(kb[j & 1], j + 2);
+    __builtin_amdgcn_sched_barrier(0);  // keep the two-group pipeline as written
+    // within the group: exchanges over lane bits LPK/2 .. LPK/QK keep instruction j + RK (c / RK)
+#pragma unroll
+    for (int n = QK, m = LPK / 2; n > 1; n >>= 1, m >>= 1) {
+      const bool hi = (c & m) != 0;
+#pragma unroll
+      for (int k = 0; k < n / 2; ++k)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float send = hi ? v[k][h] : v[k + n / 2][h];
+          const float keep = hi ? v[k + n / 2][h] : v[k][h];
+          v[k][h] = keep + __shfl_xor(send, m, WAVE);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) ret[j][h] = v[0][h];
+  }
+  // value loads (instructions 4 j .. 4 j + 3 in group j), the first groups in flight during the softmax
+  auto vload = [&](u32x4 (&buf)[QV], int j) {
+#pragma unroll
+    for (int t = 0; t < QV; ++t) {
+      const int k = KPV * (QV * j + t);
+      buf[t] = __builtin_amdgcn_raw_buffer_load_b128(vr_[k / PS], voff + (k % PS) * D * (int)sizeof(TV), 0, kNonTemp);
+    }
+  };
+  u32x4 vb[2][QV];
+  vload(vb[0], 0);
+  if constexpr (RV > 1) vload(vb[1], 1);
+  // across the groups: exchanges over lane bits RK/2 .. 1 keep group c % RK
+#pragma unroll
+  for (int n = RK, m = RK / 2; n > 1; n >>= 1, m >>= 1) {
+    const bool hi = (c & m) != 0;
+#pragma unroll
+    for (int k = 0; k < n / 2; ++k)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float send = hi ? ret[k][h] : ret[k + n / 2][h];
+        const float keep = hi ? ret[k + n / 2][h] : ret[k][h];
+        ret[k][h] = keep + __shfl_xor(send, m, WAVE);
+      }
+  }
+  // lane (r, c) now holds the scores of key KPI c + r; the new position (read as zeros) gets
+  // its score from LDS
+  const int kq = KPI * c + r;
+  const bool live = kq < nk;
+  if (jn >= 0 && jn < CH) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) t = fmaf(q_s[h][lane + i * WAVE], kn_s[lane + i * WAVE], t);
+      t = wave_sum(t);
+      if (kq == jn) ret[0][h] = t;
+    }
+  }
+  float mh[G], lh[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mh[h] = wave_max(live ? ret[0][h] : -INFINITY);
+    const float pw = live ? expf(ret[0][h] - mh[h]) : 0.f;
+    lh[h] = wave_sum(pw);
+    p_s[w][kq][h] = pw;
+  }
+  __syncthreads();
+
+  // ---- weighted sum
+  float o[G][EPV];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) o[h][e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < RV; ++j) {
+#pragma unroll
+    for (int t = 0; t < QV; ++t) {
+      const int kk = KPV * (QV * j + t) + rv;
+      float vx[EPV];
+      const u32x4 vr = vb[j & 1][t];
+      if constexpr (VB) {
+        vx[0] = bf_lo(vr.x); vx[1] = bf_hi(vr.x); vx[2] = bf_lo(vr.y); vx[3] = bf_hi(vr.y);
+        vx[4] = bf_lo(vr.z); vx[5] = bf_hi(vr.z); vx[6] = bf_lo(vr.w); vx[7] = bf_hi(vr.w);
+      } else {
+        vx[0] = __uint_as_float(vr.x); vx[1] = __uint_as_float(vr.y);
+        vx[2] = __uint_as_float(vr.z); vx[3] = __uint_as_float(vr.w);
+      }
+      float pk[G];
+      if constexpr (G == 4) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&p_s[w][kk][0]);
+        pk[0] = p4.x; pk[1] = p4.y; pk[2] = p4.z; pk[3] = p4.w;
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) pk[h] = p_s[w][kk][h];
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) o[h][e] = fmaf(pk[h], vx[e], o[h][e]);
+    }
+    if (j + 2 < RV) vload(vb[j & 1], j + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the new position's value (read as zeros), weighted once, in key lane 0
+  if (jn >= 0 && jn < CH) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pn = rv == 0 ? p_s[w][jn][h] : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) o[h][e] = fmaf(pn, vn_s[cv * EPV + e], o[h][e]);
+    }
+  }
+  // add the KPV key lanes of each column
+#pragma unroll
+  for (int m = LPV; m < WAVE; m <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) o[h][e] += __shfl_xor(o[h][e], m, WAVE);
+  if (rv == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) o_s[w][h][cv * EPV + e] = o[h][e];
+  if (lane == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m_s[w][h] = mh[h];
+      l_s[w][h] = lh[h];
+    }
+  __syncthreads();
+  // merge the four wavefronts in wavefront order
+  for (int idx = tid; idx < G * D; idx += NW * WAVE) {
+    const int h = idx / D, d = idx % D;
+    float M = m_s[0][h];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) M = fmaxf(M, m_s[v][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float e = m_s[v][h] == -INFINITY ? 0.f : expf(m_s[v][h] - M);
+      L = fmaf(e, l_s[v][h], L);
+      O = fmaf(e, o_s[v][h][d], O);
+    }
+    const int hq = g * G + h;
+    if (nsplit == 1) {
+      a.out[((size_t)b * a.Hq + hq) * D + d] = O / L;
+    } else {
+      const size_t pi = ((size_t)b * a.Hq + hq) * a.max_splits + sp;
+      a.part_o[pi * D + d] = O;
+      if (d == 0) {
+        a.part_ml[pi * 2] = M;
+        a.part_ml[pi * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+hipError_t launch_attention_long(const AttnArgs& a, hipStream_t s) {
+  if (a.split != LONG_SPLIT || a.page_size != 16 || a.Hkv <= 0 || a.Hq % a.Hkv) return hipErrorInvalidValue;
+  const int G = a.Hq / a.Hkv;
+  const dim3 grid(a.max_splits, a.Hkv, a.M);
+#define S2_ATL(DD, GG)                                                                                        \
+  if (a.D == DD && G == GG) {                                                                                 \
+    if (a.k_bf16 && a.v_bf16) hipLaunchKernelGGL((k_attn_long<DD, GG, true, true>), grid, dim3(256), 0, s, a);  \
+    else if (a.k_bf16) hipLaunchKernelGGL((k_attn_long<DD, GG, true, false>), grid, dim3(256), 0, s, a);        \
+    else if (a.v_bf16) hipLaunchKernelGGL((k_attn_long<DD, GG, false, true>), grid, dim3(256), 0, s, a);        \
+    else hipLaunchKernelGGL((k_attn_long<DD, GG, false, false>), grid, dim3(256), 0, s, a);                     \
+    return hipGetLastError();                                                                                 \
+  }
+  S2_ATL(64, 1) S2_ATL(64, 2) S2_ATL(64, 4)
+  S2_ATL(128, 1) S2_ATL(128, 2) S2_ATL(128, 4)
+#undef S2_ATL
+  return hipErrorInvalidValue;
+}
+
+bool attention_long_supports(int D, int Hq, int Hkv) {
+  return (D == 64 || D == 128) && Hkv > 0 && Hq % Hkv == 0 && (Hq / Hkv == 1 || Hq / Hkv == 2 || Hq / Hkv == 4);
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.split > 256 || a.split % 64 || a.page_size != 16) return hipErrorInvalidValue;
   const int G = a.Hq / a.Hkv;
