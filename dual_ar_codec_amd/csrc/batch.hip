@@ -38,10 +38,11 @@ constexpr int XROW = KC + 8;          // LDS row stride in bf16 (padded against 
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t a = __float_as_uint(f);
-  a += 0x7fffu + ((a >> 16) & 1u);
-  return a >> 16;
+// two floats as one packed bf16 pair (a in the low half), one conversion instruction
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  typedef float f32v2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32v2{a, b}, bf16v2));
 }
 
 __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
@@ -50,10 +51,9 @@ __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
   uint32_t* lp = reinterpret_cast<uint32_t*>(&l);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t h0 = bf16_bits(v[2 * i]), h1 = bf16_bits(v[2 * i + 1]);
-    const float r0 = v[2 * i] - __uint_as_float(h0 << 16), r1 = v[2 * i + 1] - __uint_as_float(h1 << 16);
-    hp[i] = h0 | (h1 << 16);
-    lp[i] = bf16_bits(r0) | (bf16_bits(r1) << 16);
+    const uint32_t h = bf16_pair(v[2 * i], v[2 * i + 1]);
+    hp[i] = h;
+    lp[i] = bf16_pair(v[2 * i] - __uint_as_float(h << 16), v[2 * i + 1] - __uint_as_float(h & 0xffff0000u));
   }
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, l);

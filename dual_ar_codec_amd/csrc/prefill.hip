@@ -24,10 +24,14 @@ namespace {
 
 constexpr int WAVE = 64;
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t a = __float_as_uint(f);
-  a += 0x7fffu + ((a >> 16) & 1u);
-  return a >> 16;
+// bf16 of f rounded to nearest even, by gfx950's conversion instruction
+__device__ __forceinline__ uint32_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two floats as one packed bf16 pair (a in the low half), one conversion instruction
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  typedef float f32v2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32v2{a, b}, bf16v2));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -563,36 +567,40 @@ hipError_t launch_prefill_append(const PrefillKvArgs& a, int rows, hipStream_t s
 // already holds, with V read from the transposed planes 8 bytes at a time.  The running softmax
 // (max, sum) is per query row; the 16-row x 16-dimension output tiles are rescaled with the row
 // factors fetched from the lanes that own those rows.  Keys and values must already be cached.
-constexpr int PA_QR = 16, PA_KT = 64;  // query rows per row block, keys per tile
+constexpr int PA_QR = 16, PA_KT = 64;  // query rows per row tile (one wavefront), keys per tile
 constexpr int PA_MAXT = 8;              // most tiles per workgroup (longer key ranges are split)
+// row tiles per workgroup: the workgroup's G x RT wavefronts share each staged key/value tile, so a
+// tile is read from the cache once per RT x 16 query rows (at most 8 wavefronts per workgroup)
+__host__ __device__ constexpr int pa_row_tiles(int G) { return G >= 8 ? 1 : 2; }
 
-// key splits of row block rb (tiles of its causal key range over tps, at least 1)
-__host__ __device__ inline int pa_splits(int rb, int rows, int pos0, int tps) {
-  const int tiles = (pos0 + min(rb * PA_QR + PA_QR, rows) + PA_KT - 1) / PA_KT;
+// key splits of row block rb of qr rows (tiles of its causal key range over tps, at least 1)
+__host__ __device__ inline int pa_splits(int rb, int rows, int pos0, int tps, int qr) {
+  const int tiles = (pos0 + min(rb * qr + qr, rows) + PA_KT - 1) / PA_KT;
   return tps > 0 ? (tiles + tps - 1) / tps : 1;
 }
 
-int prefill_attn_splits(int rows, int pos0, int tps) { return pa_splits((rows + PA_QR - 1) / PA_QR - 1, rows, pos0, tps); }
+// (the last row block has the longest key range whatever the row-block height)
+int prefill_attn_splits(int rows, int pos0, int tps) { return pa_splits((rows + PA_QR - 1) / PA_QR - 1, rows, pos0, tps, PA_QR); }
 
 // two bf16 halves (element 0 low) of hi and lo of four fp32 values
 __device__ __forceinline__ void split4(const float (&x)[4], uint2& hi, uint2& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = bf16_bits(x[e]);
-    l[e] = bf16_bits(x[e] - __uint_as_float(h[e] << 16));
-  }
-  hi = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  lo = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  const uint32_t h01 = bf16_pair(x[0], x[1]), h23 = bf16_pair(x[2], x[3]);
+  hi = uint2{h01, h23};
+  lo = uint2{bf16_pair(x[0] - __uint_as_float(h01 << 16), x[1] - __uint_as_float(h01 & 0xffff0000u)),
+             bf16_pair(x[2] - __uint_as_float(h23 << 16), x[3] - __uint_as_float(h23 & 0xffff0000u))};
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint2 a, uint2 b) {
   return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
+// e^x as 2^(x log2 e) on the hardware base-2 exponential (0 at x = -inf): the softmax weights'
+// exponentials, a large share of the attention's vector work
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 template <int D, int G, bool KB, bool VB>
-__global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a) {
-  constexpr int QR = PA_QR, KT = PA_KT, NT = 64 * G, NDS = D / 32, NDT = D / 16;
+__global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const PrefillAttnArgs a) {
+  constexpr int RT = pa_row_tiles(G), QR = PA_QR * RT, KT = PA_KT, NT = 64 * G * RT, NDS = D / 32, NDT = D / 16;
   constexpr int KS = D + 8;    // bf16 row stride of the K planes [key][dim]
   constexpr int VS = KT + 12;  // bf16 row stride of the transposed V planes [dim][key]
   __shared__ __attribute__((aligned(16))) uint16_t kh[KT * KS];
@@ -602,12 +610,12 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
   __shared__ int rowoff[PA_MAXT * KT];
   const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int i = lane & 15, c = lane >> 4;
-  const int h = g * G + w;
+  const int h = g * G + w % G, rt = w / G;  // q head and row tile of this wavefront
   // workgroup -> (row block, key split): the workgroups walk the row blocks from the last (the most
   // keys) down, each row block taking its splits of at most tps tiles in order
   int rb = (a.rows + QR - 1) / QR - 1, sp = blockIdx.x, nsp;
   while (true) {
-    nsp = pa_splits(rb, a.rows, a.pos0, a.tps);
+    nsp = pa_splits(rb, a.rows, a.pos0, a.tps, QR);
     if (sp < nsp || rb == 0) break;
     sp -= nsp;
     --rb;
@@ -628,7 +636,10 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
 
   // q of row i (lanes (i, 0..3) share it): per-head RMSNorm, RoPE, scale; lane (i, c) keeps the
   // dimensions 32 ds + 8 c + r as the bf16 hi / lo operands qh[ds], ql[ds]
-  const int qrow = row0 + min(i, nrows - 1);
+  // this wavefront's 16 rows of the block (the last block's second row tile may hold none: its q
+  // row is clamped into the prompt and it writes nothing)
+  const int wrow0 = row0 + PA_QR * rt, wrows = min(PA_QR, a.rows - wrow0);
+  const int qrow = min(wrow0 + min(i, max(wrows, 1) - 1), a.rows - 1);
   const int rpos = a.pos0 + qrow;
   bf16x8 qh[NDS], ql[NDS];
   {
@@ -787,13 +798,13 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
     // a later split a row may have no key yet (m still -inf), and then every weight is 0
     const float m_new = fmaxf(m_i, mx);
     const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    const float corr = expf(m_i - m_ref);
+    const float corr = exp_hw(m_i - m_ref);
     float ps = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT / 16; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = expf(st[kt][r] - m_ref);
+        const float p = exp_hw(st[kt][r] - m_ref);
         st[kt][r] = p;
         ps += p;
       }
@@ -829,15 +840,15 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
   if (nsp > 1) {  // a split's unnormalised output and row state, merged by k_prefill_attn_combine
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 4 * c + r;
-      if (row - row0 < nrows) {
+      const int row = wrow0 + 4 * c + r;
+      if (row - wrow0 < wrows) {
         float* po = a.part_o + (((size_t)sp * a.rows + row) * a.Hq + h) * D + i;
 #pragma unroll
         for (int t = 0; t < NDT; ++t) po[16 * t] = o[t][r];
       }
     }
-    if (c == 0 && i < nrows) {
-      float* pml = a.part_ml + (((size_t)sp * a.rows + row0 + i) * a.Hq + h) * 2;
+    if (c == 0 && i < wrows) {
+      float* pml = a.part_ml + (((size_t)sp * a.rows + wrow0 + i) * a.Hq + h) * 2;
       pml[0] = m_i;
       pml[1] = l_i;
     }
@@ -848,8 +859,8 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
   for (int r = 0; r < 4; ++r) inv[r] = 1.0f / __shfl(l_i, 4 * c + r, WAVE);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = row0 + 4 * c + r;
-    if (row - row0 < nrows) {
+    const int row = wrow0 + 4 * c + r;
+    if (row - wrow0 < wrows) {
       uint16_t* oh = a.out_hi + (size_t)row * a.ld_out + h * D + i;
       uint16_t* ol = a.out_lo + (size_t)row * a.ld_out + h * D + i;
 #pragma unroll
@@ -865,13 +876,14 @@ __global__ __launch_bounds__(64 * G) void k_prefill_attn(const PrefillAttnArgs a
 
 // Merge the key splits of the row blocks that have several, in split order: per row and q head,
 // M = max m_s, L = sum e^(m_s - M) l_s, y = sum e^(m_s - M) o_s / L, written as the bf16 planes.
-// grid = (row blocks, Hq), 4 wavefronts of 4 rows each; lane holds dimensions lane + 64 u.  A row's
-// loads for up to 8 splits are all issued before the first is used (longer ranges loop).
+// grid = (16-row tiles, Hq), 4 wavefronts of 4 rows each; lane holds dimensions lane + 64 u.  A
+// row's loads for up to 8 splits are all issued before the first is used (longer ranges loop).
 template <int D>
 __global__ __launch_bounds__(256) void k_prefill_attn_combine(const PrefillAttnArgs a) {
   constexpr int PER = D / 64, SB = 8;
   const int rb = blockIdx.x, h = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nsp = pa_splits(rb, a.rows, a.pos0, a.tps);
+  const int qr = PA_QR * pa_row_tiles(a.Hq / a.Hkv);  // rows of the attention's row blocks
+  const int nsp = pa_splits(rb * PA_QR / qr, a.rows, a.pos0, a.tps, qr);
   if (nsp == 1) return;  // written by the attention kernel
   const int row0 = rb * PA_QR, nrows = min(PA_QR, a.rows - row0);
   for (int ri = wv; ri < nrows; ri += 4) {
@@ -916,18 +928,20 @@ __global__ __launch_bounds__(256) void k_prefill_attn_combine(const PrefillAttnA
 
 template <int D, int G>
 static void launch_pa_kernel(const PrefillAttnArgs& a, dim3 grid, hipStream_t s) {
-  if (a.k_bf16 && a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, true>), grid, dim3(64 * G), 0, s, a);
-  else if (a.k_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, false>), grid, dim3(64 * G), 0, s, a);
-  else if (a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, false, true>), grid, dim3(64 * G), 0, s, a);
-  else hipLaunchKernelGGL((k_prefill_attn<D, G, false, false>), grid, dim3(64 * G), 0, s, a);
+  const dim3 block(64 * G * pa_row_tiles(G));
+  if (a.k_bf16 && a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, true>), grid, block, 0, s, a);
+  else if (a.k_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, false>), grid, block, 0, s, a);
+  else if (a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, false, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_prefill_attn<D, G, false, false>), grid, block, 0, s, a);
 }
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int nb = (a.rows + PA_QR - 1) / PA_QR;
+  if (a.Hkv < 1 || a.Hq % a.Hkv) return hipErrorInvalidValue;
+  const int G = a.Hq / a.Hkv, qr = PA_QR * pa_row_tiles(G);
+  const int nb = (a.rows + qr - 1) / qr, nb16 = (a.rows + PA_QR - 1) / PA_QR;
   if (a.tps < 1 || a.tps > PA_MAXT || a.rows < 1) return hipErrorInvalidValue;
   int blocks = 0;
-  for (int rb = 0; rb < nb; ++rb) blocks += pa_splits(rb, a.rows, a.pos0, a.tps);
+  for (int rb = 0; rb < nb; ++rb) blocks += pa_splits(rb, a.rows, a.pos0, a.tps, qr);
   if (blocks > nb && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;
   const dim3 grid(blocks, a.Hkv);
   // some row block has several splits: the attention, then the merge
@@ -936,7 +950,7 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
     launch_pa_kernel<DD, GG>(a, grid, s);                                                 \
     hipError_t e = hipGetLastError();                                                     \
     if (e != hipSuccess || blocks == nb) return e;                                        \
-    hipLaunchKernelGGL(k_prefill_attn_combine<DD>, dim3(nb, a.Hq), dim3(256), 0, s, a);   \
+    hipLaunchKernelGGL(k_prefill_attn_combine<DD>, dim3(nb16, a.Hq), dim3(256), 0, s, a); \
     return hipGetLastError();                                                             \
   }
   S2_PA(64, 1) S2_PA(64, 2) S2_PA(64, 4) S2_PA(64, 8)
