@@ -781,17 +781,25 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const
         st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb8, qh[ds], st[kt], 0, 0, 0);
         st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[ds], st[kt], 0, 0, 0);
       }
-    // causal mask and online softmax of row i over this tile (lane (i, c) holds keys 16 kt + 4 c + r)
+    // causal mask and online softmax of row i over this tile (lane (i, c) holds keys 16 kt + 4 c + r);
+    // a whole tile at or below every row of the wavefront needs no mask
     float mx = -INFINITY;
+    if (nk == KT && j0 + KT - 1 <= a.pos0 + wrow0) {
 #pragma unroll
-    for (int kt = 0; kt < KT / 16; ++kt)
+      for (int kt = 0; kt < KT / 16; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jl = kt * 16 + 4 * c + r;
-        const float v = (jl < nk && j0 + jl <= rpos) ? st[kt][r] : -INFINITY;
-        st[kt][r] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kt][r]);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < KT / 16; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jl = kt * 16 + 4 * c + r;
+          const float v = (jl < nk && j0 + jl <= rpos) ? st[kt][r] : -INFINITY;
+          st[kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
     // A row's first key split always holds key 0 <= rpos, so m is finite from its first tile on; in
