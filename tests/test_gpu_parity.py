@@ -601,6 +601,30 @@ def test_batched_sixteen_streams_mid():
     ctx.close()
 
 
+@pytest.mark.parametrize("G,D,kv", [(1, 128, "f32"), (2, 64, "v_bf16")])
+def test_batched_slow_attention_split_and_wavefront_boundaries(G, D, kv):
+    """The batched Slow attention takes 256-key splits of four 64-key wavefronts.  Twelve streams
+    whose two decoded positions fall on every boundary of that layout: the first and second
+    positions, the last key of wavefront 0 and the first of wavefront 1, the last key of a split
+    and the first of the next, and past them, at 1 and 2 q heads per KV head (the mid and full
+    shapes have 4) and head_dim 128 and 64."""
+    cfg = synth.micro_config(seed=60 + G, slow_layers=2, fast_layers=1, hidden=512, n_q_heads=512 // D,
+                             n_kv_heads=512 // D // G, head_dim=D, ffn=1024, vocab_text=1000,
+                             codebook_size=256, weight_dtype="bf16", max_context=704)
+    cfg["kv_dtype"] = kv
+    w = synth.make_weights(cfg)
+    lens = [1, 62, 63, 64, 127, 254, 255, 256, 300, 510, 511, 600]
+    prompts = _ragged_prompts(cfg, lens, 70 + G)
+    per_stream = _oracle_frames_per_stream(cfg, w, prompts, 2)
+    ctx = _ctx(cfg, w, max_streams=12)
+    ids = list(range(12))
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
+    _say(f"[parity] batched split boundaries, G {G}, D {D}, {kv} KV: {rep}")
+    ctx.close()
+
+
 @pytest.mark.timeout(1500)
 def test_batched_multi_stream_teacher_forced_full_shape():
     """Batched decode at the full S2 shape, three streams with different contexts."""
