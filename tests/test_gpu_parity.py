@@ -625,6 +625,26 @@ def test_batched_slow_attention_split_and_wavefront_boundaries(G, D, kv):
     ctx.close()
 
 
+def test_batched_slow_attention_eight_heads_per_kv_head():
+    """Eight q heads per KV head: the batched Slow attention runs the LDS-tiled kernel with
+    192-position splits instead of the four-wavefront kernel; positions on its split and chunk
+    boundaries."""
+    cfg = synth.micro_config(seed=68, slow_layers=2, fast_layers=1, hidden=512, n_q_heads=8, n_kv_heads=1,
+                             head_dim=64, ffn=1024, vocab_text=1000, codebook_size=256, weight_dtype="bf16",
+                             max_context=512)
+    w = synth.make_weights(cfg)
+    lens = [1, 63, 127, 190, 191, 192, 383, 384, 450]
+    prompts = _ragged_prompts(cfg, lens, 78)
+    per_stream = _oracle_frames_per_stream(cfg, w, prompts, 2)
+    ctx = _ctx(cfg, w, max_streams=9)
+    ids = list(range(9))
+    for s_, p in zip(ids, prompts):
+        ctx.prefill(s_, p)
+    rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
+    _say(f"[parity] batched G 8: {rep}")
+    ctx.close()
+
+
 @pytest.mark.timeout(1500)
 def test_batched_multi_stream_teacher_forced_full_shape():
     """Batched decode at the full S2 shape, three streams with different contexts."""
