@@ -515,6 +515,20 @@ __global__ __launch_bounds__(1024) void k_norm_rows(NormRowsArgs a) {
   for (int e = threadIdx.x; e < a.H; e += 1024) xn[e] = x[e] * scale * a.gain[e];
 }
 
+// acc + p[0] + p[st] + ... + p[(S - 1) st], added in split order; the first 24 loads all go out
+// before the first add (one memory round trip for every split count of the model's shapes)
+__device__ __forceinline__ float add_splits(float acc, const float* p, size_t st, int S) {
+  constexpr int CAP = 24;
+  float v[CAP];
+#pragma unroll
+  for (int u = 0; u < CAP; ++u) v[u] = u < S ? p[u * st] : 0.f;
+#pragma unroll
+  for (int u = 0; u < CAP; ++u)
+    if (u < S) acc += v[u];
+  for (int u = CAP; u < S; ++u) acc += p[u * st];
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void k_fold_rows(const FoldArgs f) {
   __shared__ float red[4];
   const int j = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
@@ -523,15 +537,7 @@ __global__ __launch_bounds__(256) void k_fold_rows(const FoldArgs f) {
     float* x = f.x + (size_t)j * f.ldx;
     t = x[e];
     const float* p = f.part + (size_t)j * mgemv_ldp(f.H) + e;
-    const size_t st = (size_t)MB * mgemv_ldp(f.H);
-    for (int s0 = 0; s0 < f.S; s0 += 8) {  // eight loads in flight at a time, added in split order
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (s0 + u < f.S) ? p[(s0 + u) * st] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < f.S) t += v[u];
-    }
+    t = add_splits(t, p, (size_t)MB * mgemv_ldp(f.H), f.S);
     if (f.S > 0) x[e] = t;
   }
   float ss = t * t;
@@ -563,16 +569,13 @@ __global__ __launch_bounds__(256) void k_mgemv_reduce(const MgemvArgs a) {
   const bool live = n < a.N;
   const size_t ldp = mgemv_ldp(a.N);
   float v = 0.f;
-  if (live)
-    for (int s = 0; s < a.S; ++s) v += a.part[((size_t)s * MB + j) * ldp + n];
+  if (live) v = add_splits(0.f, a.part + (size_t)j * ldp + n, (size_t)MB * ldp, a.S);
   if constexpr (EPI == MG_STORE) {
     if (live) a.out[(size_t)j * a.ldo + n] = v;
   } else if constexpr (EPI == MG_SWIGLU) {
-    if (live && (n & 1) == 0) {
-      float u = 0.f;
-      for (int s = 0; s < a.S; ++s) u += a.part[((size_t)s * MB + j) * ldp + n + 1];
-      a.out[(size_t)j * a.ldo + (n >> 1)] = v / (1.0f + expf(-v)) * u;
-    }
+    // row n + 1 (the up half of the pair) is the next lane's sum
+    const float u = __shfl_down(v, 1, WAVE);
+    if (live && (n & 1) == 0) a.out[(size_t)j * a.ldo + (n >> 1)] = v / (1.0f + expf(-v)) * u;
   } else if constexpr (EPI == MG_ARGMAX) {
     if (live) a.out[(size_t)j * a.ldo + n] = v;
     float bv = (live && n >= a.am_lo && n < a.am_hi) ? v : -INFINITY;

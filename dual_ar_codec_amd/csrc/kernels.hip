@@ -1064,6 +1064,13 @@ __global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
   const int nsplit = (pos + 1 + a.split - 1) / a.split;
   if (nsplit == 1) return;  // the attention kernel wrote the output itself
   const size_t base = ((size_t)b * a.Hq + h) * a.max_splits;
+  // the first 16 splits' outputs are loaded before anything else (they do not depend on the max)
+  constexpr int SF = 16;
+  float tf[SF][PER];
+#pragma unroll
+  for (int u = 0; u < SF; ++u)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) tf[u][i] = u < nsplit ? a.part_o[(base + u) * D + lane + i * WAVE] : 0.f;
   // the splits' (max, sum) are read one split per lane, 64 at a time, and each split's weight is
   // passed from its lane; the sums still run in split order, so the loads of up to eight splits'
   // outputs go out together instead of one dependent round trip per split
@@ -1081,7 +1088,20 @@ __global__ __launch_bounds__(WAVE) void k_attn_combine(const AttnArgs a) {
       e = expf(a.part_ml[(base + c0 + lane) * 2] - M);
       l = a.part_ml[(base + c0 + lane) * 2 + 1];
     }
-    for (int u0 = 0; u0 < cn; u0 += 8) {
+    int u0 = 0;
+    if (c0 == 0) {  // splits 0 .. SF - 1, loaded up front
+#pragma unroll
+      for (int u = 0; u < SF; ++u) {
+        const float eu = __shfl(e, u, WAVE), lu = __shfl(l, u, WAVE);
+        if (u < cn) {
+          L = fmaf(eu, lu, L);
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] = fmaf(eu, tf[u][i], acc[i]);
+        }
+      }
+      u0 = SF;
+    }
+    for (; u0 < cn; u0 += 8) {
       float t[8][PER];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
