@@ -278,7 +278,8 @@ def main():
     ap.add_argument("--slice-steps", type=int, default=60, help="batch-1 frames with the semantic-slice head (0 = skip)")
     ap.add_argument("--mid", type=int, default=1, help="also time the mid workload (32 frames)")
     ap.add_argument("--counter-pass", type=int, default=0,
-                    help="for rocprofv3 --pmc passes: prefill, 2 frames enqueued without graphs, the gate/up and "
+                    help="for rocprofv3 --pmc passes: prefill, 2 frames enqueued without graphs, the voice-clone "
+                         "prefill (unless --prefill 0), the gate/up and "
                          "streaming-read launches (--kernel-iters each) and the 256 MiB copy probe, then exit")
     ap.add_argument("--prefix-share", type=int, default=1,
                     help="time to first frame of the voice-clone prompt with its 1000-position prefix shared")
@@ -310,6 +311,9 @@ def main():
     if args.counter_pass:
         ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
         out = ctx.decode_frames_noalloc(0, 2)
+        if vc is not None:  # the voice-clone prefill (matrix-core GEMMs and attention, no graph)
+            vt, vm, vcodes = synth.make_prompt(vc)
+            ctx.prefill(1, vt, vm, vcodes)
         ms, nbytes = ctx.time_kernel(0, args.kernel_iters)
         sms, sbytes = ctx.time_kernel(1, args.kernel_iters)
         ctx.close()
@@ -377,6 +381,21 @@ def main():
                              "ms_per_frame": round(dt_vc / vc_frames * 1e3, 4), "frame_bytes": fb_vc["total"],
                              "hbm_frac": round(fb_vc["total"] * vc_frames / dt_vc / 1e9 / HBM_PEAK_GBPS, 4)}
         ctx.release(1)
+        # the same prefill with one fp16 activation plane per product (prefill precision 1)
+        ctx.set_prefill_precision(1)
+        ctx.prefill(1, vt[:64], vm[:64], vcodes[:64])  # warm-up of the fp16 kernels
+        ctx.release(1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ctx.prefill(1, vt, vm, vcodes)
+        torch.cuda.synchronize()
+        pt16 = time.perf_counter() - t0
+        ctx.release(1)
+        ctx.set_prefill_precision(0)
+        prefill["fp16"] = {"ms": round(pt16 * 1e3, 2), "tflop_s": round((lin + att) / pt16 / 1e12, 1),
+                           "mfma_frac": round((lin + att) / pt16 / 1e12 / 2500.0, 4),
+                           "note": "prefill precision 1: activations rounded once to fp16, weights taken as "
+                                   "fp16, one fp16 MFMA pass per product (attention keeps its bf16 split)"}
         if args.prefix_share:
             prefill["prefix_sharing"] = prefix_sharing(ctx, vc, vt, vm, vcodes)
 

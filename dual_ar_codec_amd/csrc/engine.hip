@@ -151,6 +151,10 @@ struct s2ar_ctx {
   float* pgemm_part = nullptr;
   size_t pgemm_part_floats = 0;
   bool mfma_prefill = false;
+  // prefill products on the fp16 matrix cores (one fp16 activation plane) instead of the bf16 hi/lo
+  // split; f16_prefill_ok: every prefill K is a multiple of 64
+  bool prefill_f16 = false, f16_prefill_ok = false;
+  int* d_range = nullptr;  // raised by a prefill producer whose value fp16 cannot hold
   float *px = nullptr, *pqkv = nullptr;
   // prefill attention key splits: unnormalised outputs and row states of the splits
   float *patt_o = nullptr, *patt_ml = nullptr;
@@ -756,6 +760,8 @@ int create_impl(const s2ar_config* cfg, const s2ar_tensor* t, int32_t n_tensors,
       C_TRY(dev_alloc(c, &c->pactl, sizeof(uint16_t) * (size_t)c->pch * st.ffn));
       c->pgemm_part_floats = (size_t)4 * 256 * std::max(std::max(qkvd_s, 2 * st.ffn), H);
       C_TRY(dev_alloc(c, &c->pgemm_part, sizeof(float) * c->pgemm_part_floats));
+      C_TRY(dev_alloc(c, &c->d_range, 256));
+      c->f16_prefill_ok = H % 64 == 0 && qd_s % 64 == 0 && st.ffn % 64 == 0;
       std::vector<int> iota(g.max_context);
       for (int i = 0; i < g.max_context; ++i) iota[i] = i;
       C_TRY(dev_alloc(c, &c->d_iota, sizeof(int) * g.max_context));
@@ -1072,6 +1078,11 @@ struct Enq {
     const float eps = (float)g.rms_eps;
     chk(s2k::launch_embed_rows(c->bf16, c->embed, c->codebook, g.codebook_size, H, g.n_codebooks, c->d_tokens,
                                has_mask ? c->d_mask : nullptr, c->d_pcodes, p0, rows, c->px, H, s));
+    // the fp16 mode writes and reads one activation plane (the lo planes stay unused)
+    const bool f16 = c->prefill_f16;
+    uint16_t* const pxl = f16 ? nullptr : c->pxl;
+    uint16_t* const pattl = f16 ? nullptr : c->pattl;
+    uint16_t* const pactl = f16 ? nullptr : c->pactl;
     auto gemm = [&](const uint16_t* a_hi, const uint16_t* a_lo, int lda, const void* w, const float* wscale, float* out,
                     uint16_t* out_hi, uint16_t* out_lo, int ldc, int N, int K, int epi) {
       s2k::GemmArgs ga{};
@@ -1091,12 +1102,14 @@ struct Enq {
       ga.epi = epi;
       ga.part = c->pgemm_part;
       ga.part_floats = c->pgemm_part_floats;
+      ga.a_f16 = f16;
+      ga.range_flag = c->d_range;
       chk(s2k::launch_gemm(ga, s));
     };
     for (int l = 0; l < st.n_layers; ++l) {
       const LayerW& L = c->slow[l];
-      chk(s2k::launch_norm_split(c->px, H, H, eps, L.attn_norm, c->pxh, c->pxl, H, rows, s));
-      gemm(c->pxh, c->pxl, H, L.wqkv, L.sqkv, c->pqkv, nullptr, nullptr, qkvd, qkvd, H, s2k::GEMM_STORE);
+      chk(s2k::launch_norm_split(c->px, H, H, eps, L.attn_norm, c->pxh, pxl, H, rows, c->d_range, s));
+      gemm(c->pxh, pxl, H, L.wqkv, L.sqkv, c->pqkv, nullptr, nullptr, qkvd, qkvd, H, s2k::GEMM_STORE);
       s2k::PrefillKvArgs kv{};
       kv.qkv = c->pqkv;
       kv.ld = qkvd;
@@ -1128,7 +1141,8 @@ struct Enq {
       pa.block_table = kv.block_table;
       pa.page_size = kPageSize;
       pa.out_hi = c->patth;
-      pa.out_lo = c->pattl;
+      pa.out_lo = pattl;
+      pa.range_flag = c->d_range;
       pa.ld_out = qd;
       pa.rows = rows;
       pa.pos0 = pos0;
@@ -1141,10 +1155,10 @@ struct Enq {
       pa.part_o = c->patt_o;
       pa.part_ml = c->patt_ml;
       chk(s2k::launch_prefill_attn(pa, s));
-      gemm(c->patth, c->pattl, qd, L.wo, L.so, c->px, nullptr, nullptr, H, H, qd, s2k::GEMM_ADD);
-      chk(s2k::launch_norm_split(c->px, H, H, eps, L.mlp_norm, c->pxh, c->pxl, H, rows, s));
-      gemm(c->pxh, c->pxl, H, L.wgu, L.sgu, nullptr, c->pacth, c->pactl, F, 2 * F, H, s2k::GEMM_SWIGLU);
-      gemm(c->pacth, c->pactl, F, L.wdown, L.sdown, c->px, nullptr, nullptr, H, H, F, s2k::GEMM_ADD);
+      gemm(c->patth, pattl, qd, L.wo, L.so, c->px, nullptr, nullptr, H, H, qd, s2k::GEMM_ADD);
+      chk(s2k::launch_norm_split(c->px, H, H, eps, L.mlp_norm, c->pxh, pxl, H, rows, c->d_range, s));
+      gemm(c->pxh, pxl, H, L.wgu, L.sgu, nullptr, c->pacth, pactl, F, 2 * F, H, s2k::GEMM_SWIGLU);
+      gemm(c->pacth, pactl, F, L.wdown, L.sdown, c->px, nullptr, nullptr, H, H, F, s2k::GEMM_ADD);
     }
   }
 
@@ -1590,6 +1604,8 @@ int s2ar_prefill(s2ar_ctx* c, int32_t sid, const int32_t* tokens, const uint8_t*
     HIP_TRY(c, hipMemcpyAsync(c->d_pcodes, codes, sizeof(int) * (size_t)n * NC, hipMemcpyHostToDevice, c->stream));
   }
   Enq q{c, c->stream};
+  const bool f16 = c->mfma_prefill && n >= 2 && c->prefill_f16;
+  if (f16) q.chk(hipMemsetAsync(c->d_range, 0, sizeof(int), c->stream));
   if (c->mfma_prefill && n >= 2) {
     const int H = g.slow.hidden;
     for (int p0 = 0; p0 < n && q.e == hipSuccess; p0 += c->pch) {
@@ -1613,11 +1629,30 @@ int s2ar_prefill(s2ar_ctx* c, int32_t sid, const int32_t* tokens, const uint8_t*
       if (q.e != hipSuccess) break;
     }
   }
+  if (f16) q.chk(hipMemcpyAsync(c->h_pos_stage + 8, c->d_range, sizeof(int), hipMemcpyDeviceToHost, c->stream));
   if (q.e != hipSuccess) return set_err(c, S2AR_E_DEVICE, std::string("prefill launch: ") + hipGetErrorString(q.e));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
+  if (f16 && c->h_pos_stage[8]) {
+    // an activation beyond fp16's range: the new positions are dropped (the device position goes
+    // back to the host's) and the stream's pending pick is gone, so it is not ready to decode
+    c->h_pos_stage[0] = c->pos[sid];
+    HIP_TRY(c, hipMemcpyAsync(c->d_pos + sid, c->h_pos_stage, sizeof(int), hipMemcpyHostToDevice, c->stream));
+    HIP_TRY(c, hipStreamSynchronize(c->stream));
+    c->ready[sid] = 0;
+    return set_err(c, S2AR_E_NUMERIC, "prefill activation outside the fp16 range (use prefill precision 0)");
+  }
   c->pos[sid] += n;
   c->ready[sid] = 1;
   c->ended[sid] = 0;  // the new positions end with a fresh Slow pick
+  return S2AR_OK;
+}
+
+int s2ar_set_prefill_precision(s2ar_ctx* c, int32_t precision) {
+  if (!c) return S2AR_E_ARG;
+  if (precision != 0 && precision != 1) return set_err(c, S2AR_E_ARG, "prefill precision must be 0 or 1");
+  if (precision == 1 && !(c->mfma_prefill && c->f16_prefill_ok))
+    return set_err(c, S2AR_E_ARG, "the fp16 prefill needs the matrix-core prefill and every K a multiple of 64");
+  c->prefill_f16 = precision == 1;
   return S2AR_OK;
 }
 

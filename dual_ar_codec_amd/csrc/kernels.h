@@ -135,12 +135,18 @@ struct GemmArgs {
   float* part;
   size_t part_floats;
   int split;
+  // 1: a_hi holds the activations as IEEE fp16 (a_lo unused), the products run on the fp16 matrix
+  // cores with the weights converted to fp16, and GEMM_SWIGLU writes one fp16 plane to c_hi,
+  // raising *range_flag (device int) for a value fp16 cannot hold.  Needs K % 64 == 0.
+  int a_f16;
+  int* range_flag;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 // RMSNorm of M rows and the bf16 split of the result: hi/lo planes of x[m] * (scale[m] * gain),
-// scale = 1 / sqrt(mean(x[m]^2) + eps).  One 256-thread block per row.
+// scale = 1 / sqrt(mean(x[m]^2) + eps).  One 256-thread block per row.  lo == nullptr: one IEEE
+// fp16 plane in hi instead, raising *range_flag for a value fp16 cannot hold.
 hipError_t launch_norm_split(const float* x, int ld, int H, float eps, const float* gain, uint16_t* hi, uint16_t* lo,
-                             int ldo, int M, hipStream_t s);
+                             int ldo, int M, int* range_flag, hipStream_t s);
 
 struct PrefillKvArgs {
   const float* qkv;        // [rows][ld] projections of the prompt rows
@@ -173,7 +179,8 @@ struct PrefillAttnArgs {
   const int* block_table;  // the stream's row of the block table
   int page_size;
   uint16_t* out_hi;        // [rows][ld_out] attention output as bf16 high and low planes (the
-  uint16_t* out_lo;        // O projection's input)
+  uint16_t* out_lo;        // O projection's input); out_lo == nullptr: one IEEE fp16 plane in out_hi,
+  int* range_flag;         // raising *range_flag for a value fp16 cannot hold
   int ld_out;
   int rows, pos0, Hq, Hkv, D;
   float eps, scale;

@@ -19,6 +19,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -34,15 +35,43 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32v2{a, b}, bf16v2));
 }
 
+// IEEE fp16 bits of f, rounded to nearest even
+__device__ __forceinline__ uint32_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// two floats as one packed fp16 pair (a in the low half), one conversion instruction, nearest even
+__device__ __forceinline__ uint32_t f16_pair(float a, float b) {
+  typedef float f32v2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16v2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32v2{a, b}, f16v2));
+}
+
+// The fp16 prefill mode writes each activation once as fp16; a value that fp16 cannot hold (beyond
+// 65504 in magnitude after rounding, or not a number) raises the caller's range flag, which the
+// host turns into an error.  The stored bits are the rounded value (infinity for such a value).
+__device__ __forceinline__ uint16_t f16_checked(float y, int* range_flag) {
+  const uint32_t h = f16_bits(y);
+  if ((h & 0x7c00u) == 0x7c00u) *range_flag = 1;  // exponent all ones: infinity or NaN
+  return (uint16_t)h;
+}
+
+// eight bf16 (one u32x4) as eight fp16, each rounded to nearest even: exact for magnitudes from
+// 2^-17 to 65504 (bf16 keeps 8 significant bits, fp16 11, and its subnormals reach 2^-24)
+__device__ __forceinline__ u32x4 bf16x8_to_f16(const u32x4 p) {
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = f16_pair(__uint_as_float(p[q] << 16), __uint_as_float(p[q] & 0xffff0000u));
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
   return v;
 }
 
-// eight 8-bit weight codes (int8, or OCP FP8 E4M3 through the hardware conversion) as eight bf16,
-// exactly (a code has at most 8 significant bits)
-template <int WF>
+// eight 8-bit weight codes (int8, or OCP FP8 E4M3 through the hardware conversion) as eight bf16
+// (or, F16, eight fp16), exactly (a code has at most 8 significant bits)
+template <int WF, bool F16 = false>
 __device__ __forceinline__ u32x4 widen8(const u32x2 p) {
   uint32_t o[4];
   const uint32_t wd[2] = {p.x, p.y};
@@ -60,8 +89,13 @@ __device__ __forceinline__ u32x4 widen8(const u32x2 p) {
       f[2] = hi[0];
       f[3] = hi[1];
     }
-    o[2 * q] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
-    o[2 * q + 1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
+    if constexpr (F16) {  // an int8 code or an E4M3 value is exact in fp16 as well
+      o[2 * q] = f16_pair(f[0], f[1]);
+      o[2 * q + 1] = f16_pair(f[2], f[3]);
+    } else {
+      o[2 * q] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+      o[2 * q + 1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
+    }
   }
   return u32x4{o[0], o[1], o[2], o[3]};
 }
@@ -186,10 +220,12 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
 // stages before its compute.  Tiles are numbered with M fastest, and the blocks of one XCD
 // (block ids round-robin over the 8 XCDs) take a contiguous range of tiles, so the blocks that
 // share a weight column sit on one XCD and reuse it from that XCD's L2.
-template <int BM, int BN, int NW, int WM, int EPI, int WF = W_BF16>
+// F16: the activations are one IEEE fp16 plane (g.a_hi), the weights are converted to fp16 when
+// staged, and every product is one v_mfma_f32_16x16x32_f16; the SwiGLU epilogue writes fp16.
+template <int BM, int BN, int NW, int WM, int EPI, int WF = W_BF16, bool F16 = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
-  // WF: bf16 weights, or 8-bit codes loaded 8 bytes per lane, widened to bf16 when staged in LDS and
-  // scaled per output column (weight row) in the epilogue
+  // WF: bf16 weights, or 8-bit codes loaded 8 bytes per lane, widened to bf16 (fp16) when staged in
+  // LDS and scaled per output column (weight row) in the epilogue
   using WR = typename std::conditional<WF == W_BF16, u32x4, u32x2>::type;
   // LDS row stride (bf16): 64 + 16.  Measured on the 1200-position prefill: 64 (no pad) 31.1 ms,
   // 72 26.5 ms, 80 25.9 ms; 80 fills the 160 KB of LDS exactly with the 128 x 256 tiles.
@@ -199,7 +235,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   // row, 16 bytes each) of an activation plane or of the weights
   constexpr int AI = BM / (8 * NW);                   // load instructions per thread per stage and A plane
   constexpr int WI = BN / (8 * NW);                   // W load instructions per thread per stage
-  constexpr int STAGE = (2 * BM + BN) * LS;           // bf16 elements: A hi, A lo, W
+  constexpr int NPL = F16 ? 1 : 2;                    // activation planes
+  constexpr int STAGE = (NPL * BM + BN) * LS;         // 16-bit elements: A hi (or fp16), A lo, W
   static_assert(AI >= 1 && WI >= 1, "tile too small for the loaders");
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
@@ -235,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       ah[i] = *reinterpret_cast<const u32x4*>(g.a_hi + a_off[i] + k);
-      al[i] = *reinterpret_cast<const u32x4*>(g.a_lo + a_off[i] + k);
+      if constexpr (!F16) al[i] = *reinterpret_cast<const u32x4*>(g.a_lo + a_off[i] + k);
     }
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
@@ -250,16 +287,19 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   auto stash = [&](int st, const u32x4 (&ah)[AI], const u32x4 (&al)[AI], const WR (&wr)[WI]) {
     uint16_t* sh = lds + st * STAGE;
     uint16_t* sl = sh + BM * LS;
-    uint16_t* sw = sl + BM * LS;
+    uint16_t* sw = sh + NPL * BM * LS;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       *reinterpret_cast<u32x4*>(sh + (a_row0 + 8 * i) * LS + r_k) = ah[i];
-      *reinterpret_cast<u32x4*>(sl + (a_row0 + 8 * i) * LS + r_k) = al[i];
+      if constexpr (!F16) *reinterpret_cast<u32x4*>(sl + (a_row0 + 8 * i) * LS + r_k) = al[i];
     }
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
-      if constexpr (WF == W_BF16) *reinterpret_cast<u32x4*>(sw + (w_row0 + 8 * i) * LS + r_k) = wr[i];
-      else *reinterpret_cast<u32x4*>(sw + (w_row0 + 8 * i) * LS + r_k) = widen8<WF>(wr[i]);
+      u32x4 v;
+      if constexpr (WF != W_BF16) v = widen8<WF, F16>(wr[i]);
+      else if constexpr (F16) v = bf16x8_to_f16(wr[i]);
+      else v = wr[i];
+      *reinterpret_cast<u32x4*>(sw + (w_row0 + 8 * i) * LS + r_k) = v;
     }
   };
 
@@ -272,22 +312,35 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   auto compute = [&](int st) {
     const uint16_t* ah = lds + st * STAGE;
     const uint16_t* al = ah + BM * LS;
-    const uint16_t* ws = al + BM * LS;
+    const uint16_t* ws = ah + NPL * BM * LS;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 bfr[TN];
+      if constexpr (F16) {
+        f16x8 bfr[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(ws + (wn * (BN / WN) + j * 16 + fr) * LS + ks * 32 + fk);
+        for (int j = 0; j < TN; ++j)
+          bfr[j] = *reinterpret_cast<const f16x8*>(ws + (wn * (BN / WN) + j * 16 + fr) * LS + ks * 32 + fk);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {  // one A row tile at a time keeps few fragments live
-        const int r = (wm * (BM / WM) + i * 16 + fr) * LS + ks * 32 + fk;
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(ah + r);
-        const bf16x8 afl = *reinterpret_cast<const bf16x8*>(al + r);
+        for (int i = 0; i < TM; ++i) {
+          const f16x8 af = *reinterpret_cast<const f16x8*>(ah + (wm * (BM / WM) + i * 16 + fr) * LS + ks * 32 + fk);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afl, bfr[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr[j], acc[i][j], 0, 0, 0);
+        }
+      } else {
+        bf16x8 bfr[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8*>(ws + (wn * (BN / WN) + j * 16 + fr) * LS + ks * 32 + fk);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {  // one A row tile at a time keeps few fragments live
+          const int r = (wm * (BM / WM) + i * 16 + fr) * LS + ks * 32 + fk;
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(ah + r);
+          const bf16x8 afl = *reinterpret_cast<const bf16x8*>(al + r);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afl, bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+          }
         }
       }
     }
@@ -349,9 +402,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
           const float up = __shfl_xor(v, 1, WAVE);  // columns 2i (gate) and 2i+1 (up) sit in adjacent lanes
           if (m < g.M && (n & 1) == 0) {
             const float y = v / (1.0f + expf(-v)) * up;
-            const uint32_t h = bf16_bits(y);
-            g.c_hi[(size_t)m * g.ldc + (n >> 1)] = (uint16_t)h;
-            g.c_lo[(size_t)m * g.ldc + (n >> 1)] = (uint16_t)bf16_bits(y - __uint_as_float(h << 16));
+            if constexpr (F16) {
+              g.c_hi[(size_t)m * g.ldc + (n >> 1)] = f16_checked(y, g.range_flag);
+            } else {
+              const uint32_t h = bf16_bits(y);
+              g.c_hi[(size_t)m * g.ldc + (n >> 1)] = (uint16_t)h;
+              g.c_lo[(size_t)m * g.ldc + (n >> 1)] = (uint16_t)bf16_bits(y - __uint_as_float(h << 16));
+            }
           }
         } else if (m < g.M) {
           if constexpr (EPI == GEMM_ADD) g.c[(size_t)m * g.ldc + n] += v;
@@ -377,6 +434,10 @@ __global__ __launch_bounds__(256) void k_gemm_split_reduce(const GemmArgs g) {
       up += p[k * slice + 2 * e + 1];
     }
     const float y = gt / (1.0f + expf(-gt)) * up;
+    if (g.a_f16) {  // the fp16 mode: the down product reads one fp16 plane
+      g.c_hi[(size_t)m * g.ldc + e] = f16_checked(y, g.range_flag);
+      return;
+    }
     const uint32_t h = bf16_bits(y);
     g.c_hi[(size_t)m * g.ldc + e] = (uint16_t)h;
     g.c_lo[(size_t)m * g.ldc + e] = (uint16_t)bf16_bits(y - __uint_as_float(h << 16));
@@ -407,9 +468,17 @@ static hipError_t gemm2_launch(GemmArgs g, hipStream_t s) {
   const int ntiles = (g.M + BM - 1) / BM * (g.N / BN);
   g.split = gemm_splits(g, ntiles);
   const dim3 grid(ntiles * g.split), block(512);
-  if (g.w_fmt == W_I8) hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_I8>), grid, block, 0, s, g);
-  else if (g.w_fmt == W_F8) hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_F8>), grid, block, 0, s, g);
-  else hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI>), grid, block, 0, s, g);
+  if (g.a_f16) {
+    if (g.w_fmt == W_I8) hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_I8, true>), grid, block, 0, s, g);
+    else if (g.w_fmt == W_F8) hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_F8, true>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_BF16, true>), grid, block, 0, s, g);
+  } else if (g.w_fmt == W_I8) {
+    hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_I8>), grid, block, 0, s, g);
+  } else if (g.w_fmt == W_F8) {
+    hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_F8>), grid, block, 0, s, g);
+  } else {
+    hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI>), grid, block, 0, s, g);
+  }
   if (g.split > 1) {
     const int cols = EPI == GEMM_SWIGLU ? g.N / 2 : g.N;
     hipLaunchKernelGGL(k_gemm_split_reduce<EPI>, dim3((cols + 255) / 256, g.M), dim3(256), 0, s, g);
@@ -423,7 +492,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // the 8-wavefront kernel for every prompt length (rows past M repeat the last row and are not
   // stored): at 64..200 rows it ran the full-shape prefill in 14-15 ms against 25-30 ms for the
   // 4-wavefront kernel, which remains for K not divisible by 64
-  if (g.epi == GEMM_SWIGLU ? (!g.c_hi || !g.c_lo) : !g.c) return hipErrorInvalidValue;
+  if (g.epi == GEMM_SWIGLU ? (!g.c_hi || (!g.a_f16 && !g.c_lo)) : !g.c) return hipErrorInvalidValue;
+  if (g.a_f16 && (g.K % 64 || !g.range_flag)) return hipErrorInvalidValue;  // fp16: k_gemm2 only
   if (g.K % 64 == 0) {
     // Measured at P = 1200 on the full shape (copy-only stage loaders): the wide gate/up + SwiGLU
     // product runs best on 128 x 256 tiles (64 x 128 per wavefront; its store and add forms would
@@ -457,9 +527,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
 
 // ---------------------------------------------------------------------------------------------
 // RMSNorm of a row and its bf16 split: hi = bf16(y), lo = bf16(y - hi) with y = x * (scale * gain),
-// scale = 1 / sqrt(mean(x^2) + eps).  One block per row; the GEMMs read the two planes.
+// scale = 1 / sqrt(mean(x^2) + eps).  One block per row; the GEMMs read the two planes (lo ==
+// nullptr: the fp16 mode, one plane of fp16(y)).
 __global__ __launch_bounds__(256) void k_norm_split(const float* x, int ld, int H, float eps, const float* gain,
-                                                    uint16_t* hi, uint16_t* lo, int ldo) {
+                                                    uint16_t* hi, uint16_t* lo, int ldo, int* range_flag) {
   __shared__ float red[4];
   const float* r = x + (size_t)blockIdx.x * ld;
   float ss = 0.f;
@@ -469,6 +540,10 @@ __global__ __launch_bounds__(256) void k_norm_split(const float* x, int ld, int 
   __syncthreads();
   const float scale = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
   uint16_t* oh = hi + (size_t)blockIdx.x * ldo;
+  if (!lo) {
+    for (int k = threadIdx.x; k < H; k += 256) oh[k] = f16_checked(r[k] * (scale * gain[k]), range_flag);
+    return;
+  }
   uint16_t* ol = lo + (size_t)blockIdx.x * ldo;
   for (int k = threadIdx.x; k < H; k += 256) {
     const float y = r[k] * (scale * gain[k]);
@@ -479,8 +554,9 @@ __global__ __launch_bounds__(256) void k_norm_split(const float* x, int ld, int 
 }
 
 hipError_t launch_norm_split(const float* x, int ld, int H, float eps, const float* gain, uint16_t* hi, uint16_t* lo,
-                             int ldo, int M, hipStream_t s) {
-  hipLaunchKernelGGL(k_norm_split, dim3(M), dim3(256), 0, s, x, ld, H, eps, gain, hi, lo, ldo);
+                             int ldo, int M, int* range_flag, hipStream_t s) {
+  if (!lo && !range_flag) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_norm_split, dim3(M), dim3(256), 0, s, x, ld, H, eps, gain, hi, lo, ldo, range_flag);
   return hipGetLastError();
 }
 
@@ -870,6 +946,11 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const
     const int row = wrow0 + 4 * c + r;
     if (row - wrow0 < wrows) {
       uint16_t* oh = a.out_hi + (size_t)row * a.ld_out + h * D + i;
+      if (!a.out_lo) {
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) oh[16 * t] = f16_checked(o[t][r] * inv[r], a.range_flag);
+        continue;
+      }
       uint16_t* ol = a.out_lo + (size_t)row * a.ld_out + h * D + i;
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
@@ -923,6 +1004,11 @@ __global__ __launch_bounds__(256) void k_prefill_attn_combine(const PrefillAttnA
     }
     const float inv = 1.0f / L;
     uint16_t* oh = a.out_hi + (size_t)row * a.ld_out + h * D;
+    if (!a.out_lo) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) oh[lane + 64 * u] = f16_checked(acc[u] * inv, a.range_flag);
+      continue;
+    }
     uint16_t* ol = a.out_lo + (size_t)row * a.ld_out + h * D;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -948,6 +1034,7 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv, qr = PA_QR * pa_row_tiles(G);
   const int nb = (a.rows + qr - 1) / qr, nb16 = (a.rows + PA_QR - 1) / PA_QR;
   if (a.tps < 1 || a.tps > PA_MAXT || a.rows < 1) return hipErrorInvalidValue;
+  if (!a.out_hi || (!a.out_lo && !a.range_flag)) return hipErrorInvalidValue;
   int blocks = 0;
   for (int rb = 0; rb < nb; ++rb) blocks += pa_splits(rb, a.rows, a.pos0, a.tps, qr);
   if (blocks > nb && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;

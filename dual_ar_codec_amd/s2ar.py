@@ -24,7 +24,7 @@ ERRORS = {-1: "S2AR_E_ARG", -2: "S2AR_E_RANGE", -3: "S2AR_E_CAPACITY", -4: "S2AR
 SYMBOLS = ("s2ar_create", "s2ar_prefill", "s2ar_decode_frame", "s2ar_decode_frames", "s2ar_release_stream",
            "s2ar_stream_position", "s2ar_destroy", "s2ar_last_error", "s2ar_error_name", "s2ar_debug_frame",
            "s2ar_time_kernel", "s2ar_debug_frame_batch", "s2ar_share_prefix", "s2ar_time_frames",
-           "s2ar_decode_frames_noalloc")
+           "s2ar_decode_frames_noalloc", "s2ar_set_prefill_precision")
 
 i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 
@@ -90,6 +90,7 @@ def lib():
         L.s2ar_debug_frame_batch.argtypes = [vp, vp, i32, vp, ctypes.POINTER(Taps)]
         L.s2ar_time_frames.argtypes = [vp, i32, i32, vp]
         L.s2ar_decode_frames_noalloc.argtypes = [vp, i32, i32, vp]
+        L.s2ar_set_prefill_precision.argtypes = [vp, i32]
         _lib = L
     return _lib
 
@@ -208,6 +209,10 @@ class Context:
         m = None if mask is None else np.ascontiguousarray(mask, np.uint8)
         c = None if codes is None else np.ascontiguousarray(codes, np.int32)
         self._check(lib().s2ar_prefill(self.h, int(stream_id), _p(t), _p(m), _p(c), len(t)))
+
+    def set_prefill_precision(self, precision):
+        """0: bf16 hi/lo activation split (default); 1: one fp16 activation plane."""
+        self._check(lib().s2ar_set_prefill_precision(self.h, int(precision)))
 
     def decode_frame(self, stream_ids):
         ids = np.ascontiguousarray(np.atleast_1d(stream_ids), np.int32)

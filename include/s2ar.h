@@ -142,6 +142,24 @@ int s2ar_prefill(s2ar_ctx* ctx, int32_t stream_id, const int32_t* tokens, const 
                  const int32_t* vq_codes, int32_t n);
 
 /*
+ * Arithmetic of the prefill's matrix-core products for later s2ar_prefill calls of the context.  The
+ * pages fix no precision for prompt prefill; the acceptance bar (hidden-state cosine >= 0.9999 at
+ * every layer, logits within 2e-2 of their largest magnitude) holds in both modes at the S2 shape.
+ *   0 (default): each fp32 activation enters the bf16 matrix cores as two bf16 halves, hi = bf16(x)
+ *     and lo = bf16(x - hi) (about 16 significant bits), against the exact bf16 weights: two
+ *     products per weight.
+ *   1: each activation is rounded once to IEEE fp16 (11 significant bits) and the weights are taken
+ *     as fp16, rounded to nearest (exact for bf16 magnitudes from 2^-17 to 65504; int8 and E4M3 codes
+ *     are exact), one product per weight on the fp16 matrix cores.  An activation that fp16 cannot
+ *     hold (beyond 65504 in magnitude) makes that s2ar_prefill return S2AR_E_NUMERIC: its positions
+ *     are dropped and the stream is not ready to decode until a later prefill succeeds.
+ * The prefill attention keeps its bf16 three-product split in both modes; decoding is unaffected.
+ * Errors: S2AR_E_ARG (precision not 0 or 1; 1 on a context whose prefill does not run on the
+ * matrix cores, fp32 weights, or whose hidden, q-projection or ffn width is not a multiple of 64).
+ */
+int s2ar_set_prefill_precision(s2ar_ctx* ctx, int32_t precision);
+
+/*
  * Decode one frame for each listed stream (distinct ids, each prefilled).
  * codes_out: [n_streams][n_codebooks]; entry 0 is the semantic code, 1..9 the
  * residual codes, each in [0, codebook_size).  Each stream then advances by

@@ -35,7 +35,7 @@ def _ctx(cfg, w, **kw):
     return ctx
 
 
-def _teacher_forced(name, n_frames=None, gains="unit", prompt=None, **over):
+def _teacher_forced(name, n_frames=None, gains="unit", prompt=None, prefill_precision=0, **over):
     cfg = synth.config(name, **over)
     _say(f"[parity] {name}: generating weights")
     w = synth.make_weights(cfg, gains=gains)
@@ -47,9 +47,11 @@ def _teacher_forced(name, n_frames=None, gains="unit", prompt=None, **over):
     ctx = _ctx(cfg, w)
     del w
     gc.collect()
+    if prefill_precision:
+        ctx.set_prefill_precision(prefill_precision)
     ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
     rep = compare_frames(ctx, 0, frames, cfg).finish()
-    _say(f"[parity] {name}: {rep}")
+    _say(f"[parity] {name} (prefill precision {prefill_precision}): {rep}")
     ctx.close()
     return rep
 
@@ -323,7 +325,7 @@ def test_shared_prefix_errors_leave_state_unchanged():
     ctx.close()
 
 
-def _int8_teacher_forced(name, n_frames, fmt="i8", prompt=None, **over):
+def _int8_teacher_forced(name, n_frames, fmt="i8", prompt=None, prefill_precision=0, **over):
     cfg = synth.config(name, **over)
     _say(f"[parity] {name} {fmt}: generating weights")
     w = synth.make_weights(cfg)
@@ -338,9 +340,11 @@ def _int8_teacher_forced(name, n_frames, fmt="i8", prompt=None, **over):
     ctx = _ctx(dict(cfg, weight_dtype=fmt), w)
     del w
     gc.collect()
+    if prefill_precision:
+        ctx.set_prefill_precision(prefill_precision)
     ctx.prefill(0, toks, mk, cd)
     rep = compare_frames(ctx, 0, frames, cfg).finish()
-    _say(f"[parity] {name} {fmt}: {rep}")
+    _say(f"[parity] {name} {fmt} (prefill precision {prefill_precision}): {rep}")
     ctx.close()
     return rep
 
@@ -366,6 +370,83 @@ def test_int8_voice_clone_prefill_teacher_forced():
     prefilled on the matrix cores in one row block, then 2 frames against the oracle on the same
     quantisation."""
     assert _int8_teacher_forced("voice_clone", 2)["tokens_checked"] > 0
+
+
+# ------------------------------------------------------------------ fp16 prefill (precision 1)
+
+@pytest.mark.timeout(1500)
+def test_voice_clone_prefill_fp16_teacher_forced():
+    """The 1200-position voice-clone prompt at the full S2 shape prefilled with one fp16 activation
+    plane per product (fp16 matrix cores), then 2 frames checked layer by layer against the oracle."""
+    rep = _teacher_forced("voice_clone", n_frames=2, prefill_precision=1)
+    assert rep["tokens_checked"] > 5
+
+
+@pytest.mark.parametrize("case", ["split_k", "two_row_blocks", "int8", "fp8"])
+def test_fp16_prefill_mid(case):
+    """fp16 prefill at the mid shape: a 41-token prompt (its GEMMs split K, the SwiGLU written by
+    the split reduction), a 2100-position prompt (two row blocks of 2048 + 52), and a VQ-masked
+    300-position prompt with int8 and FP8 weights (codes widened to fp16 in LDS)."""
+    if case == "split_k":
+        rep = _teacher_forced("mid", n_frames=4, prefill_precision=1)
+    elif case == "two_row_blocks":
+        cfg = synth.config("mid", max_context=2176)
+        toks = synth.uniform_ints(77, 0, 2100, 0, cfg["vocab_text"])
+        mask = np.zeros(len(toks), np.uint8)
+        codes = np.zeros((len(toks), cfg["n_codebooks"]), np.int32)
+        rep = _teacher_forced("mid", n_frames=2, prompt=(toks, mask, codes), max_context=2176,
+                              prefill_precision=1)
+    else:
+        cfg = synth.config("mid", max_context=384)
+        r = np.random.default_rng(71)
+        n = 300
+        toks = r.integers(0, cfg["vocab_text"], n).astype(np.int32)
+        codes = r.integers(0, cfg["codebook_size"], (n, 10)).astype(np.int32)
+        mask = np.zeros(n, np.uint8)
+        mask[:200] = 1
+        rep = _int8_teacher_forced("mid", 3, "i8" if case == "int8" else "f8", prompt=(toks, mask, codes),
+                                   max_context=384, prefill_precision=1)
+    assert rep["tokens_checked"] > 0
+
+
+def test_fp16_prefill_out_of_range_is_an_error():
+    """An attention-norm gain of 30000 in the first Slow layer puts normed activations beyond fp16's
+    65504: the fp16 prefill fails with S2AR_E_NUMERIC, keeps the stream's position and leaves it not
+    ready to decode; the default precision then prefills the same prompt and decodes."""
+    cfg = synth.config("mid", max_context=256)
+    w = synth.make_weights(cfg)
+    names = [n for n, _, _ in synth.tensor_specs(cfg)]
+    big = np.array([30000.0], np.float32).view(np.uint32) >> 16  # bf16 bits of 30000 (exact)
+    w[names.index("slow.layers.0.attn_norm")][:] = np.uint16(big[0])
+    toks, _, _ = synth.make_prompt(cfg)
+    ctx = _ctx(cfg, w)
+    with pytest.raises(s2ar.S2arError) as e:
+        ctx.set_prefill_precision(2)
+    assert e.value.code == -1
+    ctx.set_prefill_precision(1)
+    with pytest.raises(s2ar.S2arError) as e:
+        ctx.prefill(0, toks)
+    assert e.value.code == -7 and ctx.position(0) == 0
+    with pytest.raises(s2ar.S2arError) as e:
+        ctx.decode_frames([0], 1)
+    assert e.value.code == -4
+    ctx.set_prefill_precision(0)
+    ctx.prefill(0, toks)
+    assert ctx.position(0) == len(toks)
+    out = ctx.decode_frames([0], 2)
+    assert out.shape == (2, 1, cfg["n_codebooks"]) and (out >= 0).all()
+    ctx.close()
+
+
+def test_fp16_prefill_needs_the_matrix_core_prefill():
+    """fp32 weights prefill position by position: precision 1 is refused there."""
+    cfg = synth.config("tiny")
+    ctx = _ctx(cfg, synth.make_weights(cfg))
+    with pytest.raises(s2ar.S2arError) as e:
+        ctx.set_prefill_precision(1)
+    assert e.value.code == -1
+    ctx.set_prefill_precision(0)
+    ctx.close()
 
 
 @pytest.mark.parametrize("fmt", ["i8", "f8"])
