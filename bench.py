@@ -394,8 +394,8 @@ def main():
         ctx.set_prefill_precision(0)
         prefill["fp16"] = {"ms": round(pt16 * 1e3, 2), "tflop_s": round((lin + att) / pt16 / 1e12, 1),
                            "mfma_frac": round((lin + att) / pt16 / 1e12 / 2500.0, 4),
-                           "note": "prefill precision 1: activations rounded once to fp16, weights taken as "
-                                   "fp16, one fp16 MFMA pass per product (attention keeps its bf16 split)"}
+                           "note": "prefill precision 1: activations, attention operands and softmax weights rounded "
+                                   "once to fp16, weights taken as fp16, one fp16 MFMA pass per product"}
         if args.prefix_share:
             prefill["prefix_sharing"] = prefix_sharing(ctx, vc, vt, vm, vcodes)
 

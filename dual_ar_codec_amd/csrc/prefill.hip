@@ -674,19 +674,30 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint2 a, uint2 b) {
   return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
+// four fp32 values as two packed fp16 pairs (element 0 low), rounded to nearest even
+__device__ __forceinline__ uint2 f16x4_bits(const float (&x)[4]) { return uint2{f16_pair(x[0], x[1]), f16_pair(x[2], x[3])}; }
+
+__device__ __forceinline__ f16x8 as_f16x8(uint2 a, uint2 b) {
+  return __builtin_bit_cast(f16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
 // e^x as 2^(x log2 e) on the hardware base-2 exponential (0 at x = -inf): the softmax weights'
 // exponentials, a large share of the attention's vector work
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-template <int D, int G, bool KB, bool VB>
-__global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const PrefillAttnArgs a) {
+// F16 (the fp16 prefill, out_lo == nullptr): q, the staged keys and values and the softmax weights are
+// rounded once to fp16 and every product is one v_mfma_f32_16x16x32_f16; K and V take one LDS plane.
+// The fp16 form fits 128 VGPRs (two spilled), so two workgroups of 8 wavefronts share a CU: 1200-position
+// prefill 18.1 -> 17.7 ms against its natural 130 VGPRs at one workgroup per CU.
+template <int D, int G, bool KB, bool VB, bool F16>
+__global__ __launch_bounds__(64 * G * pa_row_tiles(G), F16 && G >= 2 ? 4 : 1) void k_prefill_attn(const PrefillAttnArgs a) {
   constexpr int RT = pa_row_tiles(G), QR = PA_QR * RT, KT = PA_KT, NT = 64 * G * RT, NDS = D / 32, NDT = D / 16;
-  constexpr int KS = D + 8;    // bf16 row stride of the K planes [key][dim]
-  constexpr int VS = KT + 12;  // bf16 row stride of the transposed V planes [dim][key]
+  constexpr int KS = D + 8;    // 16-bit row stride of the K planes [key][dim]
+  constexpr int VS = KT + 12;  // 16-bit row stride of the transposed V planes [dim][key]
   __shared__ __attribute__((aligned(16))) uint16_t kh[KT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t kl[KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t kl[F16 ? 8 : KT * KS];
   __shared__ __attribute__((aligned(16))) uint16_t vh[D * VS];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[F16 ? 8 : D * VS];
   __shared__ int rowoff[PA_MAXT * KT];
   const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int i = lane & 15, c = lane >> 4;
@@ -722,6 +733,7 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const
   const int qrow = min(wrow0 + min(i, max(wrows, 1) - 1), a.rows - 1);
   const int rpos = a.pos0 + qrow;
   bf16x8 qh[NDS], ql[NDS];
+  f16x8 qf[NDS];
   {
     float q[NDS][8];
     const float* qp = a.qkv + (size_t)qrow * a.ld + h * D + 8 * c;
@@ -759,11 +771,16 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const
       }
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      uint2 h0, l0, h1, l1;
-      split4({q[ds][0], q[ds][1], q[ds][2], q[ds][3]}, h0, l0);
-      split4({q[ds][4], q[ds][5], q[ds][6], q[ds][7]}, h1, l1);
-      qh[ds] = as_bf16x8(h0, h1);
-      ql[ds] = as_bf16x8(l0, l1);
+      if constexpr (F16) {
+        qf[ds] = as_f16x8(f16x4_bits({q[ds][0], q[ds][1], q[ds][2], q[ds][3]}),
+                          f16x4_bits({q[ds][4], q[ds][5], q[ds][6], q[ds][7]}));
+      } else {
+        uint2 h0, l0, h1, l1;
+        split4({q[ds][0], q[ds][1], q[ds][2], q[ds][3]}, h0, l0);
+        split4({q[ds][4], q[ds][5], q[ds][6], q[ds][7]}, h1, l1);
+        qh[ds] = as_bf16x8(h0, h1);
+        ql[ds] = as_bf16x8(l0, l1);
+      }
     }
   }
 
@@ -827,6 +844,14 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const
               vx[x][y] = live ? vr[u][x][y] : 0.f;
             }
           }
+          if constexpr (F16) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) *reinterpret_cast<uint2*>(&kh[(4 * kg + x) * KS + 4 * dg]) = f16x4_bits(kx[x]);
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+              *reinterpret_cast<uint2*>(&vh[(4 * dg + y) * VS + 4 * kg]) = f16x4_bits({vx[0][y], vx[1][y], vx[2][y], vx[3][y]});
+            continue;
+          }
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             uint2 hh, ll;
@@ -855,6 +880,10 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const
 #pragma unroll
       for (int kt = 0; kt < KT / 16; ++kt) {
         const int ko = (kt * 16 + i) * KS + 32 * ds + 8 * c;
+        if constexpr (F16) {
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const f16x8*>(&kh[ko]), qf[ds], st[kt], 0, 0, 0);
+          continue;
+        }
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kh[ko]);
         const bf16x8 kb8 = *reinterpret_cast<const bf16x8*>(&kl[ko]);
         st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[ds], st[kt], 0, 0, 0);
@@ -910,6 +939,17 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G)) void k_prefill_attn(const
     // O += P V over 32-key blocks m: lane (i, c) contracts keys 32 m + 4 c + r and 32 m + 16 + 4 c + r
 #pragma unroll
     for (int m = 0; m < KT / 32; ++m) {
+      if constexpr (F16) {
+        const f16x8 pf = as_f16x8(f16x4_bits({st[2 * m][0], st[2 * m][1], st[2 * m][2], st[2 * m][3]}),
+                                  f16x4_bits({st[2 * m + 1][0], st[2 * m + 1][1], st[2 * m + 1][2], st[2 * m + 1][3]}));
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+          const int vo = (16 * t + i) * VS + 32 * m + 4 * c;
+          const f16x8 vf = as_f16x8(*reinterpret_cast<const uint2*>(&vh[vo]), *reinterpret_cast<const uint2*>(&vh[vo + 16]));
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf, o[t], 0, 0, 0);
+        }
+        continue;
+      }
       uint2 p0h, p0l, p1h, p1l;
       split4({st[2 * m][0], st[2 * m][1], st[2 * m][2], st[2 * m][3]}, p0h, p0l);
       split4({st[2 * m + 1][0], st[2 * m + 1][1], st[2 * m + 1][2], st[2 * m + 1][3]}, p1h, p1l);
@@ -1024,13 +1064,13 @@ __global__ __launch_bounds__(256) void k_prefill_attn_combine(const PrefillAttnA
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool F16>
 static void launch_pa_kernel(const PrefillAttnArgs& a, dim3 grid, hipStream_t s) {
   const dim3 block(64 * G * pa_row_tiles(G));
-  if (a.k_bf16 && a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, true>), grid, block, 0, s, a);
-  else if (a.k_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, false>), grid, block, 0, s, a);
-  else if (a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, false, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((k_prefill_attn<D, G, false, false>), grid, block, 0, s, a);
+  if (a.k_bf16 && a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, true, F16>), grid, block, 0, s, a);
+  else if (a.k_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, true, false, F16>), grid, block, 0, s, a);
+  else if (a.v_bf16) hipLaunchKernelGGL((k_prefill_attn<D, G, false, true, F16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_prefill_attn<D, G, false, false, F16>), grid, block, 0, s, a);
 }
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
@@ -1046,7 +1086,8 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   // some row block has several splits: the attention, then the merge
 #define S2_PA(DD, GG)                                                                     \
   if (a.D == DD && G == GG) {                                                             \
-    launch_pa_kernel<DD, GG>(a, grid, s);                                                 \
+    if (a.out_lo) launch_pa_kernel<DD, GG, false>(a, grid, s);                            \
+    else launch_pa_kernel<DD, GG, true>(a, grid, s);                                      \
     hipError_t e = hipGetLastError();                                                     \
     if (e != hipSuccess || blocks == nb) return e;                                        \
     hipLaunchKernelGGL(k_prefill_attn_combine<DD>, dim3(nb16, a.Hq), dim3(256), 0, s, a); \

@@ -150,10 +150,12 @@ int s2ar_prefill(s2ar_ctx* ctx, int32_t stream_id, const int32_t* tokens, const 
  *     products per weight.
  *   1: each activation is rounded once to IEEE fp16 (11 significant bits) and the weights are taken
  *     as fp16, rounded to nearest (exact for bf16 magnitudes from 2^-17 to 65504; int8 and E4M3 codes
- *     are exact), one product per weight on the fp16 matrix cores.  An activation that fp16 cannot
- *     hold (beyond 65504 in magnitude) makes that s2ar_prefill return S2AR_E_NUMERIC: its positions
- *     are dropped and the stream is not ready to decode until a later prefill succeeds.
- * The prefill attention keeps its bf16 three-product split in both modes; decoding is unaffected.
+ *     are exact), one product per weight on the fp16 matrix cores; the prefill attention likewise
+ *     rounds q, the cached keys and values and its softmax weights once to fp16 (one product
+ *     instead of three).  An activation that fp16 cannot hold (beyond 65504 in magnitude) makes
+ *     that s2ar_prefill return S2AR_E_NUMERIC: its positions are dropped and the stream is not
+ *     ready to decode until a later prefill succeeds.
+ * Decoding is the same in both modes (the cache holds the same fp32 or bf16 keys and values).
  * Errors: S2AR_E_ARG (precision not 0 or 1; 1 on a context whose prefill does not run on the
  * matrix cores, fp32 weights, or whose hidden, q-projection or ffn width is not a multiple of 64).
  */
