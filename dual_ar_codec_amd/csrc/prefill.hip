@@ -501,7 +501,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     if (g.epi == GEMM_SWIGLU && g.N % 256 == 0 && g.N >= 16384) return gemm2_launch<128, 256, GEMM_SWIGLU>(g, s);
     // fp16 (one activation plane, a smaller LDS stage): QKV on 128 x 256 tiles and the residual
     // products on 128 x 128 (1200 rows: 19.4-19.6 ms each against 20.4 ms on 64 x 256)
-    if (g.a_f16 && g.epi == GEMM_STORE && g.N % 256 == 0) return gemm2_launch<128, 256, GEMM_STORE>(g, s);
+    // (8-bit weights keep 64 x 256 for QKV: their 128 x 256 form spills)
+    if (g.a_f16 && g.epi == GEMM_STORE && g.N % 256 == 0 && g.w_fmt == W_BF16)
+      return gemm2_launch<128, 256, GEMM_STORE>(g, s);
     if (g.a_f16 && g.epi == GEMM_ADD) return gemm2_launch<128, 128, GEMM_ADD>(g, s);
     if (g.N % 256 == 0) {
       if (g.epi == GEMM_STORE) return gemm2_launch<64, 256, GEMM_STORE>(g, s);
