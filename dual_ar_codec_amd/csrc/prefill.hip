@@ -692,7 +692,7 @@ __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f
 // The fp16 form fits 128 VGPRs (two spilled), so two workgroups of 8 wavefronts share a CU: 1200-position
 // prefill 18.1 -> 17.7 ms against its natural 130 VGPRs at one workgroup per CU.
 template <int D, int G, bool KB, bool VB, bool F16>
-__global__ __launch_bounds__(64 * G * pa_row_tiles(G), F16 && G >= 2 ? 4 : 1) void k_prefill_attn(const PrefillAttnArgs a) {
+__global__ __launch_bounds__(64 * G * pa_row_tiles(G), F16 && G >= 4 ? 4 : 1) void k_prefill_attn(const PrefillAttnArgs a) {
   constexpr int RT = pa_row_tiles(G), QR = PA_QR * RT, KT = PA_KT, NT = 64 * G * RT, NDS = D / 32, NDT = D / 16;
   constexpr int KS = D + 8;    // 16-bit row stride of the K planes [key][dim]
   constexpr int VS = KT + 12;  // 16-bit row stride of the transposed V planes [dim][key]
