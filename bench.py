@@ -279,7 +279,7 @@ def main():
     ap.add_argument("--mid", type=int, default=1, help="also time the mid workload (32 frames)")
     ap.add_argument("--counter-pass", type=int, default=0,
                     help="for rocprofv3 --pmc passes: prefill, 2 frames enqueued without graphs, the voice-clone "
-                         "prefill (unless --prefill 0), the gate/up and "
+                         "prefill at both precisions (unless --prefill 0), the gate/up and "
                          "streaming-read launches (--kernel-iters each) and the 256 MiB copy probe, then exit")
     ap.add_argument("--prefix-share", type=int, default=1,
                     help="time to first frame of the voice-clone prompt with its 1000-position prefix shared")
@@ -311,9 +311,13 @@ def main():
     if args.counter_pass:
         ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
         out = ctx.decode_frames_noalloc(0, 2)
-        if vc is not None:  # the voice-clone prefill (matrix-core GEMMs and attention, no graph)
+        if vc is not None:  # the voice-clone prefill (matrix-core GEMMs and attention, no graph), both precisions
             vt, vm, vcodes = synth.make_prompt(vc)
             ctx.prefill(1, vt, vm, vcodes)
+            ctx.release(1)
+            ctx.set_prefill_precision(1)
+            ctx.prefill(1, vt, vm, vcodes)
+            ctx.set_prefill_precision(0)
         ms, nbytes = ctx.time_kernel(0, args.kernel_iters)
         sms, sbytes = ctx.time_kernel(1, args.kernel_iters)
         ctx.close()
