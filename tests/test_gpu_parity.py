@@ -420,16 +420,36 @@ def test_fp16_prefill_mid(case):
     assert rep["tokens_checked"] > 0
 
 
-def test_fp16_prefill_out_of_range_is_an_error():
-    """An attention-norm gain of 30000 in the first Slow layer puts normed activations beyond fp16's
-    65504: the fp16 prefill fails with S2AR_E_NUMERIC, keeps the stream's position and leaves it not
-    ready to decode; the default precision then prefills the same prompt and decodes."""
-    cfg = synth.config("mid", max_context=256)
+def _scaled_bf16(a, k):
+    """bf16 bits of the tensor times 2^k (exact: a power-of-two scale keeps every bf16 value)."""
+    f = synth.as_f32(a) * np.float32(2.0 ** k)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("where", ["norm", "swiglu_split", "swiglu", "attention"])
+def test_fp16_prefill_out_of_range_is_an_error(where):
+    """A first Slow layer whose prefill activations leave fp16's range, at each kind of producer: an
+    attention-norm gain of 30000 (the RMSNorm split), gate and up rows scaled by 256 (the SwiGLU
+    written by the split-K reduction for a 64-token prompt, and by the GEMM epilogue for 600 tokens),
+    value rows scaled by 2^17 (values beyond 65504 reach the fp16 attention and its output).  The
+    fp16 prefill fails with S2AR_E_NUMERIC, keeps the stream's position and leaves it not ready to
+    decode; the default precision then prefills the same prompt and decodes."""
+    cfg = synth.config("mid", max_context=704)
     w = synth.make_weights(cfg)
     names = [n for n, _, _ in synth.tensor_specs(cfg)]
-    big = np.array([30000.0], np.float32).view(np.uint32) >> 16  # bf16 bits of 30000 (exact)
-    w[names.index("slow.layers.0.attn_norm")][:] = np.uint16(big[0])
-    toks, _, _ = synth.make_prompt(cfg)
+    pre = "slow.layers.0."
+    if where == "norm":
+        big = np.array([30000.0], np.float32).view(np.uint32) >> 16  # bf16 bits of 30000 (exact)
+        w[names.index(pre + "attn_norm")][:] = np.uint16(big[0])
+    elif where.startswith("swiglu"):
+        for t in ("w_gate", "w_up"):
+            w[names.index(pre + t)] = _scaled_bf16(w[names.index(pre + t)], 8)
+    else:
+        w[names.index(pre + "wv")] = _scaled_bf16(w[names.index(pre + "wv")], 17)
+    if where == "swiglu":
+        toks = synth.uniform_ints(79, 0, 600, 0, cfg["vocab_text"])
+    else:
+        toks, _, _ = synth.make_prompt(cfg)
     ctx = _ctx(cfg, w)
     with pytest.raises(s2ar.S2arError) as e:
         ctx.set_prefill_precision(2)
