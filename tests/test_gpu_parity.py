@@ -420,6 +420,26 @@ def test_fp16_prefill_mid(case):
     assert rep["tokens_checked"] > 0
 
 
+@pytest.mark.parametrize("G,D", [(1, 128), (2, 64), (8, 64), (8, 128)])
+def test_fp16_prefill_attention_group_sizes(G, D):
+    """The fp16 prefill attention at 1, 2 and 8 q heads per KV head (two 16-row tiles per workgroup
+    below 8, one at 8; the 128-VGPR form only from 4 up): a 530-position prompt, so row blocks of
+    every height and key ranges split over workgroups, then 2 frames against the oracle."""
+    hq = 4 if (G, D) == (1, 128) else 8
+    cfg = synth.micro_config(seed=90 + G + D, slow_layers=2, fast_layers=1, hidden=512, n_q_heads=hq,
+                             n_kv_heads=hq // G, head_dim=D, ffn=1024, vocab_text=1000, codebook_size=256,
+                             weight_dtype="bf16", max_context=576)
+    w = synth.make_weights(cfg)
+    toks = synth.uniform_ints(91, 0, 530, 0, cfg["vocab_text"])
+    frames = oracle_run(cfg, w, toks, None, None, 2)
+    ctx = _ctx(cfg, w)
+    ctx.set_prefill_precision(1)
+    ctx.prefill(0, toks)
+    rep = compare_frames(ctx, 0, frames, cfg).finish()
+    _say(f"[parity] fp16 prefill G {G} D {D}: {rep}")
+    ctx.close()
+
+
 def _scaled_bf16(a, k):
     """bf16 bits of the tensor times 2^k (exact: a power-of-two scale keeps every bf16 value)."""
     f = synth.as_f32(a) * np.float32(2.0 ** k)
