@@ -222,19 +222,21 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
 // share a weight column sit on one XCD and reuse it from that XCD's L2.
 // F16: the activations are one IEEE fp16 plane (g.a_hi), the weights are converted to fp16 when
 // staged, and every product is one v_mfma_f32_16x16x32_f16; the SwiGLU epilogue writes fp16.
-template <int BM, int BN, int NW, int WM, int EPI, int WF = W_BF16, bool F16 = false>
+template <int BM, int BN, int NW, int WM, int EPI, int WF = W_BF16, bool F16 = false, int BK = 64>
 __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   // WF: bf16 weights, or 8-bit codes loaded 8 bytes per lane, widened to bf16 (fp16) when staged in
   // LDS and scaled per output column (weight row) in the epilogue
   using WR = typename std::conditional<WF == W_BF16, u32x4, u32x2>::type;
-  // LDS row stride (bf16): 64 + 16.  Measured on the 1200-position prefill: 64 (no pad) 31.1 ms,
-  // 72 26.5 ms, 80 25.9 ms; 80 fills the 160 KB of LDS exactly with the 128 x 256 tiles.
-  constexpr int NT = NW * 64, WN = NW / WM, BK = 64, LS = BK + 16;
+  // LDS row stride (16-bit elements): BK 64: 64 + 16.  Measured on the 1200-position prefill: 64 (no
+  // pad) 31.1 ms, 72 26.5 ms, 80 25.9 ms; 80 fills the 160 KB of LDS exactly with the 128 x 256
+  // tiles.  BK 32: 32 + 8 (rows 20 words apart: the 16 rows a fragment read touches hit distinct banks).
+  constexpr int NT = NW * 64, WN = NW / WM, LS = BK == 64 ? BK + 16 : BK + 8;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  // coalesced stage loads: one load instruction of a wavefront covers 8 rows x 64 bf16 (8 lanes per
-  // row, 16 bytes each) of an activation plane or of the weights
-  constexpr int AI = BM / (8 * NW);                   // load instructions per thread per stage and A plane
-  constexpr int WI = BN / (8 * NW);                   // W load instructions per thread per stage
+  // coalesced stage loads: one load instruction of a wavefront covers RPI rows x BK elements (LPR
+  // lanes per row, 16 bytes each) of an activation plane or of the weights
+  constexpr int LPR = BK / 8, RPI = WAVE / LPR;
+  constexpr int AI = BM / (RPI * NW);                 // load instructions per thread per stage and A plane
+  constexpr int WI = BN / (RPI * NW);                 // W load instructions per thread per stage
   constexpr int NPL = F16 ? 1 : 2;                    // activation planes
   constexpr int STAGE = (NPL * BM + BN) * LS;         // 16-bit elements: A hi (or fp16), A lo, W
   static_assert(AI >= 1 && WI >= 1, "tile too small for the loaders");
@@ -255,14 +257,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
   const int nk = g.K / BK / max(g.split, 1), kbeg = ks * nk;  // this block's stages
   (void)NT;
 
-  // A rows of this thread: a_row0 + 8 i, columns 8 (lane % 8) .. + 7 of the stage, both planes
-  const int r_k = (lane & 7) * 8;
-  const int a_row0 = wv * (BM / NW) + (lane >> 3);
+  // A rows of this thread: a_row0 + RPI i, columns 8 (lane % LPR) .. + 7 of the stage, both planes
+  const int r_k = (lane % LPR) * 8;
+  const int a_row0 = wv * (BM / NW) + lane / LPR;
   size_t a_off[AI];  // row offsets into A (rows past M repeat the last row)
 #pragma unroll
-  for (int i = 0; i < AI; ++i) a_off[i] = (size_t)min(m0 + a_row0 + 8 * i, g.M - 1) * g.lda + r_k;
-  // W rows: w_row0 + 8 i
-  const int w_row0 = wv * (BN / NW) + (lane >> 3);
+  for (int i = 0; i < AI; ++i) a_off[i] = (size_t)min(m0 + a_row0 + RPI * i, g.M - 1) * g.lda + r_k;
+  // W rows: w_row0 + RPI i
+  const int w_row0 = wv * (BN / NW) + lane / LPR;
   const size_t w_off = (size_t)(n0 + w_row0) * g.K + r_k;  // element (= byte for 8-bit codes) offset
 
   u32x4 ah0[AI], al0[AI], ah1[AI], al1[AI];
@@ -278,10 +280,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
     for (int i = 0; i < WI; ++i) {
       if constexpr (WF == W_BF16)
         wr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.w) + w_off + (size_t)8 * i * g.K + k));
+            reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(g.w) + w_off + (size_t)RPI * i * g.K + k));
       else
         wr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(g.w) + w_off + (size_t)8 * i * g.K + k));
+            reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(g.w) + w_off + (size_t)RPI * i * g.K + k));
     }
   };
   auto stash = [&](int st, const u32x4 (&ah)[AI], const u32x4 (&al)[AI], const WR (&wr)[WI]) {
@@ -290,8 +292,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
     uint16_t* sw = sh + NPL * BM * LS;
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      *reinterpret_cast<u32x4*>(sh + (a_row0 + 8 * i) * LS + r_k) = ah[i];
-      if constexpr (!F16) *reinterpret_cast<u32x4*>(sl + (a_row0 + 8 * i) * LS + r_k) = al[i];
+      *reinterpret_cast<u32x4*>(sh + (a_row0 + RPI * i) * LS + r_k) = ah[i];
+      if constexpr (!F16) *reinterpret_cast<u32x4*>(sl + (a_row0 + RPI * i) * LS + r_k) = al[i];
     }
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm2(const GemmArgs g) {
       if constexpr (WF != W_BF16) v = widen8<WF, F16>(wr[i]);
       else if constexpr (F16) v = bf16x8_to_f16(wr[i]);
       else v = wr[i];
-      *reinterpret_cast<u32x4*>(sw + (w_row0 + 8 * i) * LS + r_k) = v;
+      *reinterpret_cast<u32x4*>(sw + (w_row0 + RPI * i) * LS + r_k) = v;
     }
   };
 
@@ -463,21 +465,21 @@ static int gemm_splits(const GemmArgs& g, int ntiles) {
   return S;
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, int NW = 8, int BK = 64>
 static hipError_t gemm2_launch(GemmArgs g, hipStream_t s) {
   const int ntiles = (g.M + BM - 1) / BM * (g.N / BN);
   g.split = gemm_splits(g, ntiles);
-  const dim3 grid(ntiles * g.split), block(512);
+  const dim3 grid(ntiles * g.split), block(NW * 64);
   if (g.a_f16) {
-    if (g.w_fmt == W_I8) hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_I8, true>), grid, block, 0, s, g);
-    else if (g.w_fmt == W_F8) hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_F8, true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_BF16, true>), grid, block, 0, s, g);
+    if (g.w_fmt == W_I8) hipLaunchKernelGGL((k_gemm2<BM, BN, NW, 2, EPI, W_I8, true, BK>), grid, block, 0, s, g);
+    else if (g.w_fmt == W_F8) hipLaunchKernelGGL((k_gemm2<BM, BN, NW, 2, EPI, W_F8, true, BK>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((k_gemm2<BM, BN, NW, 2, EPI, W_BF16, true, BK>), grid, block, 0, s, g);
   } else if (g.w_fmt == W_I8) {
-    hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_I8>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((k_gemm2<BM, BN, NW, 2, EPI, W_I8, false, BK>), grid, block, 0, s, g);
   } else if (g.w_fmt == W_F8) {
-    hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI, W_F8>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((k_gemm2<BM, BN, NW, 2, EPI, W_F8, false, BK>), grid, block, 0, s, g);
   } else {
-    hipLaunchKernelGGL((k_gemm2<BM, BN, 8, 2, EPI>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((k_gemm2<BM, BN, NW, 2, EPI, W_BF16, false, BK>), grid, block, 0, s, g);
   }
   if (g.split > 1) {
     const int cols = EPI == GEMM_SWIGLU ? g.N / 2 : g.N;
