@@ -99,6 +99,7 @@ static float bf16_bits_f32(uint16_t b) {
 }
 
 void orc_quantize_rows_i8(const uint16_t* w, int64_t rows, int64_t cols, int8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
     float m = 0.0f;
     for (int64_t k = 0; k < cols; ++k) {
@@ -117,6 +118,7 @@ void orc_quantize_rows_i8(const uint16_t* w, int64_t rows, int64_t cols, int8_t*
 }
 
 void orc_dequantize_rows_i8(const int8_t* q, const float* s, int64_t rows, int64_t cols, float* out) {
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t k = 0; k < cols; ++k) out[r * cols + k] = (float)q[r * cols + k] * s[r];
 }
@@ -169,6 +171,7 @@ void orc_quantize_rows_f8(const uint16_t* w, int64_t rows, int64_t cols, uint8_t
 }
 
 void orc_dequantize_rows_f8(const uint8_t* q, const float* s, int64_t rows, int64_t cols, float* out) {
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t k = 0; k < cols; ++k) out[r * cols + k] = (float)orc_f8_value(q[r * cols + k]) * s[r];
 }
