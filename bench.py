@@ -6,7 +6,7 @@ synthetic bf16 weights: 41-token prompt, then frames of greedy decode, one
 stream ("s2pro-native", Where it stands, measures this workload).  The timed
 region holds exactly K frames; weights, KV and state are resident in HBM.
 
-Prints one JSON line.  --gpus N with N > 1 exits: this build drives one GPU.
+Prints one JSON line.  --gpus N with N > 1 exits: the benchmark drives one GPU.
 """
 from __future__ import annotations
 
@@ -285,7 +285,7 @@ def main():
                     help="time to first frame of the voice-clone prompt with its 1000-position prefix shared")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py drives one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        print(f"bench.py drives one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
