@@ -45,12 +45,34 @@ def cpu_baseline(cfg, weights, budget_s: float):
         s = st.slow_step(codes)
         h, c0 = s["h"], s["c0"]
         frames += 1
-        if time.perf_counter() - t0 >= budget_s:
+        if time.perf_counter() - t0 >= budget_s or frames + 2 >= cfg["max_context"]:
             break
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    from dual_ar_codec_amd import metrics
+    wbytes = metrics.frame_bytes(cfg, 2)["total"]  # the frame's bf16-stored weights (+ a 2-position KV)
     return {"value": frames / dt, "unit": "frames/s", "cores": min(cores, os.cpu_count() or cores), "kind": "oracle",
-            "sample": f"{frames} frames of the {cfg['name']} shape after a 1-token prompt ({dt:.1f} s, fp64 oracle)"}
+            "sample": f"{frames} frames of the {cfg['name']} shape after a 1-token prompt ({dt:.1f} s, fp64 oracle)",
+            "host": host_cpu(), "effective_host_gbps": round(wbytes * frames / dt / 1e9, 2)}
+
+
+def host_cpu():
+    """Model name, sockets and logical CPUs of this host (from /proc/cpuinfo)."""
+    model, sockets, cpus = None, set(), 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "processor":
+                    cpus += 1
+                elif key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    sockets.add(val)
+    except OSError:
+        pass
+    return {"model": model, "sockets": len(sockets) or None, "logical_cpus": cpus or os.cpu_count()}
 
 
 def measured_traffic():
