@@ -159,18 +159,22 @@ def test_full_mixed_kv_cache_teacher_forced(kv):
     assert rep["tokens_checked"] > 0
 
 
-@pytest.mark.parametrize("kv", ["k_bf16", "v_bf16"])
-def test_batched_mixed_kv_cache_mid_ragged(kv):
+@pytest.mark.parametrize("kv,precision", [("k_bf16", 0), ("v_bf16", 0), ("k_bf16", 1), ("v_bf16", 1)])
+def test_batched_mixed_kv_cache_mid_ragged(kv, precision):
+    """Mixed KV caches through the batched kernels, five ragged streams; precision 1 prefills them
+    with the fp16 products (its attention converts the bf16 or fp32 cache entries to fp16)."""
     cfg = synth.config("mid", max_context=640, kv_dtype=kv)
     w = synth.make_weights(cfg)
     prompts = _ragged_prompts(cfg, [64, 17, 300, 130, 5], 31)
     per_stream = _oracle_frames_per_stream(cfg, w, prompts, 3)
     ctx = _ctx(cfg, w, max_streams=6)
+    if precision:
+        ctx.set_prefill_precision(precision)
     ids = [0, 2, 3, 4, 5]
     for s_, p in zip(ids, prompts):
         ctx.prefill(s_, p)
     rep = _compare_batch(ctx, ids, per_stream, cfg, Report()).finish()
-    _say(f"[parity] batched mid, {kv} KV: {rep}")
+    _say(f"[parity] batched mid, {kv} KV, prefill precision {precision}: {rep}")
     ctx.close()
 
 
