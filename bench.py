@@ -300,9 +300,10 @@ def main():
     ap.add_argument("--slice-steps", type=int, default=60, help="batch-1 frames with the semantic-slice head (0 = skip)")
     ap.add_argument("--mid", type=int, default=1, help="also time the mid workload (32 frames)")
     ap.add_argument("--counter-pass", type=int, default=0,
-                    help="for rocprofv3 --pmc passes: prefill, 2 frames enqueued without graphs, the voice-clone "
+                    help="for rocprofv3 --pmc passes (1): prefill, 2 frames enqueued without graphs, the voice-clone "
                          "prefill at both precisions (unless --prefill 0), the gate/up and "
-                         "streaming-read launches (--kernel-iters each) and the 256 MiB copy probe, then exit")
+                         "streaming-read launches (--kernel-iters each) and the 256 MiB copy probe, then exit; "
+                         "(2): one eager batched step of the 16-stream workload and the copy probe")
     ap.add_argument("--prefix-share", type=int, default=1,
                     help="time to first frame of the voice-clone prompt with its 1000-position prefix shared")
     args = ap.parse_args()
@@ -330,6 +331,25 @@ def main():
     log(f"[bench] weights in {time.perf_counter() - t:.1f} s; uploading")
     toks, mask, codes = synth.make_prompt(cfg)
     ctx = s2ar.Context(cfg, w, max_streams=3 if args.prefix_share else 2)
+    if args.counter_pass == 2:
+        # one batched step of the 16-stream workload (bf16 keys), enqueued eagerly (no graph), then
+        # the copy probe
+        mcfg = synth.config("multi_stream", kv_dtype="k_bf16")
+        n = mcfg["n_streams"]
+        ctx.close()
+        mctx = s2ar.Context(mcfg, w, max_streams=n)
+        for s_ in range(n):
+            mt, _, _ = synth.make_prompt(mcfg, s_)
+            mctx.prefill(s_, mt)
+        mctx.debug_frame_batch(list(range(n)))
+        mctx.close()
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_pass": 2, "streams": n, "copy_bytes": 256 << 20}))
+        return
     if args.counter_pass:
         ctx.prefill(0, toks, mask if mask.any() else None, codes if mask.any() else None)
         out = ctx.decode_frames_noalloc(0, 2)
