@@ -53,7 +53,8 @@ def cpu_baseline(cfg, weights, budget_s: float):
     wbytes = metrics.frame_bytes(cfg, 2)["total"]  # the frame's bf16-stored weights (+ a 2-position KV)
     return {"value": frames / dt, "unit": "frames/s", "cores": min(cores, os.cpu_count() or cores), "kind": "oracle",
             "sample": f"{frames} frames of the {cfg['name']} shape after a 1-token prompt ({dt:.1f} s, fp64 oracle)",
-            "host": host_cpu(), "effective_host_gbps": round(wbytes * frames / dt / 1e9, 2)}
+            "host": host_cpu(), "effective_host_gbps": round(wbytes * frames / dt / 1e9, 2),
+            "ms_per_frame": round(dt / frames * 1e3, 2), "codebook_tok_s": round(10 * frames / dt, 2)}
 
 
 def host_cpu():
