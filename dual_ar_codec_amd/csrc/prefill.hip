@@ -853,7 +853,8 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G), F16 && G >= 4 ? 4 : 1) vo
             for (int x = 0; x < 4; ++x) *reinterpret_cast<uint2*>(&kh[(4 * kg + x) * KS + 4 * dg]) = f16x4_bits(kx[x]);
 #pragma unroll
             for (int y = 0; y < 4; ++y)
-              *reinterpret_cast<uint2*>(&vh[(4 * dg + y) * VS + 4 * kg]) = f16x4_bits({vx[0][y], vx[1][y], vx[2][y], vx[3][y]});
+              *reinterpret_cast<uint2*>(&vh[(4 * dg + y) * VS + 4 * (kg ^ ((dg >> 2) & 3))]) =
+                  f16x4_bits({vx[0][y], vx[1][y], vx[2][y], vx[3][y]});
             continue;
           }
 #pragma unroll
@@ -867,8 +868,8 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G), F16 && G >= 4 ? 4 : 1) vo
           for (int y = 0; y < 4; ++y) {
             uint2 hh, ll;
             split4({vx[0][y], vx[1][y], vx[2][y], vx[3][y]}, hh, ll);
-            *reinterpret_cast<uint2*>(&vh[(4 * dg + y) * VS + 4 * kg]) = hh;
-            *reinterpret_cast<uint2*>(&vl[(4 * dg + y) * VS + 4 * kg]) = ll;
+            *reinterpret_cast<uint2*>(&vh[(4 * dg + y) * VS + 4 * (kg ^ ((dg >> 2) & 3))]) = hh;
+            *reinterpret_cast<uint2*>(&vl[(4 * dg + y) * VS + 4 * (kg ^ ((dg >> 2) & 3))]) = ll;
           }
         }
       }
@@ -948,7 +949,7 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G), F16 && G >= 4 ? 4 : 1) vo
                                   f16x4_bits({st[2 * m + 1][0], st[2 * m + 1][1], st[2 * m + 1][2], st[2 * m + 1][3]}));
 #pragma unroll
         for (int t = 0; t < NDT; ++t) {
-          const int vo = (16 * t + i) * VS + 32 * m + 4 * c;
+          const int vo = (16 * t + i) * VS + 32 * m + 4 * (c ^ (t & 3));
           const f16x8 vf = as_f16x8(*reinterpret_cast<const uint2*>(&vh[vo]), *reinterpret_cast<const uint2*>(&vh[vo + 16]));
           o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf, o[t], 0, 0, 0);
         }
@@ -960,7 +961,7 @@ __global__ __launch_bounds__(64 * G * pa_row_tiles(G), F16 && G >= 4 ? 4 : 1) vo
       const bf16x8 pa = as_bf16x8(p0h, p1h), pb = as_bf16x8(p0l, p1l);
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
-        const int vo = (16 * t + i) * VS + 32 * m + 4 * c;
+        const int vo = (16 * t + i) * VS + 32 * m + 4 * (c ^ (t & 3));
         const bf16x8 va = as_bf16x8(*reinterpret_cast<const uint2*>(&vh[vo]), *reinterpret_cast<const uint2*>(&vh[vo + 16]));
         const bf16x8 vb8 = as_bf16x8(*reinterpret_cast<const uint2*>(&vl[vo]), *reinterpret_cast<const uint2*>(&vl[vo + 16]));
         o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, va, o[t], 0, 0, 0);
