@@ -919,6 +919,19 @@ struct Enq {
 
   float* xf_of(int slot) const { return c->xf + (size_t)slot * s2k::pad_k(c->cfg.slow.hidden); }
 
+  // The input of the next Fast step (the codebook row of the previous step's pick), gathered by that
+  // step's first QKV GEMV: the pick's second pass runs there, behind the GEMV's first weight loads,
+  // instead of in a finisher launch of its own.  (The Slow step's input, a sum of ten rows, stays
+  // with its finisher: every GEMV block would gather all ten.)
+  struct PickIn {
+    bool on = false;
+    int j = 0, slot = 0;
+  } pick_in;
+  bool pick_fits() const {
+    const s2ar_config& g = c->cfg;
+    return c->bf16 && !c->q8 && s2k::gemv_pick_fits(g.fast.hidden, (g.codebook_size - 1) / s2k::argmax_block_rows() + 1);
+  }
+
   // pass 2 of a head's greedy pick over rows [lo, hi), then the step's bookkeeping
   void finish(int mode, int j, int slot, int lo, int hi, float* x) {
     const s2ar_config& g = c->cfg;
@@ -953,7 +966,30 @@ struct Enq {
     const int qkvd = (st.n_q_heads + 2 * st.n_kv_heads) * D;
     for (int l = 0; l < st.n_layers; ++l) {
       const LayerW& L = W[l];
-      gemv(s2k::GEMV_NORM_STORE, L.wqkv, L.sqkv, x, L.attn_norm, c->qkv, qkvd, H);
+      if (!is_slow && l == 0 && pick_in.on) {
+        const s2ar_config& g = c->cfg;
+        s2k::GemvArgs a{};
+        a.w = L.wqkv;
+        a.gain = L.attn_norm;
+        a.eps = (float)g.rms_eps;
+        a.y = c->qkv;
+        a.N = qkvd;
+        a.K = H;
+        a.pk_val = ws_am_val;
+        a.pk_idx = ws_am_idx;
+        a.pk_b0 = 0;  // the Fast head's rows [0, codebook_size)
+        a.pk_n = (g.codebook_size - 1) / s2k::argmax_block_rows() + 1;
+        a.pk_lo = 0;
+        a.pk_codebook = static_cast<const uint16_t*>(c->codebook);
+        a.pk_ncb = g.codebook_size;
+        a.pk_j = pick_in.j;
+        a.pk_codes = c->d_codes + (size_t)pick_in.slot * g.n_codebooks;
+        a.pk_x = x;
+        chk(s2k::launch_gemv_pick(a, s));
+        pick_in.on = false;
+      } else {
+        gemv(s2k::GEMV_NORM_STORE, L.wqkv, L.sqkv, x, L.attn_norm, c->qkv, qkvd, H);
+      }
       s2k::AttnArgs a{};
       a.qkv = c->qkv;
       a.q_norm = L.q_norm;
@@ -1046,7 +1082,13 @@ struct Enq {
       gemv(s2k::GEMV_NORM_ARGMAX, c->fast_head, c->fast_head_s, xf, c->fast_final, c->fast_logits, K, H,
            tp && tp->fast_z ? c->z : nullptr, 0, K);
       const int mode = tp ? s2k::FIN_CODE : (j < NC - 1 ? s2k::FIN_FAST_NEXT : s2k::FIN_FAST_LAST);
-      finish(mode, j, slot, 0, K, j < NC - 1 ? xf : c->x);
+      if (mode == s2k::FIN_FAST_NEXT && pick_fits()) {
+        pick_in.on = true;  // the next step's first QKV GEMV picks code j and gathers its input
+        pick_in.j = j;
+        pick_in.slot = slot;
+      } else {
+        finish(mode, j, slot, 0, K, j < NC - 1 ? xf : c->x);
+      }
       if (tp && tp->fast_z) d2h(tp->fast_z + (size_t)(j - 1) * H, c->z, sizeof(float) * H);
       if (tp && tp->fast_logits) d2h(tp->fast_logits + (size_t)(j - 1) * K, c->fast_logits, sizeof(float) * K);
       if (tp && tp->own) d2h(tp->own + j, codes + j, sizeof(int));

@@ -31,11 +31,29 @@ struct GemvArgs {
   int am_lo, am_hi;
   float* am_val;          // [n_blocks] per-block maxima (-inf for blocks outside the range)
   int* am_idx;            // [n_blocks] per-block arg maxima
+  // launch_gemv_pick only: the input is codebook row pk_codebook[pk_j][code] (bf16 bits,
+  // [codebooks][pk_ncb][K]), code being a head's greedy pick: the largest of the first-pass partials
+  // pk_val / pk_idx [pk_b0, pk_b0 + pk_n), lowest index on ties, minus pk_lo (0 if every partial is
+  // NaN).  Every block repeats that second pass; block 0 writes the row to pk_x [K] (the residual the
+  // layer adds into) and the code to pk_codes[pk_j].
+  const float* pk_val;
+  const int* pk_idx;
+  int pk_b0, pk_n, pk_lo;
+  const uint16_t* pk_codebook;
+  int pk_ncb, pk_j;
+  int* pk_codes;
+  float* pk_x;
 };
 
 // Number of workgroups a GEMV launch of this shape uses (sizes argmax partials).
 int gemv_blocks(int kind, int N);
 hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s);
+// GEMV_NORM_STORE of bf16 weights whose input is the codebook row of a head's greedy pick (the pk_
+// fields above): the pick's second pass and the row gather run in the GEMV's own prologue, behind
+// its first weight loads.  gemv_pick_fits says whether a launch of this shape is supported (K = 1024
+// or 2560, at most 512 partials); launch_gemv_pick returns hipErrorInvalidValue where it is not.
+bool gemv_pick_fits(int K, int n_partials);
+hipError_t launch_gemv_pick(const GemvArgs& a, hipStream_t s);
 
 struct AttnArgs {
   const float* qkv;        // [M][(Hq + 2 Hkv) D]: q heads, then k heads, then v heads

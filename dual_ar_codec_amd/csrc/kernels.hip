@@ -421,8 +421,11 @@ hipError_t launch_finish(bool bf16, const FinishArgs& f, hipStream_t s) {
 // Grid-stride weight-streaming GEMV.  A tile is WPB wavefronts x R rows; block b walks tiles
 // b, b + grid, ...  The next tile's weights are issued before the current tile is reduced
 // (register double buffer), and the input is staged in LDS once per block.  The greedy-pick
-// kind leaves one (max, argmax) per block, over all the rows the block visited.
-template <int WF, int NCH, int KIND, int R, int WPB>
+// kind leaves one (max, argmax) per block, over all the rows the block visited.  PICK: the input is
+// the codebook row of a head's greedy pick, whose second pass every block repeats after its first
+// weight loads are issued (the partials and gains load first, so only the row gather waits behind
+// the weights).
+template <int WF, int NCH, int KIND, int R, int WPB, bool PICK = false>
 __device__ __forceinline__ void gemv2_impl(const GemvArgs& a) {
   extern __shared__ float xs[];
   using F = WFmt<WF>;
@@ -443,14 +446,26 @@ __device__ __forceinline__ void gemv2_impl(const GemvArgs& a) {
   constexpr size_t row_bytes = (size_t)K * F::ESZ;
 
   f32x4 xv[XL], gv[XL];
+  constexpr int PKL = 2;  // pick partials per thread
+  float pv[PKL];
+  int pi[PKL];
+  if constexpr (PICK) {
+#pragma unroll
+    for (int u = 0; u < PKL; ++u) {
+      const int b = u * NT + threadIdx.x;
+      pv[u] = b < a.pk_n ? a.pk_val[a.pk_b0 + b] : -INFINITY;
+      pi[u] = b < a.pk_n ? a.pk_idx[a.pk_b0 + b] : INT_MAX;
+    }
+  }
 #pragma unroll
   for (int t = 0; t < XL; ++t) {
     const int k = (t * NT + threadIdx.x) * 4;
     if (XL * NT * 4 == K || k < K) {
-      xv[t] = *reinterpret_cast<const f32x4*>(a.x + k);
+      if constexpr (!PICK) xv[t] = *reinterpret_cast<const f32x4*>(a.x + k);
       if constexpr (NORM) gv[t] = *reinterpret_cast<const f32x4*>(a.gain + k);
     }
   }
+  if constexpr (PICK) __builtin_amdgcn_sched_barrier(0);  // the partials and gains ahead of the weights
   CT wa[R][NCH], wb[R][NCH];
   float sa[R], sb[R];  // int8: the rows' scales, loaded with their weights
   auto issue = [&](CT (&wv)[R][NCH], float (&sv)[R], int tl) {
@@ -465,6 +480,50 @@ __device__ __forceinline__ void gemv2_impl(const GemvArgs& a) {
   };
   issue(wa, sa, tile);
   __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (PICK) {
+    __shared__ float pk_red[WPB];
+    __shared__ int pk_bidx[WPB];
+    float v = -INFINITY;
+    int i = INT_MAX;
+    auto take = [&](float ov, int oi) {
+      if (ov > v || (ov == v && oi < i)) {
+        v = ov;
+        i = oi;
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < PKL; ++u) take(pv[u], pi[u]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(v, o, WAVE);
+      const int oi = __shfl_xor(i, o, WAVE);
+      take(ov, oi);
+    }
+    if (lane == 0) {
+      pk_red[wid] = v;
+      pk_bidx[wid] = i;
+    }
+    __syncthreads();
+    v = pk_red[0];
+    i = pk_bidx[0];
+#pragma unroll
+    for (int w = 1; w < WPB; ++w) take(pk_red[w], pk_bidx[w]);
+    const int code = i == INT_MAX ? 0 : i - a.pk_lo;
+    const uint16_t* row = a.pk_codebook + ((size_t)a.pk_j * a.pk_ncb + code) * K;
+    const bool keep_x = blockIdx.x == 0;
+#pragma unroll
+    for (int t = 0; t < XL; ++t) {
+      const int k = (t * NT + threadIdx.x) * 4;
+      if (XL * NT * 4 == K || k < K) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(row + k);
+        xv[t] = f32x4{bf_one((uint16_t)(raw.x & 0xffffu)), bf_one((uint16_t)(raw.x >> 16)),
+                      bf_one((uint16_t)(raw.y & 0xffffu)), bf_one((uint16_t)(raw.y >> 16))};
+        if (keep_x) *reinterpret_cast<f32x4*>(a.pk_x + k) = xv[t];
+      }
+    }
+    if (keep_x && threadIdx.x == 0) a.pk_codes[a.pk_j] = code;
+  }
 
   float ss = 0.f;
 #pragma unroll
@@ -586,6 +645,11 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2_q(const GemvArgs a) {
   gemv2_impl<WF, NCH, KIND, R, WPB>(a);
 }
 
+template <int NCH>
+__global__ __launch_bounds__(4 * WAVE) void k_gemv2_pick(const GemvArgs a) {
+  gemv2_impl<WF_BF16, NCH, GEMV_NORM_STORE, 1, 4, true>(a);
+}
+
 int pad_k(int K) { return (K + 1023) / 1024 * 1024; }
 
 int gemv_blocks(int kind, int N) {
@@ -668,6 +732,22 @@ static hipError_t gemv2_launch_q(const GemvArgs& a, int blocks_per_cu, hipStream
   const int tiles = (a.N + R * WPB - 1) / (R * WPB);
   const int grid = std::min(tiles, g_cus * blocks_per_cu);
   hipLaunchKernelGGL((k_gemv2_q<WF, NCH, KIND, R, WPB>), dim3(grid), dim3(WPB * WAVE), (size_t)pad_k(a.K) * 4, s, a);
+  return hipGetLastError();
+}
+
+bool gemv_pick_fits(int K, int n_partials) {
+  return (K == 2 * WAVE * 8 || K == 5 * WAVE * 8) && n_partials >= 1 && n_partials <= 2 * 4 * WAVE;
+}
+
+hipError_t launch_gemv_pick(const GemvArgs& a, hipStream_t s) {
+  if (!gemv_pick_fits(a.K, a.pk_n) || a.wscale || !a.pk_val || !a.pk_idx || !a.pk_codebook || !a.pk_codes ||
+      !a.pk_x || a.pk_j < 0 || a.pk_ncb < 1)
+    return hipErrorInvalidValue;
+  const int tiles = (a.N + 4 - 1) / 4;
+  const int grid = std::min(tiles, g_cus * 2);  // the launch shape of the plain QKV GEMV
+  const size_t lds = (size_t)pad_k(a.K) * 4;
+  if (a.K == 5 * WAVE * 8) hipLaunchKernelGGL(k_gemv2_pick<5>, dim3(grid), dim3(4 * WAVE), lds, s, a);
+  else hipLaunchKernelGGL(k_gemv2_pick<2>, dim3(grid), dim3(4 * WAVE), lds, s, a);
   return hipGetLastError();
 }
 

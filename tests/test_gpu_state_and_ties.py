@@ -256,6 +256,33 @@ def test_argmax_ties_go_to_the_lowest_index(kind, head_slice):
     ctx.close()
 
 
+@pytest.mark.parametrize("kind", ["wave", "block", "lane", "same_lane"])
+def test_graph_frames_break_ties_like_the_eager_path(kind):
+    """Free-running frames from the frame graph, where the first QKV GEMV of Fast steps 2..9 repeats
+    the second pass of the previous Fast head's pick and gathers its own input, on a model whose
+    heads hold exact copies of the winning rows: every code equals the eager path's (whose tie rule
+    the oracle pins above), and the copies do meet at a Fast step's maximum."""
+    cfg, w2, toks, _, _, _ = _tie_case(kind, 0)
+    ctx = _ctx(cfg, w2, max_streams=2)
+    ctx.prefill(0, toks)
+    ctx.prefill(1, toks)
+    n = 2
+    graph = ctx.decode_frames([0], n)[:, 0]
+    eager = [ctx.debug_frame(1) for _ in range(n)]
+    assert np.array_equal(graph, np.stack([e["own_codes"] for e in eager])), "graph and eager picks differ"
+    ties = 0
+    for e in eager:
+        for j in range(9):
+            lg = np.asarray(e["fast_logits"][j])
+            top = np.flatnonzero(lg == lg.max())
+            if len(top) > 1:
+                ties += 1
+                assert int(e["own_codes"][j + 1]) == int(top[0])
+    assert ties > 0, "no Fast step met a tie"
+    _say(f"[ties] graph frames, {kind}: {ties} tied Fast picks")
+    ctx.close()
+
+
 # ------------------------------------------------------------------ device-memory hook
 
 def _tensor_allocator(log, fail_at=None):
