@@ -929,7 +929,7 @@ struct Enq {
   } pick_in;
   bool pick_fits() const {
     const s2ar_config& g = c->cfg;
-    return c->bf16 && !c->q8 && s2k::gemv_pick_fits(g.fast.hidden, (g.codebook_size - 1) / s2k::argmax_block_rows() + 1);
+    return c->bf16 && s2k::gemv_pick_fits(g.fast.hidden, (g.codebook_size - 1) / s2k::argmax_block_rows() + 1);
   }
 
   // pass 2 of a head's greedy pick over rows [lo, hi), then the step's bookkeeping
@@ -970,6 +970,8 @@ struct Enq {
         const s2ar_config& g = c->cfg;
         s2k::GemvArgs a{};
         a.w = L.wqkv;
+        a.wscale = L.sqkv;
+        a.w_f8 = c->f8 ? 1 : 0;
         a.gain = L.attn_norm;
         a.eps = (float)g.rms_eps;
         a.y = c->qkv;

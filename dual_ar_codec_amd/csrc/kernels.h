@@ -48,8 +48,8 @@ struct GemvArgs {
 // Number of workgroups a GEMV launch of this shape uses (sizes argmax partials).
 int gemv_blocks(int kind, int N);
 hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s);
-// GEMV_NORM_STORE of bf16 weights whose input is the codebook row of a head's greedy pick (the pk_
-// fields above): the pick's second pass and the row gather run in the GEMV's own prologue, behind
+// GEMV_NORM_STORE (bf16 weights, or 8-bit codes with wscale / w_f8 as in launch_gemv) whose input is
+// the codebook row of a head's greedy pick (the pk_ fields above): the pick's second pass and the row gather run in the GEMV's own prologue, behind
 // its first weight loads.  gemv_pick_fits says whether a launch of this shape is supported (K = 1024
 // or 2560, at most 512 partials); launch_gemv_pick returns hipErrorInvalidValue where it is not.
 bool gemv_pick_fits(int K, int n_partials);

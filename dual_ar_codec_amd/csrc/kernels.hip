@@ -645,9 +645,9 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2_q(const GemvArgs a) {
   gemv2_impl<WF, NCH, KIND, R, WPB>(a);
 }
 
-template <int NCH>
+template <int WF, int NCH>
 __global__ __launch_bounds__(4 * WAVE) void k_gemv2_pick(const GemvArgs a) {
-  gemv2_impl<WF_BF16, NCH, GEMV_NORM_STORE, 1, 4, true>(a);
+  gemv2_impl<WF, NCH, GEMV_NORM_STORE, 1, 4, true>(a);
 }
 
 int pad_k(int K) { return (K + 1023) / 1024 * 1024; }
@@ -740,14 +740,20 @@ bool gemv_pick_fits(int K, int n_partials) {
 }
 
 hipError_t launch_gemv_pick(const GemvArgs& a, hipStream_t s) {
-  if (!gemv_pick_fits(a.K, a.pk_n) || a.wscale || !a.pk_val || !a.pk_idx || !a.pk_codebook || !a.pk_codes ||
-      !a.pk_x || a.pk_j < 0 || a.pk_ncb < 1)
+  if (!gemv_pick_fits(a.K, a.pk_n) || !a.pk_val || !a.pk_idx || !a.pk_codebook || !a.pk_codes || !a.pk_x ||
+      a.pk_j < 0 || a.pk_ncb < 1)
     return hipErrorInvalidValue;
   const int tiles = (a.N + 4 - 1) / 4;
   const int grid = std::min(tiles, g_cus * 2);  // the launch shape of the plain QKV GEMV
   const size_t lds = (size_t)pad_k(a.K) * 4;
-  if (a.K == 5 * WAVE * 8) hipLaunchKernelGGL(k_gemv2_pick<5>, dim3(grid), dim3(4 * WAVE), lds, s, a);
-  else hipLaunchKernelGGL(k_gemv2_pick<2>, dim3(grid), dim3(4 * WAVE), lds, s, a);
+  const bool k5 = a.K == 5 * WAVE * 8;  // else 2 chunks (K 1024); bf16 and 8-bit codes take 8 per lane
+#define S2_PK(WF)                                                                                         \
+  if (k5) hipLaunchKernelGGL((k_gemv2_pick<WF, 5>), dim3(grid), dim3(4 * WAVE), lds, s, a);              \
+  else hipLaunchKernelGGL((k_gemv2_pick<WF, 2>), dim3(grid), dim3(4 * WAVE), lds, s, a);
+  if (!a.wscale) { S2_PK(WF_BF16) }
+  else if (a.w_f8) { S2_PK(WF_F8) }
+  else { S2_PK(WF_I8) }
+#undef S2_PK
   return hipGetLastError();
 }
 

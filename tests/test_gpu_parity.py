@@ -544,6 +544,26 @@ def test_int8_weights_batched_full_shape():
     ctx.close()
 
 
+@pytest.mark.parametrize("name,fmt", [("mid", "i8"), ("mid", "f8"), ("full", "i8")])
+def test_8bit_weights_graph_frames_equal_the_eager_path(name, fmt):
+    """Graph-replayed frames with 8-bit weights, whose Fast steps 2..9 finish the previous Fast pick
+    inside their first QKV GEMV, give the eager path's codes (which the teacher-forced tests hold to
+    the oracle) bit for bit."""
+    cfg = synth.config(name)
+    w = synth.make_weights(cfg)
+    toks, _, _ = synth.make_prompt(cfg)
+    ctx = _ctx(dict(cfg, weight_dtype=fmt), w, max_streams=2)
+    del w
+    gc.collect()
+    ctx.prefill(0, toks)
+    ctx.prefill(1, toks)
+    n = 4
+    graph = ctx.decode_frames([0], n)[:, 0]
+    eager = np.stack([ctx.debug_frame(1)["own_codes"] for _ in range(n)])
+    assert np.array_equal(graph, eager), "graph replay and the eager path disagree"
+    ctx.close()
+
+
 def test_int8_weights_mid_teacher_forced():
     """Int8 layer matrices and heads with per-row scales (quantised by the library at create) against
     the oracle fed the same quantisation (its own quantiser, dequantised): the bf16 acceptance bar."""
