@@ -451,7 +451,7 @@ def main():
     k_gbps = nbytes / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
-                "kernel": "k_gemv2<bf16, NCH=5, GEMV_NORM_SWIGLU, R=2, WPB=4> (Slow gate/up, 19456x2560)",
+                "kernel": "k_gemv2<bf16, NCH=5, GEMV_NORM_SWIGLU, R=2, WPB=8> (Slow gate/up, 19456x2560)",
                 "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2)}
     # context: a plain streaming read of the same weights, the rate no arithmetic slows down
     ctx.time_kernel(1, 4)  # first launches load the kernel's code object: not timed

@@ -176,14 +176,22 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
   // 1. loads: the input vector (and gain) first, then every weight chunk of this wavefront's
   //    rows.  vmcnt retires in issue order, so staging the input only waits for the input.
   constexpr int XL = NCH > 0 ? (NCH * WAVE * EPC + NT * 4 - 1) / (NT * 4) : 1;
+  // x and gain are zero-padded to KP floats (a multiple of 1024), and so is the LDS copy: a block
+  // whose threads do not divide KP (5 wavefronts) stops at KP
+  constexpr int KP = (NCH * WAVE * EPC + 1023) / 1024 * 1024;
+  constexpr bool XFULL = XL * NT * 4 <= KP;
   f32x4 xv[XL], gv[XL];
   CT wv[R][NCH > 0 ? NCH : 1];
   if constexpr (NCH > 0) {
 #pragma unroll
-    for (int t = 0; t < XL; ++t) {  // x and gain are zero-padded to a multiple of 1024 floats
+    for (int t = 0; t < XL; ++t) {
       const int k = (t * NT + threadIdx.x) * 4;
-      xv[t] = *reinterpret_cast<const f32x4*>(a.x + k);
-      if constexpr (NORM) gv[t] = *reinterpret_cast<const f32x4*>(a.gain + k);
+      xv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (XFULL || k < KP) {
+        xv[t] = *reinterpret_cast<const f32x4*>(a.x + k);
+        if constexpr (NORM) gv[t] = *reinterpret_cast<const f32x4*>(a.gain + k);
+      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -202,7 +210,7 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
     for (int t = 0; t < XL; ++t) {
       const int k = (t * NT + threadIdx.x) * 4;
       const f32x4 v = xv[t];
-      *reinterpret_cast<f32x4*>(xs + k) = v;
+      if (XFULL || k < KP) *reinterpret_cast<f32x4*>(xs + k) = v;
       ss = fmaf(v.x, v.x, ss);
       ss = fmaf(v.y, v.y, ss);
       ss = fmaf(v.z, v.z, ss);
@@ -238,7 +246,10 @@ __device__ __forceinline__ void gemv_impl(const GemvArgs& a) {
     };
     if constexpr (NCH > 0) {
 #pragma unroll
-      for (int t = 0; t < XL; ++t) norm4((t * NT + threadIdx.x) * 4, gv[t]);
+      for (int t = 0; t < XL; ++t) {
+        const int k = (t * NT + threadIdx.x) * 4;
+        if (XFULL || k < KP) norm4(k, gv[t]);
+      }
     } else {
       for (int k = threadIdx.x * 4; k < K; k += NT * 4) norm4(k, *reinterpret_cast<const f32x4*>(a.gain + k));
     }
@@ -446,7 +457,7 @@ __device__ __forceinline__ void gemv2_impl(const GemvArgs& a) {
   constexpr size_t row_bytes = (size_t)K * F::ESZ;
 
   f32x4 xv[XL], gv[XL];
-  constexpr int PKL = 2;  // pick partials per thread
+  constexpr int PKL = (2 * 4 * WAVE + NT - 1) / NT;  // pick partials per thread (at most 512 in all)
   float pv[PKL];
   int pi[PKL];
   if constexpr (PICK) {
@@ -646,8 +657,8 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv2_q(const GemvArgs a) {
 }
 
 template <int WF, int NCH>
-__global__ __launch_bounds__(4 * WAVE) void k_gemv2_pick(const GemvArgs a) {
-  gemv2_impl<WF, NCH, GEMV_NORM_STORE, 1, 4, true>(a);
+__global__ __launch_bounds__(8 * WAVE) void k_gemv2_pick(const GemvArgs a) {
+  gemv2_impl<WF, NCH, GEMV_NORM_STORE, 1, 8, true>(a);
 }
 
 int pad_k(int K) { return (K + 1023) / 1024 * 1024; }
@@ -743,13 +754,13 @@ hipError_t launch_gemv_pick(const GemvArgs& a, hipStream_t s) {
   if (!gemv_pick_fits(a.K, a.pk_n) || !a.pk_val || !a.pk_idx || !a.pk_codebook || !a.pk_codes || !a.pk_x ||
       a.pk_j < 0 || a.pk_ncb < 1)
     return hipErrorInvalidValue;
-  const int tiles = (a.N + 4 - 1) / 4;
-  const int grid = std::min(tiles, g_cus * 2);  // the launch shape of the plain QKV GEMV
+  const int tiles = (a.N + 8 - 1) / 8;
+  const int grid = std::min(tiles, g_cus);  // the launch shape of the plain QKV GEMV
   const size_t lds = (size_t)pad_k(a.K) * 4;
   const bool k5 = a.K == 5 * WAVE * 8;  // else 2 chunks (K 1024); bf16 and 8-bit codes take 8 per lane
 #define S2_PK(WF)                                                                                         \
-  if (k5) hipLaunchKernelGGL((k_gemv2_pick<WF, 5>), dim3(grid), dim3(4 * WAVE), lds, s, a);              \
-  else hipLaunchKernelGGL((k_gemv2_pick<WF, 2>), dim3(grid), dim3(4 * WAVE), lds, s, a);
+  if (k5) hipLaunchKernelGGL((k_gemv2_pick<WF, 5>), dim3(grid), dim3(8 * WAVE), lds, s, a);              \
+  else hipLaunchKernelGGL((k_gemv2_pick<WF, 2>), dim3(grid), dim3(8 * WAVE), lds, s, a);
   if (!a.wscale) { S2_PK(WF_BF16) }
   else if (a.w_f8) { S2_PK(WF_F8) }
   else { S2_PK(WF_I8) }
@@ -761,8 +772,8 @@ hipError_t launch_gemv_pick(const GemvArgs& a, hipStream_t s) {
 template <int WF>
 static hipError_t launch_gemv_q(int kind, const GemvArgs& a, hipStream_t s) {
   const int nch = a.K % (WAVE * 8) == 0 ? a.K / (WAVE * 8) : -1;
-  if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch_q<WF, 5, GEMV_NORM_STORE, 1, 4>(a, 2, s);
-  if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch_q<WF, 5, GEMV_NORM_SWIGLU, 2, 4>(a, 2, s);
+  if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch_q<WF, 5, GEMV_NORM_STORE, 1, 8>(a, 1, s);
+  if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch_q<WF, 5, GEMV_NORM_SWIGLU, 2, 8>(a, 1, s);
   switch (kind) {
     case GEMV_NORM_STORE: return gemv_dispatch_q<WF, GEMV_NORM_STORE>(a, s);
     case GEMV_RESID: return gemv_dispatch_q<WF, GEMV_RESID>(a, s);
@@ -779,16 +790,19 @@ hipError_t launch_gemv(int kind, bool bf16, const GemvArgs& a, hipStream_t s) {
   }
   if (bf16 && a.K % (WAVE * 8) == 0) {
     const int nch = a.K / (WAVE * 8);
-    if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch<5, GEMV_NORM_STORE, 1, 4>(a, 2, s);
-    if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch<5, GEMV_NORM_SWIGLU, 2, 4>(a, 2, s);
-    // residual projections of 2560 rows (O, down at the S2 shape): blocks of 5 wavefronts, one row
-    // each, so the 512 blocks sit exactly two per CU (4-wavefront blocks leave 2.5 per CU, and the
-    // CUs holding three set the launch's length: 267.3 -> 271.9 frames/s at the S2 shape)
-    if (kind == GEMV_RESID && a.N % (5 * g_cus) == 0 && (nch == 8 || nch == 19)) {
-      const dim3 grid(a.N / 5), block(5 * WAVE);
+    // QKV and gate/up: one block of 8 wavefronts per CU, which stages the input once per CU (two
+    // blocks of 4 per CU: 273.7 against 274.8 frames/s at the S2 shape)
+    if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch<5, GEMV_NORM_STORE, 1, 8>(a, 1, s);
+    if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch<5, GEMV_NORM_SWIGLU, 2, 8>(a, 1, s);
+    // residual projections of 2560 rows (O, down at the S2 shape): blocks of 10 wavefronts, one row
+    // each, so the 256 blocks sit exactly one per CU (4-wavefront blocks leave 2.5 per CU, and the
+    // CUs holding three set the launch's length: 267.3 -> 271.9 frames/s with 5-wavefront blocks;
+    // 10 wavefronts halve the input staged per CU again: 272.7 -> 274.1)
+    if (kind == GEMV_RESID && a.N % (10 * g_cus) == 0 && (nch == 8 || nch == 19)) {
+      const dim3 grid(a.N / 10), block(10 * WAVE);
       const size_t lds = (size_t)pad_k(a.K) * sizeof(float);
-      if (nch == 8) hipLaunchKernelGGL((k_gemv<true, 8, GEMV_RESID, 5>), grid, block, lds, s, a);
-      else hipLaunchKernelGGL((k_gemv<true, 19, GEMV_RESID, 5>), grid, block, lds, s, a);
+      if (nch == 8) hipLaunchKernelGGL((k_gemv<true, 8, GEMV_RESID, 10>), grid, block, lds, s, a);
+      else hipLaunchKernelGGL((k_gemv<true, 19, GEMV_RESID, 10>), grid, block, lds, s, a);
       return hipGetLastError();
     }
   }
