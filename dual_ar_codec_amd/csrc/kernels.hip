@@ -339,9 +339,9 @@ __global__ __launch_bounds__(WPB * WAVE) void k_gemv(const GemvArgs a) {
   gemv_impl<BF16 ? WF_BF16 : WF_F32, NCH, KIND, WPB>(a);
 }
 
-template <int WF, int NCH, int KIND>
-__global__ __launch_bounds__(GEMV_THREADS) void k_gemv_q(const GemvArgs a) {
-  gemv_impl<WF, NCH, KIND>(a);
+template <int WF, int NCH, int KIND, int WPB = GEMV_WAVES>
+__global__ __launch_bounds__(WPB * WAVE) void k_gemv_q(const GemvArgs a) {
+  gemv_impl<WF, NCH, KIND, WPB>(a);
 }
 
 int argmax_block_rows() { return GEMV_WAVES * rows_per_wave(GEMV_NORM_ARGMAX); }
@@ -774,6 +774,14 @@ static hipError_t launch_gemv_q(int kind, const GemvArgs& a, hipStream_t s) {
   const int nch = a.K % (WAVE * 8) == 0 ? a.K / (WAVE * 8) : -1;
   if (kind == GEMV_NORM_STORE && nch == 5) return gemv2_launch_q<WF, 5, GEMV_NORM_STORE, 1, 8>(a, 1, s);
   if (kind == GEMV_NORM_SWIGLU && nch == 5) return gemv2_launch_q<WF, 5, GEMV_NORM_SWIGLU, 2, 8>(a, 1, s);
+  // O and down: one block of 10 wavefronts per CU, as for bf16 weights
+  if (kind == GEMV_RESID && a.N % (10 * g_cus) == 0 && (nch == 8 || nch == 19)) {
+    const dim3 grid(a.N / 10), block(10 * WAVE);
+    const size_t lds = (size_t)pad_k(a.K) * sizeof(float);
+    if (nch == 8) hipLaunchKernelGGL((k_gemv_q<WF, 8, GEMV_RESID, 10>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_gemv_q<WF, 19, GEMV_RESID, 10>), grid, block, lds, s, a);
+    return hipGetLastError();
+  }
   switch (kind) {
     case GEMV_NORM_STORE: return gemv_dispatch_q<WF, GEMV_NORM_STORE>(a, s);
     case GEMV_RESID: return gemv_dispatch_q<WF, GEMV_RESID>(a, s);
