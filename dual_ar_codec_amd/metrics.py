@@ -64,6 +64,9 @@ def kv_bytes_per_position(cfg) -> int:
     return s["n_layers"] * s["n_kv_heads"] * s["head_dim"] * (k_esz + v_esz)
 
 
+GAIN_BYTES = 4  # norm gains are held in fp32 on the device, whatever the weights' dtype
+
+
 def frame_bytes(cfg, context_len: int) -> dict:
     """Algorithmic HBM bytes of one batch-1 frame at a Slow context of context_len.
 
@@ -74,8 +77,8 @@ def frame_bytes(cfg, context_len: int) -> dict:
     esz = _esz(cfg)
     s, f = cfg["slow"], cfg["fast"]
     w = params_per_frame(cfg) * esz
-    w += (s["n_layers"] * layer_gain_params(s) + s["hidden"]) * esz
-    w += N_FAST_STEPS * (f["n_layers"] * layer_gain_params(f) + f["hidden"]) * esz
+    w += (s["n_layers"] * layer_gain_params(s) + s["hidden"]) * GAIN_BYTES
+    w += N_FAST_STEPS * (f["n_layers"] * layer_gain_params(f) + f["hidden"]) * GAIN_BYTES
     kv = kv_bytes_per_position(cfg) * (context_len + 1)
     embed = (N_CODEBOOKS + N_FAST_STEPS - 1) * s["hidden"] * esz
     return dict(weights=w, kv=kv, embed=embed, total=w + kv + embed)
@@ -102,4 +105,4 @@ def gate_up_launch_bytes(cfg, stack: str = "slow") -> int:
     both weight matrices, the gain, the fp32 input and the fp32 output."""
     s = cfg[stack]
     esz = _esz(cfg)
-    return 2 * s["ffn"] * s["hidden"] * esz + s["hidden"] * esz + s["hidden"] * 4 + s["ffn"] * 4
+    return 2 * s["ffn"] * s["hidden"] * esz + s["hidden"] * GAIN_BYTES + s["hidden"] * 4 + s["ffn"] * 4
