@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -131,6 +132,17 @@ def test_product_path_never_imports_the_oracle():
         for f in files:
             if f.endswith((".py", ".hip", ".h", ".c", ".cpp")):
                 assert not pat.search(open(os.path.join(dirpath, f)).read()), f
+
+
+def test_a_missing_library_is_an_error_not_a_fallback(tmp_path):
+    """With no built libs2ar.so the binding raises on first use; nothing runs in its place."""
+    code = ("from dual_ar_codec_amd import s2ar\n"
+            "try:\n    s2ar.lib()\nexcept RuntimeError as e:\n    print('raised:', e)\n")
+    env = dict(os.environ, S2AR_LIB=str(tmp_path / "libs2ar.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "not built" in r.stdout
 
 
 def test_allocator_callbacks_must_come_in_pairs(L):
